@@ -1,0 +1,186 @@
+"""CPU oracle for NVFP4 quantization and the block-scaled FP4 GEMM.
+
+TEST INFRASTRUCTURE ONLY: tests/, __graft_entry__.smoke() and bench.py's
+cpu_baseline leg may import this package; the product path never does.  The
+arithmetic lives in nvfp4_oracle.c (plain C, gcc); this module only marshals
+numpy arrays through ctypes.  See nvfp4_oracle.c for the passages each step
+follows and the readings taken where the pages are silent.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+PRO_NONE, PRO_SMOOTH, PRO_SILU = 0, 1, 2
+STATIC, DYNAMIC = 0, 1
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB) or (
+            os.path.getmtime(_build.LIB) < os.path.getmtime(_build.SRC)
+        ):
+            _build.build()
+        L = ctypes.CDLL(_build.LIB)
+        u8p = ctypes.POINTER(ctypes.c_uint8)
+        L.nvo_bf16_to_f32.restype = ctypes.c_float
+        L.nvo_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        L.nvo_f32_to_bf16.restype = ctypes.c_uint16
+        L.nvo_f32_to_bf16.argtypes = [ctypes.c_float]
+        L.nvo_e2m1_value.restype = ctypes.c_double
+        L.nvo_e2m1_value.argtypes = [ctypes.c_uint8]
+        L.nvo_e2m1_encode.restype = ctypes.c_uint8
+        L.nvo_e2m1_encode.argtypes = [ctypes.c_float]
+        L.nvo_ue4m3_value.restype = ctypes.c_double
+        L.nvo_ue4m3_value.argtypes = [ctypes.c_uint8]
+        L.nvo_ue4m3_encode.restype = ctypes.c_uint8
+        L.nvo_ue4m3_encode.argtypes = [ctypes.c_float]
+        L.nvo_silu.restype = ctypes.c_float
+        L.nvo_silu.argtypes = [ctypes.c_float]
+        L.nvo_global_scale.restype = ctypes.c_float
+        L.nvo_global_scale.argtypes = [ctypes.c_float]
+        L.nvo_sf_size.restype = ctypes.c_int64
+        L.nvo_sf_size.argtypes = [ctypes.c_int64, ctypes.c_int64]
+        L.nvo_sf_offset.restype = ctypes.c_int64
+        L.nvo_sf_offset.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
+        L.nvo_quantize.restype = ctypes.c_int
+        L.nvo_quantize.argtypes = [
+            ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+            u8p, u8p,
+        ]
+        L.nvo_gemm_rows.restype = ctypes.c_int
+        L.nvo_gemm_rows.argtypes = [
+            u8p, u8p, u8p, u8p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+        ]
+        L.nvo_num_threads.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _u8(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
+
+
+def _vp(a):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+# ---- scalar codecs (vectorised by plain loops; small inputs only) ----------
+
+def bf16_to_f32(h):
+    return (np.asarray(h, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def f32_to_bf16(f):
+    L = lib()
+    f = np.asarray(f, dtype=np.float32).ravel()
+    return np.array([L.nvo_f32_to_bf16(float(v)) for v in f], dtype=np.uint16)
+
+
+def e2m1_value(code):
+    return lib().nvo_e2m1_value(int(code))
+
+
+def e2m1_encode(v):
+    return lib().nvo_e2m1_encode(float(np.float32(v)))
+
+
+def ue4m3_value(code):
+    return lib().nvo_ue4m3_value(int(code))
+
+
+def ue4m3_encode(v):
+    return lib().nvo_ue4m3_encode(float(np.float32(v)))
+
+
+def silu(g):
+    return np.float32(lib().nvo_silu(float(np.float32(g))))
+
+
+def global_scale(amax):
+    return np.float32(lib().nvo_global_scale(float(np.float32(amax))))
+
+
+def sf_size(rows, k):
+    return lib().nvo_sf_size(rows, k)
+
+
+def sf_offset(r, c, k):
+    return lib().nvo_sf_offset(r, c, k)
+
+
+def num_threads():
+    return lib().nvo_num_threads()
+
+
+# ---- tensors ----------------------------------------------------------------
+
+def quantize(x, *, prologue=PRO_NONE, pqs=None, mask=None, gs=None, gs_mode=DYNAMIC,
+             out_fp4=None):
+    """Quantize x: numpy uint16 (bf16 bits) or float32 of shape [m, k] or
+    [b, m, k].  Returns (fp4 [b?, m, K/2] uint8, sf [b?, sf_size] uint8,
+    gs [b] float32).  out_fp4 may be given pre-filled (rows >= mask stay)."""
+    x = np.ascontiguousarray(x)
+    squeeze = x.ndim == 2
+    x3 = x[None] if squeeze else x
+    b, m, k_in = x3.shape
+    if x3.dtype == np.uint16:
+        x_dtype = 0
+    elif x3.dtype == np.float32:
+        x_dtype = 1
+    else:
+        raise TypeError("x must be bf16 bits (uint16) or float32")
+    K = k_in // 2 if prologue == PRO_SILU else k_in
+    if gs is None:
+        gs = np.zeros(b, dtype=np.float32)
+    gs = np.ascontiguousarray(np.asarray(gs, dtype=np.float32).reshape(b)).copy()
+    if out_fp4 is None:
+        out_fp4 = np.zeros((b, m, K // 2), dtype=np.uint8)
+    else:
+        out_fp4 = np.ascontiguousarray(out_fp4.reshape(b, m, K // 2)).copy()
+    sfsz = sf_size(m, K)
+    out_sf = np.zeros((b, sfsz), dtype=np.uint8)
+    if pqs is not None:
+        pqs = np.ascontiguousarray(pqs, dtype=np.uint16)
+    if mask is not None:
+        mask = np.ascontiguousarray(mask, dtype=np.int32)
+    rc = lib().nvo_quantize(_vp(x3), x_dtype, b, m, k_in, prologue, _vp(pqs), _vp(mask),
+                            _vp(gs), gs_mode, _u8(out_fp4), _u8(out_sf))
+    if rc != 0:
+        raise ValueError(f"oracle quantize rejected the arguments (status {rc})")
+    if squeeze:
+        return out_fp4[0], out_sf[0], gs
+    return out_fp4, out_sf, gs
+
+
+def gemm_rows(a, b, a_sf, b_sf, alpha, m, n, k, rows=None, bias=None, d=None, l1=None):
+    """fp64 alpha*(Adq @ Bdq^T + d @ l1^T) + bias for the given A rows."""
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    a_sf = np.ascontiguousarray(a_sf, dtype=np.uint8)
+    b_sf = np.ascontiguousarray(b_sf, dtype=np.uint8)
+    if rows is None:
+        rows = np.arange(m, dtype=np.int64)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    r = 0
+    if d is not None:
+        d = np.ascontiguousarray(d, dtype=np.uint16)
+        l1 = np.ascontiguousarray(l1, dtype=np.uint16)
+        r = d.shape[-1]
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.uint16)
+    out = np.zeros((len(rows), n), dtype=np.float64)
+    rc = lib().nvo_gemm_rows(_u8(a), _u8(b), _u8(a_sf), _u8(b_sf), float(np.float32(alpha)),
+                             _vp(bias), _vp(d), _vp(l1), r, m, n, k, _vp(rows), len(rows),
+                             _vp(out))
+    if rc != 0:
+        raise ValueError(f"oracle gemm rejected the arguments (status {rc})")
+    return out

@@ -1,0 +1,137 @@
+"""Pins for the oracle's block-scaled GEMM (CPU only).
+
+The eager meaning of an NVFP4 matmul on the nvFuser page is "dequantize, then
+a plain linear".  The checks:
+  * exact rational arithmetic on tiny shapes (Fractions, with the codes decoded
+    from the format definitions written out here);
+  * torch float64 matmul of matrices dequantized independently (torch's
+    float8_e4m3fn decode for scales, format-definition decode for e2m1);
+  * the SVDQuant special cases on the flashinfer mm_nvfp4_svdquant page:
+    d = l1 = 0 gives the plain GEMM; an all-zero residual gives
+    alpha*(d@l1^T) + bias.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from nvfp4_block_scaled_04_amd import synth
+
+
+def e2m1_frac(code):
+    code = int(code)
+    s = -1 if code & 8 else 1
+    e = (code >> 1) & 3
+    m = code & 1
+    if e == 0:
+        return s * Fraction(m, 2)
+    return s * (1 + Fraction(m, 2)) * Fraction(2) ** (e - 1)
+
+
+def e4m3_frac(code):
+    code = int(code)
+    e = (code >> 3) & 15
+    m = code & 7
+    if e == 0:
+        return Fraction(m, 2 ** 9)
+    return (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+
+
+def swz(r, c, k):
+    cp = -(-(k // 16) // 4) * 4
+    return ((r // 128) * (cp // 4) + c // 4) * 512 + (r % 32) * 16 + ((r % 128) // 32) * 4 + c % 4
+
+
+def dequant_torch(q, sf, rows, k):
+    """Independent dequantization: nibble table from the e2m1 definition,
+    scales through torch's float8_e4m3fn decode."""
+    lut = torch.tensor([float(e2m1_frac(c)) for c in range(16)], dtype=torch.float64)
+    qt = torch.from_numpy(q.astype(np.int64))
+    codes = torch.stack([qt & 15, qt >> 4], dim=-1).reshape(rows, k)
+    vals = lut[codes]
+    sdec = torch.from_numpy(sf.copy()).view(torch.float8_e4m3fn).to(torch.float64)
+    idx = torch.tensor([[swz(r, c, k) for c in range(k // 16)] for r in range(rows)])
+    scales = sdec[idx].repeat_interleave(16, dim=1)
+    return vals * scales
+
+
+def rand_quant(rng, rows, k, scale=1.0):
+    x = (rng.standard_normal((rows, k)) * scale).astype(np.float32)
+    q, sf, gs = O.quantize(x)
+    return q, sf, gs[0]
+
+
+def test_tiny_gemm_exact_rational():
+    rng = np.random.default_rng(11)
+    m, n, k = 3, 4, 48
+    a, asf, ga = rand_quant(rng, m, k, 3.0)
+    b, bsf, gb = rand_quant(rng, n, k, 0.5)
+    alpha = np.float32(1.0) / (ga * gb)
+    out = O.gemm_rows(a, b, asf, bsf, alpha, m, n, k)
+    for i in range(m):
+        for j in range(n):
+            acc = Fraction(0)
+            for kk in range(k):
+                ca = (a[i, kk // 2] >> (4 * (kk & 1))) & 15
+                cb = (b[j, kk // 2] >> (4 * (kk & 1))) & 15
+                acc += (e2m1_frac(ca) * e4m3_frac(asf[swz(i, kk // 16, k)])
+                        * e2m1_frac(cb) * e4m3_frac(bsf[swz(j, kk // 16, k)]))
+            ref = Fraction(float(alpha)) * acc
+            # every product is exact in fp64; only the k-term summation rounds
+            assert abs(Fraction(out[i, j]) - ref) <= Fraction(k) * Fraction(2) ** -52 * (abs(ref) + 1)
+
+
+@pytest.mark.parametrize("m,n,k", [(128, 256, 256), (37, 19, 80), (1, 5, 16)])
+def test_gemm_matches_torch_float64(m, n, k):
+    rng = np.random.default_rng(m + n + k)
+    a, asf, ga = rand_quant(rng, m, k, 2.0)
+    b, bsf, gb = rand_quant(rng, n, k, 0.02)
+    alpha = np.float32(1.0) / (ga * gb)
+    out = O.gemm_rows(a, b, asf, bsf, alpha, m, n, k)
+    ref = float(alpha) * (dequant_torch(a, asf, m, k) @ dequant_torch(b, bsf, n, k).T)
+    np.testing.assert_allclose(out, ref.numpy(), rtol=1e-12, atol=1e-12 * float(np.abs(ref).max()))
+
+
+def test_gemm_row_subset_and_bias():
+    rng = np.random.default_rng(12)
+    m, n, k = 20, 33, 64
+    a, asf, ga = rand_quant(rng, m, k)
+    b, bsf, gb = rand_quant(rng, n, k)
+    bias = torch.randn(n).to(torch.bfloat16)
+    bias_bits = synth.bits(bias)
+    full = O.gemm_rows(a, b, asf, bsf, 0.5, m, n, k, bias=bias_bits)
+    rows = np.array([19, 0, 7])
+    sub = O.gemm_rows(a, b, asf, bsf, 0.5, m, n, k, rows=rows, bias=bias_bits)
+    assert np.array_equal(sub, full[rows])
+    nob = O.gemm_rows(a, b, asf, bsf, 0.5, m, n, k)
+    np.testing.assert_allclose(full - nob, np.broadcast_to(bias.double().numpy(), (m, n)), rtol=0, atol=1e-12)
+
+
+def test_svdquant_zero_lora_reduces_to_plain():
+    rng = np.random.default_rng(13)
+    m, n, k, r = 16, 24, 64, 32
+    a, asf, ga = rand_quant(rng, m, k)
+    b, bsf, gb = rand_quant(rng, n, k)
+    d = np.zeros((m, r), dtype=np.uint16)
+    l1 = np.zeros((n, r), dtype=np.uint16)
+    x = O.gemm_rows(a, b, asf, bsf, 0.25, m, n, k, d=d, l1=l1)
+    y = O.gemm_rows(a, b, asf, bsf, 0.25, m, n, k)
+    assert np.array_equal(x, y)
+
+
+def test_svdquant_zero_residual_is_lora_plus_bias():
+    rng = np.random.default_rng(14)
+    m, n, k, r = 16, 24, 64, 32
+    a, asf, _ = rand_quant(rng, m, k)
+    b = np.zeros((n, k // 2), dtype=np.uint8)
+    bsf = np.zeros(O.sf_size(n, k), dtype=np.uint8)
+    alpha = np.float32(0.125)
+    d = torch.randn(m, r).to(torch.bfloat16)
+    l1 = torch.randn(n, r).to(torch.bfloat16)
+    bias = torch.randn(n).to(torch.bfloat16)
+    out = O.gemm_rows(a, b, asf, bsf, alpha, m, n, k, bias=synth.bits(bias),
+                      d=synth.bits(d), l1=synth.bits(l1))
+    ref = float(alpha) * (d.double() @ l1.double().T) + bias.double()
+    np.testing.assert_allclose(out, ref.numpy(), rtol=1e-13, atol=1e-13)
