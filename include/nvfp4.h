@@ -1,0 +1,183 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 quantization and block-scaled
+ * FP4 GEMM library (libnvfp4_amd.so).
+ *
+ * Formats (shared by every entry point):
+ *   - e2m1 ("FP4"): 4-bit code, bit 3 = sign, magnitudes {0, 0.5, 1, 1.5, 2,
+ *     3, 4, 6}.  Packed two per byte, element 2i in the low nibble of byte i.
+ *     A matrix of `rows` x `k` elements is `rows` x `k/2` bytes, row-major
+ *     (TensorRT-LLM NVFP4LinearMethod.create_weights: weight [out, in/2] of
+ *     float4_e2m1x2; flashinfer mm_nvfp4_svdquant: a, b are (rows, k/2)
+ *     uint8, row-major).
+ *   - ue4m3 block scale: one byte per 16 consecutive elements of a row (the
+ *     e4m3 layout with the sign bit 0; max 448), stored in the "128x4
+ *     swizzled" padded layout (flashinfer mm_nvfp4_svdquant, parameter
+ *     a_sf; TensorRT-LLM create_weights, weight_scale "Padding is
+ *     required"): a buffer of pad_up(rows,128) * pad_up(k/16,4) bytes in
+ *     which scale (r, c) sits at byte
+ *        ((r/128)*(Cp/4) + c/4)*512 + (r%32)*16 + ((r%128)/32)*4 + c%4,
+ *     Cp = pad_up(k/16,4).  Every padding byte is written as 0.
+ *   - global scale gs: fp32, gs = 448*6 / max(amax, 1e-12) where amax is the
+ *     largest |x| after NaN -> 0 and +-inf -> +-FLT_MAX (FastVideo PR #1350
+ *     review thread, _global_sf; TensorRT-LLM input_scale comment).
+ *   - block scale s = ue4m3((block_amax / 6) * gs), round-to-nearest-even,
+ *     saturating at 448; element code = e2m1(x * (gs / dec(s))),
+ *     round-to-nearest-even, saturating at 6 (0 when dec(s) = 0); all fp32.
+ *   - alpha = 1 / (gs_a * gs_b) (TensorRT-LLM alpha comment: amax_in *
+ *     amax_w / (448*6)^2).
+ *
+ * Conventions:
+ *   - Every tensor pointer is a device pointer on the current HIP device and
+ *     must be 16-byte aligned.  Outputs are caller-allocated; the library
+ *     allocates and frees no memory and keeps no state between calls.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default
+ *     stream.  Calls only enqueue work and return (no host synchronisation).
+ *   - Every argument is validated before anything is enqueued; on a non-zero
+ *     status nothing has been written.  NVFP4_LAUNCH_FAILED reports an error
+ *     from the HIP launch itself; device faults surface at the caller's next
+ *     synchronisation, as for any HIP call.
+ *   - Calls that overlap on the same buffers race like any kernels.
+ *   - In DYNAMIC mode the call uses global_scale[] as accumulator and the
+ *     first bytes of out_sf as a counter while it runs; both hold their final
+ *     values when the call's work completes.
+ */
+#ifndef NVFP4_AMD_H
+#define NVFP4_AMD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum nvfp4_status {
+    NVFP4_OK = 0,
+    NVFP4_NULL_POINTER = 1,   /* a required pointer is NULL */
+    NVFP4_BAD_SHAPE = 2,      /* a size is out of range or k % 16 != 0 */
+    NVFP4_MISALIGNED = 3,     /* a pointer is not 16-byte aligned */
+    NVFP4_BAD_RANK = 4,       /* svdquant rank r is not a positive multiple of 32 */
+    NVFP4_BAD_DTYPE = 5,      /* unknown x_dtype */
+    NVFP4_UNSUPPORTED = 6,    /* unknown gs_mode, or a size beyond the kernels' limits */
+    NVFP4_LAUNCH_FAILED = 7   /* hipLaunchKernel (or hipGetLastError) failed */
+};
+
+enum nvfp4_dtype { NVFP4_BF16 = 0, NVFP4_F32 = 1 };
+enum nvfp4_gs_mode {
+    NVFP4_GS_STATIC = 0,      /* read global_scale[] (a calibrated input scale) */
+    NVFP4_GS_DYNAMIC = 1      /* compute global_scale[] from the amax and write it */
+};
+
+static inline const char *nvfp4_status_string(int s)
+{
+    switch (s) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_NULL_POINTER: return "null pointer";
+    case NVFP4_BAD_SHAPE: return "bad shape";
+    case NVFP4_MISALIGNED: return "pointer not 16-byte aligned";
+    case NVFP4_BAD_RANK: return "rank must be a positive multiple of 32";
+    case NVFP4_BAD_DTYPE: return "unknown dtype";
+    case NVFP4_UNSUPPORTED: return "unsupported argument";
+    case NVFP4_LAUNCH_FAILED: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+/*
+ * Quantize x [m, k] to NVFP4.
+ *   x:               [m, k] row-major, bf16 (x_dtype 0) or fp32 (x_dtype 1).
+ *   pre_quant_scale: NULL, or [k] bf16; x is multiplied by it element-wise in
+ *                    fp32 before quantization (the SVDQuant smoothing folded
+ *                    into quantization, flashinfer mm_nvfp4_svdquant,
+ *                    parameter a).
+ *   global_scale:    [1] fp32; read (STATIC) or written (DYNAMIC).
+ *   out_fp4:         [m, k/2] bytes.
+ *   out_sf:          pad_up(m,128)*pad_up(k/16,4) bytes, swizzled.
+ * Requires m >= 1, k >= 16, k % 16 == 0.
+ */
+int nvfp4_quantize(const void *x, int x_dtype, int64_t m, int64_t k,
+                   const void *pre_quant_scale, float *global_scale, int gs_mode,
+                   uint8_t *out_fp4, uint8_t *out_sf, void *stream);
+
+/*
+ * Batched, optionally masked quantization (flashinfer PR #1774, the
+ * nvfp4_batched_quantize op and its per-item global scale).
+ *   x:            [b, m, k] bf16.
+ *   mask:         NULL (all m rows valid) or [b] int32 valid-row counts,
+ *                 clamped to [0, m]; rows >= mask[e] do not enter item e's
+ *                 amax, their FP4 bytes are not written and their scale bytes
+ *                 are written as 0.
+ *   global_scale: [b] fp32, one per item (read or written).
+ *   out_fp4:      [b, m, k/2];  out_sf: [b, pad_up(m,128)*pad_up(k/16,4)].
+ * Requires b >= 1, m >= 1, k >= 16, k % 16 == 0.
+ */
+int nvfp4_quantize_masked_batched(const void *x, int64_t b, int64_t m, int64_t k,
+                                  const int32_t *mask, float *global_scale, int gs_mode,
+                                  uint8_t *out_fp4, uint8_t *out_sf, void *stream);
+
+/*
+ * silu_and_mul fused before batched, optionally masked quantization
+ * (flashinfer PR #1774, silu_and_mul_fp4_batched_quantize: a row of width
+ * k2 = 2*h maps to h).  Gate is the first half of the row, up the second:
+ *   h = bf16(fp32(silu(gate) * up)), silu(g) = g / (1 + e^-g) correctly
+ *   rounded to fp32; h is then quantized as in nvfp4_quantize_masked_batched.
+ *   x:       [b, m, k2] bf16;  out_fp4: [b, m, k2/4];
+ *   out_sf:  [b, pad_up(m,128)*pad_up(k2/32,4)].
+ * Requires k2 even and (k2/2) % 16 == 0.
+ */
+int silu_mul_nvfp4_quantize(const void *x, int64_t b, int64_t m, int64_t k2,
+                            const int32_t *mask, float *global_scale, int gs_mode,
+                            uint8_t *out_fp4, uint8_t *out_sf, void *stream);
+
+/*
+ * out[m, n] = bf16(alpha * (A @ B^T) (+ bias[n])) with A [m, k] and B [n, k]
+ * in NVFP4 (flashinfer mm_nvfp4_svdquant without the LoRA term; the FP4
+ * linear of FastVideo PR #1350 and the scaled_mm of NVIDIA/Fuser PR #5737).
+ *   a: [m, k/2], b: [n, k/2], a_sf / b_sf: swizzled scales of a / b.
+ *   alpha: device fp32 scalar (numel >= 1).  bias: NULL or [n] bf16.
+ *   out: [m, n] bf16, row-major.  Accumulation is fp32.
+ * Requires m, n >= 1, k >= 16, k % 16 == 0.
+ */
+int nvfp4_gemm(const uint8_t *a, const uint8_t *b, const uint8_t *a_sf, const uint8_t *b_sf,
+               const float *alpha, const void *bias, void *out,
+               int64_t m, int64_t n, int64_t k, void *stream);
+
+/*
+ * Grouped masked GEMM over E experts (flashinfer PR #1774: the quantized
+ * batched outputs feed grouped_gemm_nt_masked): for each e and each row
+ * i < mask[e] (clamped to [0, m]):
+ *   out[e, i, :] = bf16(alpha[e] * (A[e] @ B[e]^T)[i, :]).
+ *   a: [E, m, k/2]; b: [E, n, k/2]; a_sf: [E, pad_up(m,128)*pad_up(k/16,4)];
+ *   b_sf: [E, pad_up(n,128)*pad_up(k/16,4)]; alpha, mask: [E] on device;
+ *   out: [E, m, n] bf16, rows >= mask[e] are not written.
+ */
+int nvfp4_gemm_grouped_masked(const uint8_t *a, const uint8_t *b, const uint8_t *a_sf,
+                              const uint8_t *b_sf, const float *alpha, const int32_t *mask,
+                              void *out, int64_t E, int64_t m, int64_t n, int64_t k,
+                              void *stream);
+
+/*
+ * SVDQuant fused GEMM (flashinfer docs, flashinfer.gemm.mm_nvfp4_svdquant):
+ *   out = bf16(alpha * (A @ B^T + d @ l1^T) (+ bias)), the rank-r term
+ *   added to the same fp32 accumulator after the NVFP4 K loop; l1 must be
+ *   pre-divided by alpha by the caller so the term comes out unscaled.
+ *   d: [m, r] bf16 (the LoRA-down output); l1: [n, r] bf16; bias: NULL or
+ *   [n] bf16.  Requires r > 0 and r % 32 == 0.
+ */
+int nvfp4_gemm_svdquant(const uint8_t *a, const uint8_t *b, const uint8_t *a_sf,
+                        const uint8_t *b_sf, const float *alpha, const void *d, const void *l1,
+                        const void *bias, void *out, int64_t m, int64_t n, int64_t k, int64_t r,
+                        void *stream);
+
+/*
+ * alpha[i] = 1 / (gs_a[i] * gs_b[i]) in fp32 for i < count, on the device
+ * (TensorRT-LLM create_weights, the alpha parameter).  Lets a caller that
+ * quantizes activations in DYNAMIC mode form the GEMM's alpha without a host
+ * round trip.  gs_a, gs_b, alpha: [count] fp32 device pointers.
+ */
+int nvfp4_alpha(const float *gs_a, const float *gs_b, float *alpha, int64_t count, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_AMD_H */

@@ -1,0 +1,134 @@
+// abi.cpp -- the extern "C" entry points declared in include/nvfp4.h:
+// argument validation (before anything is enqueued) and dispatch to the
+// kernel launchers.  The library allocates no memory and keeps no state.
+#include <hip/hip_runtime.h>
+
+#include "../../include/nvfp4.h"
+#include "internal.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool dim_ok(int64_t v) { return v >= 1 && v <= kMaxDim; }
+
+int launch_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_LAUNCH_FAILED; }
+
+// Sizes must keep every per-item element count and every grid dimension in
+// range of the kernels' 32-bit tile indices.
+bool quant_sizes_ok(int64_t b, int64_t m, int64_t K) {
+    if (!dim_ok(b) || !dim_ok(m) || !dim_ok(K)) return false;
+    if (b > 65535) return false;
+    int64_t nrt = (m + 127) / 128, nct = (K + 63) / 64;
+    if (nrt > 65535 || nct > ((int64_t)1 << 31) - 1) return false;
+    if (nrt * nct > ((int64_t)1 << 31) - 1) return false;
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_quantize(const void* x, int x_dtype, int64_t m, int64_t k, const void* pre_quant_scale,
+                   float* global_scale, int gs_mode, uint8_t* out_fp4, uint8_t* out_sf,
+                   void* stream) {
+    if (!x || !global_scale || !out_fp4 || !out_sf) return NVFP4_NULL_POINTER;
+    if (x_dtype != NVFP4_BF16 && x_dtype != NVFP4_F32) return NVFP4_BAD_DTYPE;
+    if (gs_mode != NVFP4_GS_STATIC && gs_mode != NVFP4_GS_DYNAMIC) return NVFP4_UNSUPPORTED;
+    if (k < 16 || k % 16 != 0 || !quant_sizes_ok(1, m, k)) return NVFP4_BAD_SHAPE;
+    if (!aligned16(x) || !aligned16(out_fp4) || !aligned16(out_sf) ||
+        (pre_quant_scale && !aligned16(pre_quant_scale)) || ((uintptr_t)global_scale & 3u))
+        return NVFP4_MISALIGNED;
+    nvfp4::QuantizeArgs a{};
+    a.x = x; a.x_dtype = x_dtype; a.pqs = pre_quant_scale; a.mask = nullptr;
+    a.gs = global_scale; a.out_fp4 = out_fp4; a.out_sf = out_sf;
+    a.b = 1; a.m = m; a.k_in = k; a.silu = false; a.dynamic = gs_mode == NVFP4_GS_DYNAMIC;
+    return launch_status(nvfp4::launch_quantize(a, (hipStream_t)stream));
+}
+
+int nvfp4_quantize_masked_batched(const void* x, int64_t b, int64_t m, int64_t k,
+                                  const int32_t* mask, float* global_scale, int gs_mode,
+                                  uint8_t* out_fp4, uint8_t* out_sf, void* stream) {
+    if (!x || !global_scale || !out_fp4 || !out_sf) return NVFP4_NULL_POINTER;
+    if (gs_mode != NVFP4_GS_STATIC && gs_mode != NVFP4_GS_DYNAMIC) return NVFP4_UNSUPPORTED;
+    if (k < 16 || k % 16 != 0 || !quant_sizes_ok(b, m, k)) return NVFP4_BAD_SHAPE;
+    if (!aligned16(x) || !aligned16(out_fp4) || !aligned16(out_sf) || ((uintptr_t)global_scale & 3u) ||
+        ((uintptr_t)mask & 3u))
+        return NVFP4_MISALIGNED;
+    nvfp4::QuantizeArgs a{};
+    a.x = x; a.x_dtype = NVFP4_BF16; a.pqs = nullptr; a.mask = mask;
+    a.gs = global_scale; a.out_fp4 = out_fp4; a.out_sf = out_sf;
+    a.b = b; a.m = m; a.k_in = k; a.silu = false; a.dynamic = gs_mode == NVFP4_GS_DYNAMIC;
+    return launch_status(nvfp4::launch_quantize(a, (hipStream_t)stream));
+}
+
+int silu_mul_nvfp4_quantize(const void* x, int64_t b, int64_t m, int64_t k2, const int32_t* mask,
+                            float* global_scale, int gs_mode, uint8_t* out_fp4, uint8_t* out_sf,
+                            void* stream) {
+    if (!x || !global_scale || !out_fp4 || !out_sf) return NVFP4_NULL_POINTER;
+    if (gs_mode != NVFP4_GS_STATIC && gs_mode != NVFP4_GS_DYNAMIC) return NVFP4_UNSUPPORTED;
+    if (k2 < 32 || k2 % 2 != 0 || (k2 / 2) % 16 != 0 || !quant_sizes_ok(b, m, k2 / 2))
+        return NVFP4_BAD_SHAPE;
+    if (!aligned16(x) || !aligned16(out_fp4) || !aligned16(out_sf) || ((uintptr_t)global_scale & 3u) ||
+        ((uintptr_t)mask & 3u))
+        return NVFP4_MISALIGNED;
+    nvfp4::QuantizeArgs a{};
+    a.x = x; a.x_dtype = NVFP4_BF16; a.pqs = nullptr; a.mask = mask;
+    a.gs = global_scale; a.out_fp4 = out_fp4; a.out_sf = out_sf;
+    a.b = b; a.m = m; a.k_in = k2; a.silu = true; a.dynamic = gs_mode == NVFP4_GS_DYNAMIC;
+    return launch_status(nvfp4::launch_quantize(a, (hipStream_t)stream));
+}
+
+static int gemm_common(const uint8_t* a, const uint8_t* b, const uint8_t* a_sf, const uint8_t* b_sf,
+                       const float* alpha, const int32_t* mask, const void* bias, const void* d,
+                       const void* l1, void* out, int64_t E, int64_t m, int64_t n, int64_t k,
+                       int64_t r, void* stream) {
+    if (!a || !b || !a_sf || !b_sf || !alpha || !out) return NVFP4_NULL_POINTER;
+    if (!dim_ok(E) || !dim_ok(m) || !dim_ok(n) || k < 16 || k % 16 != 0 || k > kMaxDim)
+        return NVFP4_BAD_SHAPE;
+    if (E > 65535 || ((m + 63) / 64) * ((n + 63) / 64) > ((int64_t)1 << 31) - 1) return NVFP4_BAD_SHAPE;
+    if (!aligned16(a) || !aligned16(b) || !aligned16(a_sf) || !aligned16(b_sf) || !aligned16(out) ||
+        ((uintptr_t)alpha & 3u) || (bias && !aligned16(bias)) || (d && !aligned16(d)) ||
+        (l1 && !aligned16(l1)) || ((uintptr_t)mask & 3u))
+        return NVFP4_MISALIGNED;
+    nvfp4::GemmArgs g{};
+    g.a = a; g.b = b; g.a_sf = a_sf; g.b_sf = b_sf; g.alpha = alpha; g.mask = mask;
+    g.bias = (const uint16_t*)bias; g.d = (const uint16_t*)d; g.l1 = (const uint16_t*)l1;
+    g.out = (uint16_t*)out; g.E = E; g.m = m; g.n = n; g.k = k; g.r = r;
+    return launch_status(nvfp4::launch_gemm(g, (hipStream_t)stream));
+}
+
+int nvfp4_gemm(const uint8_t* a, const uint8_t* b, const uint8_t* a_sf, const uint8_t* b_sf,
+               const float* alpha, const void* bias, void* out, int64_t m, int64_t n, int64_t k,
+               void* stream) {
+    return gemm_common(a, b, a_sf, b_sf, alpha, nullptr, bias, nullptr, nullptr, out, 1, m, n, k, 0,
+                       stream);
+}
+
+int nvfp4_gemm_grouped_masked(const uint8_t* a, const uint8_t* b, const uint8_t* a_sf,
+                              const uint8_t* b_sf, const float* alpha, const int32_t* mask,
+                              void* out, int64_t E, int64_t m, int64_t n, int64_t k, void* stream) {
+    if (!mask) return NVFP4_NULL_POINTER;
+    return gemm_common(a, b, a_sf, b_sf, alpha, mask, nullptr, nullptr, nullptr, out, E, m, n, k, 0,
+                       stream);
+}
+
+int nvfp4_gemm_svdquant(const uint8_t* a, const uint8_t* b, const uint8_t* a_sf, const uint8_t* b_sf,
+                        const float* alpha, const void* d, const void* l1, const void* bias,
+                        void* out, int64_t m, int64_t n, int64_t k, int64_t r, void* stream) {
+    if (!d || !l1) return NVFP4_NULL_POINTER;
+    if (r <= 0 || r % 32 != 0 || r > 4096) return NVFP4_BAD_RANK;
+    return gemm_common(a, b, a_sf, b_sf, alpha, nullptr, bias, d, l1, out, 1, m, n, k, r, stream);
+}
+
+int nvfp4_alpha(const float* gs_a, const float* gs_b, float* alpha, int64_t count, void* stream) {
+    if (!gs_a || !gs_b || !alpha) return NVFP4_NULL_POINTER;
+    if (!dim_ok(count)) return NVFP4_BAD_SHAPE;
+    if (((uintptr_t)gs_a & 3u) || ((uintptr_t)gs_b & 3u) || ((uintptr_t)alpha & 3u))
+        return NVFP4_MISALIGNED;
+    return launch_status(nvfp4::launch_alpha(gs_a, gs_b, alpha, count, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,42 @@
+// internal.h -- launcher interfaces between the C ABI (abi.cpp) and the
+// kernels.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+struct QuantizeArgs {
+    const void* x;
+    int x_dtype;          // 0 bf16, 1 fp32
+    const void* pqs;      // [K] bf16 or null
+    const int32_t* mask;  // [b] or null
+    float* gs;            // [b]
+    uint8_t* out_fp4;
+    uint8_t* out_sf;
+    int64_t b, m, k_in;   // k_in: input row width (2*K for silu)
+    bool silu;
+    bool dynamic;
+};
+
+hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t st);
+hipError_t launch_alpha(const float* ga, const float* gb, float* alpha, int64_t n, hipStream_t st);
+
+struct GemmArgs {
+    const uint8_t* a;      // [E, m, k/2]
+    const uint8_t* b;      // [E, n, k/2]
+    const uint8_t* a_sf;   // [E, sfa]
+    const uint8_t* b_sf;   // [E, sfb]
+    const float* alpha;    // [E]
+    const int32_t* mask;   // [E] or null
+    const uint16_t* bias;  // [n] or null
+    const uint16_t* d;     // [m, r] or null
+    const uint16_t* l1;    // [n, r] or null
+    uint16_t* out;         // [E, m, n]
+    int64_t E, m, n, k, r;
+};
+
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
+
+}  // namespace nvfp4

@@ -1,0 +1,186 @@
+"""The C-ABI library loads, exports every entry point include/nvfp4.h declares,
+and rejects bad arguments before enqueuing anything (CPU only: every call
+here fails validation, so no HIP work is started and no pointer is touched).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+LIB = os.path.join(ROOT, "nvfp4_block_scaled_04_amd", "libnvfp4_amd.so")
+
+OK, NULLP, SHAPE, MISAL, RANK, DTYPE, UNSUP = 0, 1, 2, 3, 4, 5, 6
+P = 0x10000  # a 16-byte aligned address that is never dereferenced here
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^int\s+(\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail(f"{LIB} not built; run __graft_entry__.build()")
+    L = ctypes.CDLL(LIB)
+    return L
+
+
+def test_header_declares_the_entry_points():
+    assert declared() == sorted([
+        "nvfp4_alpha", "nvfp4_gemm", "nvfp4_gemm_grouped_masked", "nvfp4_gemm_svdquant",
+        "nvfp4_quantize", "nvfp4_quantize_masked_batched", "silu_mul_nvfp4_quantize",
+    ])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (\w+)$", out, flags=re.M))
+    for name in declared():
+        assert name in exported, name
+        assert getattr(lib, name)
+
+
+def test_binding_names_match_header():
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "ops_src", os.path.join(ROOT, "nvfp4_block_scaled_04_amd", "ops.py"))
+    src = open(spec.origin).read()
+    exports = re.search(r"EXPORTS = \((.*?)\)", src, flags=re.S).group(1)
+    names = sorted(re.findall(r'"(\w+)"', exports))
+    assert names == declared()
+
+
+def call(lib, name, *args):
+    f = getattr(lib, name)
+    f.restype = ctypes.c_int
+    conv = []
+    for a in args:
+        if isinstance(a, float):
+            conv.append(ctypes.c_float(a))
+        else:
+            conv.append(ctypes.c_int64(a) if a is not None else ctypes.c_void_p(None))
+    return f(*conv)
+
+
+def q(lib, x=P, dt=0, m=128, k=256, pqs=None, gs=P, mode=1, o=P, s=P):
+    return lib.nvfp4_quantize(ctypes.c_void_p(x), ctypes.c_int(dt), ctypes.c_int64(m),
+                              ctypes.c_int64(k), ctypes.c_void_p(pqs), ctypes.c_void_p(gs),
+                              ctypes.c_int(mode), ctypes.c_void_p(o), ctypes.c_void_p(s),
+                              ctypes.c_void_p(None))
+
+
+def test_quantize_validation(lib):
+    assert q(lib, x=None) == NULLP
+    assert q(lib, gs=None) == NULLP
+    assert q(lib, o=None) == NULLP
+    assert q(lib, s=None) == NULLP
+    assert q(lib, dt=2) == DTYPE
+    assert q(lib, mode=5) == UNSUP
+    assert q(lib, k=15) == SHAPE
+    assert q(lib, k=24) == SHAPE
+    assert q(lib, k=0) == SHAPE
+    assert q(lib, m=0) == SHAPE
+    assert q(lib, m=-3) == SHAPE
+    assert q(lib, x=P + 8) == MISAL
+    assert q(lib, o=P + 4) == MISAL
+    assert q(lib, s=P + 1) == MISAL
+    assert q(lib, pqs=P + 2) == MISAL
+    assert q(lib, gs=P + 2) == MISAL
+
+
+def qb(lib, fn, x=P, b=2, m=128, k=256, mask=None, gs=P, mode=1, o=P, s=P):
+    f = getattr(lib, fn)
+    return f(ctypes.c_void_p(x), ctypes.c_int64(b), ctypes.c_int64(m), ctypes.c_int64(k),
+             ctypes.c_void_p(mask), ctypes.c_void_p(gs), ctypes.c_int(mode), ctypes.c_void_p(o),
+             ctypes.c_void_p(s), ctypes.c_void_p(None))
+
+
+@pytest.mark.parametrize("fn", ["nvfp4_quantize_masked_batched", "silu_mul_nvfp4_quantize"])
+def test_batched_validation(lib, fn):
+    assert qb(lib, fn, x=None) == NULLP
+    assert qb(lib, fn, gs=None) == NULLP
+    assert qb(lib, fn, b=0) == SHAPE
+    assert qb(lib, fn, m=0) == SHAPE
+    assert qb(lib, fn, k=8) == SHAPE
+    assert qb(lib, fn, mode=2) == UNSUP
+    assert qb(lib, fn, x=P + 2) == MISAL
+    assert qb(lib, fn, mask=P + 1) == MISAL
+
+
+def test_silu_width_rules(lib):
+    fn = "silu_mul_nvfp4_quantize"
+    assert qb(lib, fn, k=33) == SHAPE        # odd gate|up width
+    assert qb(lib, fn, k=48) == SHAPE        # h = 24 is not a multiple of 16
+    assert qb(lib, fn, k=16) == SHAPE        # h = 8
+
+
+def g(lib, a=P, b=P, asf=P, bsf=P, alpha=P, bias=None, out=P, m=128, n=128, k=256):
+    return lib.nvfp4_gemm(*[ctypes.c_void_p(v) for v in (a, b, asf, bsf, alpha, bias, out)],
+                          ctypes.c_int64(m), ctypes.c_int64(n), ctypes.c_int64(k),
+                          ctypes.c_void_p(None))
+
+
+def test_gemm_validation(lib):
+    for kw in ("a", "b", "asf", "bsf", "alpha", "out"):
+        assert g(lib, **{kw: None}) == NULLP, kw
+    assert g(lib, k=40) == SHAPE
+    assert g(lib, k=0) == SHAPE
+    assert g(lib, m=0) == SHAPE
+    assert g(lib, n=-1) == SHAPE
+    assert g(lib, a=P + 8) == MISAL
+    assert g(lib, out=P + 2) == MISAL
+    assert g(lib, bias=P + 2) == MISAL
+    assert g(lib, alpha=P + 1) == MISAL
+
+
+def test_grouped_validation(lib):
+    f = lib.nvfp4_gemm_grouped_masked
+    args = lambda mask=P, E=4, k=256: [ctypes.c_void_p(P)] * 5 + [ctypes.c_void_p(mask), ctypes.c_void_p(P),
+                                         ctypes.c_int64(E), ctypes.c_int64(64), ctypes.c_int64(64),
+                                         ctypes.c_int64(k), ctypes.c_void_p(None)]
+    assert f(*args(mask=None)) == NULLP
+    assert f(*args(E=0)) == SHAPE
+    assert f(*args(k=17)) == SHAPE
+    assert f(*args(mask=P + 2)) == MISAL
+
+
+def test_svdquant_rank_and_alignment(lib):
+    f = lib.nvfp4_gemm_svdquant
+
+    def run(r=32, d=P, l1=P, k=256):
+        return f(*[ctypes.c_void_p(P)] * 5, ctypes.c_void_p(d), ctypes.c_void_p(l1),
+                 ctypes.c_void_p(None), ctypes.c_void_p(P), ctypes.c_int64(64), ctypes.c_int64(64),
+                 ctypes.c_int64(k), ctypes.c_int64(r), ctypes.c_void_p(None))
+    assert run(r=0) == RANK
+    assert run(r=16) == RANK
+    assert run(r=48) == RANK
+    assert run(r=-32) == RANK
+    assert run(d=None) == NULLP
+    assert run(l1=None) == NULLP
+    assert run(d=P + 8) == MISAL     # d must be 16-byte aligned
+    assert run(k=40) == SHAPE
+
+
+def test_alpha_validation(lib):
+    f = lib.nvfp4_alpha
+    assert f(ctypes.c_void_p(None), ctypes.c_void_p(P), ctypes.c_void_p(P), ctypes.c_int64(1),
+             ctypes.c_void_p(None)) == NULLP
+    assert f(ctypes.c_void_p(P), ctypes.c_void_p(P), ctypes.c_void_p(P), ctypes.c_int64(0),
+             ctypes.c_void_p(None)) == SHAPE
+
+
+def test_product_does_not_touch_oracle():
+    """The library sources and the binding never name the oracle."""
+    pkg = os.path.join(ROOT, "nvfp4_block_scaled_04_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".cpp", ".h")):
+                txt = open(os.path.join(dirpath, fn)).read()
+                assert "import oracle" not in txt and "from oracle" not in txt, fn
+                assert "nvfp4_oracle" not in txt and "nvo_" not in txt, fn
