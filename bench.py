@@ -1,0 +1,316 @@
+"""Benchmark of the NVFP4 hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input that
+is already resident in HBM: NVFP4 quantization of the bf16 activation with a
+dynamic global scale (clear, amax pass, quantize pass), alpha = 1/(gs_a*gs_w)
+on the device, and the block-scaled GEMM to bf16.  Weights are quantized once
+before timing (same kernels, untimed).
+
+Default workload: the large prefill linear, activation [8192, 5120] bf16
+(0.5% outlier channels x30) against a [16384, 5120] weight, output [8192,
+16384] bf16.  Other workloads (--workload dense|decode|moe|svdquant|tiny)
+are for development measurements.
+
+Prints one JSON line.  `value` is whole-step GEMM throughput (GEMM flops per
+step / step time); the quantize and GEMM kernels are also reported on their
+own, and `roofline` covers the dominant kernel (the GEMM), timed with HIP
+events on the stream it runs on.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, TFLOP/s
+
+
+def sf_size(rows, k):
+    return (rows + 127) // 128 * 128 * ((k // 16 + 3) // 4 * 4)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="prefill",
+                   choices=["prefill", "dense", "decode", "moe", "svdquant", "tiny"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--rotate", type=int, default=0,
+                   help="activation copies cycled per step (0: enough to exceed 512 MB)")
+    return p.parse_args()
+
+
+class Workload:
+    """Device-resident inputs plus the step closure and its algorithmic work."""
+
+
+def build_workload(name, ops, synth, torch):
+    w = Workload()
+    dev = "cuda"
+    if name in ("prefill", "dense", "decode", "tiny"):
+        if name == "prefill":
+            d = synth.prefill()
+            a_cpu, w_cpu = d.a, d.w
+            w.desc = "prefill linear 8192x16384x5120: bf16 activation -> dynamic NVFP4 quantize -> block-scaled GEMM -> bf16"
+        elif name == "dense":
+            d, _ = synth.dense()
+            a_cpu, w_cpu = d.a, d.w
+            w.desc = "dense linear 2048x4096x4096: bf16 activation -> dynamic NVFP4 quantize -> block-scaled GEMM -> bf16"
+        elif name == "decode":
+            d, a16 = synth.dense()
+            a_cpu, w_cpu = a16, d.w
+            w.desc = "decode linear 16x4096x4096: bf16 activation -> dynamic NVFP4 quantize -> block-scaled GEMM -> bf16"
+        else:
+            d = synth.tiny()
+            a_cpu, w_cpu = d.a, d.w
+            w.desc = "tiny 128x256x256: fp32 activation -> dynamic NVFP4 quantize -> block-scaled GEMM -> bf16"
+        m, k = a_cpu.shape
+        n = w_cpu.shape[0]
+        fw, sfw, gsw = ops.nvfp4_quantize(w_cpu.to(dev))
+        esz = a_cpu.element_size()
+        act_bytes = m * k * esz
+        copies = w.rotate_hint = max(1, -(-512 * 2 ** 20 // act_bytes))
+        w.acts = None
+        w.a_cpu, w.w_cpu = a_cpu, w_cpu
+        w.m, w.n, w.k = m, n, k
+        w.flops = 2.0 * m * n * k
+        w.q_bytes = m * k * esz + m * k // 2 + sf_size(m, k)     # quantize pass
+        w.amax_bytes = m * k * esz                                 # amax pass
+        w.gemm_bytes = m * k // 2 + sf_size(m, k) + n * k // 2 + sf_size(n, k) + 2 * m * n
+        fa = torch.empty(m, k // 2, dtype=torch.uint8, device=dev)
+        sfa = torch.empty(sf_size(m, k), dtype=torch.uint8, device=dev)
+        gsa = torch.zeros(1, dtype=torch.float32, device=dev)
+        alpha = torch.empty(1, dtype=torch.float32, device=dev)
+        out = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+
+        def quant(a, mode=ops.GS_DYNAMIC):
+            ops.nvfp4_quantize(a, gsa, mode, out_fp4=fa, out_sf=sfa)
+
+        def gemm():
+            ops.nvfp4_gemm(fa, fw, sfa, sfw, alpha, out=out)
+
+        def step(a, ev=None):
+            if ev is not None:
+                ev[0].record()
+            quant(a)
+            ops.nvfp4_alpha(gsa, gsw, out=alpha)
+            if ev is not None:
+                ev[1].record()
+            gemm()
+            if ev is not None:
+                ev[2].record()
+
+        w.make_acts = lambda n_copies: [a_cpu.to(dev) for _ in range(n_copies)]
+        w.step, w.quant, w.gemm = step, quant, gemm
+        w.cfg = {"m": m, "n": n, "k": k}
+        w.cpu_sample = lambda O, np: cpu_baseline_dense(O, np, a_cpu, w_cpu, synth)
+        return w
+
+    if name == "moe":
+        mo = synth.moe()
+        E, m, h, n = mo.e, mo.m, mo.h, mo.n
+        fws, sfws, gsws = [], [], []
+        for e in range(E):
+            f_, s_, g_ = ops.nvfp4_quantize(mo.w[e].to(dev))
+            fws.append(f_); sfws.append(s_); gsws.append(g_)
+        fw = torch.stack(fws); sfw = torch.stack(sfws); gsw = torch.cat(gsws)
+        mask = mo.mask.to(dev)
+        valid = int(mo.mask.clamp(0, m).sum())
+        fa = torch.empty(E, m, h // 2, dtype=torch.uint8, device=dev)
+        sfa = torch.empty(E, sf_size(m, h), dtype=torch.uint8, device=dev)
+        gsa = torch.zeros(E, dtype=torch.float32, device=dev)
+        alpha = torch.empty(E, dtype=torch.float32, device=dev)
+        out = torch.empty(E, m, n, dtype=torch.bfloat16, device=dev)
+
+        def quant(x, mode=ops.GS_DYNAMIC):
+            ops.silu_mul_nvfp4_quantize(x, mask, gsa, mode, out_fp4=fa, out_sf=sfa)
+
+        def gemm():
+            ops.nvfp4_gemm_grouped_masked(fa, fw, sfa, sfw, alpha, mask, out=out)
+
+        def step(x, ev=None):
+            if ev is not None:
+                ev[0].record()
+            quant(x)
+            ops.nvfp4_alpha(gsa, gsw, out=alpha)
+            if ev is not None:
+                ev[1].record()
+            gemm()
+            if ev is not None:
+                ev[2].record()
+
+        w.desc = ("Llama4-style routed experts: E=8 gate|up [512,16384] bf16, valid rows "
+                  f"{mo.mask.tolist()} -> fused silu_and_mul + NVFP4 quantize -> grouped masked GEMM vs [8,5120,8192]")
+        act_bytes = mo.x.numel() * 2
+        w.rotate_hint = max(1, -(-512 * 2 ** 20 // act_bytes))
+        w.make_acts = lambda n_copies: [mo.x.to(dev) for _ in range(n_copies)]
+        w.step, w.quant, w.gemm = step, quant, gemm
+        w.flops = 2.0 * n * h * valid
+        w.q_bytes = valid * 2 * h * 2 + E * m * h // 2 + E * sf_size(m, h)
+        w.amax_bytes = valid * 2 * h * 2
+        w.gemm_bytes = valid * h // 2 + E * sf_size(m, h) + E * n * h // 2 + E * sf_size(n, h) + 2 * valid * n
+        w.m, w.n, w.k = valid, n, h
+        w.cfg = {"experts": E, "m_max": m, "valid_rows": mo.mask.tolist(), "n": n, "k": h}
+        w.cpu_sample = None
+        return w
+
+    if name == "svdquant":
+        s = synth.svdquant()
+        m, n, k, r = s.m, s.n, s.k, s.r
+        fw, sfw, gsw = ops.nvfp4_quantize(s.w.to(dev))
+        x0 = s.x.to(dev)
+        pqs = s.pqs.to(dev)
+        # calibrated (static) input scale, as the smoothing pipeline uses a fixed
+        # alpha to pre-divide l1; calibration = one dynamic pass, untimed
+        _, _, gsa = ops.nvfp4_quantize(x0, pre_quant_scale=pqs)
+        alpha = ops.nvfp4_alpha(gsa, gsw)
+        al = float(alpha.item())
+        d = synth.lora_down(s).to(dev)
+        l1 = synth.lora_up(s, al).to(dev)
+        bias = s.bias.to(dev)
+        fa = torch.empty(m, k // 2, dtype=torch.uint8, device=dev)
+        sfa = torch.empty(sf_size(m, k), dtype=torch.uint8, device=dev)
+        out = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+
+        def quant(x, mode=ops.GS_STATIC):
+            ops.nvfp4_quantize(x, gsa, mode, pre_quant_scale=pqs, out_fp4=fa, out_sf=sfa)
+
+        def gemm():
+            ops.nvfp4_gemm_svdquant(fa, fw, sfa, sfw, alpha, d, l1, bias=bias, out=out)
+
+        def step(x, ev=None):
+            if ev is not None:
+                ev[0].record()
+            quant(x)
+            if ev is not None:
+                ev[1].record()
+            gemm()
+            if ev is not None:
+                ev[2].record()
+
+        w.desc = "SVDQuant linear 4096x3072x3072, r=32: smooth NVFP4 quantize (static gs) -> fused GEMM + LoRA-up + bias"
+        w.rotate_hint = max(1, -(-512 * 2 ** 20 // (m * k * 2)))
+        w.make_acts = lambda n_copies: [s.x.to(dev) for _ in range(n_copies)]
+        w.step, w.quant, w.gemm = step, quant, gemm
+        w.flops = 2.0 * m * n * k + 2.0 * m * n * r
+        w.q_bytes = m * k * 2 + k * 2 + m * k // 2 + sf_size(m, k)
+        w.amax_bytes = 0
+        w.gemm_bytes = m * k // 2 + sf_size(m, k) + n * k // 2 + sf_size(n, k) + 2 * m * n + 2 * (m + n) * r + 2 * n
+        w.m, w.n, w.k = m, n, k
+        w.cfg = {"m": m, "n": n, "k": k, "r": r}
+        w.cpu_sample = None
+        return w
+    raise ValueError(name)
+
+
+def cpu_baseline_dense(O, np, a_cpu, w_cpu, synth):
+    """The oracle on a bounded sample of the same step: dynamic quantize of
+    the full weight is skipped (offline in the GPU step too); it quantizes a
+    slice of activation rows and computes the GEMM for those rows."""
+    rows = 64
+    a = synth.bits(a_cpu[:rows])
+    wq = O.quantize(synth.bits(w_cpu))          # untimed, like the GPU's weights
+    m, k = a_cpu.shape
+    n = w_cpu.shape[0]
+    t0 = time.perf_counter()
+    qa, sa, ga = O.quantize(a)
+    alpha = np.float32(1.0) / (ga[0] * wq[2][0])
+    O.gemm_rows(qa, wq[0], sa, wq[1], alpha, rows, n, k)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * n * k
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": O.num_threads(),
+        "kind": "oracle",
+        "sample": f"{rows} of {m} activation rows: oracle dynamic quantize of those rows + "
+                  f"oracle dequant-GEMM {rows}x{n}x{k} (fp64 accumulation), {dt:.2f} s wall",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from nvfp4_block_scaled_04_amd import ops, synth
+
+    torch.cuda.set_device(0)
+    w = build_workload(args.workload, ops, synth, torch)
+    n_copies = args.rotate or w.rotate_hint
+    acts = w.make_acts(n_copies)
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        w.step(acts[i % n_copies])
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        w.step(acts[i % n_copies], evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_ms = (t1 - t0) * 1e3 / args.steps
+    quant_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    gemm_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+
+    # quantize pass alone (STATIC mode: the quantize kernel only), cold inputs
+    qe = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        qe[i][0].record()
+        w.quant(acts[i % n_copies], ops.GS_STATIC)
+        qe[i][1].record()
+    torch.cuda.synchronize()
+    qpass_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in qe]))
+
+    gemm_tflops = w.flops / (gemm_ms * 1e-3) / 1e12
+    value = w.flops / (step_ms * 1e-3) / 1e12
+    q_gbs = w.q_bytes / (qpass_ms * 1e-3) / 1e9
+    e2e_bytes = w.q_bytes + w.amax_bytes
+    res = {
+        "metric": "NVFP4 GEMM TFLOP/s (+% peak) and quantize GB/s (+% HBM peak), 1xMI355X",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (seeded N(0,1) activations with outlier channels, N(0,0.02) weights)",
+        "config": {"workload": w.desc, **w.cfg, "operands": "NVFP4 (e2m1 + ue4m3 per 16, 128x4 swizzled)",
+                   "parallelism": "none (1 GPU)", "activation_copies_rotated": n_copies},
+        "gemm": {"ms": round(gemm_ms, 4), "tflops": round(gemm_tflops, 2),
+                 "frac_f16_mfma_peak": round(gemm_tflops / MFMA_F16_PEAK_TFLOPS, 4)},
+        "quantize": {"pass_ms": round(qpass_ms, 4), "pass_gbs": round(q_gbs, 1),
+                     "pass_frac_hbm": round(q_gbs / HBM_PEAK_GBS, 4),
+                     "dynamic_call_ms": round(quant_ms, 4),
+                     "dynamic_call_gbs": round(e2e_bytes / (quant_ms * 1e-3) / 1e9, 1),
+                     "pass_bytes": w.q_bytes, "amax_pass_bytes": w.amax_bytes},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "k_gemm (block-scaled NVFP4 GEMM)",
+                     "flops_per_launch": w.flops},
+    }
+    if not args.no_cpu_baseline and w.cpu_sample is not None:
+        import oracle as O
+        res["cpu_baseline"] = w.cpu_sample(O, np)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

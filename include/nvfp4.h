@@ -37,9 +37,10 @@
  *     from the HIP launch itself; device faults surface at the caller's next
  *     synchronisation, as for any HIP call.
  *   - Calls that overlap on the same buffers race like any kernels.
- *   - In DYNAMIC mode the call uses global_scale[] as accumulator and the
- *     first bytes of out_sf as a counter while it runs; both hold their final
- *     values when the call's work completes.
+ *   - In DYNAMIC mode the call uses the first bytes of each item's out_sf
+ *     region as scratch for partial maxima before it writes the scales; out_sf
+ *     and global_scale hold their final values when the call's work
+ *     completes.
  */
 #ifndef NVFP4_AMD_H
 #define NVFP4_AMD_H

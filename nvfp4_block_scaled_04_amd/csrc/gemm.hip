@@ -67,14 +67,145 @@ __device__ __forceinline__ f16x8 dequant8(uint32_t w, f16x2 s) {
     return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+// Global -> register staging of one K step (128 elements) of the A and B
+// tiles and their scales.  Addresses are clamped into the buffers so every
+// load is issued unconditionally (all of them stay in flight together);
+// values from rows or K blocks outside the matrix are zeroed when stored.
+template <int BM, int BN, bool ALIGNED>
+struct Stage {
+    static constexpr int CH = ALIGNED ? 16 : 8;          // bytes per chunk
+    static constexpr int CPR = 64 / CH;                  // chunks per row
+    static constexpr int NA = (BM * CPR + 255) / 256;    // A chunks per thread
+    static constexpr int NB = (BN * CPR + 255) / 256;
+    static constexpr int NSA = (BM * 2 + 255) / 256;     // A scale dwords per thread
+    static constexpr int NSB = (BN * 2 + 255) / 256;
+    uint4 ra[NA], rb[NB];
+    uint32_t sa[NSA], sb[NSB];
+};
+
+template <int BM, int BN, bool ALIGNED>
+__device__ __forceinline__ void stage_load(Stage<BM, BN, ALIGNED>& st, const GParams& p,
+                                           const uint8_t* A, const uint8_t* B,
+                                           const uint8_t* SA, const uint8_t* SB,
+                                           int64_t m0, int64_t n0, int kt, int t) {
+    using S = Stage<BM, BN, ALIGNED>;
+    const int64_t rowb = p.K / 2;
+#pragma unroll
+    for (int i = 0; i < S::NA; i++) {
+        const int idx = t + 256 * i;
+        const int r = idx / S::CPR, c = idx % S::CPR;
+        int64_t row = m0 + r;
+        row = row < p.M ? row : p.M - 1;
+        if constexpr (ALIGNED) {
+            st.ra[i] = *(const uint4*)(A + row * rowb + kt * 64 + c * 16);
+        } else {
+            int64_t kb = (int64_t)kt * 64 + c * 8;
+            kb = kb < rowb ? kb : rowb - 8;
+            uint2 v = *(const uint2*)(A + row * rowb + kb);
+            st.ra[i] = uint4{v.x, v.y, 0u, 0u};
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < S::NB; i++) {
+        const int idx = t + 256 * i;
+        const int r = idx / S::CPR, c = idx % S::CPR;
+        int64_t row = n0 + r;
+        row = row < p.N ? row : p.N - 1;
+        if constexpr (ALIGNED) {
+            st.rb[i] = *(const uint4*)(B + row * rowb + kt * 64 + c * 16);
+        } else {
+            int64_t kb = (int64_t)kt * 64 + c * 8;
+            kb = kb < rowb ? kb : rowb - 8;
+            uint2 v = *(const uint2*)(B + row * rowb + kb);
+            st.rb[i] = uint4{v.x, v.y, 0u, 0u};
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < S::NSA; i++) {
+        const int idx = (t + 256 * i) % (BM * 2);
+        const int r = idx >> 1, g = idx & 1;
+        int64_t row = m0 + r;
+        row = row < p.rpa ? row : p.rpa - 1;
+        int cg = kt * 2 + g;
+        cg = cg < p.cpa4 ? cg : p.cpa4 - 1;
+        st.sa[i] = *(const uint32_t*)(SA + ((row >> 7) * p.cpa4 + cg) * 512 + (row & 31) * 16 + ((row & 127) >> 5) * 4);
+    }
+#pragma unroll
+    for (int i = 0; i < S::NSB; i++) {
+        const int idx = (t + 256 * i) % (BN * 2);
+        const int r = idx >> 1, g = idx & 1;
+        int64_t row = n0 + r;
+        row = row < p.rpb ? row : p.rpb - 1;
+        int cg = kt * 2 + g;
+        cg = cg < p.cpa4 ? cg : p.cpa4 - 1;
+        st.sb[i] = *(const uint32_t*)(SB + ((row >> 7) * p.cpa4 + cg) * 512 + (row & 31) * 16 + ((row & 127) >> 5) * 4);
+    }
+}
+
+template <int BM, int BN, bool ALIGNED>
+__device__ __forceinline__ void stage_store(const Stage<BM, BN, ALIGNED>& st, const GParams& p,
+                                            uint8_t* sA, uint8_t* sB, uint8_t* sSA, uint8_t* sSB,
+                                            int64_t m0, int64_t n0, int kt, int t) {
+    using S = Stage<BM, BN, ALIGNED>;
+#pragma unroll
+    for (int i = 0; i < S::NA; i++) {
+        const int idx = t + 256 * i;
+        if (S::NA * 256 > BM * S::CPR && idx >= BM * S::CPR) break;
+        const int r = idx / S::CPR, c = idx % S::CPR;
+        bool ok = m0 + r < p.M;
+        if constexpr (ALIGNED) {
+            uint4 v = st.ra[i];
+            if (!ok) v = uint4{0u, 0u, 0u, 0u};
+            *(uint4*)(sA + r * kPitch + c * 16) = v;
+        } else {
+            ok = ok && (int64_t)kt * 128 + c * 16 < p.K;
+            uint2 v = uint2{st.ra[i].x, st.ra[i].y};
+            if (!ok) v = uint2{0u, 0u};
+            *(uint2*)(sA + r * kPitch + c * 8) = v;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < S::NB; i++) {
+        const int idx = t + 256 * i;
+        if (S::NB * 256 > BN * S::CPR && idx >= BN * S::CPR) break;
+        const int r = idx / S::CPR, c = idx % S::CPR;
+        bool ok = n0 + r < p.N;
+        if constexpr (ALIGNED) {
+            uint4 v = st.rb[i];
+            if (!ok) v = uint4{0u, 0u, 0u, 0u};
+            *(uint4*)(sB + r * kPitch + c * 16) = v;
+        } else {
+            ok = ok && (int64_t)kt * 128 + c * 16 < p.K;
+            uint2 v = uint2{st.rb[i].x, st.rb[i].y};
+            if (!ok) v = uint2{0u, 0u};
+            *(uint2*)(sB + r * kPitch + c * 8) = v;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < S::NSA; i++) {
+        const int idx = t + 256 * i;
+        if (idx >= BM * 2) break;
+        const int r = idx >> 1, g = idx & 1;
+        const bool ok = m0 + r < p.rpa && kt * 2 + g < p.cpa4;
+        *(uint32_t*)(sSA + r * 8 + g * 4) = ok ? st.sa[i] : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < S::NSB; i++) {
+        const int idx = t + 256 * i;
+        if (idx >= BN * 2) break;
+        const int r = idx >> 1, g = idx & 1;
+        const bool ok = n0 + r < p.rpb && kt * 2 + g < p.cpa4;
+        *(uint32_t*)(sSB + r * 8 + g * 4) = ok ? st.sb[i] : 0u;
+    }
+}
+
 template <int BM, int BN, bool ALIGNED, bool LORA>
 __global__ __launch_bounds__(256) void k_gemm(GParams p) {
     constexpr int WM = BM / 2, WN = BN / 2;
     constexpr int FM = WM / 32, FN = WN / 32;
-    __shared__ __align__(16) uint8_t sA[BM * kPitch];
-    __shared__ __align__(16) uint8_t sB[BN * kPitch];
-    __shared__ __align__(16) uint8_t sSA[BM * 8];
-    __shared__ __align__(16) uint8_t sSB[BN * 8];
+    constexpr int OFF_B = BM * kPitch, OFF_SA = OFF_B + BN * kPitch, OFF_SB = OFF_SA + BM * 8;
+    constexpr int STAGE = OFF_SB + BN * 8;
+    __shared__ __align__(16) uint8_t smem[2 * STAGE];
 
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
@@ -103,81 +234,40 @@ __global__ __launch_bounds__(256) void k_gemm(GParams p) {
     const int nkt = (int)((p.K + 127) / 128);
     const int h = lane >> 5, l32 = lane & 31;
 
+    Stage<BM, BN, ALIGNED> st;
+    stage_load<BM, BN, ALIGNED>(st, p, A, B, SA, SB, m0, n0, 0, t);
+    stage_store<BM, BN, ALIGNED>(st, p, smem, smem + OFF_B, smem + OFF_SA, smem + OFF_SB, m0, n0, 0, t);
+    __syncthreads();
+
     for (int kt = 0; kt < nkt; kt++) {
-        __syncthreads();  // previous step's LDS reads are done
-        // ---- FP4 tiles -> LDS
-        if constexpr (ALIGNED) {
-#pragma unroll
-            for (int idx = t; idx < BM * 4; idx += 256) {
-                const int r = idx >> 2, c = idx & 3;
-                uint4 v = {0u, 0u, 0u, 0u};
-                if (m0 + r < p.M) v = *(const uint4*)(A + (m0 + r) * rowb + kt * 64 + c * 16);
-                *(uint4*)(sA + r * kPitch + c * 16) = v;
-            }
-#pragma unroll
-            for (int idx = t; idx < BN * 4; idx += 256) {
-                const int r = idx >> 2, c = idx & 3;
-                uint4 v = {0u, 0u, 0u, 0u};
-                if (n0 + r < p.N) v = *(const uint4*)(B + (n0 + r) * rowb + kt * 64 + c * 16);
-                *(uint4*)(sB + r * kPitch + c * 16) = v;
-            }
-        } else {
-#pragma unroll
-            for (int idx = t; idx < BM * 8; idx += 256) {
-                const int r = idx >> 3, c = idx & 7;
-                const int64_t k = (int64_t)kt * 128 + c * 16;
-                uint2 v = {0u, 0u};
-                if (m0 + r < p.M && k < p.K) v = *(const uint2*)(A + (m0 + r) * rowb + k / 2);
-                *(uint2*)(sA + r * kPitch + c * 8) = v;
-            }
-#pragma unroll
-            for (int idx = t; idx < BN * 8; idx += 256) {
-                const int r = idx >> 3, c = idx & 7;
-                const int64_t k = (int64_t)kt * 128 + c * 16;
-                uint2 v = {0u, 0u};
-                if (n0 + r < p.N && k < p.K) v = *(const uint2*)(B + (n0 + r) * rowb + k / 2);
-                *(uint2*)(sB + r * kPitch + c * 8) = v;
-            }
-        }
-        // ---- scales -> LDS as 8 bytes (blocks 8kt..8kt+7) per row
-#pragma unroll
-        for (int idx = t; idx < BM * 2; idx += 256) {
-            const int r = idx >> 1, g = idx & 1;
-            const int64_t row = m0 + r;
-            const int cg = kt * 2 + g;
-            uint32_t v = 0;
-            if (row < p.rpa && cg < p.cpa4)
-                v = *(const uint32_t*)(SA + ((row >> 7) * p.cpa4 + cg) * 512 + (row & 31) * 16 + ((row & 127) >> 5) * 4);
-            *(uint32_t*)(sSA + r * 8 + g * 4) = v;
-        }
-#pragma unroll
-        for (int idx = t; idx < BN * 2; idx += 256) {
-            const int r = idx >> 1, g = idx & 1;
-            const int64_t row = n0 + r;
-            const int cg = kt * 2 + g;
-            uint32_t v = 0;
-            if (row < p.rpb && cg < p.cpa4)
-                v = *(const uint32_t*)(SB + ((row >> 7) * p.cpa4 + cg) * 512 + (row & 31) * 16 + ((row & 127) >> 5) * 4);
-            *(uint32_t*)(sSB + r * 8 + g * 4) = v;
-        }
-        __syncthreads();
+        const bool more = kt + 1 < nkt;
+        if (more) stage_load<BM, BN, ALIGNED>(st, p, A, B, SA, SB, m0, n0, kt + 1, t);
+        const uint8_t* cur = smem + (kt & 1) * STAGE;
+        const uint8_t* sA = cur;
+        const uint8_t* sB = cur + OFF_B;
+        const uint8_t* sSA = cur + OFF_SA;
+        const uint8_t* sSB = cur + OFF_SB;
 
         // ---- compute: two 64-element halves, four 16-element K-slices each
 #pragma unroll
         for (int q = 0; q < 2; q++) {
             uint4 fa[FM], fb[FN];
-            uint32_t sa[FM], sb[FN];
+            f16x2 ca[FM][2], cb[FN][2];
 #pragma unroll
             for (int i = 0; i < FM; i++) {
                 const int r = wm * WM + i * 32 + l32;
                 fa[i] = *(const uint4*)(sA + r * kPitch + q * 32 + h * 16);
-                sa[i] = *(const uint16_t*)(sSA + r * 8 + q * 4 + h * 2);
+                const uint32_t s2 = *(const uint16_t*)(sSA + r * 8 + q * 4 + h * 2);
+                ca[i][0] = dup_scale_f16(s2 & 0xFFu);
+                ca[i][1] = dup_scale_f16(s2 >> 8);
             }
 #pragma unroll
             for (int i = 0; i < FN; i++) {
                 const int r = wn * WN + i * 32 + l32;
                 fb[i] = *(const uint4*)(sB + r * kPitch + q * 32 + h * 16);
-                sb[i] = *(const uint16_t*)(sSB + r * 8 + q * 4 + h * 2);
+                const uint32_t s2 = *(const uint16_t*)(sSB + r * 8 + q * 4 + h * 2);
+                cb[i][0] = dup_scale_f16(s2 & 0xFFu);
+                cb[i][1] = dup_scale_f16(s2 >> 8);
             }
 #pragma unroll
             for (int j = 0; j < 4; j++) {
@@ -185,12 +275,12 @@ __global__ __launch_bounds__(256) void k_gemm(GParams p) {
 #pragma unroll
                 for (int i = 0; i < FM; i++) {
                     const uint32_t w = j == 0 ? fa[i].x : j == 1 ? fa[i].y : j == 2 ? fa[i].z : fa[i].w;
-                    oa[i] = dequant8(w, dup_scale_f16((sa[i] >> (8 * (j >> 1))) & 0xFFu));
+                    oa[i] = dequant8(w, ca[i][j >> 1]);
                 }
 #pragma unroll
                 for (int i = 0; i < FN; i++) {
                     const uint32_t w = j == 0 ? fb[i].x : j == 1 ? fb[i].y : j == 2 ? fb[i].z : fb[i].w;
-                    ob[i] = dequant8(w, dup_scale_f16((sb[i] >> (8 * (j >> 1))) & 0xFFu));
+                    ob[i] = dequant8(w, cb[i][j >> 1]);
                 }
 #pragma unroll
                 for (int in = 0; in < FN; in++)
@@ -199,6 +289,11 @@ __global__ __launch_bounds__(256) void k_gemm(GParams p) {
                         acc[in][im] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ob[in], oa[im], acc[in][im], 0, 0, 0);
             }
         }
+        if (more) {
+            uint8_t* nxt = smem + ((kt + 1) & 1) * STAGE;
+            stage_store<BM, BN, ALIGNED>(st, p, nxt, nxt + OFF_B, nxt + OFF_SA, nxt + OFF_SB, m0, n0, kt + 1, t);
+        }
+        __syncthreads();
     }
 
     if constexpr (LORA) {

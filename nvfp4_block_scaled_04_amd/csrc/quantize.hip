@@ -18,10 +18,12 @@
 // 8 rows x 128 contiguous bytes per load.  The 512 scale bytes are gathered
 // in LDS and written with 32 16-byte stores.
 //
-// DYNAMIC mode runs three kernels on the caller's stream: a one-block clear
-// of the accumulators, the amax pass (one atomic max per workgroup on the
-// fp32 bit pattern, which orders non-negative floats, then the last workgroup
-// to finish turns each amax into gs), and the quantize pass.
+// DYNAMIC mode runs three kernels on the caller's stream: the amax pass, in
+// which every workgroup writes its partial maximum into the call's own scale
+// buffer (free until the quantize pass overwrites it; it holds at least one
+// float per amax workgroup), a one-block-per-item finish that reduces the
+// partials and writes gs, and the quantize pass.  No atomics and no
+// device-wide fences are involved.
 #include "device_common.h"
 #include "internal.h"
 
@@ -36,7 +38,6 @@ struct QParams {
     float* gs;             // [b]
     uint8_t* out_fp4;      // [b, m, K/2]
     uint8_t* out_sf;       // [b, sfsz]
-    uint32_t* counter;     // DYNAMIC: scratch word (first bytes of out_sf)
     int64_t m;             // rows per item
     int64_t K;             // quantized width
     int64_t k_in;          // input row stride in elements
@@ -44,7 +45,7 @@ struct QParams {
     int b;
     int nct;               // column tiles = ceil(K/64) = Cp/4
     int nrt;               // row tiles = ceil(m/128)
-    int total_blocks;      // amax grid size (for the finish counter)
+    int amax_blocks;       // amax workgroups per item (partials per item)
 };
 
 // silu(g) = g / (1 + e^-g), evaluated in fp64 and rounded once to fp32.
@@ -58,23 +59,43 @@ struct Chunk {
     float amax;
 };
 
-// Eight consecutive elements (row, col..col+7) of item e after the prologue
-// and nan_to_num, plus their largest magnitude.
+// Raw bytes behind eight consecutive elements: x (or the gate half) in `a`,
+// the up half (silu) or the second 16 bytes of fp32 input in `b`.
+struct Raw {
+    uint4 a, b;
+};
+
 template <int V>
-__device__ __forceinline__ Chunk load_chunk(const QParams& p, int64_t e, int64_t row, int64_t col) {
-    Chunk c;
+__device__ __forceinline__ Raw load_raw(const QParams& p, int64_t e, int64_t row, int64_t col) {
+    Raw r;
     const int64_t roff = (e * p.m + row) * p.k_in;
+    if constexpr (V == V_F32 || V == V_F32_SMOOTH) {
+        const float* xf = (const float*)p.x + roff + col;
+        r.a = *(const uint4*)xf;
+        r.b = *(const uint4*)(xf + 4);
+    } else if constexpr (V == V_SILU) {
+        const uint16_t* xb = (const uint16_t*)p.x + roff;
+        r.a = *(const uint4*)(xb + col);
+        r.b = *(const uint4*)(xb + p.K + col);
+    } else {
+        r.a = *(const uint4*)((const uint16_t*)p.x + roff + col);
+        r.b = uint4{0u, 0u, 0u, 0u};
+    }
+    return r;
+}
+
+// Eight elements after the prologue and nan_to_num, plus their largest
+// magnitude.  pq holds the eight pre_quant_scale values (smooth variants).
+template <int V>
+__device__ __forceinline__ Chunk process(const Raw& raw, const uint4& pq) {
+    Chunk c;
     if constexpr (V == V_BF16 || V == V_SILU) {
         uint32_t w[4];
         if constexpr (V == V_BF16) {
-            uint4 v = *(const uint4*)((const uint16_t*)p.x + roff + col);
-            w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+            w[0] = raw.a.x; w[1] = raw.a.y; w[2] = raw.a.z; w[3] = raw.a.w;
         } else {
-            const uint16_t* xb = (const uint16_t*)p.x;
-            uint4 gv = *(const uint4*)(xb + roff + col);
-            uint4 uv = *(const uint4*)(xb + roff + p.K + col);
-            uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
-            uint32_t uw[4] = {uv.x, uv.y, uv.z, uv.w};
+            const uint32_t gw[4] = {raw.a.x, raw.a.y, raw.a.z, raw.a.w};
+            const uint32_t uw[4] = {raw.b.x, raw.b.y, raw.b.z, raw.b.w};
 #pragma unroll
             for (int j = 0; j < 4; j++) {
                 float h0 = silu_f32(bf16_lo(gw[j])) * bf16_lo(uw[j]);
@@ -100,16 +121,12 @@ __device__ __forceinline__ Chunk load_chunk(const QParams& p, int64_t e, int64_t
             c.amax = bits_f(mb << 16);
         }
     } else {
-        uint32_t bad = 0;
         if constexpr (V == V_F32 || V == V_F32_SMOOTH) {
-            const float* xf = (const float*)p.x + roff + col;
-            float4 v0 = *(const float4*)xf;
-            float4 v1 = *(const float4*)(xf + 4);
-            c.f[0] = v0.x; c.f[1] = v0.y; c.f[2] = v0.z; c.f[3] = v0.w;
-            c.f[4] = v1.x; c.f[5] = v1.y; c.f[6] = v1.z; c.f[7] = v1.w;
+            const uint32_t w[8] = {raw.a.x, raw.a.y, raw.a.z, raw.a.w, raw.b.x, raw.b.y, raw.b.z, raw.b.w};
+#pragma unroll
+            for (int j = 0; j < 8; j++) c.f[j] = bits_f(w[j]);
         } else {
-            uint4 v = *(const uint4*)((const uint16_t*)p.x + roff + col);
-            uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            const uint32_t w[4] = {raw.a.x, raw.a.y, raw.a.z, raw.a.w};
 #pragma unroll
             for (int j = 0; j < 4; j++) {
                 c.f[2 * j] = bf16_lo(w[j]);
@@ -117,14 +134,14 @@ __device__ __forceinline__ Chunk load_chunk(const QParams& p, int64_t e, int64_t
             }
         }
         if constexpr (V == V_BF16_SMOOTH || V == V_F32_SMOOTH) {
-            uint4 pv = *(const uint4*)(p.pqs + col);
-            uint32_t pw[4] = {pv.x, pv.y, pv.z, pv.w};
+            const uint32_t pw[4] = {pq.x, pq.y, pq.z, pq.w};
 #pragma unroll
             for (int j = 0; j < 4; j++) {
                 c.f[2 * j] = c.f[2 * j] * bf16_lo(pw[j]);
                 c.f[2 * j + 1] = c.f[2 * j + 1] * bf16_hi(pw[j]);
             }
         }
+        uint32_t bad = 0;
         float a = 0.0f;
 #pragma unroll
         for (int j = 0; j < 8; j++) {
@@ -144,33 +161,61 @@ __device__ __forceinline__ Chunk load_chunk(const QParams& p, int64_t e, int64_t
     return c;
 }
 
-// ---------------------------------------------------------------------------
-// DYNAMIC mode: clear, amax (+ finish), then quantize.
-// ---------------------------------------------------------------------------
-
-__global__ void k_clear_dynamic(float* gs, int b, uint32_t* counter) {
-    for (int i = threadIdx.x; i < b; i += blockDim.x) gs[i] = 0.0f;
-    if (threadIdx.x == 0) *counter = 0u;
+template <int V>
+__device__ __forceinline__ uint4 load_pqs(const QParams& p, int64_t col) {
+    if constexpr (V == V_BF16_SMOOTH || V == V_F32_SMOOTH) return *(const uint4*)(p.pqs + col);
+    return uint4{0u, 0u, 0u, 0u};
 }
 
-template <int V>
+// ---------------------------------------------------------------------------
+// DYNAMIC mode: amax partials, finish, then quantize.
+// ---------------------------------------------------------------------------
+
+// Thread layout of a workgroup tile of 128 rows x CT*64 columns (CT 64-column
+// swizzle tiles): LPR = 8*CT lanes cover a row segment (8 elements each, a
+// lane pair per 16-element block), RPP = 256/LPR rows are covered per pass,
+// NP = 128/RPP passes.  A wave reads 64/LPR rows x 16*LPR contiguous bytes.
+template <int CT>
+struct TileMap {
+    static constexpr int LPR = 8 * CT;
+    static constexpr int RPP = 256 / LPR;
+    static constexpr int NP = 128 / RPP;
+};
+
+// Partial maxima of item e live at the start of its scale buffer.
+__device__ __forceinline__ float* partials(const QParams& p, int e) {
+    return (float*)(p.out_sf + (int64_t)e * p.sfsz);
+}
+
+template <int V, int CT>
 __global__ __launch_bounds__(256) void k_amax(QParams p) {
+    using TM = TileMap<CT>;
     const int e = blockIdx.y;
     const int t = threadIdx.x;
-    const int rho = t >> 3, l8 = t & 7;
+    const int rsub = t / TM::LPR, lane = t % TM::LPR;
     const int valid = clamp_rows(p.mask, e, (int)p.m);
-    const int ntiles = p.nrt * p.nct;
+    const int nwct = (p.nct + CT - 1) / CT;
+    const int ntiles = p.nrt * nwct;
     float amax = 0.0f;
     for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-        const int rt = tile / p.nct, ct = tile - rt * p.nct;
-        const int64_t col = (int64_t)ct * 64 + l8 * 8;
-        if (col >= p.K) continue;
+        const int rt = tile / nwct, wct = tile - rt * nwct;
+        if ((int64_t)rt * 128 >= valid) continue;  // tile entirely past the valid rows
+        int64_t col = (int64_t)wct * 64 * CT + lane * 8;
+        const bool col_ok = col < p.K;
+        col = col_ok ? col : p.K - 8;
+        const uint4 pq = load_pqs<V>(p, col);
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int64_t row = (int64_t)rt * 128 + rho + 32 * i;
-            if (row < valid) {
-                Chunk c = load_chunk<V>(p, e, row, col);
-                amax = __builtin_fmaxf(amax, c.amax);
+        for (int i0 = 0; i0 < TM::NP; i0 += 4) {
+            Raw raw[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {  // four loads in flight before any use
+                const int64_t row = (int64_t)rt * 128 + rsub + TM::RPP * (i0 + i);
+                raw[i] = load_raw<V>(p, e, row < p.m ? row : p.m - 1, col);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int64_t row = (int64_t)rt * 128 + rsub + TM::RPP * (i0 + i);
+                if (col_ok && row < valid) amax = __builtin_fmaxf(amax, process<V>(raw[i], pq).amax);
             }
         }
     }
@@ -180,67 +225,93 @@ __global__ __launch_bounds__(256) void k_amax(QParams p) {
     __shared__ float wmax[4];
     if ((t & 63) == 0) wmax[t >> 6] = amax;
     __syncthreads();
+    if (t == 0)
+        partials(p, e)[blockIdx.x] =
+            __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
+}
+
+// gs[e] = 2688 / max(amax_e, 1e-12) from item e's partial maxima.
+__global__ __launch_bounds__(256) void k_finish_gs(QParams p) {
+    const int e = blockIdx.x, t = threadIdx.x;
+    const float* part = partials(p, e);
+    float a = 0.0f;
+    for (int i = t; i < p.amax_blocks; i += 256) a = __builtin_fmaxf(a, part[i]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) a = __builtin_fmaxf(a, __shfl_xor(a, off));
+    __shared__ float wmax[4];
+    if ((t & 63) == 0) wmax[t >> 6] = a;
+    __syncthreads();
     if (t == 0) {
-        float a = __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
-        atomicMax((unsigned int*)&p.gs[e], f_bits(a));
-        __threadfence();
-        unsigned int done = atomicAdd(p.counter, 1u);
-        if (done == (unsigned int)p.total_blocks - 1u) {
-            // last workgroup: every amax is final; turn each into gs
-            __threadfence();
-            for (int i = 0; i < p.b; i++) {
-                float am = bits_f(atomicOr((unsigned int*)&p.gs[i], 0u));
-                const float lo = 1e-12f;
-                p.gs[i] = 2688.0f / (am < lo ? lo : am);
-            }
-        }
+        const float am = __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
+        const float lo = 1e-12f;
+        p.gs[e] = 2688.0f / (am < lo ? lo : am);
     }
 }
 
-template <int V>
+template <int V, int CT>
 __global__ __launch_bounds__(256) void k_quantize(QParams p) {
-    const int ct = blockIdx.x, rt = blockIdx.y, e = blockIdx.z;
+    using TM = TileMap<CT>;
+    const int wct = blockIdx.x, rt = blockIdx.y, e = blockIdx.z;
     const int t = threadIdx.x;
-    const int rho = t >> 3, l8 = t & 7;
+    const int rsub = t / TM::LPR, lane = t % TM::LPR;
+    const int c = lane >> 3;                 // swizzle tile within the workgroup
+    const int blk = (lane & 7) >> 1;         // 16-element block within that tile
     const int valid = clamp_rows(p.mask, e, (int)p.m);
     const float gs = p.gs[e];
-    const int64_t col = (int64_t)ct * 64 + l8 * 8;
+    int64_t col = (int64_t)wct * 64 * CT + lane * 8;
     const bool col_ok = col < p.K;
-    __shared__ __align__(16) uint8_t sbuf[512];
+    col = col_ok ? col : p.K - 8;
+    __shared__ __align__(16) uint8_t sbuf[512 * CT];
     uint8_t* q = p.out_fp4 + (int64_t)e * p.m * (p.K / 2);
+    // swizzle tiles this workgroup owns that exist in the buffer
+    const int ntile_here = (p.nct - wct * CT) < CT ? (p.nct - wct * CT) : CT;
+    uint8_t* sf_dst = p.out_sf + (int64_t)e * p.sfsz + ((int64_t)rt * p.nct + (int64_t)wct * CT) * 512;
 
+    if ((int64_t)rt * 128 >= valid) {  // tile entirely past the valid rows: zero scales only
+        for (int i = t; i < ntile_here * 32; i += 256) *(uint4*)(sf_dst + i * 16) = uint4{0u, 0u, 0u, 0u};
+        return;
+    }
+    const uint4 pq = load_pqs<V>(p, col);
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int64_t row = (int64_t)rt * 128 + rho + 32 * i;
-        const bool active = col_ok && row < valid;
-        Chunk c;
-        if (active) {
-            c = load_chunk<V>(p, e, row, col);
-        } else {
+    for (int i0 = 0; i0 < TM::NP; i0 += 4) {
+        Raw raw[4];
 #pragma unroll
-            for (int j = 0; j < 8; j++) c.f[j] = 0.0f;
-            c.amax = 0.0f;
+        for (int i = 0; i < 4; i++) {  // four loads in flight before any use
+            const int64_t row = (int64_t)rt * 128 + rsub + TM::RPP * (i0 + i);
+            raw[i] = load_raw<V>(p, e, row < p.m ? row : p.m - 1, col);
         }
-        // block amax over the lane pair sharing this 16-element block
-        const float bamax = __builtin_fmaxf(c.amax, xor1(c.amax));
-        const uint32_t s = ue4m3_encode((bamax / 6.0f) * gs);
-        const float dec = ue4m3_decode(s);
-        const float r = dec == 0.0f ? 0.0f : gs / dec;
-        if (active) {
-            uint32_t w = 0;
-            w = NVFP4_PACK_FP4(w, c.f[0] * r, c.f[1] * r, 0);
-            w = NVFP4_PACK_FP4(w, c.f[2] * r, c.f[3] * r, 1);
-            w = NVFP4_PACK_FP4(w, c.f[4] * r, c.f[5] * r, 2);
-            w = NVFP4_PACK_FP4(w, c.f[6] * r, c.f[7] * r, 3);
-            *(uint32_t*)(q + row * (p.K / 2) + col / 2) = w;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int rl = rsub + TM::RPP * (i0 + i);       // row within the 128-row tile
+            const int64_t row = (int64_t)rt * 128 + rl;
+            const bool active = col_ok && row < valid;
+            Chunk ch;
+            if (active) {
+                ch = process<V>(raw[i], pq);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; j++) ch.f[j] = 0.0f;
+                ch.amax = 0.0f;
+            }
+            // block amax over the lane pair sharing this 16-element block
+            const float bamax = __builtin_fmaxf(ch.amax, xor1(ch.amax));
+            const uint32_t sc = ue4m3_encode((bamax / 6.0f) * gs);
+            const float dec = ue4m3_decode(sc);
+            const float r = dec == 0.0f ? 0.0f : gs / dec;
+            if (active) {
+                uint32_t w = 0;
+                w = NVFP4_PACK_FP4(w, ch.f[0] * r, ch.f[1] * r, 0);
+                w = NVFP4_PACK_FP4(w, ch.f[2] * r, ch.f[3] * r, 1);
+                w = NVFP4_PACK_FP4(w, ch.f[4] * r, ch.f[5] * r, 2);
+                w = NVFP4_PACK_FP4(w, ch.f[6] * r, ch.f[7] * r, 3);
+                *(uint32_t*)(q + row * (p.K / 2) + col / 2) = w;
+            }
+            if ((lane & 1) == 0)
+                sbuf[c * 512 + (rl & 31) * 16 + (rl >> 5) * 4 + blk] = active ? (uint8_t)sc : (uint8_t)0;
         }
-        if ((l8 & 1) == 0) sbuf[rho * 16 + i * 4 + (l8 >> 1)] = active ? (uint8_t)s : (uint8_t)0;
     }
     __syncthreads();
-    if (t < 32) {
-        uint8_t* dst = p.out_sf + (int64_t)e * p.sfsz + ((int64_t)rt * p.nct + ct) * 512 + t * 16;
-        *(uint4*)dst = *(const uint4*)(sbuf + t * 16);
-    }
+    for (int i = t; i < ntile_here * 32; i += 256) *(uint4*)(sf_dst + i * 16) = *(const uint4*)(sbuf + i * 16);
 }
 
 __global__ void k_alpha(const float* ga, const float* gb, float* alpha, int64_t n) {
@@ -252,21 +323,24 @@ __global__ void k_alpha(const float* ga, const float* gb, float* alpha, int64_t 
 // host-side launch
 // ---------------------------------------------------------------------------
 
+// 64-column swizzle tiles per workgroup: two for the memory-bound variants
+// (longer contiguous row segments per wave); one for the silu variant, whose
+// fp64 silu makes it compute-heavy, so more workgroups pay off (measured).
+template <int V>
+constexpr int quant_ct() { return V == V_SILU ? 1 : 2; }
+
 template <int V>
 static hipError_t launch_variant(QParams p, bool dynamic, hipStream_t st) {
+    constexpr int CT = quant_ct<V>();
     if (dynamic) {
-        k_clear_dynamic<<<1, 256, 0, st>>>(p.gs, p.b, p.counter);
-        int ntiles = p.nrt * p.nct;
-        int g = ntiles < 1024 ? ntiles : 1024;
-        if (p.b > 1) {
-            int per = (2048 + p.b - 1) / p.b;
-            g = ntiles < per ? ntiles : per;
-        }
-        if (g < 1) g = 1;
-        p.total_blocks = g * p.b;
-        k_amax<V><<<dim3(g, p.b), 256, 0, st>>>(p);
+        const int ntiles = p.nrt * ((p.nct + CT - 1) / CT);
+        int g = (1024 + p.b - 1) / p.b;
+        g = g < ntiles ? g : ntiles;
+        p.amax_blocks = g < 1 ? 1 : g;
+        k_amax<V, CT><<<dim3(p.amax_blocks, p.b), 256, 0, st>>>(p);
+        k_finish_gs<<<p.b, 256, 0, st>>>(p);
     }
-    k_quantize<V><<<dim3(p.nct, p.nrt, p.b), 256, 0, st>>>(p);
+    k_quantize<V, CT><<<dim3((p.nct + CT - 1) / CT, p.nrt, p.b), 256, 0, st>>>(p);
     return hipGetLastError();
 }
 
@@ -278,7 +352,6 @@ hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t st) {
     p.gs = a.gs;
     p.out_fp4 = a.out_fp4;
     p.out_sf = a.out_sf;
-    p.counter = (uint32_t*)a.out_sf;
     p.m = a.m;
     p.K = a.silu ? a.k_in / 2 : a.k_in;
     p.k_in = a.k_in;
