@@ -25,7 +25,7 @@
  *         alpha*(a@b^T) + d@l1^T [+bias]; a,b (rows, k/2) uint8 packed e2m1;
  *         ue4m3 scales in the 128x4 swizzled layout; l1 pre-divided by alpha.
  *
- * Readings where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *   - e2m1 and ue4m3 encoders round to nearest, ties to the even code, and
  *     saturate (6 and 448); the sign of zero is kept for e2m1.
  *   - ue4m3 is the OCP e4m3 bit layout with the sign bit 0 (bias 7,
