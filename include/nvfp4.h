@@ -136,7 +136,9 @@ int silu_mul_nvfp4_quantize(const void *x, int64_t b, int64_t m, int64_t k2,
  *   a: [m, k/2], b: [n, k/2], a_sf / b_sf: swizzled scales of a / b.
  *   alpha: device fp32 scalar (numel >= 1).  bias: NULL or [n] bf16.
  *   out: [m, n] bf16, row-major.  Accumulation is fp32.
- * Requires m, n >= 1, k >= 16, k % 16 == 0.
+ * Requires m, n >= 1, k >= 16, k % 16 == 0.  Returns NVFP4_UNSUPPORTED when
+ * an FP4 operand (per expert, for the grouped form) spans more than
+ * 2^32 - 64 bytes (the kernels address a matrix with 32-bit offsets).
  */
 int nvfp4_gemm(const uint8_t *a, const uint8_t *b, const uint8_t *a_sf, const uint8_t *b_sf,
                const float *alpha, const void *bias, void *out,

@@ -89,6 +89,8 @@ static int gemm_common(const uint8_t* a, const uint8_t* b, const uint8_t* a_sf, 
     if (!dim_ok(E) || !dim_ok(m) || !dim_ok(n) || k < 16 || k % 16 != 0 || k > kMaxDim)
         return NVFP4_BAD_SHAPE;
     if (E > 65535 || ((m + 63) / 64) * ((n + 63) / 64) > ((int64_t)1 << 31) - 1) return NVFP4_BAD_SHAPE;
+    // the GEMM kernels address one FP4 matrix with 32-bit byte offsets
+    if (m * (k / 2) > ((int64_t)1 << 32) - 64 || n * (k / 2) > ((int64_t)1 << 32) - 64) return NVFP4_UNSUPPORTED;
     if (!aligned16(a) || !aligned16(b) || !aligned16(a_sf) || !aligned16(b_sf) || !aligned16(out) ||
         ((uintptr_t)alpha & 3u) || (bias && !aligned16(bias)) || (d && !aligned16(d)) ||
         (l1 && !aligned16(l1)) || ((uintptr_t)mask & 3u))

@@ -21,17 +21,28 @@
 //
 // Tiling: a 256-thread workgroup computes a BM x BN tile, 2 x 2 waves of
 // (BM/2) x (BN/2), each wave a grid of 32 x 32 MFMA fragments.  K advances
-// 128 elements (64 bytes of a row) per step; the FP4 tiles and their scales
-// are staged in LDS.  Within a 64-element half-step, lane l of a fragment
-// (row l%32, half h = l/32) owns the 32 consecutive elements 32h.. of its
-// row: one 16-byte LDS read, two block scales, four MFMA K-slices.  The same
-// K permutation is used for both operands, so the contraction is unchanged.
-// The MFMA's first operand is the B fragment and its second the A fragment,
-// which puts 4 consecutive output columns of one output row in each lane.
+// 128 elements (64 bytes of a row) per step.  A step's FP4 rows and raw scale
+// bytes go from global memory straight into LDS (buffer loads with the LDS
+// bit: no registers), three stages deep, so a step's loads are issued two
+// steps before it is consumed.  Within a 64-element half step q, lane l of a
+// fragment (row l%32, half h = l/32) owns the 32 consecutive elements
+// 64q+32h.. of its row: one 16-byte LDS read, two block scales, four MFMA
+// K-slices.  The same K permutation is used for both operands, so the
+// contraction is unchanged.  The dequantization of slice s+1 is issued
+// between the MFMAs of slice s, and the MFMAs of a step's last slice run
+// after the step barrier, next to the next step's first LDS reads.  The
+// MFMA's first operand is the B fragment and its second the A fragment, which
+// puts 4 consecutive output columns of one output row in each lane.
 #include "device_common.h"
 #include "internal.h"
 
 namespace nvfp4 {
+
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+// native vectors (not HIP's struct types) keep loaded values in registers
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 struct GParams {
     const uint8_t* a;
@@ -47,181 +58,161 @@ struct GParams {
     int64_t M, N, K, r, E;
     int64_t sfa, sfb;    // per-expert scale buffer bytes
     int cpa4;            // column groups of the scale layout = pad_up(K/16,4)/4
+    int nblk;            // 16-element blocks per row = K/16
     int rpa, rpb;        // padded rows of the scale buffers
     int tiles_m, tiles_n;
+    int xcd_chunk;       // tiles per XCD when the tile count splits evenly over 8, else 0
 };
 
-constexpr int kPitch = 80;  // LDS row pitch of a 64-byte FP4 row (+16 avoids bank conflicts)
-
-__device__ __forceinline__ f16x2 dup_scale_f16(uint32_t code) {
-    _Float16 h = (_Float16)ue4m3_decode(code);
-    return f16x2{h, h};
+// Raw buffer resource (gfx9 word 3: 32-bit untyped records).  Loads past
+// `bytes` return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// s_waitcnt immediate waiting until at most N vector-memory operations are
+// outstanding, other counters unconstrained (gfx9 encoding: vmcnt bits 3:0
+// and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// LDS layout of a staged FP4 tile: rows of 64 bytes (the 128 elements of one
+// K step); 16-byte chunk c of row r sits in slot c ^ swz(r).  A wave's staging
+// load covers 16 whole rows (1 KB, contiguous), and a fragment read (32
+// consecutive rows, one chunk each) touches every bank group once per 8 or 16
+// lanes.  The scale region follows: row t of the tile (A rows, then B rows)
+// holds its two raw scale dwords (blocks 0-3, 4-7 of the step) at 8t.
+__device__ __forceinline__ int swz(int r) { return ((r >> 2) ^ (r & 2)) & 3; }
+
 // 8 FP4 codes of one dword times one block scale -> 8 fp16 (exact).
-__device__ __forceinline__ f16x8 dequant8(uint32_t w, f16x2 s) {
-    f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
-    f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
-    f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s;
-    f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s;
+__device__ __forceinline__ f16x8 dequant8(uint32_t w, _Float16 s) {
+    const f16x2 ss = f16x2{s, s};
+    const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * ss;
+    const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * ss;
+    const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * ss;
+    const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * ss;
     return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-// Global -> register staging of one K step (128 elements) of the A and B
-// tiles and their scales.  Addresses are clamped into the buffers so every
-// load is issued unconditionally (all of them stay in flight together);
-// values from rows or K blocks outside the matrix are zeroed when stored.
-template <int BM, int BN, bool ALIGNED>
-struct Stage {
-    static constexpr int CH = ALIGNED ? 16 : 8;          // bytes per chunk
-    static constexpr int CPR = 64 / CH;                  // chunks per row
-    static constexpr int NA = (BM * CPR + 255) / 256;    // A chunks per thread
-    static constexpr int NB = (BN * CPR + 255) / 256;
-    static constexpr int NSA = (BM * 2 + 255) / 256;     // A scale dwords per thread
-    static constexpr int NSB = (BN * 2 + 255) / 256;
-    uint4 ra[NA], rb[NB];
-    uint32_t sa[NSA], sb[NSB];
-};
-
-template <int BM, int BN, bool ALIGNED>
-__device__ __forceinline__ void stage_load(Stage<BM, BN, ALIGNED>& st, const GParams& p,
-                                           const uint8_t* A, const uint8_t* B,
-                                           const uint8_t* SA, const uint8_t* SB,
-                                           int64_t m0, int64_t n0, int kt, int t) {
-    using S = Stage<BM, BN, ALIGNED>;
-    const int64_t rowb = p.K / 2;
-#pragma unroll
-    for (int i = 0; i < S::NA; i++) {
-        const int idx = t + 256 * i;
-        const int r = idx / S::CPR, c = idx % S::CPR;
-        int64_t row = m0 + r;
-        row = row < p.M ? row : p.M - 1;
-        if constexpr (ALIGNED) {
-            st.ra[i] = *(const uint4*)(A + row * rowb + kt * 64 + c * 16);
-        } else {
-            int64_t kb = (int64_t)kt * 64 + c * 8;
-            kb = kb < rowb ? kb : rowb - 8;
-            uint2 v = *(const uint2*)(A + row * rowb + kb);
-            st.ra[i] = uint4{v.x, v.y, 0u, 0u};
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < S::NB; i++) {
-        const int idx = t + 256 * i;
-        const int r = idx / S::CPR, c = idx % S::CPR;
-        int64_t row = n0 + r;
-        row = row < p.N ? row : p.N - 1;
-        if constexpr (ALIGNED) {
-            st.rb[i] = *(const uint4*)(B + row * rowb + kt * 64 + c * 16);
-        } else {
-            int64_t kb = (int64_t)kt * 64 + c * 8;
-            kb = kb < rowb ? kb : rowb - 8;
-            uint2 v = *(const uint2*)(B + row * rowb + kb);
-            st.rb[i] = uint4{v.x, v.y, 0u, 0u};
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < S::NSA; i++) {
-        const int idx = (t + 256 * i) % (BM * 2);
-        const int r = idx >> 1, g = idx & 1;
-        int64_t row = m0 + r;
-        row = row < p.rpa ? row : p.rpa - 1;
-        int cg = kt * 2 + g;
-        cg = cg < p.cpa4 ? cg : p.cpa4 - 1;
-        st.sa[i] = *(const uint32_t*)(SA + ((row >> 7) * p.cpa4 + cg) * 512 + (row & 31) * 16 + ((row & 127) >> 5) * 4);
-    }
-#pragma unroll
-    for (int i = 0; i < S::NSB; i++) {
-        const int idx = (t + 256 * i) % (BN * 2);
-        const int r = idx >> 1, g = idx & 1;
-        int64_t row = n0 + r;
-        row = row < p.rpb ? row : p.rpb - 1;
-        int cg = kt * 2 + g;
-        cg = cg < p.cpa4 ? cg : p.cpa4 - 1;
-        st.sb[i] = *(const uint32_t*)(SB + ((row >> 7) * p.cpa4 + cg) * 512 + (row & 31) * 16 + ((row & 127) >> 5) * 4);
-    }
+__device__ __forceinline__ uint32_t word(const u32x4& v, int j) {
+    return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
 }
 
-template <int BM, int BN, bool ALIGNED>
-__device__ __forceinline__ void stage_store(const Stage<BM, BN, ALIGNED>& st, const GParams& p,
-                                            uint8_t* sA, uint8_t* sB, uint8_t* sSA, uint8_t* sSB,
-                                            int64_t m0, int64_t n0, int kt, int t) {
-    using S = Stage<BM, BN, ALIGNED>;
-#pragma unroll
-    for (int i = 0; i < S::NA; i++) {
-        const int idx = t + 256 * i;
-        if (S::NA * 256 > BM * S::CPR && idx >= BM * S::CPR) break;
-        const int r = idx / S::CPR, c = idx % S::CPR;
-        bool ok = m0 + r < p.M;
-        if constexpr (ALIGNED) {
-            uint4 v = st.ra[i];
-            if (!ok) v = uint4{0u, 0u, 0u, 0u};
-            *(uint4*)(sA + r * kPitch + c * 16) = v;
-        } else {
-            ok = ok && (int64_t)kt * 128 + c * 16 < p.K;
-            uint2 v = uint2{st.ra[i].x, st.ra[i].y};
-            if (!ok) v = uint2{0u, 0u};
-            *(uint2*)(sA + r * kPitch + c * 8) = v;
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < S::NB; i++) {
-        const int idx = t + 256 * i;
-        if (S::NB * 256 > BN * S::CPR && idx >= BN * S::CPR) break;
-        const int r = idx / S::CPR, c = idx % S::CPR;
-        bool ok = n0 + r < p.N;
-        if constexpr (ALIGNED) {
-            uint4 v = st.rb[i];
-            if (!ok) v = uint4{0u, 0u, 0u, 0u};
-            *(uint4*)(sB + r * kPitch + c * 16) = v;
-        } else {
-            ok = ok && (int64_t)kt * 128 + c * 16 < p.K;
-            uint2 v = uint2{st.rb[i].x, st.rb[i].y};
-            if (!ok) v = uint2{0u, 0u};
-            *(uint2*)(sB + r * kPitch + c * 8) = v;
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < S::NSA; i++) {
-        const int idx = t + 256 * i;
-        if (idx >= BM * 2) break;
-        const int r = idx >> 1, g = idx & 1;
-        const bool ok = m0 + r < p.rpa && kt * 2 + g < p.cpa4;
-        *(uint32_t*)(sSA + r * 8 + g * 4) = ok ? st.sa[i] : 0u;
-    }
-#pragma unroll
-    for (int i = 0; i < S::NSB; i++) {
-        const int idx = t + 256 * i;
-        if (idx >= BN * 2) break;
-        const int r = idx >> 1, g = idx & 1;
-        const bool ok = n0 + r < p.rpb && kt * 2 + g < p.cpa4;
-        *(uint32_t*)(sSB + r * 8 + g * 4) = ok ? st.sb[i] : 0u;
-    }
+// Byte offset of scale dword (row, column group cg) in the swizzled layout.
+__device__ __forceinline__ uint32_t scale_dword_off(int64_t row, int cg, int cpa4) {
+    return (uint32_t)(((row >> 7) * cpa4 + cg) * 512 + (row & 31) * 16 + ((row & 127) >> 5) * 4);
 }
 
-template <int BM, int BN, bool ALIGNED, bool LORA>
-__global__ __launch_bounds__(256) void k_gemm(GParams p) {
+// Tile coordinates of this workgroup.  Workgroups are dealt to the 8 XCDs
+// round-robin; when the tile count splits evenly, XCD x is given the x-th
+// contiguous eighth of the tile order, and within it tiles advance down
+// groups of 8 tile rows, so the workgroups that run together on one XCD share
+// A and B panels in that XCD's L2.
+__device__ __forceinline__ void tile_coords(const GParams& p, int& tm, int& tn) {
+    int L = blockIdx.x;
+    if (p.xcd_chunk) L = (L & 7) * p.xcd_chunk + (L >> 3);
+    constexpr int G = 8;
+    const int per_group = G * p.tiles_n;
+    const int grp = L / per_group;
+    const int first = grp * G;
+    const int rows = p.tiles_m - first < G ? p.tiles_m - first : G;
+    const int in = L - grp * per_group;
+    tm = first + in % rows;
+    tn = in / rows;
+}
+
+// Waves per SIMD each tile is compiled for: the 256x256 tile takes the whole
+// register file (256 accumulators per lane); the smaller tiles are held to
+// 256 registers so at least two workgroups share a CU.
+template <int BM, int BN>
+constexpr int kWavesPerEU = BM * BN >= 65536 ? 1 : 2;
+
+template <int BM, int BN, int NST, bool ALIGNED, bool LORA>
+__global__ __launch_bounds__(256, (kWavesPerEU<BM, BN>)) void k_gemm(GParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
     constexpr int WM = BM / 2, WN = BN / 2;
     constexpr int FM = WM / 32, FN = WN / 32;
-    constexpr int OFF_B = BM * kPitch, OFF_SA = OFF_B + BN * kPitch, OFF_SB = OFF_SA + BM * 8;
-    constexpr int STAGE = OFF_SB + BN * 8;
-    __shared__ __align__(16) uint8_t smem[2 * STAGE];
+    // one LDS stage: FP4 A rows, FP4 B rows, raw scale dwords (padded to whole
+    // wave loads of 64 dwords per wave)
+    constexpr int OFF_B = BM * 64, OFF_S = OFF_B + BN * 64;
+    constexpr int SC_DW = ((BM + BN) * 2 + 255) / 256 * 256;
+    constexpr int STAGE = OFF_S + SC_DW * 4;
+    constexpr int NFA = BM / 64, NFB = BN / 64, NSC = SC_DW / 256;  // loads per wave per step
+    constexpr int ND = NFA + NFB + NSC;
+    static_assert(BM % 64 == 0 && BN % 64 == 0, "whole 16-row blocks per wave");
+    static_assert(NST == 2 || NST == 3, "two or three LDS stages");
+    __shared__ __align__(16) uint8_t smem[NST * STAGE];
 
     const int t = threadIdx.x;
-    const int lane = t & 63, wave = t >> 6;
+    const int lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int wm = wave & 1, wn = wave >> 1;
     const int e = blockIdx.z;
-    const int tile = blockIdx.x;
-    const int tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
+    int tm, tn;
+    tile_coords(p, tm, tn);
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
     const int valid = clamp_rows(p.mask, e, (int)p.M);
     if (m0 >= valid) return;  // whole tile past this expert's valid rows
 
     const int64_t rowb = p.K / 2;
-    const uint8_t* A = p.a + (int64_t)e * p.M * rowb;
-    const uint8_t* B = p.b + (int64_t)e * p.N * rowb;
-    const uint8_t* SA = p.a_sf + (int64_t)e * p.sfa;
-    const uint8_t* SB = p.b_sf + (int64_t)e * p.sfb;
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.a + (int64_t)e * p.M * rowb, (uint32_t)(p.M * rowb));
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.b + (int64_t)e * p.N * rowb, (uint32_t)(p.N * rowb));
+    const __amdgpu_buffer_rsrc_t rSA = make_rsrc(p.a_sf + (int64_t)e * p.sfa, (uint32_t)p.sfa);
+    const __amdgpu_buffer_rsrc_t rSB = make_rsrc(p.b_sf + (int64_t)e * p.sfb, (uint32_t)p.sfb);
+
+    // Per-lane source offsets of this wave's staging loads (the step adds a
+    // uniform 64 bytes of FP4 or 1024 bytes of scales per K step).  Lane l of
+    // a 16-row FP4 load lands at byte 16*l of its 1 KB block: row l/4, slot
+    // l%4, so it fetches chunk slot ^ swz(row).  Rows past the matrix read its
+    // last row; they feed only outputs that are never stored.
+    uint32_t voA[NFA], voB[NFB], voS[NSC];
+#pragma unroll
+    for (int i = 0; i < NFA; i++) {
+        const int r = (i * 4 + wave) * 16 + (lane >> 2);
+        const int64_t row = m0 + r < p.M ? m0 + r : p.M - 1;
+        voA[i] = (uint32_t)(row * rowb) + (uint32_t)((((lane & 3) ^ swz(r)) << 4));
+    }
+#pragma unroll
+    for (int i = 0; i < NFB; i++) {
+        const int r = (i * 4 + wave) * 16 + (lane >> 2);
+        const int64_t row = n0 + r < p.N ? n0 + r : p.N - 1;
+        voB[i] = (uint32_t)(row * rowb) + (uint32_t)((((lane & 3) ^ swz(r)) << 4));
+    }
+#pragma unroll
+    for (int i = 0; i < NSC; i++) {
+        const int dw = (i * 4 + wave) * 64 + lane;  // scale dword of the stage
+        const int tr = dw >> 1, g = dw & 1;         // tile row, column group of the step
+        if (tr < BM) {
+            const int64_t row = m0 + tr < p.rpa ? m0 + tr : p.rpa - 1;
+            voS[i] = scale_dword_off(row, g, p.cpa4);
+        } else if (tr < BM + BN) {
+            const int64_t row = n0 + (tr - BM) < p.rpb ? n0 + (tr - BM) : p.rpb - 1;
+            voS[i] = scale_dword_off(row, g, p.cpa4);
+        } else {
+            voS[i] = 0;  // padding dwords: any in-bounds source
+        }
+    }
+    lds_u8* const sm = (lds_u8*)smem;
+    auto issue = [&](int step, lds_u8* st) {
+#pragma unroll
+        for (int i = 0; i < NFA; i++)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (__attribute__((address_space(3))) void*)(st + (i * 4 + wave) * 1024),
+                                                     16, voA[i], step * 64, 0, 0);
+#pragma unroll
+        for (int i = 0; i < NFB; i++)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (__attribute__((address_space(3))) void*)(st + OFF_B + (i * 4 + wave) * 1024),
+                                                     16, voB[i], step * 64, 0, 0);
+#pragma unroll
+        for (int i = 0; i < NSC; i++) {
+            const bool isA = (i * 4 + wave) * 32 < BM;  // a wave load covers 32 tile rows: all A or all B
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? rSA : rSB,
+                                                     (__attribute__((address_space(3))) void*)(st + OFF_S + (i * 4 + wave) * 256),
+                                                     4, voS[i], step * 1024, 0, 0);
+        }
+    };
 
     f32x16 acc[FN][FM];
 #pragma unroll
@@ -233,68 +224,137 @@ __global__ __launch_bounds__(256) void k_gemm(GParams p) {
 
     const int nkt = (int)((p.K + 127) / 128);
     const int h = lane >> 5, l32 = lane & 31;
+    // per-lane LDS offsets, fixed for the whole K loop (fragment i adds i*32 rows)
+    const int ra_off = (wm * WM + l32) * 64, rb_off = OFF_B + (wn * WN + l32) * 64;
+    const int xr = swz(l32);
+    const int cq0 = ((h ^ xr) << 4), cq1 = (((2 + h) ^ xr) << 4);
+    const int sa_off = OFF_S + (wm * WM + l32) * 8;
+    const int sb_off = OFF_S + (BM + wn * WN + l32) * 8;
+    const int hsh = 16 * h;  // this lane's blocks sit in the high half of each scale dword when h = 1
 
-    Stage<BM, BN, ALIGNED> st;
-    stage_load<BM, BN, ALIGNED>(st, p, A, B, SA, SB, m0, n0, 0, t);
-    stage_store<BM, BN, ALIGNED>(st, p, smem, smem + OFF_B, smem + OFF_SA, smem + OFF_SB, m0, n0, 0, t);
-    __syncthreads();
+    // fragment registers of one half step q (lane: 32 elements = 4 dwords per
+    // fragment row) and the fp16 scales of the whole K step
+    u32x4 fa[FM], fb[FN];
+    f16x2 sa2[FM][2], sb2[FN][2];
+    // Scales of step `step` from stage st: blocks 2h, 2h+1 (q = 0) and
+    // 4+2h, 5+2h (q = 1) of the step, converted to fp16 (exact).  Blocks past
+    // K (only when K % 128 != 0) are zeroed: their FP4 bytes are the next
+    // row's or zeros, and must not contribute.
+    auto load_scales = [&](const lds_u8* st, int step) {
+        u32x2 ra[FM], rb[FN];
+#pragma unroll
+        for (int i = 0; i < FM; i++) ra[i] = *(const __attribute__((address_space(3))) u32x2*)(st + sa_off + i * 256);
+#pragma unroll
+        for (int i = 0; i < FN; i++) rb[i] = *(const __attribute__((address_space(3))) u32x2*)(st + sb_off + i * 256);
+        uint32_t m0w = 0xFFFFFFFFu, m1w = 0xFFFFFFFFu;
+        if constexpr (!ALIGNED) {
+            const int left = p.nblk - step * 8;  // valid blocks in this step (<= 0 past the end)
+            const int l0 = left < 0 ? 0 : left > 4 ? 4 : left, l1 = left < 4 ? 0 : left > 8 ? 4 : left - 4;
+            m0w = (uint32_t)(((uint64_t)1 << (8 * l0)) - 1);
+            m1w = (uint32_t)(((uint64_t)1 << (8 * l1)) - 1);
+        }
+#pragma unroll
+        for (int i = 0; i < FM; i++) {
+            sa2[i][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((ra[i].x & m0w) >> hsh, 1.0f, false);
+            sa2[i][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((ra[i].y & m1w) >> hsh, 1.0f, false);
+        }
+#pragma unroll
+        for (int i = 0; i < FN; i++) {
+            sb2[i][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((rb[i].x & m0w) >> hsh, 1.0f, false);
+            sb2[i][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((rb[i].y & m1w) >> hsh, 1.0f, false);
+        }
+    };
+    auto load_half = [&](const lds_u8* st, int cq) {
+#pragma unroll
+        for (int i = 0; i < FM; i++) fa[i] = *(const __attribute__((address_space(3))) u32x4*)(st + ra_off + i * 2048 + cq);
+#pragma unroll
+        for (int i = 0; i < FN; i++) fb[i] = *(const __attribute__((address_space(3))) u32x4*)(st + rb_off + i * 2048 + cq);
+    };
+    // K slice s = 4q + j of the current step, dequantized into buffer s & 1
+    f16x8 oa[2][FM], ob[2][FN];
+    auto dequant_slice = [&](int s) {
+        const int q = s >> 2, j = s & 3;
+#pragma unroll
+        for (int i = 0; i < FM; i++) oa[s & 1][i] = dequant8(word(fa[i], j), sa2[i][q][j >> 1]);
+#pragma unroll
+        for (int i = 0; i < FN; i++) ob[s & 1][i] = dequant8(word(fb[i], j), sb2[i][q][j >> 1]);
+    };
+    auto mfma_slice = [&](int s) {
+#pragma unroll
+        for (int in = 0; in < FN; in++)
+#pragma unroll
+            for (int im = 0; im < FM; im++)
+                acc[in][im] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ob[s & 1][in], oa[s & 1][im], acc[in][im],
+                                                                     0, 0, 0);
+    };
+    // one MFMA, then its share of the dequantization VALU work, repeated
+    constexpr int VPM = (8 * (FM + FN) + FM * FN - 1) / (FM * FN);
+    constexpr int kLead = FM * FN >= 8 ? 4 : 1;  // MFMAs issued while a step's first LDS reads land
+    constexpr int VPT = (8 * (FM + FN) + 4 * (FM + FN) + (FM * FN - kLead) - 1) /
+                        (FM * FN - kLead > 0 ? FM * FN - kLead : 1);
+    auto interleave = [&]() {
+#pragma unroll
+        for (int k = 0; k < FM * FN; k++) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+        }
+    };
+    // Workgroup barrier of the LDS pipeline: the waits that matter are
+    // explicit (this wave's loads into the next stage, its LDS reads), and the
+    // "memory" clobber keeps the compiler from moving LDS accesses across it.
+    auto barrier = [&]() {
+        __builtin_amdgcn_s_waitcnt((0x3F & 0xF) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));  // lgkmcnt(0)
+        asm volatile("s_barrier" ::: "memory");
+    };
 
+    // Step kt lives in stage kt % NST; its loads are issued NST-1 steps ahead.
+    issue(0, sm);
+    if constexpr (NST == 3) issue(nkt > 1 ? 1 : 0, sm + STAGE);
+    wait_vmcnt<ND * (NST - 2)>();  // step 0 has landed (this wave's part)
+    barrier();
+    load_scales(sm, 0);
+    load_half(sm, cq0);
+    dequant_slice(0);
+
+    int sc = 0;  // stage of step kt
     for (int kt = 0; kt < nkt; kt++) {
-        const bool more = kt + 1 < nkt;
-        if (more) stage_load<BM, BN, ALIGNED>(st, p, A, B, SA, SB, m0, n0, kt + 1, t);
-        const uint8_t* cur = smem + (kt & 1) * STAGE;
-        const uint8_t* sA = cur;
-        const uint8_t* sB = cur + OFF_B;
-        const uint8_t* sSA = cur + OFF_SA;
-        const uint8_t* sSB = cur + OFF_SB;
-
-        // ---- compute: two 64-element halves, four 16-element K-slices each
+        const int s1 = sc == NST - 1 ? 0 : sc + 1;
+        const int sl = NST == 2 ? s1 : (s1 == 2 ? 0 : s1 + 1);  // stage of step kt+NST-1
+        const lds_u8* cur = sm + sc * STAGE;
+        // step kt+NST-1 into the stage that step kt-1 used (the last steps
+        // reload the final K step into a stage nobody reads again, keeping the
+        // loop branch-free)
+        issue(kt + NST - 1 < nkt ? kt + NST - 1 : nkt - 1, sm + sl * STAGE);
 #pragma unroll
-        for (int q = 0; q < 2; q++) {
-            uint4 fa[FM], fb[FN];
-            f16x2 ca[FM][2], cb[FN][2];
-#pragma unroll
-            for (int i = 0; i < FM; i++) {
-                const int r = wm * WM + i * 32 + l32;
-                fa[i] = *(const uint4*)(sA + r * kPitch + q * 32 + h * 16);
-                const uint32_t s2 = *(const uint16_t*)(sSA + r * 8 + q * 4 + h * 2);
-                ca[i][0] = dup_scale_f16(s2 & 0xFFu);
-                ca[i][1] = dup_scale_f16(s2 >> 8);
-            }
-#pragma unroll
-            for (int i = 0; i < FN; i++) {
-                const int r = wn * WN + i * 32 + l32;
-                fb[i] = *(const uint4*)(sB + r * kPitch + q * 32 + h * 16);
-                const uint32_t s2 = *(const uint16_t*)(sSB + r * 8 + q * 4 + h * 2);
-                cb[i][0] = dup_scale_f16(s2 & 0xFFu);
-                cb[i][1] = dup_scale_f16(s2 >> 8);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                f16x8 oa[FM], ob[FN];
-#pragma unroll
-                for (int i = 0; i < FM; i++) {
-                    const uint32_t w = j == 0 ? fa[i].x : j == 1 ? fa[i].y : j == 2 ? fa[i].z : fa[i].w;
-                    oa[i] = dequant8(w, ca[i][j >> 1]);
-                }
-#pragma unroll
-                for (int i = 0; i < FN; i++) {
-                    const uint32_t w = j == 0 ? fb[i].x : j == 1 ? fb[i].y : j == 2 ? fb[i].z : fb[i].w;
-                    ob[i] = dequant8(w, cb[i][j >> 1]);
-                }
-#pragma unroll
-                for (int in = 0; in < FN; in++)
-#pragma unroll
-                    for (int im = 0; im < FM; im++)
-                        acc[in][im] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ob[in], oa[im], acc[in][im], 0, 0, 0);
-            }
+        for (int s = 0; s < 7; s++) {
+            dequant_slice(s + 1);
+            if (s == 2) load_half(cur, cq1);  // the q = 0 words are dead after slice 3
+            mfma_slice(s);
+            interleave();
+            if (s == 2) __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
         }
-        if (more) {
-            uint8_t* nxt = smem + ((kt + 1) & 1) * STAGE;
-            stage_store<BM, BN, ALIGNED>(st, p, nxt, nxt + OFF_B, nxt + OFF_SA, nxt + OFF_SB, m0, n0, kt + 1, t);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<ND * (NST - 2)>();  // step kt+1 has landed; later steps may be in flight
+        barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        const lds_u8* nx = sm + s1 * STAGE;
+        load_scales(nx, kt + 1);
+        load_half(nx, cq0);
+        dequant_slice(0);  // buffer 0: slice 7 lives in buffer 1
+        mfma_slice(7);
+        // LDS reads first, a few MFMAs while they are in flight, then the
+        // scale conversion and slice-0 dequantization of step kt+1
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (FM + FN), 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, kLead, 0);
+#pragma unroll
+        for (int k = kLead; k < FM * FN; k++) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, VPT, 0);
         }
-        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        sc = s1;
     }
+    wait_vmcnt<0>();  // nothing may land in LDS after the workgroup ends
 
     if constexpr (LORA) {
         // rank-r bf16 correction into the same accumulator
@@ -354,22 +414,42 @@ __global__ __launch_bounds__(256) void k_gemm(GParams p) {
             }
         }
     }
+#endif
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int NST>
 static hipError_t launch_tile(GParams p, bool lora, hipStream_t st) {
     p.tiles_m = (int)((p.M + BM - 1) / BM);
     p.tiles_n = (int)((p.N + BN - 1) / BN);
-    dim3 grid(p.tiles_m * p.tiles_n, 1, (unsigned)p.E ? (unsigned)p.E : 1u);
+    const int tiles = p.tiles_m * p.tiles_n;
+    p.xcd_chunk = tiles % 8 == 0 ? tiles / 8 : 0;
+    dim3 grid(tiles, 1, (unsigned)p.E ? (unsigned)p.E : 1u);
     const bool aligned = (p.K % 128) == 0;
     if (lora) {
-        if (aligned) k_gemm<BM, BN, true, true><<<grid, 256, 0, st>>>(p);
-        else k_gemm<BM, BN, false, true><<<grid, 256, 0, st>>>(p);
+        if (aligned) k_gemm<BM, BN, NST, true, true><<<grid, 256, 0, st>>>(p);
+        else k_gemm<BM, BN, NST, false, true><<<grid, 256, 0, st>>>(p);
     } else {
-        if (aligned) k_gemm<BM, BN, true, false><<<grid, 256, 0, st>>>(p);
-        else k_gemm<BM, BN, false, false><<<grid, 256, 0, st>>>(p);
+        if (aligned) k_gemm<BM, BN, NST, true, false><<<grid, 256, 0, st>>>(p);
+        else k_gemm<BM, BN, NST, false, false><<<grid, 256, 0, st>>>(p);
     }
     return hipGetLastError();
+}
+
+enum class Tile { T256x256, T128x256, T128x128, T64x128 };
+
+// Workgroup tile per problem.  Larger wave tiles need fewer dequantization
+// instructions per MFMA (256x256: 4, 128x256: 6, 128x128: 8), but
+// the grid must still spread evenly over the 256 CUs (measured on the
+// workload shapes: the 256x256 tile needs at least two tiles per CU, the
+// 128x128 tile wins when it gives three per CU, its occupancy; grouped
+// problems, whose masked tiles exit at once, do best with 128x256).
+static Tile pick_tile(int64_t m, int64_t n, int64_t E) {
+    auto tiles = [&](int64_t bm, int64_t bn) { return E * ((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
+    if (m <= 64) return Tile::T64x128;
+    if (tiles(256, 256) >= 2 * 256) return Tile::T256x256;
+    if (E == 1 && tiles(128, 128) >= 3 * 256) return Tile::T128x128;
+    if (tiles(128, 256) >= 128) return Tile::T128x256;
+    return Tile::T128x128;
 }
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
@@ -381,17 +461,18 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
     p.E = g.E;
     const int64_t cp = ((g.k / 16) + 3) / 4 * 4;
     p.cpa4 = (int)(cp / 4);
+    p.nblk = (int)(g.k / 16);
     p.rpa = (int)((g.m + 127) / 128 * 128);
     p.rpb = (int)((g.n + 127) / 128 * 128);
     p.sfa = (int64_t)p.rpa * cp;
     p.sfb = (int64_t)p.rpb * cp;
     const bool lora = g.d != nullptr;
-    const int64_t work = g.m * g.n;
-    if (g.m >= 2048 && g.n >= 2048 && work >= (int64_t)4096 * 4096)
-        return launch_tile<256, 256>(p, lora, st);
-    if (g.m <= 64)
-        return launch_tile<64, 128>(p, lora, st);
-    return launch_tile<128, 128>(p, lora, st);
+    switch (pick_tile(g.m, g.n, g.E)) {
+    case Tile::T256x256: return launch_tile<256, 256, 3>(p, lora, st);
+    case Tile::T128x256: return launch_tile<128, 256, 2>(p, lora, st);
+    case Tile::T64x128: return launch_tile<64, 128, 2>(p, lora, st);
+    default: return launch_tile<128, 128, 2>(p, lora, st);
+    }
 }
 
 }  // namespace nvfp4

@@ -137,6 +137,9 @@ def test_gemm_validation(lib):
     assert g(lib, out=P + 2) == MISAL
     assert g(lib, bias=P + 2) == MISAL
     assert g(lib, alpha=P + 1) == MISAL
+    # 32-bit offsets inside one FP4 matrix: 2^32 - 64 bytes is the limit
+    assert g(lib, m=(1 << 20), k=8192) == UNSUP      # 4 GiB of A
+    assert g(lib, n=(1 << 20) + 1, k=8192) == UNSUP
 
 
 def test_grouped_validation(lib):

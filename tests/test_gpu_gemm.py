@@ -87,6 +87,23 @@ def test_bias(ops, shape):
     gemm_case(ops, a, w, bias=bias, label="bias")
 
 
+@pytest.mark.parametrize("m,n,k", [
+    (4100, 8200, 272),   # 256x256 tiles (3-stage), ragged M and N, K % 128 != 0
+    (1024, 8320, 400),   # 128x256 tiles, K % 128 != 0
+    (200, 32800, 128),   # 128x256 tiles, a single partial tile row
+    (3000, 4200, 144),   # 128x128 tiles (at least three per CU), ragged
+])
+def test_tile_shapes(ops, m, n, k):
+    """Each workgroup tile shape the launcher picks, with ragged edges."""
+    g = torch.Generator().manual_seed(m + n + k)
+    a = torch.randn(m, k, generator=g).to(torch.bfloat16)
+    w = (torch.randn(n, k, generator=g) * 0.02).to(torch.bfloat16)
+    rows = sample_rows(m, 160, 5) if m > 1024 else None
+    if rows is not None:
+        rows = np.unique(np.concatenate([rows, np.arange(m - 8, m), np.arange(250, 262)]))
+    gemm_case(ops, a, w, rows=rows, label="tile shape")
+
+
 def test_tiny_workload(ops):
     t = synth.tiny()
     gemm_case(ops, t.a, t.w, label="tiny fp32 workload")
@@ -252,3 +269,34 @@ def test_end_to_end_dynamic_pipeline(ops):
     rows = sample_rows(d.m, 64, 9)
     ref = O.gemm_rows(qa, qb, sa, sb, ref_alpha, d.m, d.n, d.k, rows=rows)
     assert row_tolerance_check(out.float().cpu().numpy()[rows], ref) <= TOL
+
+
+def test_every_scale_code_k16(ops):
+    """K = 16 (one block): out[m, n] = alpha * dec(sa[m]) * dec(sb[n]) *
+    sum_j e2m1(a) e2m1(b), so every output element depends on one pair of
+    scale codes.  Rows and columns walk all 127 finite ue4m3 codes, including
+    the subnormals, and each element is compared on its own (relative 2^-7,
+    one bf16 ulp: the two sides may round alpha * acc differently before the
+    bf16 rounding), so a code decoded wrongly anywhere in the staging -- off
+    by at least one e4m3 step, 1/8 -- fails here even where the row tolerance
+    would hide it."""
+    m = n = 254
+    k = 16
+    rng = np.random.default_rng(11)
+    qa = rng.integers(0, 256, size=(m, k // 2), dtype=np.uint8)
+    qb = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    sa = np.zeros(O.sf_size(m, k), np.uint8)
+    sb = np.zeros(O.sf_size(n, k), np.uint8)
+    for r in range(m):
+        sa[O.sf_offset(r, 0, k)] = r % 127
+    for r in range(n):
+        sb[O.sf_offset(r, 0, k)] = (r * 5 + 3) % 127
+    alpha = np.float32(0.75)
+    say("every scale code, k=16", (m, n, k))
+    out = ops.nvfp4_gemm(t_u8(qa), t_u8(qb), t_u8(sa), t_u8(sb),
+                         torch.tensor([alpha], dtype=torch.float32, device="cuda"), k=k)
+    torch.cuda.synchronize()
+    ref = O.gemm_rows(qa, qb, sa, sb, alpha, m, n, k)
+    got = out.float().cpu().numpy()
+    err = np.abs(got - ref)
+    assert np.all(err <= np.abs(ref) * 2.0 ** -7), float((err / np.maximum(np.abs(ref), 1e-30)).max())
