@@ -2,9 +2,10 @@
 
 A step is one pass of the whole path over one batch of synthetic input that
 is already resident in HBM: NVFP4 quantization of the bf16 activation with a
-dynamic global scale (clear, amax pass, quantize pass), alpha = 1/(gs_a*gs_w)
-on the device, and the block-scaled GEMM to bf16.  Weights are quantized once
-before timing (same kernels, untimed).
+dynamic global scale (amax pass, finish, quantize pass), alpha =
+1/(gs_a*gs_w) on the device, and the block-scaled GEMM to bf16.  Weights are
+quantized once before timing (same kernels, untimed).  HIP events between
+the quantize part and the GEMM time the two parts of each step.
 
 Default workload: the large prefill linear, activation [8192, 5120] bf16
 (0.5% outlier channels x30) against a [16384, 5120] weight, output [8192,
@@ -13,8 +14,10 @@ are for development measurements.
 
 Prints one JSON line.  `value` is whole-step GEMM throughput (GEMM flops per
 step / step time); the quantize and GEMM kernels are also reported on their
-own, and `roofline` covers the dominant kernel (the GEMM), timed with HIP
-events on the stream it runs on.
+own (the quantize pass and the whole dynamic call timed back to back over
+every activation copy, next to a plain device copy for reference), and
+`roofline` covers the dominant kernel (the GEMM), timed with HIP events on
+the stream it runs on.
 """
 import argparse
 import json
@@ -98,19 +101,13 @@ def build_workload(name, ops, synth, torch):
         def gemm():
             ops.nvfp4_gemm(fa, fw, sfa, sfw, alpha, out=out)
 
-        def step(a, ev=None):
-            if ev is not None:
-                ev[0].record()
+        def pre(a):
             quant(a)
             ops.nvfp4_alpha(gsa, gsw, out=alpha)
-            if ev is not None:
-                ev[1].record()
-            gemm()
-            if ev is not None:
-                ev[2].record()
 
         w.make_acts = lambda n_copies: [a_cpu.to(dev) for _ in range(n_copies)]
-        w.step, w.quant, w.gemm = step, quant, gemm
+        w.pre, w.quant, w.gemm = pre, quant, gemm
+        w.outputs = (fa, sfa, gsa, alpha, out)
         w.cfg = {"m": m, "n": n, "k": k}
         w.cpu_sample = lambda O, np: cpu_baseline_dense(O, np, a_cpu, w_cpu, synth)
         return w
@@ -137,23 +134,17 @@ def build_workload(name, ops, synth, torch):
         def gemm():
             ops.nvfp4_gemm_grouped_masked(fa, fw, sfa, sfw, alpha, mask, out=out)
 
-        def step(x, ev=None):
-            if ev is not None:
-                ev[0].record()
+        def pre(x):
             quant(x)
             ops.nvfp4_alpha(gsa, gsw, out=alpha)
-            if ev is not None:
-                ev[1].record()
-            gemm()
-            if ev is not None:
-                ev[2].record()
 
         w.desc = ("Llama4-style routed experts: E=8 gate|up [512,16384] bf16, valid rows "
                   f"{mo.mask.tolist()} -> fused silu_and_mul + NVFP4 quantize -> grouped masked GEMM vs [8,5120,8192]")
         act_bytes = mo.x.numel() * 2
         w.rotate_hint = max(1, -(-512 * 2 ** 20 // act_bytes))
         w.make_acts = lambda n_copies: [mo.x.to(dev) for _ in range(n_copies)]
-        w.step, w.quant, w.gemm = step, quant, gemm
+        w.pre, w.quant, w.gemm = pre, quant, gemm
+        w.outputs = (fa, sfa, gsa, alpha, out)
         w.flops = 2.0 * n * h * valid
         w.q_bytes = valid * 2 * h * 2 + E * m * h // 2 + E * sf_size(m, h)
         w.amax_bytes = valid * 2 * h * 2
@@ -187,20 +178,14 @@ def build_workload(name, ops, synth, torch):
         def gemm():
             ops.nvfp4_gemm_svdquant(fa, fw, sfa, sfw, alpha, d, l1, bias=bias, out=out)
 
-        def step(x, ev=None):
-            if ev is not None:
-                ev[0].record()
+        def pre(x):
             quant(x)
-            if ev is not None:
-                ev[1].record()
-            gemm()
-            if ev is not None:
-                ev[2].record()
 
         w.desc = "SVDQuant linear 4096x3072x3072, r=32: smooth NVFP4 quantize (static gs) -> fused GEMM + LoRA-up + bias"
         w.rotate_hint = max(1, -(-512 * 2 ** 20 // (m * k * 2)))
         w.make_acts = lambda n_copies: [s.x.to(dev) for _ in range(n_copies)]
-        w.step, w.quant, w.gemm = step, quant, gemm
+        w.pre, w.quant, w.gemm = pre, quant, gemm
+        w.outputs = (fa, sfa, out)
         w.flops = 2.0 * m * n * k + 2.0 * m * n * r
         w.q_bytes = m * k * 2 + k * 2 + m * k // 2 + sf_size(m, k)
         w.amax_bytes = 0
@@ -271,6 +256,30 @@ def gemm_traffic(workload):
     return round(1024 * (rec["fetch_kib"] * rec["fetch_factor"] + rec["write_kib"] * rec["write_factor"]))
 
 
+def capture(torch, fn):
+    """A HIP graph of fn()'s launches on the capture stream (no memset nodes:
+    the library launches kernels only)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+def time_graph(torch, g, reps=3):
+    """Average time of one replay of g (ms), best of `reps` replays, bracketed
+    by HIP events on the replay stream."""
+    best = None
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1)
+        best = t if best is None else min(best, t)
+    return best
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -284,12 +293,13 @@ def main():
 
     torch.cuda.set_device(0)
     w = build_workload(args.workload, ops, synth, torch)
-    n_copies = args.rotate or w.rotate_hint
+    n_copies = min(args.rotate or w.rotate_hint, 64)
     acts = w.make_acts(n_copies)
     torch.cuda.synchronize()
 
     for i in range(args.warmup):
-        w.step(acts[i % n_copies])
+        w.pre(acts[i % n_copies])
+        w.gemm()
     torch.cuda.synchronize()
 
     if args.copy_calibration:
@@ -300,29 +310,42 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # ---- the timed steps (eager launches on the current stream; HIP events
+    # between the quantize part and the GEMM)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        w.step(acts[i % n_copies], evs[i])
+        evs[i][0].record()
+        w.pre(acts[i % n_copies])
+        evs[i][1].record()
+        w.gemm()
+        evs[i][2].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     step_ms = (t1 - t0) * 1e3 / args.steps
     quant_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     gemm_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
 
-    # quantize pass alone (STATIC mode: the quantize kernel only), cold inputs
-    qe = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        qe[i][0].record()
-        w.quant(acts[i % n_copies], ops.GS_STATIC)
-        qe[i][1].record()
-    torch.cuda.synchronize()
-    qpass_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in qe]))
+    # ---- kernel passes back to back, over every activation copy (cold inputs),
+    # as HIP graphs so the host's launch latency stays out of the kernel times
+    g_pass = capture(torch, lambda: [w.quant(a, ops.GS_STATIC) for a in acts])
+    qpass_ms = time_graph(torch, g_pass) / n_copies
+    if w.amax_bytes:
+        g_dyn = capture(torch, lambda: [w.quant(a, ops.GS_DYNAMIC) for a in acts])
+        qdyn_ms = time_graph(torch, g_dyn) / n_copies
+    else:
+        qdyn_ms = qpass_ms
+    src = torch.ones(64 * 2 ** 20, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    g_copy = capture(torch, lambda: [torch.neg(src, out=dst) for _ in range(4)])
+    copy_gbs = 2 * src.numel() * 4 / (time_graph(torch, g_copy) / 4 * 1e-3) / 1e9
+    del src, dst, g_copy
 
     gemm_tflops = w.flops / (gemm_ms * 1e-3) / 1e12
     value = w.flops / (step_ms * 1e-3) / 1e12
     q_gbs = w.q_bytes / (qpass_ms * 1e-3) / 1e9
+    amax_ms = qdyn_ms - qpass_ms
     e2e_bytes = w.q_bytes + w.amax_bytes
     res = {
         "metric": "NVFP4 GEMM TFLOP/s (+% peak) and quantize GB/s (+% HBM peak), 1xMI355X",
@@ -343,9 +366,13 @@ def main():
                  "frac_f16_mfma_peak": round(gemm_tflops / MFMA_F16_PEAK_TFLOPS, 4)},
         "quantize": {"pass_ms": round(qpass_ms, 4), "pass_gbs": round(q_gbs, 1),
                      "pass_frac_hbm": round(q_gbs / HBM_PEAK_GBS, 4),
-                     "dynamic_call_ms": round(quant_ms, 4),
-                     "dynamic_call_gbs": round(e2e_bytes / (quant_ms * 1e-3) / 1e9, 1),
-                     "pass_bytes": w.q_bytes, "amax_pass_bytes": w.amax_bytes},
+                     "amax_and_finish_ms": round(amax_ms, 4),
+                     "amax_gbs": round(w.amax_bytes / (amax_ms * 1e-3) / 1e9, 1) if w.amax_bytes else None,
+                     "dynamic_call_ms": round(qdyn_ms, 4),
+                     "dynamic_call_gbs": round(e2e_bytes / (qdyn_ms * 1e-3) / 1e9, 1),
+                     "in_step_ms": round(quant_ms, 4),
+                     "pass_bytes": w.q_bytes, "amax_pass_bytes": w.amax_bytes,
+                     "copy_kernel_gbs": round(copy_gbs, 1)},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / MFMA_F16_PEAK_TFLOPS, 4),
                      "traffic": gemm_traffic(args.workload), "kernel": "k_gemm (block-scaled NVFP4 GEMM)",

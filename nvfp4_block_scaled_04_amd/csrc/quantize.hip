@@ -10,24 +10,30 @@
 //   q   = e2m1(x' * (gs / dec(s)))                      packed two per byte
 //   scales in the 128x4 swizzled, zero-padded layout.
 //
-// Work decomposition: one workgroup of 256 threads owns one 128-row x
-// 64-column tile of the output, i.e. exactly one 512-byte tile of the
-// swizzled scale layout.  Thread t handles rows (t/8) + 32*i, i = 0..3, and
-// the 8 consecutive columns 8*(t%8).. of the tile, so a 16-element block is
-// shared by a lane pair (block amax via one DPP exchange), and a wave reads
-// 8 rows x 128 contiguous bytes per load.  The 512 scale bytes are gathered
-// in LDS and written with 32 16-byte stores.
+// Work decomposition: one workgroup of 256 threads owns a 128-row x 64*CT
+// column tile, i.e. CT whole 512-byte tiles of the swizzled scale layout
+// (CT per pass and shape, see quant_ct_for).
+// A lane owns whole 16-element blocks: BPR = 4*CT consecutive lanes cover one
+// row segment of the tile (a wave reads 64/BPR rows x 32*BPR contiguous bytes
+// of bf16 per load pair), so the block scale is computed once per block with
+// no cross-lane traffic, and every load of a lane is issued before any of it
+// is used.  The element factor r = gs / dec(s) comes from a 128-entry
+// per-workgroup LDS table (dec(s) takes only the ue4m3 code values), so the
+// only division per block is bamax / 6.  The scale bytes are gathered in LDS
+// and written with 16-byte stores.
 //
-// DYNAMIC mode runs three kernels on the caller's stream: the amax pass, in
-// which every workgroup writes its partial maximum into the call's own scale
-// buffer (free until the quantize pass overwrites it; it holds at least one
-// float per amax workgroup), a one-block-per-item finish that reduces the
-// partials and writes gs, and the quantize pass.  No atomics and no
-// device-wide fences are involved.
+// DYNAMIC mode runs three kernels on the caller's stream: the amax pass (one
+// workgroup per quantize tile, each writing its partial maximum into the
+// call's own scale buffer, which is free until the quantize pass overwrites
+// it and holds at least one float per tile), a one-block-per-item finish that
+// reduces the partials and writes gs, and the quantize pass.  No atomics and
+// no device-wide fences are involved.
 #include "device_common.h"
 #include "internal.h"
 
 namespace nvfp4 {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 enum Variant { V_BF16 = 0, V_F32 = 1, V_BF16_SMOOTH = 2, V_F32_SMOOTH = 3, V_SILU = 4 };
 
@@ -43,142 +49,172 @@ struct QParams {
     int64_t k_in;          // input row stride in elements
     int64_t sfsz;          // per-item scale bytes
     int b;
-    int nct;               // column tiles = ceil(K/64) = Cp/4
+    int nct;               // 64-column tiles = ceil(K/64) = Cp/4
     int nrt;               // row tiles = ceil(m/128)
     int amax_blocks;       // amax workgroups per item (partials per item)
 };
 
 // silu(g) = g / (1 + e^-g), evaluated in fp64 and rounded once to fp32.
-__device__ __forceinline__ float silu_f32(float g) {
+// Kept out of line: the fast path below needs it only rarely.
+__device__ __attribute__((noinline)) float silu_f32(float g) {
     double x = (double)g;
     return (float)(x / (1.0 + exp(-x)));
 }
 
-struct Chunk {
-    float f[8];
-    float amax;
-};
-
-// Raw bytes behind eight consecutive elements: x (or the gate half) in `a`,
-// the up half (silu) or the second 16 bytes of fp32 input in `b`.
-struct Raw {
-    uint4 a, b;
-};
-
-template <int V>
-__device__ __forceinline__ Raw load_raw(const QParams& p, int64_t e, int64_t row, int64_t col) {
-    Raw r;
-    const int64_t roff = (e * p.m + row) * p.k_in;
-    if constexpr (V == V_F32 || V == V_F32_SMOOTH) {
-        const float* xf = (const float*)p.x + roff + col;
-        r.a = *(const uint4*)xf;
-        r.b = *(const uint4*)(xf + 4);
-    } else if constexpr (V == V_SILU) {
-        const uint16_t* xb = (const uint16_t*)p.x + roff;
-        r.a = *(const uint4*)(xb + col);
-        r.b = *(const uint4*)(xb + p.K + col);
-    } else {
-        r.a = *(const uint4*)((const uint16_t*)p.x + roff + col);
-        r.b = uint4{0u, 0u, 0u, 0u};
-    }
-    return r;
+// h = bf16(fp32(S * u)) with S = silu(g) correctly rounded to fp32, as a bf16
+// bit pattern: the fast path and its exactness test.
+//
+// y = g * rcp(1 + expf(-g)) in fp32 is within a few ulp of S (expf and rcp 1
+// ulp each, two roundings of 1/2 ulp: relative error below 3 * 2^-23, i.e. at
+// most 7 ulp from the rounded S), so the rounded S lies in [y - 16 ulp,
+// y + 16 ulp]; in value, |S - y| < 7 * 2^-23 |y|, so fp32(S * u) lies within
+// 15 ulp of p = fp32(y * u) (fp32(s * u) is monotonic in s).  bf16 rounding
+// changes its result only where the low 16 bits of the pattern cross 0x8000,
+// which no interval of that width does when they sit more than 64 away from
+// it (a binade change inside the interval puts them next to 0 or 0xFFFF), so
+// then bf16(p) is the exact h.  The test also requires |y| and |p| inside
+// [2^-100, 2^100) (normal, no overflow).  Elements that fail it -- about 1
+// in 500 -- take the exact fp64 path.
+__device__ __forceinline__ uint32_t silu_mul_fast(float g, float u, bool& exact) {
+    const float y = g * __builtin_amdgcn_rcpf(1.0f + expf(-g));
+    const float p = y * u;
+    const uint32_t yb = f_bits(y) & 0x7FFFFFFFu, pb = f_bits(p) & 0x7FFFFFFFu;
+    const int d = (int)(pb & 0xFFFFu) - 0x8000;
+    exact = yb - 0x0D800000u < 0x64000000u && pb - 0x0D800000u < 0x64000000u && (d > 64 || d < -64);
+    return f32_to_bf16_rne(p);
 }
 
-// Eight elements after the prologue and nan_to_num, plus their largest
-// magnitude.  pq holds the eight pre_quant_scale values (smooth variants).
+__device__ __forceinline__ uint32_t silu_mul_exact(float g, float u) {
+    return f32_to_bf16_rne(silu_f32(g) * u);
+}
+
+// 16-byte loads behind one 16-element block of a row.
 template <int V>
-__device__ __forceinline__ Chunk process(const Raw& raw, const uint4& pq) {
-    Chunk c;
+constexpr int loads_per_block() {
+    return V == V_BF16 || V == V_BF16_SMOOTH ? 2 : 4;  // fp32: 64 bytes; silu: gate 32 + up 32
+}
+
+template <int V>
+__device__ __forceinline__ void load_block(const QParams& p, int64_t e, int64_t row, int64_t col,
+                                           u32x4 (&r)[loads_per_block<V>()]) {
+    const int64_t roff = (e * p.m + row) * p.k_in;
+    if constexpr (V == V_F32 || V == V_F32_SMOOTH) {
+        const u32x4* src = (const u32x4*)((const float*)p.x + roff + col);
+        r[0] = src[0]; r[1] = src[1]; r[2] = src[2]; r[3] = src[3];
+    } else if constexpr (V == V_SILU) {
+        const u32x4* g = (const u32x4*)((const uint16_t*)p.x + roff + col);
+        const u32x4* u = (const u32x4*)((const uint16_t*)p.x + roff + p.K + col);
+        r[0] = g[0]; r[1] = g[1]; r[2] = u[0]; r[3] = u[1];
+    } else {
+        const u32x4* src = (const u32x4*)((const uint16_t*)p.x + roff + col);
+        r[0] = src[0]; r[1] = src[1];
+    }
+}
+
+// pre_quant_scale of a block's 16 columns (bf16), smooth variants only.
+template <int V>
+__device__ __forceinline__ void load_pqs(const QParams& p, int64_t col, u32x4 (&pq)[2]) {
+    if constexpr (V == V_BF16_SMOOTH || V == V_F32_SMOOTH) {
+        const u32x4* src = (const u32x4*)(p.pqs + col);
+        pq[0] = src[0]; pq[1] = src[1];
+    } else {
+        pq[0] = u32x4{0u, 0u, 0u, 0u};
+        pq[1] = u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+// The block's 16 values after the prologue and nan_to_num, and their largest
+// magnitude.
+template <int V>
+__device__ __forceinline__ float process_block(const u32x4 (&r)[loads_per_block<V>()], const u32x4 (&pq)[2],
+                                               float (&f)[16]) {
     if constexpr (V == V_BF16 || V == V_SILU) {
-        uint32_t w[4];
+        uint32_t w[8];
         if constexpr (V == V_BF16) {
-            w[0] = raw.a.x; w[1] = raw.a.y; w[2] = raw.a.z; w[3] = raw.a.w;
+#pragma unroll
+            for (int j = 0; j < 4; j++) { w[j] = r[0][j]; w[4 + j] = r[1][j]; }
         } else {
-            const uint32_t gw[4] = {raw.a.x, raw.a.y, raw.a.z, raw.a.w};
-            const uint32_t uw[4] = {raw.b.x, raw.b.y, raw.b.z, raw.b.w};
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                float h0 = silu_f32(bf16_lo(gw[j])) * bf16_lo(uw[j]);
-                float h1 = silu_f32(bf16_hi(gw[j])) * bf16_hi(uw[j]);
-                w[j] = f32_to_bf16_rne(h0) | (f32_to_bf16_rne(h1) << 16);
-            }
-        }
-        uint32_t mb = absmax_bits_bf16x8(w);
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            c.f[2 * j] = bf16_lo(w[j]);
-            c.f[2 * j + 1] = bf16_hi(w[j]);
-        }
-        if (mb >= 0x7F80u) {  // inf or NaN present: the slow, exact path
-            float a = 0.0f;
+            // fast path for all 16 elements, then the exact path for the
+            // flagged ones (rare: one divergent branch per block)
+            uint32_t need = 0;
 #pragma unroll
             for (int j = 0; j < 8; j++) {
-                c.f[j] = nan_to_num(c.f[j]);
-                a = __builtin_fmaxf(a, __builtin_fabsf(c.f[j]));
+                const uint32_t gw = j < 4 ? r[0][j] : r[1][j - 4];
+                const uint32_t uw = j < 4 ? r[2][j] : r[3][j - 4];
+                bool ok0, ok1;
+                const uint32_t h0 = silu_mul_fast(bf16_lo(gw), bf16_lo(uw), ok0);
+                const uint32_t h1 = silu_mul_fast(bf16_hi(gw), bf16_hi(uw), ok1);
+                w[j] = h0 | (h1 << 16);
+                need |= (ok0 ? 0u : 1u << (2 * j)) | (ok1 ? 0u : 2u << (2 * j));
             }
-            c.amax = a;
-        } else {
-            c.amax = bits_f(mb << 16);
+            if (need) {
+#pragma unroll
+                for (int j = 0; j < 8; j++) {
+                    if (!(need & (3u << (2 * j)))) continue;
+                    const uint32_t gw = j < 4 ? r[0][j] : r[1][j - 4];
+                    const uint32_t uw = j < 4 ? r[2][j] : r[3][j - 4];
+                    uint32_t lo = w[j] & 0xFFFFu, hi = w[j] >> 16;
+                    if (need & (1u << (2 * j))) lo = silu_mul_exact(bf16_lo(gw), bf16_lo(uw));
+                    if (need & (2u << (2 * j))) hi = silu_mul_exact(bf16_hi(gw), bf16_hi(uw));
+                    w[j] = lo | (hi << 16);
+                }
+            }
         }
+        // bf16 magnitudes compare as integers; inf / NaN patterns sort above
+        // every finite one
+        const uint32_t mb = __builtin_elementwise_max(absmax_bits_bf16x8(w), absmax_bits_bf16x8(w + 4));
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            f[2 * j] = bf16_lo(w[j]);
+            f[2 * j + 1] = bf16_hi(w[j]);
+        }
+        if (mb < 0x7F80u) return bits_f(mb << 16);
     } else {
         if constexpr (V == V_F32 || V == V_F32_SMOOTH) {
-            const uint32_t w[8] = {raw.a.x, raw.a.y, raw.a.z, raw.a.w, raw.b.x, raw.b.y, raw.b.z, raw.b.w};
 #pragma unroll
-            for (int j = 0; j < 8; j++) c.f[j] = bits_f(w[j]);
+            for (int j = 0; j < 16; j++) f[j] = bits_f(r[j >> 2][j & 3]);
         } else {
-            const uint32_t w[4] = {raw.a.x, raw.a.y, raw.a.z, raw.a.w};
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                c.f[2 * j] = bf16_lo(w[j]);
-                c.f[2 * j + 1] = bf16_hi(w[j]);
+            for (int j = 0; j < 8; j++) {
+                const uint32_t xw = r[j >> 2][j & 3];
+                f[2 * j] = bf16_lo(xw);
+                f[2 * j + 1] = bf16_hi(xw);
             }
         }
         if constexpr (V == V_BF16_SMOOTH || V == V_F32_SMOOTH) {
-            const uint32_t pw[4] = {pq.x, pq.y, pq.z, pq.w};
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                c.f[2 * j] = c.f[2 * j] * bf16_lo(pw[j]);
-                c.f[2 * j + 1] = c.f[2 * j + 1] * bf16_hi(pw[j]);
-            }
-        }
-        uint32_t bad = 0;
-        float a = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            bad |= (f_bits(c.f[j]) & 0x7FFFFFFFu) >= 0x7F800000u;
-            a = __builtin_fmaxf(a, __builtin_fabsf(c.f[j]));
-        }
-        if (bad) {
-            a = 0.0f;
 #pragma unroll
             for (int j = 0; j < 8; j++) {
-                c.f[j] = nan_to_num(c.f[j]);
-                a = __builtin_fmaxf(a, __builtin_fabsf(c.f[j]));
+                const uint32_t pw = pq[j >> 2][j & 3];
+                f[2 * j] = f[2 * j] * bf16_lo(pw);
+                f[2 * j + 1] = f[2 * j + 1] * bf16_hi(pw);
             }
         }
-        c.amax = a;
+        float a = 0.0f;
+        uint32_t bad = 0;
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+            a = __builtin_fmaxf(a, __builtin_fabsf(f[j]));
+            bad |= (f_bits(f[j]) & 0x7FFFFFFFu) >= 0x7F800000u;
+        }
+        if (!bad) return a;
     }
-    return c;
+    // inf or NaN present: the exact nan_to_num path
+    float a = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+        f[j] = nan_to_num(f[j]);
+        a = __builtin_fmaxf(a, __builtin_fabsf(f[j]));
+    }
+    return a;
 }
 
-template <int V>
-__device__ __forceinline__ uint4 load_pqs(const QParams& p, int64_t col) {
-    if constexpr (V == V_BF16_SMOOTH || V == V_F32_SMOOTH) return *(const uint4*)(p.pqs + col);
-    return uint4{0u, 0u, 0u, 0u};
-}
-
-// ---------------------------------------------------------------------------
-// DYNAMIC mode: amax partials, finish, then quantize.
-// ---------------------------------------------------------------------------
-
-// Thread layout of a workgroup tile of 128 rows x CT*64 columns (CT 64-column
-// swizzle tiles): LPR = 8*CT lanes cover a row segment (8 elements each, a
-// lane pair per 16-element block), RPP = 256/LPR rows are covered per pass,
-// NP = 128/RPP passes.  A wave reads 64/LPR rows x 16*LPR contiguous bytes.
+// Lane layout of a workgroup tile of 128 rows x 64*CT columns: BPR = 4*CT
+// lanes own the blocks of one row segment, RPP = 256 / BPR rows are covered
+// per pass, NP = 128 / RPP passes.
 template <int CT>
 struct TileMap {
-    static constexpr int LPR = 8 * CT;
-    static constexpr int RPP = 256 / LPR;
+    static constexpr int BPR = 4 * CT;
+    static constexpr int RPP = 256 / BPR;
     static constexpr int NP = 128 / RPP;
 };
 
@@ -187,36 +223,39 @@ __device__ __forceinline__ float* partials(const QParams& p, int e) {
     return (float*)(p.out_sf + (int64_t)e * p.sfsz);
 }
 
+// ---------------------------------------------------------------------------
+// DYNAMIC mode: amax partials, finish, then quantize.
+// ---------------------------------------------------------------------------
+
 template <int V, int CT>
 __global__ __launch_bounds__(256) void k_amax(QParams p) {
     using TM = TileMap<CT>;
-    const int e = blockIdx.y;
+    constexpr int NL = loads_per_block<V>();
+    const int tile = blockIdx.x, e = blockIdx.y;
     const int t = threadIdx.x;
-    const int rsub = t / TM::LPR, lane = t % TM::LPR;
+    const int rsub = t / TM::BPR, lb = t % TM::BPR;
     const int valid = clamp_rows(p.mask, e, (int)p.m);
     const int nwct = (p.nct + CT - 1) / CT;
-    const int ntiles = p.nrt * nwct;
+    const int rt = tile / nwct, wct = tile - rt * nwct;
     float amax = 0.0f;
-    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-        const int rt = tile / nwct, wct = tile - rt * nwct;
-        if ((int64_t)rt * 128 >= valid) continue;  // tile entirely past the valid rows
-        int64_t col = (int64_t)wct * 64 * CT + lane * 8;
+    if ((int64_t)rt * 128 < valid) {  // tiles entirely past the valid rows contribute 0
+        int64_t col = (int64_t)wct * 64 * CT + lb * 16;
         const bool col_ok = col < p.K;
-        col = col_ok ? col : p.K - 8;
-        const uint4 pq = load_pqs<V>(p, col);
+        col = col_ok ? col : p.K - 16;
+        u32x4 pq[2];
+        load_pqs<V>(p, col, pq);
+        u32x4 raw[TM::NP][NL];
 #pragma unroll
-        for (int i0 = 0; i0 < TM::NP; i0 += 4) {
-            Raw raw[4];
+        for (int i = 0; i < TM::NP; i++) {  // every load in flight before any use
+            const int64_t row = (int64_t)rt * 128 + rsub + TM::RPP * i;
+            load_block<V>(p, e, row < p.m ? row : p.m - 1, col, raw[i]);
+        }
 #pragma unroll
-            for (int i = 0; i < 4; i++) {  // four loads in flight before any use
-                const int64_t row = (int64_t)rt * 128 + rsub + TM::RPP * (i0 + i);
-                raw[i] = load_raw<V>(p, e, row < p.m ? row : p.m - 1, col);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int64_t row = (int64_t)rt * 128 + rsub + TM::RPP * (i0 + i);
-                if (col_ok && row < valid) amax = __builtin_fmaxf(amax, process<V>(raw[i], pq).amax);
-            }
+        for (int i = 0; i < TM::NP; i++) {
+            const int64_t row = (int64_t)rt * 128 + rsub + TM::RPP * i;
+            float f[16];
+            const float a = process_block<V>(raw[i], pq, f);
+            if (col_ok && row < valid) amax = __builtin_fmaxf(amax, a);
         }
     }
     // workgroup max: wave reduction through shuffles, then LDS across waves
@@ -226,7 +265,7 @@ __global__ __launch_bounds__(256) void k_amax(QParams p) {
     if ((t & 63) == 0) wmax[t >> 6] = amax;
     __syncthreads();
     if (t == 0)
-        partials(p, e)[blockIdx.x] =
+        partials(p, e)[tile] =
             __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
 }
 
@@ -235,7 +274,11 @@ __global__ __launch_bounds__(256) void k_finish_gs(QParams p) {
     const int e = blockIdx.x, t = threadIdx.x;
     const float* part = partials(p, e);
     float a = 0.0f;
-    for (int i = t; i < p.amax_blocks; i += 256) a = __builtin_fmaxf(a, part[i]);
+    int i = t;
+    for (; i + 768 < p.amax_blocks; i += 1024)  // four independent loads in flight
+        a = __builtin_fmaxf(__builtin_fmaxf(a, __builtin_fmaxf(part[i], part[i + 256])),
+                            __builtin_fmaxf(part[i + 512], part[i + 768]));
+    for (; i < p.amax_blocks; i += 256) a = __builtin_fmaxf(a, part[i]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) a = __builtin_fmaxf(a, __shfl_xor(a, off));
     __shared__ float wmax[4];
@@ -251,67 +294,66 @@ __global__ __launch_bounds__(256) void k_finish_gs(QParams p) {
 template <int V, int CT>
 __global__ __launch_bounds__(256) void k_quantize(QParams p) {
     using TM = TileMap<CT>;
+    constexpr int NL = loads_per_block<V>();
     const int wct = blockIdx.x, rt = blockIdx.y, e = blockIdx.z;
     const int t = threadIdx.x;
-    const int rsub = t / TM::LPR, lane = t % TM::LPR;
-    const int c = lane >> 3;                 // swizzle tile within the workgroup
-    const int blk = (lane & 7) >> 1;         // 16-element block within that tile
+    const int rsub = t / TM::BPR, lb = t % TM::BPR;
+    const int c = lb >> 2;   // swizzle tile within the workgroup
+    const int blk = lb & 3;  // block column within that tile
     const int valid = clamp_rows(p.mask, e, (int)p.m);
-    const float gs = p.gs[e];
-    int64_t col = (int64_t)wct * 64 * CT + lane * 8;
+    int64_t col = (int64_t)wct * 64 * CT + lb * 16;
     const bool col_ok = col < p.K;
-    col = col_ok ? col : p.K - 8;
+    col = col_ok ? col : p.K - 16;
     __shared__ __align__(16) uint8_t sbuf[512 * CT];
+    __shared__ float rtab[128];
     uint8_t* q = p.out_fp4 + (int64_t)e * p.m * (p.K / 2);
     // swizzle tiles this workgroup owns that exist in the buffer
     const int ntile_here = (p.nct - wct * CT) < CT ? (p.nct - wct * CT) : CT;
     uint8_t* sf_dst = p.out_sf + (int64_t)e * p.sfsz + ((int64_t)rt * p.nct + (int64_t)wct * CT) * 512;
 
     if ((int64_t)rt * 128 >= valid) {  // tile entirely past the valid rows: zero scales only
-        for (int i = t; i < ntile_here * 32; i += 256) *(uint4*)(sf_dst + i * 16) = uint4{0u, 0u, 0u, 0u};
+        for (int i = t; i < ntile_here * 32; i += 256) *(u32x4*)(sf_dst + i * 16) = u32x4{0u, 0u, 0u, 0u};
         return;
     }
-    const uint4 pq = load_pqs<V>(p, col);
+    u32x4 pq[2];
+    load_pqs<V>(p, col, pq);
+    u32x4 raw[TM::NP][NL];
 #pragma unroll
-    for (int i0 = 0; i0 < TM::NP; i0 += 4) {
-        Raw raw[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) {  // four loads in flight before any use
-            const int64_t row = (int64_t)rt * 128 + rsub + TM::RPP * (i0 + i);
-            raw[i] = load_raw<V>(p, e, row < p.m ? row : p.m - 1, col);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int rl = rsub + TM::RPP * (i0 + i);       // row within the 128-row tile
-            const int64_t row = (int64_t)rt * 128 + rl;
-            const bool active = col_ok && row < valid;
-            Chunk ch;
-            if (active) {
-                ch = process<V>(raw[i], pq);
-            } else {
-#pragma unroll
-                for (int j = 0; j < 8; j++) ch.f[j] = 0.0f;
-                ch.amax = 0.0f;
-            }
-            // block amax over the lane pair sharing this 16-element block
-            const float bamax = __builtin_fmaxf(ch.amax, xor1(ch.amax));
-            const uint32_t sc = ue4m3_encode((bamax / 6.0f) * gs);
-            const float dec = ue4m3_decode(sc);
-            const float r = dec == 0.0f ? 0.0f : gs / dec;
-            if (active) {
-                uint32_t w = 0;
-                w = NVFP4_PACK_FP4(w, ch.f[0] * r, ch.f[1] * r, 0);
-                w = NVFP4_PACK_FP4(w, ch.f[2] * r, ch.f[3] * r, 1);
-                w = NVFP4_PACK_FP4(w, ch.f[4] * r, ch.f[5] * r, 2);
-                w = NVFP4_PACK_FP4(w, ch.f[6] * r, ch.f[7] * r, 3);
-                *(uint32_t*)(q + row * (p.K / 2) + col / 2) = w;
-            }
-            if ((lane & 1) == 0)
-                sbuf[c * 512 + (rl & 31) * 16 + (rl >> 5) * 4 + blk] = active ? (uint8_t)sc : (uint8_t)0;
-        }
+    for (int i = 0; i < TM::NP; i++) {  // every load in flight before any use
+        const int64_t row = (int64_t)rt * 128 + rsub + TM::RPP * i;
+        load_block<V>(p, e, row < p.m ? row : p.m - 1, col, raw[i]);
+    }
+    // element factors r = gs / dec(s) for every scale code (0 for code 0),
+    // computed while the loads are in flight
+    const float gs = p.gs[e];
+    if (t < 128) {
+        const float dec = ue4m3_decode((uint32_t)t);
+        rtab[t] = dec == 0.0f ? 0.0f : gs / dec;
     }
     __syncthreads();
-    for (int i = t; i < ntile_here * 32; i += 256) *(uint4*)(sf_dst + i * 16) = *(const uint4*)(sbuf + i * 16);
+#pragma unroll
+    for (int i = 0; i < TM::NP; i++) {
+        const int rl = rsub + TM::RPP * i;  // row within the 128-row tile
+        const int64_t row = (int64_t)rt * 128 + rl;
+        const bool active = col_ok && row < valid;
+        float f[16];
+        const float bamax = process_block<V>(raw[i], pq, f);
+        const uint32_t sc = active ? ue4m3_encode((bamax / 6.0f) * gs) : 0u;
+        const float r = rtab[sc];
+        uint32_t w0 = 0, w1 = 0;
+        w0 = NVFP4_PACK_FP4(w0, f[0] * r, f[1] * r, 0);
+        w0 = NVFP4_PACK_FP4(w0, f[2] * r, f[3] * r, 1);
+        w0 = NVFP4_PACK_FP4(w0, f[4] * r, f[5] * r, 2);
+        w0 = NVFP4_PACK_FP4(w0, f[6] * r, f[7] * r, 3);
+        w1 = NVFP4_PACK_FP4(w1, f[8] * r, f[9] * r, 0);
+        w1 = NVFP4_PACK_FP4(w1, f[10] * r, f[11] * r, 1);
+        w1 = NVFP4_PACK_FP4(w1, f[12] * r, f[13] * r, 2);
+        w1 = NVFP4_PACK_FP4(w1, f[14] * r, f[15] * r, 3);
+        if (active) *(uint2*)(q + row * (p.K / 2) + col / 2) = uint2{w0, w1};
+        sbuf[c * 512 + (rl & 31) * 16 + (rl >> 5) * 4 + blk] = (uint8_t)sc;
+    }
+    __syncthreads();
+    for (int i = t; i < ntile_here * 32; i += 256) *(u32x4*)(sf_dst + i * 16) = *(const u32x4*)(sbuf + i * 16);
 }
 
 __global__ void k_alpha(const float* ga, const float* gb, float* alpha, int64_t n) {
@@ -323,24 +365,38 @@ __global__ void k_alpha(const float* ga, const float* gb, float* alpha, int64_t 
 // host-side launch
 // ---------------------------------------------------------------------------
 
-// 64-column swizzle tiles per workgroup: two for the memory-bound variants
-// (longer contiguous row segments per wave); one for the silu variant, whose
-// fp64 silu makes it compute-heavy, so more workgroups pay off (measured).
+// 64-column swizzle tiles per workgroup (CT), picked per pass and shape
+// (measured): the amax pass reads best from many small workgroups (CT = 2);
+// the quantize pass writes whole 128-byte lines of FP4 per row with CT = 4,
+// which pays when it still leaves at least 1024 workgroups.  The silu
+// variant reads gate and up and carries the silu work, so it keeps CT = 1.
 template <int V>
-constexpr int quant_ct() { return V == V_SILU ? 1 : 2; }
+static int quant_ct_for(const QParams& p) {
+    if (V == V_SILU) return 1;
+    const int64_t wgs4 = (int64_t)p.nrt * ((p.nct + 3) / 4) * p.b;
+    return wgs4 >= 1024 ? 4 : 2;
+}
+
+template <int V, int CT>
+static void launch_quantize_pass(const QParams& p, hipStream_t st) {
+    k_quantize<V, CT><<<dim3((p.nct + CT - 1) / CT, p.nrt, p.b), 256, 0, st>>>(p);
+}
 
 template <int V>
 static hipError_t launch_variant(QParams p, bool dynamic, hipStream_t st) {
-    constexpr int CT = quant_ct<V>();
+    constexpr int CTA = V == V_SILU ? 1 : 2;
     if (dynamic) {
-        const int ntiles = p.nrt * ((p.nct + CT - 1) / CT);
-        int g = (1024 + p.b - 1) / p.b;
-        g = g < ntiles ? g : ntiles;
-        p.amax_blocks = g < 1 ? 1 : g;
-        k_amax<V, CT><<<dim3(p.amax_blocks, p.b), 256, 0, st>>>(p);
+        // one amax workgroup, and one partial maximum, per amax tile
+        p.amax_blocks = p.nrt * ((p.nct + CTA - 1) / CTA);
+        k_amax<V, CTA><<<dim3(p.amax_blocks, p.b), 256, 0, st>>>(p);
         k_finish_gs<<<p.b, 256, 0, st>>>(p);
     }
-    k_quantize<V, CT><<<dim3((p.nct + CT - 1) / CT, p.nrt, p.b), 256, 0, st>>>(p);
+    if constexpr (V == V_SILU) {
+        launch_quantize_pass<V, 1>(p, st);
+    } else {
+        if (quant_ct_for<V>(p) == 4) launch_quantize_pass<V, 4>(p, st);
+        else launch_quantize_pass<V, 2>(p, st);
+    }
     return hipGetLastError();
 }
 

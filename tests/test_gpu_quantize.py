@@ -48,7 +48,8 @@ def run_single(ops, x_cpu, mode, gs=None, pqs=None):
 # ---- single tensor -------------------------------------------------------------
 
 @pytest.mark.parametrize("m,k", [(1, 16), (16, 64), (127, 48), (129, 80), (128, 256), (300, 1040),
-                                 (257, 4096)])
+                                 (257, 4096),
+                                 (8200, 4112)])   # wide quantize tiles (4 swizzle tiles), ragged both ways
 def test_bf16_dynamic_ragged(ops, m, k):
     g = torch.Generator().manual_seed(m * 1000 + k)
     x = (torch.randn(m, k, generator=g) * 3).to(torch.bfloat16)
@@ -182,6 +183,24 @@ def test_silu_every_bf16_gate(ops):
             x[:, 0, :16] = gate[half * 32768:(half + 1) * 32768, None]
             x[:, 0, 16:] = ub
             run_batched(ops, x, None, ops.GS_DYNAMIC, silu=True)
+
+
+def test_silu_random_pairs(ops):
+    """One million (gate, up) pairs: gates uniform over the finite bf16 bit
+    patterns (every binade), up values N(0,1) times random powers of two.
+    The kernel decides most products of silu(g) and u on a fast fp32 path
+    and only the ones next to a bf16 rounding boundary exactly; every byte
+    must still equal the oracle's."""
+    rng = np.random.default_rng(2024)
+    b, m, h = 16, 128, 512
+    bits = rng.integers(0, 65536, size=(b, m, h), dtype=np.uint32).astype(np.uint16)
+    finite = (bits & 0x7F80) != 0x7F80
+    bits = np.where(finite, bits, bits & 0x807F)   # non-finite patterns -> small values
+    gate = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+    up = torch.from_numpy(rng.standard_normal((b, m, h)).astype(np.float32) *
+                          np.exp2(rng.integers(-20, 21, size=(b, m, h))).astype(np.float32)).to(torch.bfloat16)
+    x = torch.cat([gate, up], dim=-1).contiguous()
+    run_batched(ops, x, None, ops.GS_DYNAMIC, silu=True)
 
 
 # ---- workload sizes ------------------------------------------------------------
