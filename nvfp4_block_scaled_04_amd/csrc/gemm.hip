@@ -101,6 +101,11 @@ __device__ __forceinline__ uint32_t word(const u32x4& v, int j) {
     return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
 }
 
+// Byte offset of scale (row, block column c) in the swizzled layout.
+__device__ __forceinline__ int64_t scale_byte_off(int64_t row, int c, int cpa4) {
+    return ((row >> 7) * cpa4 + (c >> 2)) * 512 + (row & 31) * 16 + ((row & 127) >> 5) * 4 + (c & 3);
+}
+
 // Byte offset of scale dword (row, column group cg) in the swizzled layout.
 __device__ __forceinline__ uint32_t scale_dword_off(int64_t row, int cg, int cpa4) {
     return (uint32_t)(((row >> 7) * cpa4 + cg) * 512 + (row & 31) * 16 + ((row & 127) >> 5) * 4);
@@ -435,7 +440,141 @@ static hipError_t launch_tile(GParams p, bool lora, hipStream_t st) {
     return hipGetLastError();
 }
 
-enum class Tile { T256x256, T128x256, T128x128, T64x128 };
+
+// ---------------------------------------------------------------------------
+// Skinny GEMM for small M (decode-shaped: M <= 64).  A workgroup computes a
+// 16 x 16 output tile; its 4 waves split K into four contiguous ranges and
+// their fp32 partial tiles are summed through LDS.  Each lane loads its
+// operand fragments straight from global memory (no reuse to stage for):
+// lane (row r = l%16, group g = l/16) holds, per 128-element K chunk, the 32
+// consecutive elements 32g.. of its A row and of its B row plus their two
+// block scales, and feeds four v_mfma_f32_16x16x32_f16 K-slices from them
+// (the same K permutation on both operands).  With N/16 x M/16 workgroups the
+// weight is streamed once, spread over every CU.
+// ---------------------------------------------------------------------------
+template <bool ALIGNED, bool LORA>
+__global__ __launch_bounds__(256) void k_gemm_skinny(GParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int e = blockIdx.z;
+    const int64_t n0 = (int64_t)blockIdx.x * 16, m0 = (int64_t)blockIdx.y * 16;
+    const int valid = clamp_rows(p.mask, e, (int)p.M);
+    if (m0 >= valid) return;
+    const int64_t rowb = p.K / 2;
+    const int r = lane & 15, g = lane >> 4;
+    const int64_t arow = m0 + r < p.M ? m0 + r : p.M - 1;
+    const int64_t brow = n0 + r < p.N ? n0 + r : p.N - 1;
+    const uint8_t* A = p.a + (int64_t)e * p.M * rowb + arow * rowb;
+    const uint8_t* B = p.b + (int64_t)e * p.N * rowb + brow * rowb;
+    const uint8_t* SA = p.a_sf + (int64_t)e * p.sfa;
+    const uint8_t* SB = p.b_sf + (int64_t)e * p.sfb;
+
+    const int nch = (int)((p.K + 127) / 128);
+    const int per = (nch + 3) / 4;
+    const int c0 = wave * per, c1 = c0 + per < nch ? c0 + per : nch;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    constexpr int U = 8;  // chunks whose loads are in flight together
+    for (int cb = c0; cb < c1; cb += U) {
+        u32x4 fa[U], fb[U];
+        uint32_t sa[U], sb[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int c = cb + u < c1 ? cb + u : c1 - 1;  // past the range: reload, never used
+            const int64_t kb = (int64_t)c * 64 + g * 16;   // byte of this lane's 32 elements
+            const int blk = c * 8 + 2 * g;                 // first of its two blocks
+            if (ALIGNED) {
+                fa[u] = *(const u32x4*)(A + kb);
+                fb[u] = *(const u32x4*)(B + kb);
+            } else {
+                // 32, 16 or no valid elements in the group; the rest is zero
+                const int64_t left = rowb - kb;
+                const u32x2 za = left >= 8 ? *(const u32x2*)(A + kb) : u32x2{0u, 0u};
+                const u32x2 zb = left >= 8 ? *(const u32x2*)(B + kb) : u32x2{0u, 0u};
+                const u32x2 ya = left >= 16 ? *(const u32x2*)(A + kb + 8) : u32x2{0u, 0u};
+                const u32x2 yb = left >= 16 ? *(const u32x2*)(B + kb + 8) : u32x2{0u, 0u};
+                fa[u] = u32x4{za.x, za.y, ya.x, ya.y};
+                fb[u] = u32x4{zb.x, zb.y, yb.x, yb.y};
+            }
+            const int bc = blk < p.nblk ? blk : 0;  // past K: any valid (even) block column, masked below
+            uint32_t va = *(const uint16_t*)(SA + scale_byte_off(arow, bc, p.cpa4));
+            uint32_t vb = *(const uint16_t*)(SB + scale_byte_off(brow, bc, p.cpa4));
+            if (!ALIGNED) {  // blocks past K carry zero scales
+                const uint32_t keep = blk + 1 < p.nblk ? 0xFFFFu : blk < p.nblk ? 0x00FFu : 0u;
+                va &= keep;
+                vb &= keep;
+            }
+            sa[u] = va;
+            sb[u] = vb;
+        }
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            if (cb + u >= c1) break;
+            const f16x2 ssa = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sa[u], 1.0f, false);
+            const f16x2 ssb = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb[u], 1.0f, false);
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const f16x8 oa = dequant8(word(fa[u], j), ssa[j >> 1]);
+                const f16x8 ob = dequant8(word(fb[u], j), ssb[j >> 1]);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ob, oa, acc, 0, 0, 0);
+            }
+        }
+    }
+    if constexpr (LORA) {
+        if (wave == 0) {  // rank-r bf16 correction, once, into wave 0's partial
+            const int64_t drow = arow, lrow = brow;
+            for (int kr = 0; kr < p.r; kr += 32) {
+                const bf16x8 od = __builtin_bit_cast(bf16x8, *(const u32x4*)(p.d + drow * p.r + kr + g * 8));
+                const bf16x8 ol = __builtin_bit_cast(bf16x8, *(const u32x4*)(p.l1 + lrow * p.r + kr + g * 8));
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ol, od, acc, 0, 0, 0);
+            }
+        }
+    }
+    // sum the four waves' partial tiles
+    __shared__ f32x4 part[3][64];
+    if (wave > 0) part[wave - 1][lane] = acc;
+    __syncthreads();
+    if (wave != 0) return;
+    acc += part[0][lane] + part[1][lane] + part[2][lane];
+    // lane: output row m0 + r, columns n0 + 4g .. n0 + 4g + 3
+    const int64_t m = m0 + r;
+    if (m >= valid) return;
+    const float alpha = p.alpha[e];
+    uint16_t* O = p.out + (int64_t)e * p.M * p.N + m * p.N;
+    const int64_t n = n0 + 4 * g;
+    float y[4];
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+        y[v] = alpha * acc[v];
+        if (p.bias && n + v < p.N) y[v] += bf16_lo((uint32_t)p.bias[n + v]);
+    }
+    if ((p.N & 3) == 0 && n + 3 < p.N) {
+        uint2 o;
+        o.x = f32_to_bf16_rne(y[0]) | (f32_to_bf16_rne(y[1]) << 16);
+        o.y = f32_to_bf16_rne(y[2]) | (f32_to_bf16_rne(y[3]) << 16);
+        *(uint2*)(O + n) = o;
+    } else {
+#pragma unroll
+        for (int v = 0; v < 4; v++)
+            if (n + v < p.N) O[n + v] = (uint16_t)f32_to_bf16_rne(y[v]);
+    }
+#endif
+}
+
+static hipError_t launch_skinny(GParams p, bool lora, hipStream_t st) {
+    dim3 grid((unsigned)((p.N + 15) / 16), (unsigned)((p.M + 15) / 16), (unsigned)p.E);
+    const bool aligned = (p.K % 128) == 0;
+    if (lora) {
+        if (aligned) k_gemm_skinny<true, true><<<grid, 256, 0, st>>>(p);
+        else k_gemm_skinny<false, true><<<grid, 256, 0, st>>>(p);
+    } else {
+        if (aligned) k_gemm_skinny<true, false><<<grid, 256, 0, st>>>(p);
+        else k_gemm_skinny<false, false><<<grid, 256, 0, st>>>(p);
+    }
+    return hipGetLastError();
+}
+
+enum class Tile { T256x256, T128x256, T128x128, Skinny };
 
 // Workgroup tile per problem.  Larger wave tiles need fewer dequantization
 // instructions per MFMA (256x256: 4, 128x256: 6, 128x128: 8), but
@@ -445,7 +584,7 @@ enum class Tile { T256x256, T128x256, T128x128, T64x128 };
 // problems, whose masked tiles exit at once, do best with 128x256).
 static Tile pick_tile(int64_t m, int64_t n, int64_t E) {
     auto tiles = [&](int64_t bm, int64_t bn) { return E * ((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
-    if (m <= 64) return Tile::T64x128;
+    if (m <= 64) return Tile::Skinny;
     if (tiles(256, 256) >= 2 * 256) return Tile::T256x256;
     if (E == 1 && tiles(128, 128) >= 3 * 256) return Tile::T128x128;
     if (tiles(128, 256) >= 128) return Tile::T128x256;
@@ -470,7 +609,7 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
     switch (pick_tile(g.m, g.n, g.E)) {
     case Tile::T256x256: return launch_tile<256, 256, 3>(p, lora, st);
     case Tile::T128x256: return launch_tile<128, 256, 2>(p, lora, st);
-    case Tile::T64x128: return launch_tile<64, 128, 2>(p, lora, st);
+    case Tile::Skinny: return launch_skinny(p, lora, st);
     default: return launch_tile<128, 128, 2>(p, lora, st);
     }
 }

@@ -69,7 +69,8 @@ def gemm_case(ops, a_cpu, w_cpu, bias=None, rows=None, label=""):
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 1, 16), (16, 33, 48), (127, 64, 128), (129, 257, 400),
-                                   (200, 96, 1024), (64, 130, 80), (300, 500, 256)])
+                                   (200, 96, 1024), (64, 130, 80), (300, 500, 256),
+                                   (16, 4096, 4096), (64, 300, 4000), (33, 17, 2064), (7, 1000, 16)])
 def test_ragged_shapes(ops, m, n, k):
     g = torch.Generator().manual_seed(m * 7 + n * 3 + k)
     a = (torch.randn(m, k, generator=g) * 2).to(torch.bfloat16)
@@ -149,10 +150,10 @@ def test_svdquant_workload(ops):
     assert ratio <= TOL
 
 
-@pytest.mark.parametrize("r", [32, 64, 128])
-def test_svdquant_ranks_and_ragged(ops, r):
-    g = torch.Generator().manual_seed(r)
-    m, n, k = 150, 90, 192
+@pytest.mark.parametrize("r,m,n,k", [(32, 150, 90, 192), (64, 150, 90, 192), (128, 150, 90, 192),
+                                     (64, 40, 200, 272)])   # small M: the skinny kernel
+def test_svdquant_ranks_and_ragged(ops, r, m, n, k):
+    g = torch.Generator().manual_seed(r + m)
     a = torch.randn(m, k, generator=g).to(torch.bfloat16)
     w = (torch.randn(n, k, generator=g) * 0.05).to(torch.bfloat16)
     say("svdquant ragged", m, n, k, r)
@@ -221,6 +222,12 @@ def grouped_case(ops, E, m, n, h, mask, rows_per_expert=None, seed=0):
 @pytest.mark.parametrize("mask", [[0, 1, 130, 256], [256, 256, 256, 256], [7, 0, 129, 64]])
 def test_grouped_masked_small(ops, mask):
     grouped_case(ops, 4, 256, 96, 128, mask, seed=sum(mask))
+
+
+@pytest.mark.parametrize("mask", [[0, 17, 48], [48, 48, 5]])
+def test_grouped_masked_few_rows(ops, mask):
+    """m <= 64 per expert: the skinny kernel, masks inside and at the edge."""
+    grouped_case(ops, 3, 48, 100, 144, mask, seed=3 + sum(mask))
 
 
 def test_moe_workload(ops):
