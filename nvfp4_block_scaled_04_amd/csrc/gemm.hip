@@ -392,37 +392,58 @@ __global__ __launch_bounds__(64 * WGM * WGN, (kWavesPerEU<BM / WGM, BN / WGN>)) 
         }
     }
 
-    // ---- epilogue: alpha, bias, bf16, store rows < valid
+    // ---- epilogue: alpha, bias, bf16; staged through LDS (each wave its own
+    // region, one 32-row fragment row at a time) so that every output row
+    // leaves as whole 16-byte pieces covering the wave's WN columns, rows
+    // >= valid skipped.  The pipeline stages are free once every wave is past
+    // its last LDS read.
+    constexpr int PITCH = WN * 2 + 16;  // bytes per staged row (16-byte aligned, banks spread)
+    static_assert(NW * 32 * PITCH <= NST * STAGE, "epilogue staging fits in the pipeline's LDS");
+    barrier();
+    lds_u8* const ep = sm + wave * 32 * PITCH;
     const float alpha = p.alpha[e];
     uint16_t* O = p.out + (int64_t)e * p.M * p.N;
-    const bool vec_ok = (p.N & 3) == 0;
+    constexpr int CPR = WN / 8;        // 16-byte pieces per staged row
+    constexpr int RPI = 64 / CPR;      // rows per wave store instruction
 #pragma unroll
-    for (int in = 0; in < FN; in++) {
+    for (int im = 0; im < FM; im++) {
+        // lane (l32, h) of fragment in: row l32, columns in*32 + 8g + 4h .. +3
 #pragma unroll
-        for (int im = 0; im < FM; im++) {
-            const int64_t m = m0 + wm * WM + im * 32 + l32;
-            if (m >= valid) continue;
+        for (int in = 0; in < FN; in++) {
 #pragma unroll
             for (int g = 0; g < 4; g++) {
-                const int64_t n = n0 + wn * WN + in * 32 + g * 8 + h * 4;
+                const int cl = in * 32 + g * 8 + h * 4;  // column within the wave tile
+                const int64_t n = n0 + wn * WN + cl;
                 float y[4];
 #pragma unroll
                 for (int u = 0; u < 4; u++) {
                     y[u] = alpha * acc[in][im][g * 4 + u];
                     if (p.bias && n + u < p.N) y[u] += bf16_lo((uint32_t)p.bias[n + u]);
                 }
-                if (vec_ok && n + 3 < p.N) {
-                    uint2 v;
-                    v.x = f32_to_bf16_rne(y[0]) | (f32_to_bf16_rne(y[1]) << 16);
-                    v.y = f32_to_bf16_rne(y[2]) | (f32_to_bf16_rne(y[3]) << 16);
-                    *(uint2*)(O + m * p.N + n) = v;
-                } else {
-#pragma unroll
-                    for (int u = 0; u < 4; u++)
-                        if (n + u < p.N) O[m * p.N + n + u] = (uint16_t)f32_to_bf16_rne(y[u]);
-                }
+                *(__attribute__((address_space(3))) u32x2*)(ep + l32 * PITCH + cl * 2) =
+                    u32x2{f32_to_bf16_rne(y[0]) | (f32_to_bf16_rne(y[1]) << 16),
+                          f32_to_bf16_rne(y[2]) | (f32_to_bf16_rne(y[3]) << 16)};
             }
         }
+        __builtin_amdgcn_s_waitcnt((0x3F & 0xF) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));  // lgkmcnt(0)
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int it = 0; it < 32 / RPI; it++) {
+            const int rl = it * RPI + lane / CPR, c = lane % CPR;
+            const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(ep + rl * PITCH + c * 16);
+            const int64_t m = m0 + wm * WM + im * 32 + rl;
+            const int64_t n = n0 + wn * WN + c * 8;
+            if (m >= valid) continue;
+            if (n + 8 <= p.N && (p.N & 7) == 0) {
+                *(u32x4*)(O + m * p.N + n) = v;
+            } else {
+#pragma unroll
+                for (int u = 0; u < 8; u++)
+                    if (n + u < p.N) O[m * p.N + n + u] = (uint16_t)(v[u >> 1] >> (16 * (u & 1)));
+            }
+        }
+        __builtin_amdgcn_s_waitcnt((0x3F & 0xF) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));  // reads done before the region is rewritten
+        __builtin_amdgcn_sched_barrier(0);
     }
 #endif
 }
