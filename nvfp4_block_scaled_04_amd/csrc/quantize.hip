@@ -55,33 +55,47 @@ struct QParams {
 };
 
 // silu(g) = g / (1 + e^-g), evaluated in fp64 and rounded once to fp32.
-// Kept out of line: the fast path below needs it only rarely.
-__device__ __attribute__((noinline)) float silu_f32(float g) {
+__device__ __forceinline__ float silu_f32(float g) {
     double x = (double)g;
     return (float)(x / (1.0 + exp(-x)));
 }
 
-// h = bf16(fp32(S * u)) with S = silu(g) correctly rounded to fp32, as a bf16
-// bit pattern: the fast path and its exactness test.
+// h = bf16(fp32(S * u)) with S = silu(g) correctly rounded to fp32, for the
+// two bf16 pairs packed in a gate word and an up word: the fast path and its
+// exactness test.  Returns the two h as a packed bf16 pair; bit i of `bad`
+// (i = 0 low, 1 high) is set where the result must come from the exact path.
 //
-// y = g * rcp(1 + expf(-g)) in fp32 is within a few ulp of S (expf and rcp 1
-// ulp each, two roundings of 1/2 ulp: relative error below 3 * 2^-23, i.e. at
-// most 7 ulp from the rounded S), so the rounded S lies in [y - 16 ulp,
-// y + 16 ulp]; in value, |S - y| < 7 * 2^-23 |y|, so fp32(S * u) lies within
-// 15 ulp of p = fp32(y * u) (fp32(s * u) is monotonic in s).  bf16 rounding
-// changes its result only where the low 16 bits of the pattern cross 0x8000,
-// which no interval of that width does when they sit more than 64 away from
-// it (a binade change inside the interval puts them next to 0 or 0xFFFF), so
-// then bf16(p) is the exact h.  The test also requires |y| and |p| inside
-// [2^-100, 2^100) (normal, no overflow).  Elements that fail it -- about 1
-// in 500 -- take the exact fp64 path.
-__device__ __forceinline__ uint32_t silu_mul_fast(float g, float u, bool& exact) {
-    const float y = g * __builtin_amdgcn_rcpf(1.0f + expf(-g));
-    const float p = y * u;
-    const uint32_t yb = f_bits(y) & 0x7FFFFFFFu, pb = f_bits(p) & 0x7FFFFFFFu;
-    const int d = (int)(pb & 0xFFFFu) - 0x8000;
-    exact = yb - 0x0D800000u < 0x64000000u && pb - 0x0D800000u < 0x64000000u && (d > 64 || d < -64);
-    return f32_to_bf16_rne(p);
+// y = g * rcp(1 + 2^(-g * log2 e)) in fp32.  For |g| < 16 the product
+// -g * log2(e) is off by at most |g| * 2^-23 * log2(e) in absolute terms
+// (two roundings), which moves 2^t by at most |g| * 2^-23 relative; with
+// the hardware exp2 and reciprocal (at most 2 ulp and 1 ulp) and the three
+// fp32 roundings, y is within 21 * 2^-23 of S relative.  So fp32(S * u) and
+// p = fp32(y * u) differ by at most 43 ulp of p (a relative bound is worth at
+// most twice its size in ulp).  bf16 rounding changes its result only where
+// the low 16 bits of the pattern cross 0x8000, which no interval of that
+// width does when they sit more than 64 away from it (a binade change inside
+// the interval puts them next to 0 or 0xFFFF), so then bf16(p) is the exact
+// h.  The test also requires |g| >= 2^-77 (so |y| > 2^-101, far from the
+// subnormals) and |p| in [2^-100, 2^100).  Elements that fail it (about 1 in
+// 500 for N(0,1) data, and every |g| >= 16, inf and NaN) take the exact fp64
+// path.
+__device__ __forceinline__ uint32_t silu_mul_fast2(uint32_t gw, uint32_t uw, uint32_t& bad) {
+    constexpr float kLog2e = 1.44269504088896340736f;
+    const float g0 = bf16_lo(gw), g1 = bf16_hi(gw);
+    const float y0 = g0 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g0 * -kLog2e));
+    const float y1 = g1 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g1 * -kLog2e));
+    const float p0 = y0 * bf16_lo(uw), p1 = y1 * bf16_hi(uw);
+    // (bitwise, not short-circuit, so the test stays branch-free)
+    auto fails = [](float g, float p) -> uint32_t {
+        const uint32_t ga = f_bits(g) & 0x7FFFFFFFu, pb = f_bits(p), pa = pb & 0x7FFFFFFFu;
+        return (uint32_t)(ga - 0x19000000u >= 0x41800000u - 0x19000000u) |  // not 2^-77 <= |g| < 16
+               (uint32_t)(pa - 0x0D800000u >= 0x64000000u) |                 // not 2^-100 <= |p| < 2^100
+               (uint32_t)((pb & 0xFFFFu) - 0x7FC0u <= 0x80u);                // low half within 64 of 0x8000
+    };
+    bad = fails(g0, p0) | (fails(g1, p1) << 1);
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0, p1}, bf16x2));  // RNE
 }
 
 __device__ __forceinline__ uint32_t silu_mul_exact(float g, float u) {
@@ -141,23 +155,29 @@ __device__ __forceinline__ float process_block(const u32x4 (&r)[loads_per_block<
             for (int j = 0; j < 8; j++) {
                 const uint32_t gw = j < 4 ? r[0][j] : r[1][j - 4];
                 const uint32_t uw = j < 4 ? r[2][j] : r[3][j - 4];
-                bool ok0, ok1;
-                const uint32_t h0 = silu_mul_fast(bf16_lo(gw), bf16_lo(uw), ok0);
-                const uint32_t h1 = silu_mul_fast(bf16_hi(gw), bf16_hi(uw), ok1);
-                w[j] = h0 | (h1 << 16);
-                need |= (ok0 ? 0u : 1u << (2 * j)) | (ok1 ? 0u : 2u << (2 * j));
+                uint32_t bad;
+                w[j] = silu_mul_fast2(gw, uw, bad);
+                need |= bad << (2 * j);
             }
-            if (need) {
+            // The flagged elements one at a time through a single inlined
+            // copy of the exact path (a call would make the wave wait for
+            // every load it has in flight).
+            while (need) {
+                const int bit = __builtin_ctz(need);
+                need &= need - 1;
+                const int j = bit >> 1, sh = (bit & 1) * 16;
+                uint32_t gw = 0, uw = 0;
 #pragma unroll
-                for (int j = 0; j < 8; j++) {
-                    if (!(need & (3u << (2 * j)))) continue;
-                    const uint32_t gw = j < 4 ? r[0][j] : r[1][j - 4];
-                    const uint32_t uw = j < 4 ? r[2][j] : r[3][j - 4];
-                    uint32_t lo = w[j] & 0xFFFFu, hi = w[j] >> 16;
-                    if (need & (1u << (2 * j))) lo = silu_mul_exact(bf16_lo(gw), bf16_lo(uw));
-                    if (need & (2u << (2 * j))) hi = silu_mul_exact(bf16_hi(gw), bf16_hi(uw));
-                    w[j] = lo | (hi << 16);
+                for (int jj = 0; jj < 8; jj++) {
+                    if (jj == j) {
+                        gw = jj < 4 ? r[0][jj] : r[1][jj - 4];
+                        uw = jj < 4 ? r[2][jj] : r[3][jj - 4];
+                    }
                 }
+                const uint32_t h = silu_mul_exact(bits_f((gw >> sh) << 16), bits_f((uw >> sh) << 16));
+#pragma unroll
+                for (int jj = 0; jj < 8; jj++)
+                    if (jj == j) w[jj] = (w[jj] & ~(0xFFFFu << sh)) | (h << sh);
             }
         }
         // bf16 magnitudes compare as integers; inf / NaN patterns sort above
