@@ -139,10 +139,17 @@ __device__ __forceinline__ void tile_coords(const GParams& p, int& tm, int& tn) 
 template <int WM, int WN>
 constexpr int kWavesPerEU = WM * WN >= 16384 ? 1 : 2;
 
-template <int BM, int BN, int WGM, int WGN, int NST, bool ALIGNED, bool LORA>
-__global__ __launch_bounds__(64 * WGM * WGN, (kWavesPerEU<BM / WGM, BN / WGN>)) void k_gemm(GParams p) {
+// KS = 2 splits the K loop inside the workgroup: two groups of WGM x WGN
+// waves each run half of the K steps through their own LDS pipeline over the
+// same tile, then swap halves of their partial sums through LDS, so that
+// every SIMD holds two waves (one of each group) when the tile count alone
+// would leave one: one wave's dequantization then overlaps the other's MFMAs.
+// Requires an even number of K steps.
+template <int BM, int BN, int WGM, int WGN, int NST, int KS, bool ALIGNED, bool LORA>
+__global__ __launch_bounds__(64 * WGM * WGN * KS, (KS == 2 ? 2 : kWavesPerEU<BM / WGM, BN / WGN>)) void k_gemm(GParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
-    constexpr int NW = WGM * WGN;  // waves, WGM along M x WGN along N
+    static_assert(KS == 1 || (KS == 2 && BM / WGM == 64), "the K split swaps 32-row fragment rows of 64-row wave tiles");
+    constexpr int NW = WGM * WGN;  // waves of one K group, WGM along M x WGN along N
     constexpr int WM = BM / WGM, WN = BN / WGN;
     constexpr int FM = WM / 32, FN = WN / 32;
     // one LDS stage: FP4 A rows, FP4 B rows, raw scale dwords (padded to whole
@@ -154,11 +161,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, (kWavesPerEU<BM / WGM, BN / WGN>)) 
     constexpr int ND = NFA + NFB + NSC;
     static_assert(BM % (16 * NW) == 0 && BN % (16 * NW) == 0, "whole 16-row blocks per wave");
     static_assert(NST == 2 || NST == 3, "two or three LDS stages");
-    __shared__ __align__(16) uint8_t smem[NST * STAGE];
+    __shared__ __align__(16) uint8_t smem[KS * NST * STAGE];
 
     const int t = threadIdx.x;
     const int lane = t & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wave_wg = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int grp = KS == 1 ? 0 : wave_wg / NW;          // K group
+    const int wave = KS == 1 ? wave_wg : wave_wg % NW;   // wave within the group
     const int wm = wave % WGM, wn = wave / WGM;
     const int e = blockIdx.z;
     int tm, tn;
@@ -205,7 +214,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, (kWavesPerEU<BM / WGM, BN / WGN>)) 
             voS[i] = 0;  // padding dwords: any in-bounds source
         }
     }
-    lds_u8* const sm = (lds_u8*)smem;
+    lds_u8* const sm = (lds_u8*)smem + grp * (NST * STAGE);
     auto issue = [&](int step, lds_u8* st) {
 #pragma unroll
         for (int i = 0; i < NFA; i++)
@@ -233,6 +242,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, (kWavesPerEU<BM / WGM, BN / WGN>)) 
             for (int v = 0; v < 16; v++) acc[i][j][v] = 0.0f;
 
     const int nkt = (int)((p.K + 127) / 128);
+    const int kb = grp * (nkt / KS), ke = KS == 1 ? nkt : kb + nkt / KS;  // this group's K steps
     const int h = lane >> 5, l32 = lane & 31;
     // per-lane LDS offsets, fixed for the whole K loop (fragment i adds i*32 rows)
     const int ra_off = (wm * WM + l32) * 64, rb_off = OFF_B + (wn * WN + l32) * 64;
@@ -317,24 +327,26 @@ __global__ __launch_bounds__(64 * WGM * WGN, (kWavesPerEU<BM / WGM, BN / WGN>)) 
         asm volatile("s_barrier" ::: "memory");
     };
 
-    // Step kt lives in stage kt % NST; its loads are issued NST-1 steps ahead.
-    issue(0, sm);
-    if constexpr (NST == 3) issue(nkt > 1 ? 1 : 0, sm + STAGE);
-    wait_vmcnt<ND * (NST - 2)>();  // step 0 has landed (this wave's part)
+    // Step kt lives in stage (kt - kb) % NST; its loads are issued NST-1 steps
+    // ahead.  Both K groups run the same number of steps, so the workgroup
+    // barriers pair up.
+    issue(kb, sm);
+    if constexpr (NST == 3) issue(kb + 1 < ke ? kb + 1 : kb, sm + STAGE);
+    wait_vmcnt<ND * (NST - 2)>();  // step kb has landed (this wave's part)
     barrier();
-    load_scales(sm, 0);
+    load_scales(sm, kb);
     load_half(sm, cq0);
     dequant_slice(0);
 
     int sc = 0;  // stage of step kt
-    for (int kt = 0; kt < nkt; kt++) {
+    for (int kt = kb; kt < ke; kt++) {
         const int s1 = sc == NST - 1 ? 0 : sc + 1;
         const int sl = NST == 2 ? s1 : (s1 == 2 ? 0 : s1 + 1);  // stage of step kt+NST-1
         const lds_u8* cur = sm + sc * STAGE;
         // step kt+NST-1 into the stage that step kt-1 used (the last steps
         // reload the final K step into a stage nobody reads again, keeping the
         // loop branch-free)
-        issue(kt + NST - 1 < nkt ? kt + NST - 1 : nkt - 1, sm + sl * STAGE);
+        issue(kt + NST - 1 < ke ? kt + NST - 1 : ke - 1, sm + sl * STAGE);
 #pragma unroll
         for (int s = 0; s < 7; s++) {
             dequant_slice(s + 1);
@@ -366,6 +378,52 @@ __global__ __launch_bounds__(64 * WGM * WGN, (kWavesPerEU<BM / WGM, BN / WGN>)) 
     }
     wait_vmcnt<0>();  // nothing may land in LDS after the workgroup ends
 
+    if constexpr (KS == 2) {
+        // Group g keeps fragment row im = g of its wave tile and takes the
+        // other group's partial sums of it: each wave writes the fragments it
+        // gives away to its partner's LDS slot, then adds what its partner
+        // wrote (FN / 2 fragment columns per round, so a round fits in the
+        // pipeline's LDS).
+        constexpr int FRAG = 64 * 16 * 4;  // one fragment of one wave, bytes
+        constexpr int HALF = FN / 2;
+        static_assert(FM == 2 && FN % 2 == 0 && NW * HALF * 2 * FRAG <= KS * NST * STAGE, "swap rounds fit in LDS");
+        lds_u8* const xb = (lds_u8*)smem;
+#pragma unroll
+        for (int rd = 0; rd < 2; rd++) {
+            barrier();  // every wave is done with the LDS it is about to overwrite
+#pragma unroll
+            for (int i = 0; i < HALF; i++) {
+                const int in = rd * HALF + i;
+                // slot (wave, i, destination group)
+                lds_u8* dst = xb + ((wave * HALF + i) * 2 + (1 - grp)) * FRAG;
+                auto put = [&](const f32x16& a) {
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; g4++)
+                        *(__attribute__((address_space(3))) f32x4*)(dst + (g4 * 64 + lane) * 16) =
+                            f32x4{a[4 * g4], a[4 * g4 + 1], a[4 * g4 + 2], a[4 * g4 + 3]};
+                };
+                if (grp == 0) put(acc[in][1]);
+                else put(acc[in][0]);
+            }
+            barrier();
+#pragma unroll
+            for (int i = 0; i < HALF; i++) {
+                const int in = rd * HALF + i;
+                const lds_u8* src = xb + ((wave * HALF + i) * 2 + grp) * FRAG;
+                auto take = [&](f32x16& a) {
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; g4++) {
+                        const f32x4 v = *(const __attribute__((address_space(3))) f32x4*)(src + (g4 * 64 + lane) * 16);
+#pragma unroll
+                        for (int u = 0; u < 4; u++) a[4 * g4 + u] += v[u];
+                    }
+                };
+                if (grp == 0) take(acc[in][0]);
+                else take(acc[in][1]);
+            }
+        }
+    }
+
     if constexpr (LORA) {
         // rank-r bf16 correction into the same accumulator
         for (int kr = 0; kr < p.r; kr += 16) {
@@ -388,6 +446,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, (kWavesPerEU<BM / WGM, BN / WGN>)) 
             for (int in = 0; in < FN; in++)
 #pragma unroll
                 for (int im = 0; im < FM; im++)
+                    if (KS == 1 || im == grp)
                     acc[in][im] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ol[in], od[im], acc[in][im], 0, 0, 0);
         }
     }
@@ -407,6 +466,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, (kWavesPerEU<BM / WGM, BN / WGN>)) 
     constexpr int RPI = 64 / CPR;      // rows per wave store instruction
 #pragma unroll
     for (int im = 0; im < FM; im++) {
+        if (KS == 2 && im != grp) continue;  // the other K group stores this fragment row
         // lane (l32, h) of fragment in: row l32, columns in*32 + 8g + 4h .. +3
 #pragma unroll
         for (int in = 0; in < FN; in++) {
@@ -448,20 +508,21 @@ __global__ __launch_bounds__(64 * WGM * WGN, (kWavesPerEU<BM / WGM, BN / WGN>)) 
 #endif
 }
 
-template <int BM, int BN, int WGM, int WGN, int NST>
+template <int BM, int BN, int WGM, int WGN, int NST, int KS = 1>
 static hipError_t launch_tile(GParams p, bool lora, hipStream_t st) {
     p.tiles_m = (int)((p.M + BM - 1) / BM);
     p.tiles_n = (int)((p.N + BN - 1) / BN);
     const int tiles = p.tiles_m * p.tiles_n;
     p.xcd_chunk = tiles % 8 == 0 ? tiles / 8 : 0;
     dim3 grid(tiles, 1, (unsigned)p.E ? (unsigned)p.E : 1u);
+    constexpr int threads = 64 * WGM * WGN * KS;
     const bool aligned = (p.K % 128) == 0;
     if (lora) {
-        if (aligned) k_gemm<BM, BN, WGM, WGN, NST, true, true><<<grid, 64 * WGM * WGN, 0, st>>>(p);
-        else k_gemm<BM, BN, WGM, WGN, NST, false, true><<<grid, 64 * WGM * WGN, 0, st>>>(p);
+        if (aligned) k_gemm<BM, BN, WGM, WGN, NST, KS, true, true><<<grid, threads, 0, st>>>(p);
+        else k_gemm<BM, BN, WGM, WGN, NST, KS, false, true><<<grid, threads, 0, st>>>(p);
     } else {
-        if (aligned) k_gemm<BM, BN, WGM, WGN, NST, true, false><<<grid, 64 * WGM * WGN, 0, st>>>(p);
-        else k_gemm<BM, BN, WGM, WGN, NST, false, false><<<grid, 64 * WGM * WGN, 0, st>>>(p);
+        if (aligned) k_gemm<BM, BN, WGM, WGN, NST, KS, true, false><<<grid, threads, 0, st>>>(p);
+        else k_gemm<BM, BN, WGM, WGN, NST, KS, false, false><<<grid, threads, 0, st>>>(p);
     }
     return hipGetLastError();
 }
@@ -600,20 +661,24 @@ static hipError_t launch_skinny(GParams p, bool lora, hipStream_t st) {
     return hipGetLastError();
 }
 
-enum class Tile { T256x256, T128x256, T128x128, Skinny };
+enum class Tile { T256x256, T128x256, T128x256K2, T128x128, Skinny };
 
 // Workgroup tile per problem.  Larger wave tiles need fewer dequantization
-// instructions per MFMA (256x256: 4, 128x256: 6, 128x128: 8), but
-// the grid must still spread evenly over the 256 CUs (measured on the
-// workload shapes: the 256x256 tile needs at least two tiles per CU, the
-// 128x128 tile wins when it gives three per CU, its occupancy; grouped
-// problems, whose masked tiles exit at once, do best with 128x256).
-static Tile pick_tile(int64_t m, int64_t n, int64_t E) {
+// instructions per MFMA (64x128 waves of the 256x256 and 128x256 tiles: 6,
+// 64x64 waves of the 128x128 tile: 8), and two waves per SIMD hide one
+// wave's dequantization behind the other's MFMAs, but the grid must still
+// spread evenly over the 256 CUs (measured on the workload shapes: the
+// 256x256 tile needs at least two tiles per CU; the 128x128 tile wins when
+// it gives three per CU; with at most one 128x256 tile per CU the K loop is
+// split over two wave groups so each SIMD still holds two waves; grouped
+// problems, whose masked tiles exit at once, do best with plain 128x256).
+static Tile pick_tile(int64_t m, int64_t n, int64_t k, int64_t E) {
     auto tiles = [&](int64_t bm, int64_t bn) { return E * ((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
+    const bool even_steps = ((k + 127) / 128) % 2 == 0;
     if (m <= 64) return Tile::Skinny;
     if (tiles(256, 256) >= 2 * 256) return Tile::T256x256;
     if (E == 1 && tiles(128, 128) >= 3 * 256) return Tile::T128x128;
-    if (tiles(128, 256) >= 128) return Tile::T128x256;
+    if (tiles(128, 256) >= 128) return even_steps && tiles(128, 256) <= 256 ? Tile::T128x256K2 : Tile::T128x256;
     return Tile::T128x128;
 }
 
@@ -632,9 +697,10 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
     p.sfa = (int64_t)p.rpa * cp;
     p.sfb = (int64_t)p.rpb * cp;
     const bool lora = g.d != nullptr;
-    switch (pick_tile(g.m, g.n, g.E)) {
+    switch (pick_tile(g.m, g.n, g.k, g.E)) {
     case Tile::T256x256: return launch_tile<256, 256, 4, 2, 3>(p, lora, st);
     case Tile::T128x256: return launch_tile<128, 256, 2, 2, 2>(p, lora, st);
+    case Tile::T128x256K2: return launch_tile<128, 256, 2, 2, 2, 2>(p, lora, st);
     case Tile::Skinny: return launch_skinny(p, lora, st);
     default: return launch_tile<128, 128, 2, 2, 2>(p, lora, st);
     }

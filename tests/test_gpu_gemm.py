@@ -93,6 +93,8 @@ def test_bias(ops, shape):
     (1024, 8320, 400),   # 128x256 tiles, K % 128 != 0
     (200, 32800, 128),   # 128x256 tiles, a single partial tile row
     (3000, 4200, 144),   # 128x128 tiles (at least three per CU), ragged
+    (1100, 4100, 400),   # 128x256 tiles split over two K groups, ragged M, N and K
+    (640, 8000, 512),    # 128x256 tiles split over two K groups, ragged N
 ])
 def test_tile_shapes(ops, m, n, k):
     """Each workgroup tile shape the launcher picks, with ragged edges."""
@@ -151,7 +153,8 @@ def test_svdquant_workload(ops):
 
 
 @pytest.mark.parametrize("r,m,n,k", [(32, 150, 90, 192), (64, 150, 90, 192), (128, 150, 90, 192),
-                                     (64, 40, 200, 272)])   # small M: the skinny kernel
+                                     (64, 40, 200, 272),    # small M: the skinny kernel
+                                     (64, 1100, 4100, 400)])  # tiles split over two K groups
 def test_svdquant_ranks_and_ragged(ops, r, m, n, k):
     g = torch.Generator().manual_seed(r + m)
     a = torch.randn(m, k, generator=g).to(torch.bfloat16)
