@@ -376,6 +376,94 @@ __global__ __launch_bounds__(256) void k_quantize(QParams p) {
     for (int i = t; i < ntile_here * 32; i += 256) *(u32x4*)(sf_dst + i * 16) = *(const u32x4*)(sbuf + i * 16);
 }
 
+// ---------------------------------------------------------------------------
+// Small items (decode-sized activations) in DYNAMIC mode: the whole item in
+// one workgroup of 1024 threads.  Each thread loads up to kSmallBlocks 16-element blocks once
+// and keeps them in registers; the workgroup reduces the global amax, forms
+// gs, and quantizes from the registers, with the item's whole scale buffer
+// (padding included) assembled in LDS and written with 16-byte stores.  One
+// launch and one read of the input instead of the amax pass, the finish and
+// the quantize pass.  Same arithmetic, same results.
+// ---------------------------------------------------------------------------
+
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallSfBytes = 32768;     // largest padded scale buffer of an item
+// 16-element blocks per thread (the silu prologue needs more registers per
+// block, so it holds fewer)
+template <int V>
+constexpr int small_blocks() { return V == V_SILU ? 2 : 4; }
+
+template <int V>
+__global__ __launch_bounds__(1024) void k_quantize_small(QParams p) {
+    constexpr int NL = loads_per_block<V>();
+    constexpr int kSmallBlocks = small_blocks<V>();
+    const int e = blockIdx.x, t = threadIdx.x;
+    const int valid = clamp_rows(p.mask, e, (int)p.m);
+    const int bpr = (int)(p.K / 16);  // blocks per row
+    const int nb = valid * bpr;       // blocks of the valid rows
+    __shared__ __align__(16) uint8_t sfl[kSmallSfBytes];
+    __shared__ float wmax[kSmallThreads / 64];
+    for (int i = t; i < (int)(p.sfsz / 16); i += kSmallThreads) *(u32x4*)(sfl + i * 16) = u32x4{0u, 0u, 0u, 0u};
+    u32x4 raw[kSmallBlocks][NL];
+    u32x4 pq[kSmallBlocks][2];
+#pragma unroll
+    for (int i = 0; i < kSmallBlocks; i++) {  // every load in flight before any use
+        const int b = t + i * kSmallThreads;
+        const int row = b < nb ? b / bpr : 0, cb = b < nb ? b - (b / bpr) * bpr : 0;
+        load_block<V>(p, e, row, (int64_t)cb * 16, raw[i]);
+        load_pqs<V>(p, (int64_t)cb * 16, pq[i]);
+    }
+    float gs;
+    {
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kSmallBlocks; i++) {
+            float f[16];
+            const float a = process_block<V>(raw[i], pq[i], f);
+            if (t + i * kSmallThreads < nb) amax = __builtin_fmaxf(amax, a);
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, off));
+        if ((t & 63) == 0) wmax[t >> 6] = amax;
+        __syncthreads();
+        float am = wmax[0];
+#pragma unroll
+        for (int w = 1; w < kSmallThreads / 64; w++) am = __builtin_fmaxf(am, wmax[w]);
+        const float lo = 1e-12f;
+        gs = 2688.0f / (am < lo ? lo : am);
+        if (t == 0) p.gs[e] = gs;
+    }
+    uint8_t* q = p.out_fp4 + (int64_t)e * p.m * (p.K / 2);
+    const int cpa4 = p.nct;  // 4-column scale groups per row
+#pragma unroll
+    for (int i = 0; i < kSmallBlocks; i++) {
+        const int b = t + i * kSmallThreads;
+        if (b >= nb) continue;
+        const int row = b / bpr, cb = b - (b / bpr) * bpr;
+        float f[16];
+        const float bamax = process_block<V>(raw[i], pq[i], f);
+        const uint32_t sc = ue4m3_encode((bamax / 6.0f) * gs);
+        const float dec = ue4m3_decode(sc);
+        const float r = dec == 0.0f ? 0.0f : gs / dec;
+        uint32_t w0 = 0, w1 = 0;
+        w0 = NVFP4_PACK_FP4(w0, f[0] * r, f[1] * r, 0);
+        w0 = NVFP4_PACK_FP4(w0, f[2] * r, f[3] * r, 1);
+        w0 = NVFP4_PACK_FP4(w0, f[4] * r, f[5] * r, 2);
+        w0 = NVFP4_PACK_FP4(w0, f[6] * r, f[7] * r, 3);
+        w1 = NVFP4_PACK_FP4(w1, f[8] * r, f[9] * r, 0);
+        w1 = NVFP4_PACK_FP4(w1, f[10] * r, f[11] * r, 1);
+        w1 = NVFP4_PACK_FP4(w1, f[12] * r, f[13] * r, 2);
+        w1 = NVFP4_PACK_FP4(w1, f[14] * r, f[15] * r, 3);
+        *(uint2*)(q + (int64_t)row * (p.K / 2) + cb * 8) = uint2{w0, w1};
+        sfl[((row >> 7) * cpa4 + (cb >> 2)) * 512 + (row & 31) * 16 + ((row & 127) >> 5) * 4 + (cb & 3)] =
+            (uint8_t)sc;
+    }
+    __syncthreads();
+    uint8_t* sf_dst = p.out_sf + (int64_t)e * p.sfsz;
+    for (int i = t; i < (int)(p.sfsz / 16); i += kSmallThreads)
+        *(u32x4*)(sf_dst + i * 16) = *(const u32x4*)(sfl + i * 16);
+}
+
 __global__ void k_alpha(const float* ga, const float* gb, float* alpha, int64_t n) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) alpha[i] = 1.0f / (ga[i] * gb[i]);
@@ -405,6 +493,12 @@ static void launch_quantize_pass(const QParams& p, hipStream_t st) {
 template <int V>
 static hipError_t launch_variant(QParams p, bool dynamic, hipStream_t st) {
     constexpr int CTA = V == V_SILU ? 1 : 2;
+    // DYNAMIC mode on small items: one launch instead of three (a STATIC pass
+    // is one launch anyway, and spreads over more compute units)
+    if (dynamic && p.m * p.K <= (int64_t)kSmallThreads * small_blocks<V>() * 16 && p.sfsz <= kSmallSfBytes) {
+        k_quantize_small<V><<<p.b, kSmallThreads, 0, st>>>(p);
+        return hipGetLastError();
+    }
     if (dynamic) {
         // one amax workgroup, and one partial maximum, per amax tile
         p.amax_blocks = p.nrt * ((p.nct + CTA - 1) / CTA);

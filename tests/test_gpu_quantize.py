@@ -1,6 +1,12 @@
 """GPU parity of the quantizers against the oracle: FP4 bytes, scale bytes
 and global scales must be bit-identical.  Outputs start filled with a canary
-byte so that unwritten padding and masked rows are caught."""
+byte so that unwritten padding and masked rows are caught.
+
+In DYNAMIC mode, items of at most 65536 elements (32768 with the silu
+prologue) whose padded scale buffer fits 32 KB are quantized by one
+workgroup per item; larger ones, and STATIC mode, by the tiled passes.  The
+cases below cover each prologue and masking form on both sides of that
+line."""
 import numpy as np
 import pytest
 import torch
@@ -57,10 +63,17 @@ def test_bf16_dynamic_ragged(ops, m, k):
 
 
 @pytest.mark.parametrize("gs", [384.0, 1.0, 1e-3, 7.25e4])
-def test_bf16_static(ops, gs):
+@pytest.mark.parametrize("m,k", [(200, 320), (600, 1024)])
+def test_bf16_static(ops, gs, m, k):
     g = torch.Generator().manual_seed(7)
-    x = torch.randn(200, 320, generator=g).to(torch.bfloat16)
+    x = torch.randn(m, k, generator=g).to(torch.bfloat16)
     run_single(ops, x, ops.GS_STATIC, gs=gs)
+
+
+def test_fp32_dynamic_tiled(ops):
+    g = torch.Generator().manual_seed(8)
+    x = torch.randn(300, 1040, generator=g) * 5
+    run_single(ops, x, ops.GS_DYNAMIC)
 
 
 def test_tiny_workload_fp32(ops):
@@ -77,9 +90,10 @@ def test_worked_example(ops):
     assert bytes(np_bits(o4)[0]) == bytes.fromhex("D723 01F0 4612 B581 D742 F600 9374 2E81".replace(" ", ""))
 
 
-def test_nonfinite_and_denormal_inputs(ops):
+@pytest.mark.parametrize("m,k", [(64, 128), (640, 256)])
+def test_nonfinite_and_denormal_inputs(ops, m, k):
     g = torch.Generator().manual_seed(3)
-    x = torch.randn(64, 128, generator=g)
+    x = torch.randn(m, k, generator=g)
     x[0, 5] = float("nan")
     x[1, 17] = float("inf")
     x[2, 33] = float("-inf")
@@ -91,12 +105,13 @@ def test_nonfinite_and_denormal_inputs(ops):
     xb[6, 40] = float("nan")
     run_single(ops, xb, ops.GS_DYNAMIC)
     # without the non-finite values: denormal and zero rows only
-    x2 = torch.randn(64, 128, generator=g) * 1e-38
+    x2 = torch.randn(m, k, generator=g) * 1e-38
     run_single(ops, x2.to(torch.bfloat16), ops.GS_DYNAMIC)
 
 
-def test_smooth_prologue(ops):
-    s = synth.svdquant(m=300, n=64, k=320)
+@pytest.mark.parametrize("m", [100, 300])
+def test_smooth_prologue(ops, m):
+    s = synth.svdquant(m=m, n=64, k=320)
     run_single(ops, s.x, ops.GS_DYNAMIC, pqs=s.pqs)
     run_single(ops, s.x.float(), ops.GS_DYNAMIC, pqs=s.pqs)
 
@@ -142,16 +157,18 @@ def run_batched(ops, x_cpu, mask, mode, silu=False, gs=None):
 
 
 @pytest.mark.parametrize("mask", [None, [0, 1, 129, 200], [200, 200, 200, 200], [5, 0, 0, 77]])
-def test_masked_batched(ops, mask):
+@pytest.mark.parametrize("k", [96, 512])
+def test_masked_batched(ops, mask, k):
     g = torch.Generator().manual_seed(21)
-    x = (torch.randn(4, 200, 96, generator=g) * torch.tensor([1.0, 10.0, 0.1, 3.0])[:, None, None])
+    x = (torch.randn(4, 200, k, generator=g) * torch.tensor([1.0, 10.0, 0.1, 3.0])[:, None, None])
     mk = None if mask is None else torch.tensor(mask, dtype=torch.int32)
     run_batched(ops, x.to(torch.bfloat16), mk, ops.GS_DYNAMIC)
 
 
-def test_masked_batched_static(ops):
+@pytest.mark.parametrize("k", [64, 768])
+def test_masked_batched_static(ops, k):
     g = torch.Generator().manual_seed(22)
-    x = torch.randn(3, 130, 64, generator=g).to(torch.bfloat16)
+    x = torch.randn(3, 130, k, generator=g).to(torch.bfloat16)
     run_batched(ops, x, torch.tensor([130, 64, 1], dtype=torch.int32), ops.GS_STATIC,
                 gs=torch.tensor([100.0, 250.0, 3.0]))
 
@@ -163,9 +180,10 @@ def test_mask_out_of_range_is_clamped(ops):
 
 
 @pytest.mark.parametrize("mask", [[64, 0, 17], [1, 64, 33]])
-def test_silu_masked(ops, mask):
+@pytest.mark.parametrize("h", [96, 1024])
+def test_silu_masked(ops, mask, h):
     g = torch.Generator().manual_seed(31)
-    x = (torch.randn(3, 64, 2 * 96, generator=g) * 2).to(torch.bfloat16)
+    x = (torch.randn(3, 64, 2 * h, generator=g) * 2).to(torch.bfloat16)
     run_batched(ops, x, torch.tensor(mask, dtype=torch.int32), ops.GS_DYNAMIC, silu=True)
 
 
@@ -185,14 +203,14 @@ def test_silu_every_bf16_gate(ops):
             run_batched(ops, x, None, ops.GS_DYNAMIC, silu=True)
 
 
-def test_silu_random_pairs(ops):
-    """One million (gate, up) pairs: gates uniform over the finite bf16 bit
-    patterns (every binade), up values N(0,1) times random powers of two.
+@pytest.mark.parametrize("b,m,h", [(16, 128, 512), (16, 64, 256)])
+def test_silu_random_pairs(ops, b, m, h):
+    """Up to one million (gate, up) pairs: gates uniform over the finite bf16
+    bit patterns (every binade), up values N(0,1) times random powers of two.
     The kernel decides most products of silu(g) and u on a fast fp32 path
     and only the ones next to a bf16 rounding boundary exactly; every byte
     must still equal the oracle's."""
-    rng = np.random.default_rng(2024)
-    b, m, h = 16, 128, 512
+    rng = np.random.default_rng(2024 + m)
     bits = rng.integers(0, 65536, size=(b, m, h), dtype=np.uint32).astype(np.uint16)
     finite = (bits & 0x7F80) != 0x7F80
     bits = np.where(finite, bits, bits & 0x807F)   # non-finite patterns -> small values
