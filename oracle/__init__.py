@@ -60,6 +60,11 @@ def lib():
             ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
             ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
         ]
+        L.nvo_gemm_w4a16_rows.restype = ctypes.c_int
+        L.nvo_gemm_w4a16_rows.argtypes = [
+            ctypes.c_void_p, u8p, u8p, ctypes.c_float, ctypes.c_void_p, ctypes.c_int64,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+        ]
         L.nvo_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -183,4 +188,24 @@ def gemm_rows(a, b, a_sf, b_sf, alpha, m, n, k, rows=None, bias=None, d=None, l1
                              _vp(out))
     if rc != 0:
         raise ValueError(f"oracle gemm rejected the arguments (status {rc})")
+    return out
+
+
+def gemm_w4a16_rows(a_bf16, b, b_sf, alpha, m, n, k, rows=None, bias=None):
+    """fp64 alpha * (A @ Bdq^T) + bias for the given rows of the bf16
+    activation A ([NVF] f16a_nvfp4weight_scaled_mm); a_bf16: uint16 bit
+    patterns [m, k]; alpha = 1 / the weight's global scale."""
+    a_bf16 = np.ascontiguousarray(a_bf16, dtype=np.uint16)
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    b_sf = np.ascontiguousarray(b_sf, dtype=np.uint8)
+    if rows is None:
+        rows = np.arange(m, dtype=np.int64)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.uint16)
+    out = np.zeros((len(rows), n), dtype=np.float64)
+    rc = lib().nvo_gemm_w4a16_rows(_vp(a_bf16), _u8(b), _u8(b_sf), float(np.float32(alpha)), _vp(bias),
+                                   m, n, k, _vp(rows), len(rows), _vp(out))
+    if rc != 0:
+        raise ValueError(f"oracle weight-only gemm rejected the arguments (status {rc})")
     return out

@@ -13,7 +13,9 @@
  *         the module-level _global_sf helper (amax with nan_to_num, clamp at
  *         1e-12, global scale 448*6/amax).
  *   [NVF] NVIDIA/Fuser PR #5737 "Benchmark for nvfp4 scaled mm" -- the eager
- *         op is "dequantize_to_dtype() then F.linear" (sequence diagram).
+ *         op is "dequantize_to_dtype() then F.linear" (sequence diagram); the
+ *         weight-only op f16a_nvfp4weight_scaled_mm takes a 16-bit activation,
+ *         the FP4 weight, its block scales and its global scale.
  *   [FI]  flashinfer PR #1774 "Masked batch nvfp4 quantization" -- batched
  *         and masked quantize, silu_and_mul fused before quantize, per-item
  *         global scale (review comments on the test and the fake ops).
@@ -46,6 +48,9 @@
  *
  * The GEMM accumulates in fp64 (products of two dequantized NVFP4 values are
  * exact in either precision); the pages leave the accumulation order free.
+ * The weight-only GEMM multiplies the fp64 sum of activation x (e2m1 x
+ * block scale) products by 1/global_scale once, where the pages' eager path
+ * divides each dequantized weight and rounds it to bf16 first.
  */
 #include <float.h>
 #include <math.h>
@@ -393,6 +398,47 @@ int nvo_gemm_rows(const uint8_t *a, const uint8_t *b, const uint8_t *a_sf, const
             }
         }
         free(arow);
+    }
+    free(bdq);
+    return NVO_OK;
+}
+
+/*
+ * Weight-only form ([NVF] f16a_nvfp4weight_scaled_mm: the bf16 activation
+ * against the dequantized weight, then F.linear).  For each requested row i
+ * (rows[j]): out[j, n] = alpha * sum_k a[i,k] * Bdq[n,k] + bias[n] in fp64,
+ * not rounded to bf16.  a: bf16 [m, k]; alpha = 1 / the weight's global
+ * scale; bias: NULL or bf16 [n].
+ */
+int nvo_gemm_w4a16_rows(const uint16_t *a, const uint8_t *b, const uint8_t *b_sf, float alpha,
+                        const uint16_t *bias, int64_t m, int64_t n, int64_t k, const int64_t *rows,
+                        int64_t nrows, double *out)
+{
+    if (k % 16 != 0 || m < 0 || n < 0)
+        return NVO_BAD;
+    for (int64_t j = 0; j < nrows; j++)
+        if (rows[j] < 0 || rows[j] >= m)
+            return NVO_BAD;
+    double *bdq = (double *)malloc(sizeof(double) * (size_t)(n * k > 0 ? n * k : 1));
+    if (!bdq)
+        return NVO_BAD;
+#pragma omp parallel for schedule(static)
+    for (int64_t nn = 0; nn < n; nn++)
+        for (int64_t kk = 0; kk < k; kk++)
+            bdq[nn * k + kk] = dq(b, b_sf, nn, kk, k);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t j = 0; j < nrows; j++) {
+        const uint16_t *arow = a + rows[j] * k;
+        for (int64_t nn = 0; nn < n; nn++) {
+            double acc = 0.0;
+            const double *brow = bdq + nn * k;
+            for (int64_t kk = 0; kk < k; kk++)
+                acc += (double)nvo_bf16_to_f32(arow[kk]) * brow[kk];
+            double y = (double)alpha * acc;
+            if (bias)
+                y += (double)nvo_bf16_to_f32(bias[nn]);
+            out[j * n + nn] = y;
+        }
     }
     free(bdq);
     return NVO_OK;

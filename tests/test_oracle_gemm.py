@@ -135,3 +135,57 @@ def test_svdquant_zero_residual_is_lora_plus_bias():
                       d=synth.bits(d), l1=synth.bits(l1))
     ref = float(alpha) * (d.double() @ l1.double().T) + bias.double()
     np.testing.assert_allclose(out, ref.numpy(), rtol=1e-13, atol=1e-13)
+
+
+# ---- weight-only form (nvFuser page: f16a_nvfp4weight_scaled_mm) -------------------
+
+
+def test_w4a16_reduces_to_nvfp4_gemm():
+    """An activation whose bf16 values are exactly its own NVFP4 dequantization
+    (e2m1 x block scale, at most 6 significant bits) gives the NVFP4 x NVFP4
+    product bit for bit: the two oracle routines then sum identical fp64 terms."""
+    rng = np.random.default_rng(31)
+    m, n, k = 9, 21, 96
+    a, asf, ga = rand_quant(rng, m, k, 2.0)
+    b, bsf, gb = rand_quant(rng, n, k, 0.02)
+    a_dq = dequant_torch(a, asf, m, k)
+    a_bf16 = a_dq.to(torch.bfloat16)
+    assert torch.equal(a_bf16.double(), a_dq), "dequantized NVFP4 values are exact in bf16"
+    alpha = np.float32(1.0) / gb
+    bias = torch.randn(n).to(torch.bfloat16)
+    w = O.gemm_w4a16_rows(synth.bits(a_bf16), b, bsf, alpha, m, n, k, bias=synth.bits(bias))
+    ref = O.gemm_rows(a, b, asf, bsf, alpha, m, n, k, bias=synth.bits(bias))
+    assert np.array_equal(w, ref)
+
+
+def test_w4a16_matches_exact_weight():
+    """A weight built from e2m1 values times powers of two, every 16-block
+    holding its own +-6 x 2^j, quantizes without loss (gs = 448 / 2^jmax and
+    every block scale a power-of-two multiple of 448): the dequantized weight
+    is exactly w * gs, so the weight-only product must equal the float64
+    product a @ (w * gs)^T (exact: at most 14-bit products, 64 terms) times
+    the fp32 alpha = 1/gs, bit for bit."""
+    rng = np.random.default_rng(32)
+    m, n, k = 7, 12, 64
+    vals = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    w = rng.choice(vals, size=(n, k)) * rng.choice([-1.0, 1.0], size=(n, k))
+    w[:, ::16] = 6.0 * rng.choice([-1.0, 1.0], size=(n, k // 16))  # each block's maximum
+    pw = 2.0 ** rng.integers(-6, 3, size=(n, k // 16))
+    w = w * np.repeat(pw, 16, axis=1)
+    q, sf, gs = O.quantize(w.astype(np.float32))
+    assert gs[0] == np.float32(448.0 / pw.max())
+    a = torch.randn(m, k).to(torch.bfloat16)
+    alpha = np.float32(1.0) / gs[0]
+    out = O.gemm_w4a16_rows(synth.bits(a), q, sf, alpha, m, n, k)
+    ref = float(alpha) * (a.double().numpy() @ (w * float(gs[0])).T)
+    assert np.array_equal(out, ref), np.abs(out - ref).max()
+
+
+def test_w4a16_row_subset():
+    rng = np.random.default_rng(33)
+    m, n, k = 11, 9, 48
+    b, bsf, gb = rand_quant(rng, n, k)
+    a = synth.bits(torch.randn(m, k).to(torch.bfloat16))
+    full = O.gemm_w4a16_rows(a, b, bsf, 0.5, m, n, k)
+    rows = np.array([10, 0, 4])
+    assert np.array_equal(O.gemm_w4a16_rows(a, b, bsf, 0.5, m, n, k, rows=rows), full[rows])
