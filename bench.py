@@ -58,6 +58,8 @@ class Workload:
 
 def build_workload(name, ops, synth, torch):
     w = Workload()
+    w.hbm_bound = False
+    w.w4a16 = None
     dev = "cuda"
     if name in ("prefill", "dense", "decode", "tiny"):
         if name == "prefill":
@@ -109,6 +111,14 @@ def build_workload(name, ops, synth, torch):
         w.pre, w.quant, w.gemm = pre, quant, gemm
         w.outputs = (fa, sfa, gsa, alpha, out)
         w.cfg = {"m": m, "n": n, "k": k}
+        w.hbm_bound = name == "decode"   # 16 rows: the weight read bounds the GEMM
+        if name == "decode":
+            # weight-only form: the bf16 activation against the NVFP4 weight,
+            # no activation quantization (alpha = 1 / the weight's gs)
+            alpha_w = ops.nvfp4_alpha(torch.ones(1, dtype=torch.float32, device=dev), gsw)
+            out_w = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+            w.w4a16 = lambda a: ops.nvfp4_gemm_w4a16(a, fw, sfw, alpha_w, out=out_w)
+            w.w4a16_bytes = n * k // 2 + sf_size(n, k) + m * k * 2 + 2 * m * n
         w.cpu_sample = lambda O, np: cpu_baseline_dense(O, np, a_cpu, w_cpu, synth)
         return w
 
@@ -339,6 +349,19 @@ def main():
         qdyn_ms = time_graph(torch, g_dyn) / n_copies
     else:
         qdyn_ms = qpass_ms
+    # the GEMM alone, back to back (for the weight-bound decode shape, whose
+    # eager launches cost more than the kernel)
+    g_gemm = capture(torch, lambda: [w.gemm() for _ in range(n_copies)])
+    gemm_graph_ms = time_graph(torch, g_gemm) / n_copies
+    del g_gemm
+    w4 = None
+    if w.w4a16 is not None:
+        g_w4 = capture(torch, lambda: [w.w4a16(a) for a in acts])
+        w4_ms = time_graph(torch, g_w4) / n_copies
+        del g_w4
+        w4_gbs = w.w4a16_bytes / (w4_ms * 1e-3) / 1e9
+        w4 = {"ms": round(w4_ms, 5), "gbs": round(w4_gbs, 1), "frac_hbm": round(w4_gbs / HBM_PEAK_GBS, 4),
+              "bytes": w.w4a16_bytes, "kernel": "k_gemm_w4a16 (bf16 activation x NVFP4 weight, no activation quantize)"}
     src = torch.ones(64 * 2 ** 20, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     g_copy = capture(torch, lambda: [torch.neg(src, out=dst) for _ in range(4)])
@@ -366,7 +389,8 @@ def main():
         "config": {"workload": w.desc, **w.cfg, "operands": "NVFP4 (e2m1 + ue4m3 per 16, 128x4 swizzled)",
                    "parallelism": "none (1 GPU)", "activation_copies_rotated": n_copies},
         "gemm": {"ms": round(gemm_ms, 4), "tflops": round(gemm_tflops, 2),
-                 "frac_f16_mfma_peak": round(gemm_tflops / MFMA_F16_PEAK_TFLOPS, 4)},
+                 "frac_f16_mfma_peak": round(gemm_tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                 "back_to_back_ms": round(gemm_graph_ms, 5)},
         "quantize": {"pass_ms": round(qpass_ms, 4), "pass_gbs": round(q_gbs, 1),
                      "pass_frac_hbm": round(q_gbs / HBM_PEAK_GBS, 4),
                      "amax_and_finish_ms": round(amax_ms, 4),
@@ -381,6 +405,16 @@ def main():
                      "traffic": gemm_traffic(args.workload), "kernel": "k_gemm (block-scaled NVFP4 GEMM)",
                      "flops_per_launch": w.flops, "algorithmic_bytes_per_launch": w.gemm_bytes},
     }
+    if w.hbm_bound:
+        # 16 activation rows: the GEMM streams the weight once; its roofline is
+        # HBM, over the back-to-back kernel time
+        gbs = w.gemm_bytes / (gemm_graph_ms * 1e-3) / 1e9
+        res["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                           "kernel": "k_gemm_skinny (block-scaled NVFP4 GEMM, 16 rows)",
+                           "algorithmic_bytes_per_launch": w.gemm_bytes}
+    if w4 is not None:
+        res["w4a16"] = w4
     if not args.no_cpu_baseline and w.cpu_sample is not None:
         import oracle as O
         res["cpu_baseline"] = w.cpu_sample(O, np)

@@ -172,6 +172,25 @@ int nvfp4_gemm_svdquant(const uint8_t *a, const uint8_t *b, const uint8_t *a_sf,
                         void *stream);
 
 /*
+ * Weight-only GEMM (NVIDIA/Fuser PR #5737: f16a_nvfp4weight_scaled_mm, whose
+ * eager meaning is the weight dequantized, then a plain linear with the
+ * 16-bit activation):
+ *   out = bf16(alpha * (A @ Bdq^T) (+ bias)),  Bdq = e2m1(b) * ue4m3(b_sf),
+ * accumulated in fp32, alpha = 1 / the weight's global scale (nvfp4_alpha
+ * with gs_a = 1 forms it on the device).  For decode, where the weight read
+ * bounds the time and the activation is used as is, without quantization.
+ *   a: [m, k] bf16 row-major, 16-byte aligned; b: [n, k/2] uint8 packed e2m1;
+ *   b_sf: pad_up(n,128)*pad_up(k/16,4) ue4m3 in the 128x4 swizzled layout;
+ *   alpha: device fp32 scalar; bias: NULL or [n] bf16; out: [m, n] bf16.
+ * Requires m, n >= 1, k >= 16, k % 16 == 0.  All pointers are device
+ * pointers owned by the caller; nothing is allocated.  Returns
+ * NVFP4_NULL_POINTER, NVFP4_BAD_SHAPE or NVFP4_MISALIGNED before launching
+ * anything when an argument is invalid.
+ */
+int nvfp4_gemm_w4a16(const void *a, const uint8_t *b, const uint8_t *b_sf, const float *alpha,
+                     const void *bias, void *out, int64_t m, int64_t n, int64_t k, void *stream);
+
+/*
  * alpha[i] = 1 / (gs_a[i] * gs_b[i]) in fp32 for i < count, on the device
  * (TensorRT-LLM create_weights, the alpha parameter).  Lets a caller that
  * quantizes activations in DYNAMIC mode form the GEMM's alpha without a host

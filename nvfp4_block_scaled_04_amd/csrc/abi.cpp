@@ -125,6 +125,21 @@ int nvfp4_gemm_svdquant(const uint8_t* a, const uint8_t* b, const uint8_t* a_sf,
     return gemm_common(a, b, a_sf, b_sf, alpha, nullptr, bias, d, l1, out, 1, m, n, k, r, stream);
 }
 
+int nvfp4_gemm_w4a16(const void* a, const uint8_t* b, const uint8_t* b_sf, const float* alpha,
+                     const void* bias, void* out, int64_t m, int64_t n, int64_t k, void* stream) {
+    if (!a || !b || !b_sf || !alpha || !out) return NVFP4_NULL_POINTER;
+    if (!dim_ok(m) || !dim_ok(n) || k < 16 || k % 16 != 0 || k > kMaxDim) return NVFP4_BAD_SHAPE;
+    if ((m + 15) / 16 > 65535 || (n + 15) / 16 > ((int64_t)1 << 31) - 1) return NVFP4_BAD_SHAPE;
+    if (!aligned16(a) || !aligned16(b) || !aligned16(b_sf) || !aligned16(out) || ((uintptr_t)alpha & 3u) ||
+        (bias && !aligned16(bias)))
+        return NVFP4_MISALIGNED;
+    nvfp4::GemmArgs g{};
+    g.a = (const uint8_t*)a; g.b = b; g.b_sf = b_sf; g.alpha = alpha;
+    g.bias = (const uint16_t*)bias; g.out = (uint16_t*)out;
+    g.E = 1; g.m = m; g.n = n; g.k = k;
+    return launch_status(nvfp4::launch_gemm_w4a16(g, (hipStream_t)stream));
+}
+
 int nvfp4_alpha(const float* gs_a, const float* gs_b, float* alpha, int64_t count, void* stream) {
     if (!gs_a || !gs_b || !alpha) return NVFP4_NULL_POINTER;
     if (!dim_ok(count)) return NVFP4_BAD_SHAPE;

@@ -648,6 +648,137 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GParams p) {
 #endif
 }
 
+// ---------------------------------------------------------------------------
+// Weight-only GEMM (nvFuser page: f16a_nvfp4weight_scaled_mm, the bf16
+// activation against the dequantized NVFP4 weight): out = bf16(alpha *
+// (A @ Bdq^T) (+ bias)) with A bf16 [M, K] and alpha = 1 / the weight's
+// global scale.  Built for decode, where the weight read bounds the time:
+// the skinny kernel's layout (a 16 x 16 output tile per workgroup, the K
+// loop split over its 4 waves, partial tiles added through LDS, 16-byte
+// weight loads covering 32 elements of a row per lane), with the weight
+// dequantized exactly to bf16 (e2m1 times the block scale has at most 6
+// significant bits) for v_mfma_f32_16x16x32_bf16.  The activation needs no
+// conversion.  Any M works (grid y = M / 16); large M is better served by
+// quantizing the activation and using the NVFP4 x NVFP4 kernels.
+// ---------------------------------------------------------------------------
+
+// 8 FP4 codes of one dword times one block scale -> 8 bf16 (exact).
+__device__ __forceinline__ bf16x8 dequant8_bf16(uint32_t w, float s) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    const bf16x2 h0 = __builtin_convertvector(f32x2{v0[0] * s, v0[1] * s}, bf16x2);
+    const bf16x2 h1 = __builtin_convertvector(f32x2{v1[0] * s, v1[1] * s}, bf16x2);
+    const bf16x2 h2 = __builtin_convertvector(f32x2{v2[0] * s, v2[1] * s}, bf16x2);
+    const bf16x2 h3 = __builtin_convertvector(f32x2{v3[0] * s, v3[1] * s}, bf16x2);
+    return bf16x8{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+}
+
+template <bool ALIGNED>
+__global__ __launch_bounds__(256) void k_gemm_w4a16(GParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int64_t n0 = (int64_t)blockIdx.x * 16, m0 = (int64_t)blockIdx.y * 16;
+    const int64_t rowb = p.K / 2;
+    const int r = lane & 15, g = lane >> 4;
+    const int64_t arow = m0 + r < p.M ? m0 + r : p.M - 1;
+    const int64_t brow = n0 + r < p.N ? n0 + r : p.N - 1;
+    const uint16_t* A = (const uint16_t*)p.a + arow * p.K;
+    const uint8_t* B = p.b + brow * rowb;
+
+    const int nch = (int)((p.K + 127) / 128);
+    const int per = (nch + 3) / 4;
+    const int c0 = wave * per, c1 = c0 + per < nch ? c0 + per : nch;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    constexpr int U = 4;  // chunks whose loads are in flight together
+    for (int cb = c0; cb < c1; cb += U) {
+        u32x4 fa[U][4], fb[U];
+        uint32_t sb[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int c = cb + u < c1 ? cb + u : c1 - 1;  // past the range: reload, never used
+            const int64_t ke = (int64_t)c * 128 + g * 32;  // first of this lane's 32 elements
+            const int blk = c * 8 + 2 * g;                 // first of its two blocks
+            if (ALIGNED) {
+#pragma unroll
+                for (int j = 0; j < 4; j++) fa[u][j] = *(const u32x4*)(A + ke + 8 * j);
+                fb[u] = *(const u32x4*)(B + ke / 2);
+            } else {
+                // 32, 16 or no valid elements in the group; the rest is zero
+                const int64_t left = p.K - ke;
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+                    fa[u][j] = left >= 8 * (j + 1) ? *(const u32x4*)(A + ke + 8 * j) : u32x4{0u, 0u, 0u, 0u};
+                const u32x2 zb = left >= 16 ? *(const u32x2*)(B + ke / 2) : u32x2{0u, 0u};
+                const u32x2 yb = left >= 32 ? *(const u32x2*)(B + ke / 2 + 8) : u32x2{0u, 0u};
+                fb[u] = u32x4{zb.x, zb.y, yb.x, yb.y};
+            }
+            const int bc = blk < p.nblk ? blk : 0;  // past K: any valid (even) block column, masked below
+            uint32_t vb = *(const uint16_t*)(p.b_sf + scale_byte_off(brow, bc, p.cpa4));
+            if (!ALIGNED) vb &= blk + 1 < p.nblk ? 0xFFFFu : blk < p.nblk ? 0x00FFu : 0u;
+            sb[u] = vb;
+        }
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            if (cb + u >= c1) break;
+            const float s0 = __builtin_amdgcn_cvt_f32_fp8(sb[u], 0), s1 = __builtin_amdgcn_cvt_f32_fp8(sb[u], 1);
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const bf16x8 ob = dequant8_bf16(word(fb[u], j), j < 2 ? s0 : s1);
+                const bf16x8 oa = __builtin_bit_cast(bf16x8, fa[u][j]);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ob, oa, acc, 0, 0, 0);
+            }
+        }
+    }
+    // sum the four waves' partial tiles
+    __shared__ f32x4 part[3][64];
+    if (wave > 0) part[wave - 1][lane] = acc;
+    __syncthreads();
+    if (wave != 0) return;
+    acc += part[0][lane] + part[1][lane] + part[2][lane];
+    // lane: output row m0 + r, columns n0 + 4g .. n0 + 4g + 3
+    const int64_t m = m0 + r;
+    if (m >= p.M) return;
+    const float alpha = p.alpha[0];
+    uint16_t* O = p.out + m * p.N;
+    const int64_t n = n0 + 4 * g;
+    float y[4];
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+        y[v] = alpha * acc[v];
+        if (p.bias && n + v < p.N) y[v] += bf16_lo((uint32_t)p.bias[n + v]);
+    }
+    if ((p.N & 3) == 0 && n + 3 < p.N) {
+        uint2 o;
+        o.x = f32_to_bf16_rne(y[0]) | (f32_to_bf16_rne(y[1]) << 16);
+        o.y = f32_to_bf16_rne(y[2]) | (f32_to_bf16_rne(y[3]) << 16);
+        *(uint2*)(O + n) = o;
+    } else {
+#pragma unroll
+        for (int v = 0; v < 4; v++)
+            if (n + v < p.N) O[n + v] = (uint16_t)f32_to_bf16_rne(y[v]);
+    }
+#endif
+}
+
+hipError_t launch_gemm_w4a16(const GemmArgs& g, hipStream_t st) {
+    GParams p{};
+    p.a = g.a; p.b = g.b; p.b_sf = g.b_sf;
+    p.alpha = g.alpha; p.bias = g.bias; p.out = g.out;
+    p.M = g.m; p.N = g.n; p.K = g.k; p.E = 1;
+    const int64_t cp = ((g.k / 16) + 3) / 4 * 4;
+    p.cpa4 = (int)(cp / 4);
+    p.nblk = (int)(g.k / 16);
+    dim3 grid((unsigned)((p.N + 15) / 16), (unsigned)((p.M + 15) / 16), 1u);
+    if (p.K % 128 == 0) k_gemm_w4a16<true><<<grid, 256, 0, st>>>(p);
+    else k_gemm_w4a16<false><<<grid, 256, 0, st>>>(p);
+    return hipGetLastError();
+}
+
 static hipError_t launch_skinny(GParams p, bool lora, hipStream_t st) {
     dim3 grid((unsigned)((p.N + 15) / 16), (unsigned)((p.M + 15) / 16), (unsigned)p.E);
     const bool aligned = (p.K % 128) == 0;

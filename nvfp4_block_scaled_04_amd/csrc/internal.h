@@ -38,5 +38,7 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
+// Weight-only form: g.a is the bf16 activation [m, k] (a_sf unused).
+hipError_t launch_gemm_w4a16(const GemmArgs& g, hipStream_t st);
 
 }  // namespace nvfp4

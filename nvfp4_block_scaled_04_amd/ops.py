@@ -21,6 +21,7 @@ EXPORTS = (
     "nvfp4_gemm",
     "nvfp4_gemm_grouped_masked",
     "nvfp4_gemm_svdquant",
+    "nvfp4_gemm_w4a16",
     "nvfp4_alpha",
 )
 
@@ -47,6 +48,7 @@ def _load():
         "nvfp4_gemm": [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, vp],
         "nvfp4_gemm_grouped_masked": [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp],
         "nvfp4_gemm_svdquant": [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp],
+        "nvfp4_gemm_w4a16": [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp],
         "nvfp4_alpha": [vp, vp, vp, i64, vp],
     }
     for name, args in sig.items():
@@ -182,6 +184,20 @@ def nvfp4_gemm_svdquant(a, b, a_sf, b_sf, alpha, d, l1, bias=None, out=None):
     rc = _lib.nvfp4_gemm_svdquant(_ptr(a), _ptr(b), _ptr(a_sf), _ptr(b_sf), _ptr(alpha), _ptr(d),
                                   _ptr(l1), _ptr(bias), _ptr(out), m, n, k, r, _stream(a.device))
     _check(rc, "nvfp4_gemm_svdquant")
+    return out
+
+
+def nvfp4_gemm_w4a16(a, b, b_sf, alpha, bias=None, out=None):
+    """a: [m, k] bf16 activation, b: [n, k/2] packed FP4 weight ->
+    out [m, n] bf16 = alpha*(a @ dequant(b)^T) (+bias), alpha = 1/weight gs."""
+    _need(a, "a")
+    m, k = a.shape
+    n = b.shape[0]
+    if out is None:
+        out = torch.empty(m, n, dtype=torch.bfloat16, device=a.device)
+    rc = _lib.nvfp4_gemm_w4a16(_ptr(a), _ptr(b), _ptr(b_sf), _ptr(alpha), _ptr(bias), _ptr(out), m, n, k,
+                               _stream(a.device))
+    _check(rc, "nvfp4_gemm_w4a16")
     return out
 
 

@@ -34,6 +34,7 @@ def lib():
 def test_header_declares_the_entry_points():
     assert declared() == sorted([
         "nvfp4_alpha", "nvfp4_gemm", "nvfp4_gemm_grouped_masked", "nvfp4_gemm_svdquant",
+        "nvfp4_gemm_w4a16",
         "nvfp4_quantize", "nvfp4_quantize_masked_batched", "silu_mul_nvfp4_quantize",
     ])
 
@@ -168,6 +169,21 @@ def test_svdquant_rank_and_alignment(lib):
     assert run(l1=None) == NULLP
     assert run(d=P + 8) == MISAL     # d must be 16-byte aligned
     assert run(k=40) == SHAPE
+
+
+def test_w4a16_validation(lib):
+    f = lib.nvfp4_gemm_w4a16
+    f.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int64] * 3 + [ctypes.c_void_p]
+    run = lambda a=P, b=P, sf=P, alpha=P, bias=None, out=P, m=16, n=64, k=256: f(a, b, sf, alpha, bias, out, m, n, k, None)
+    assert run(a=None) == NULLP
+    assert run(alpha=None) == NULLP
+    assert run(out=None) == NULLP
+    assert run(k=40) == SHAPE
+    assert run(k=8) == SHAPE
+    assert run(m=0) == SHAPE
+    assert run(a=P + 8) == MISAL
+    assert run(bias=P + 2) == MISAL
+    assert run(alpha=P + 1) == MISAL
 
 
 def test_alpha_validation(lib):

@@ -233,6 +233,53 @@ def test_grouped_masked_few_rows(ops, mask):
     grouped_case(ops, 3, 48, 100, 144, mask, seed=3 + sum(mask))
 
 
+@pytest.mark.parametrize("m,n,k,with_bias", [(1, 1, 16, False), (7, 1000, 272, True), (16, 4096, 4096, False),
+                                             (33, 130, 2064, True), (64, 300, 400, False), (100, 257, 128, True)])
+def test_w4a16(ops, m, n, k, with_bias):
+    """Weight-only GEMM (bf16 activation x NVFP4 weight) against the oracle:
+    one or several 16-row tiles, ragged N, K % 128 != 0, bias; the 16 x 4096
+    x 4096 case is the decode shape."""
+    g = torch.Generator().manual_seed(m * 31 + n + k)
+    a = (torch.randn(m, k, generator=g) * 2).to(torch.bfloat16)
+    w = (torch.randn(n, k, generator=g) * 0.02).to(torch.bfloat16)
+    bias = (torch.randn(n, generator=g) * 0.1).to(torch.bfloat16) if with_bias else None
+    say("w4a16", (m, n, k), "bias", with_bias)
+    qb, sb, gb = oq(w)
+    alpha = np.float32(1.0) / gb[0]
+    out = torch.full((m, n), OUT_CANARY, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    ops.nvfp4_gemm_w4a16(dev(a), t_u8(qb), t_u8(sb), torch.tensor([alpha], dtype=torch.float32, device="cuda"),
+                         bias=None if bias is None else dev(bias), out=out)
+    torch.cuda.synchronize()
+    ref = O.gemm_w4a16_rows(np_bits(a), qb, sb, alpha, m, n, k,
+                            bias=None if bias is None else np_bits(bias))
+    got = out.float().cpu().numpy()
+    ratio = row_tolerance_check(got, ref)
+    print(f"  worst row error / row max = {ratio:.3e}")
+    assert ratio <= TOL
+
+
+def test_w4a16_reduces_to_nvfp4(ops):
+    """With the activation equal to its own NVFP4 dequantization (exact in
+    bf16), the weight-only GEMM and the NVFP4 x NVFP4 GEMM sum the same exact
+    products; their bf16 outputs agree to accumulation-order rounding."""
+    from test_oracle_gemm import dequant_torch   # decode written from the format definitions
+    g = torch.Generator().manual_seed(5)
+    m, n, k = 48, 384, 1024
+    a = torch.randn(m, k, generator=g).to(torch.bfloat16)
+    w = (torch.randn(n, k, generator=g) * 0.02).to(torch.bfloat16)
+    say("w4a16 vs nvfp4", (m, n, k))
+    qa, sa, ga = oq(a)
+    qb, sb, gb = oq(w)
+    a_dq = dequant_torch(qa, sa, m, k)
+    a_dq_bf16 = a_dq.to(torch.bfloat16)
+    assert torch.equal(a_dq_bf16.double(), a_dq), "dequantized values are exact in bf16"
+    alpha = torch.tensor([np.float32(1.0) / gb[0]], dtype=torch.float32, device="cuda")
+    o1 = ops.nvfp4_gemm_w4a16(dev(a_dq_bf16), t_u8(qb), t_u8(sb), alpha)
+    o2 = ops.nvfp4_gemm(t_u8(qa), t_u8(qb), t_u8(sa), t_u8(sb), alpha, k=k)
+    torch.cuda.synchronize()
+    assert row_tolerance_check(o1.float().cpu().numpy(), o2.double().cpu().numpy()) <= TOL
+
+
 def test_moe_workload(ops):
     mo = synth.moe()
     say("moe full workload", mo.mask.tolist())
