@@ -191,6 +191,18 @@ def gemm_rows(a, b, a_sf, b_sf, alpha, m, n, k, rows=None, bias=None, d=None, l1
     return out
 
 
+def lora_down(x_bf16, pqs_bf16, l2_bf16):
+    """SVDQuant's LoRA-down projection of the smoothed activation ([SVD]
+    flashinfer mm_nvfp4_svdquant: d = x @ (pqs[:, None] * L2^T), i.e. the
+    activation times pre_quant_scale, against the rank-r down weight):
+    d[i, p] = sum_k (x[i,k] * pqs[k]) * l2[p,k] in fp64, not rounded.
+    x_bf16: uint16 [m, k]; pqs_bf16: uint16 [k]; l2_bf16: uint16 [r, k]."""
+    x = bf16_to_f32(np.asarray(x_bf16, dtype=np.uint16)).astype(np.float64)
+    p = bf16_to_f32(np.asarray(pqs_bf16, dtype=np.uint16)).astype(np.float64)
+    l2 = bf16_to_f32(np.asarray(l2_bf16, dtype=np.uint16)).astype(np.float64)
+    return (x * p[None, :]) @ l2.T
+
+
 def gemm_w4a16_rows(a_bf16, b, b_sf, alpha, m, n, k, rows=None, bias=None):
     """fp64 alpha * (A @ Bdq^T) + bias for the given rows of the bf16
     activation A ([NVF] f16a_nvfp4weight_scaled_mm); a_bf16: uint16 bit

@@ -189,3 +189,37 @@ def test_w4a16_row_subset():
     full = O.gemm_w4a16_rows(a, b, bsf, 0.5, m, n, k)
     rows = np.array([10, 0, 4])
     assert np.array_equal(O.gemm_w4a16_rows(a, b, bsf, 0.5, m, n, k, rows=rows), full[rows])
+
+
+# ---- SVDQuant LoRA-down (flashinfer mm_nvfp4_svdquant: d = x @ (pqs[:, None] * L2^T)) ----
+
+
+def test_lora_down_exact_rational():
+    """A tiny case against exact rational arithmetic on the bf16 inputs."""
+    g = torch.Generator().manual_seed(41)
+    m, k, r = 3, 32, 4
+    x = torch.randn(m, k, generator=g).to(torch.bfloat16)
+    p = torch.exp(0.5 * torch.randn(k, generator=g)).to(torch.bfloat16)
+    l2 = (0.02 * torch.randn(r, k, generator=g)).to(torch.bfloat16)
+    d = O.lora_down(synth.bits(x), synth.bits(p), synth.bits(l2))
+    for i in range(m):
+        for j in range(r):
+            ref = sum(Fraction(float(x[i, kk])) * Fraction(float(p[kk])) * Fraction(float(l2[j, kk]))
+                      for kk in range(k))
+            assert abs(Fraction(d[i, j]) - ref) <= Fraction(k) * Fraction(2) ** -52 * (abs(ref) + 1)
+
+
+def test_lora_down_unit_rows_select_smoothed_columns():
+    """With L2's rows unit vectors e_c, d[:, j] is the smoothed column x * pqs
+    (exact: a product of two bf16 values fits fp32 and fp64)."""
+    g = torch.Generator().manual_seed(42)
+    m, k = 5, 48
+    x = torch.randn(m, k, generator=g).to(torch.bfloat16)
+    p = torch.exp(0.5 * torch.randn(k, generator=g)).to(torch.bfloat16)
+    cols = [3, 0, 47, 16]
+    l2 = torch.zeros(len(cols), k)
+    for j, c in enumerate(cols):
+        l2[j, c] = 1.0
+    d = O.lora_down(synth.bits(x), synth.bits(p), synth.bits(l2.to(torch.bfloat16)))
+    ref = (x.double() * p.double())[:, cols]
+    assert np.array_equal(d, ref.numpy())
