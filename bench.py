@@ -60,6 +60,7 @@ def build_workload(name, ops, synth, torch):
     w = Workload()
     w.hbm_bound = False
     w.w4a16 = None
+    w.lora_down = None
     dev = "cuda"
     if name in ("prefill", "dense", "decode", "tiny"):
         if name == "prefill":
@@ -175,7 +176,8 @@ def build_workload(name, ops, synth, torch):
         _, _, gsa = ops.nvfp4_quantize(x0, pre_quant_scale=pqs)
         alpha = ops.nvfp4_alpha(gsa, gsw)
         al = float(alpha.item())
-        d = synth.lora_down(s).to(dev)
+        l2 = s.l2.to(torch.bfloat16).to(dev)
+        d = torch.empty(m, r, dtype=torch.bfloat16, device=dev)   # formed inside the step
         l1 = synth.lora_up(s, al).to(dev)
         bias = s.bias.to(dev)
         fa = torch.empty(m, k // 2, dtype=torch.uint8, device=dev)
@@ -189,9 +191,13 @@ def build_workload(name, ops, synth, torch):
             ops.nvfp4_gemm_svdquant(fa, fw, sfa, sfw, alpha, d, l1, bias=bias, out=out)
 
         def pre(x):
-            quant(x)
+            # smooth quantize and the LoRA-down projection d, one read of x
+            ops.nvfp4_quantize_lora_down(x, pqs, l2, gsa, ops.GS_STATIC, out_fp4=fa, out_sf=sfa, d=d)
 
-        w.desc = "SVDQuant linear 4096x3072x3072, r=32: smooth NVFP4 quantize (static gs) -> fused GEMM + LoRA-up + bias"
+        w.lora_down = pre
+        w.lora_down_bytes = m * k * 2 + k * 2 + r * k * 2 + m * k // 2 + sf_size(m, k) + 2 * m * r
+        w.desc = ("SVDQuant linear 4096x3072x3072, r=32: smooth NVFP4 quantize (static gs) with the LoRA-down "
+                  "projection fused -> fused GEMM + LoRA-up + bias")
         w.rotate_hint = max(1, -(-512 * 2 ** 20 // (m * k * 2)))
         w.make_acts = lambda n_copies: [s.x.to(dev) for _ in range(n_copies)]
         w.pre, w.quant, w.gemm = pre, quant, gemm
@@ -362,6 +368,15 @@ def main():
         w4_gbs = w.w4a16_bytes / (w4_ms * 1e-3) / 1e9
         w4 = {"ms": round(w4_ms, 5), "gbs": round(w4_gbs, 1), "frac_hbm": round(w4_gbs / HBM_PEAK_GBS, 4),
               "bytes": w.w4a16_bytes, "kernel": "k_gemm_w4a16 (bf16 activation x NVFP4 weight, no activation quantize)"}
+    ld = None
+    if w.lora_down is not None:
+        g_ld = capture(torch, lambda: [w.lora_down(a) for a in acts])
+        ld_ms = time_graph(torch, g_ld) / n_copies
+        del g_ld
+        ld_gbs = w.lora_down_bytes / (ld_ms * 1e-3) / 1e9
+        ld = {"ms": round(ld_ms, 5), "gbs": round(ld_gbs, 1), "frac_hbm": round(ld_gbs / HBM_PEAK_GBS, 4),
+              "bytes": w.lora_down_bytes,
+              "kernel": "k_quantize_lora (smooth quantize + LoRA-down projection, one read of x)"}
     src = torch.ones(64 * 2 ** 20, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     g_copy = capture(torch, lambda: [torch.neg(src, out=dst) for _ in range(4)])
@@ -415,6 +430,8 @@ def main():
                            "algorithmic_bytes_per_launch": w.gemm_bytes}
     if w4 is not None:
         res["w4a16"] = w4
+    if ld is not None:
+        res["quantize_lora_down"] = ld
     if not args.no_cpu_baseline and w.cpu_sample is not None:
         import oracle as O
         res["cpu_baseline"] = w.cpu_sample(O, np)

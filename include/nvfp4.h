@@ -100,6 +100,27 @@ int nvfp4_quantize(const void *x, int x_dtype, int64_t m, int64_t k,
                    uint8_t *out_fp4, uint8_t *out_sf, void *stream);
 
 /*
+ * Smooth quantization with the SVDQuant LoRA-down projection fused
+ * (flashinfer docs, flashinfer.gemm.mm_nvfp4_svdquant: parameter a is x with
+ * pre_quant_scale folded into its quantization, and d = x @ (pqs[:, None] *
+ * L2^T) is the rank-r LoRA-down output): one read of x gives
+ *   out_fp4, out_sf, global_scale  exactly as nvfp4_quantize(x, bf16,
+ *                                  pre_quant_scale = pqs) would, and
+ *   d = bf16(sum_k x[i,k] * pqs[k] * l2[p,k]), every product exact,
+ *       accumulated in fp32.
+ *   x: [m, k] bf16; pre_quant_scale: [k] bf16; l2: [r, k] bf16 (the LoRA-down
+ *   weight, row-major); d: [m, r] bf16 (16-byte aligned, ready for
+ *   nvfp4_gemm_svdquant).  The product x * pqs enters the projection as is
+ *   (non-finite values propagate; only the quantization applies nan_to_num).
+ * Requires r in {32, 64, 96, 128} (NVFP4_BAD_RANK otherwise), 16 <= k <=
+ * 4096 (larger k: NVFP4_UNSUPPORTED), k % 16 == 0.  Device pointers owned by
+ * the caller; nothing is allocated.
+ */
+int nvfp4_quantize_lora_down(const void *x, int64_t m, int64_t k, const void *pre_quant_scale,
+                             const void *l2, int64_t r, float *global_scale, int gs_mode,
+                             uint8_t *out_fp4, uint8_t *out_sf, void *d, void *stream);
+
+/*
  * Batched, optionally masked quantization (flashinfer PR #1774, the
  * nvfp4_batched_quantize op and its per-item global scale).
  *   x:            [b, m, k] bf16.

@@ -48,6 +48,25 @@ int nvfp4_quantize(const void* x, int x_dtype, int64_t m, int64_t k, const void*
     return launch_status(nvfp4::launch_quantize(a, (hipStream_t)stream));
 }
 
+int nvfp4_quantize_lora_down(const void* x, int64_t m, int64_t k, const void* pre_quant_scale,
+                             const void* l2, int64_t r, float* global_scale, int gs_mode, uint8_t* out_fp4,
+                             uint8_t* out_sf, void* d, void* stream) {
+    if (!x || !pre_quant_scale || !l2 || !global_scale || !out_fp4 || !out_sf || !d) return NVFP4_NULL_POINTER;
+    if (gs_mode != NVFP4_GS_STATIC && gs_mode != NVFP4_GS_DYNAMIC) return NVFP4_UNSUPPORTED;
+    if (r <= 0 || r % 32 != 0 || r > 128) return NVFP4_BAD_RANK;
+    if (k < 16 || k % 16 != 0 || !quant_sizes_ok(1, m, k)) return NVFP4_BAD_SHAPE;
+    if (k > 4096) return NVFP4_UNSUPPORTED;  // the workgroup's LDS copy of its rows holds 4096 columns
+    if (!aligned16(x) || !aligned16(pre_quant_scale) || !aligned16(l2) || !aligned16(out_fp4) ||
+        !aligned16(out_sf) || !aligned16(d) || ((uintptr_t)global_scale & 3u))
+        return NVFP4_MISALIGNED;
+    nvfp4::QuantizeArgs a{};
+    a.x = x; a.x_dtype = NVFP4_BF16; a.pqs = pre_quant_scale; a.mask = nullptr;
+    a.gs = global_scale; a.out_fp4 = out_fp4; a.out_sf = out_sf;
+    a.b = 1; a.m = m; a.k_in = k; a.silu = false; a.dynamic = gs_mode == NVFP4_GS_DYNAMIC;
+    return launch_status(nvfp4::launch_quantize_lora(a, (const uint16_t*)l2, (uint16_t*)d, (int)r,
+                                                      (hipStream_t)stream));
+}
+
 int nvfp4_quantize_masked_batched(const void* x, int64_t b, int64_t m, int64_t k,
                                   const int32_t* mask, float* global_scale, int gs_mode,
                                   uint8_t* out_fp4, uint8_t* out_sf, void* stream) {

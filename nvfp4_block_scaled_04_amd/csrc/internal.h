@@ -21,6 +21,11 @@ struct QuantizeArgs {
 };
 
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t st);
+// Smooth quantize of a bf16 [m, k] (a.pqs set, a.b = 1) with the LoRA-down
+// projection d = bf16((x * pqs) @ l2^T), l2 bf16 [rank, k]; rank in
+// {32, 64, 96, 128}, k <= 4096.
+hipError_t launch_quantize_lora(const QuantizeArgs& a, const uint16_t* l2, uint16_t* d, int rank,
+                                hipStream_t st);
 hipError_t launch_alpha(const float* ga, const float* gb, float* alpha, int64_t n, hipStream_t st);
 
 struct GemmArgs {

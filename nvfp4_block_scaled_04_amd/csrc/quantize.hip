@@ -464,6 +464,214 @@ __global__ __launch_bounds__(1024) void k_quantize_small(QParams p) {
         *(u32x4*)(sf_dst + i * 16) = *(const u32x4*)(sfl + i * 16);
 }
 
+// ---------------------------------------------------------------------------
+// Smooth quantize with the SVDQuant LoRA-down projection fused (flashinfer
+// mm_nvfp4_svdquant: a is the NVFP4 quantization of x * pqs, and d = x @
+// (pqs[:, None] * L2^T) is its rank-r projection): one read of x feeds both.
+// A workgroup of 16 waves owns 16 rows across the whole K.  Phase 1: each
+// thread takes one 16-element block per 256-column chunk of a row, for up
+// to four chunks (all its loads in flight before any use), quantizes them
+// exactly as the smooth pass does, and parks the raw bf16 rows in LDS.
+// Phase 2 runs v_mfma_f32_16x16x32_bf16 over K with x from LDS as the A
+// operand and l2 * pqs as the B operand, read through the caches (every
+// workgroup reads the same L2 and pqs) and split exactly into two bf16
+// halves: the product of two bf16 values has at most 16 significant bits,
+// its bf16 rounding hi takes the top 8 and the remainder lo = product - hi
+// at most 8 more, so x * hi + x * lo is x * l2 * pqs with every product
+// exact and only fp32 accumulation rounding.  The waves take interleaved
+// 32-column slices; their partial projections are added through LDS and
+// stored as bf16.
+// ---------------------------------------------------------------------------
+
+constexpr int kLoraMaxK = 4096;   // columns of the LDS copy
+constexpr int kLoraWaves = 16;
+constexpr int kLoraPerThread = kLoraMaxK / 256 / (kLoraWaves / 4);  // chunks per thread
+
+template <int RT>  // rank tiles of 16
+__global__ __launch_bounds__(64 * kLoraWaves) void k_quantize_lora(QParams p, const uint16_t* l2, uint16_t* d_out,
+                                                                  int rank) {
+    constexpr int NT = 64 * kLoraWaves;
+    constexpr int PITCH = kLoraMaxK + 8;  // bf16 per LDS row (16 bytes of pad spread the banks)
+    constexpr int U = RT <= 4 ? 2 : 1;    // projection slices whose operands load together
+    static_assert((kLoraWaves - 1) * RT * 64 * 16 <= 16 * PITCH * 2, "partial sums fit in the LDS copy");
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    __shared__ __align__(16) uint16_t xs[16 * PITCH];
+    __shared__ float rtab[128];
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int64_t m0 = (int64_t)blockIdx.x * 16;
+    const int cg = __builtin_amdgcn_readfirstlane(t >> 8);  // chunk group: chunks cg, cg + 4, ...
+    const int rl = (t >> 4) & 15, bl = t & 15;             // row within the band, block within a chunk
+    const int64_t row = m0 + rl;
+    const bool row_ok = row < p.m;
+    const int64_t rrow = row_ok ? row : p.m - 1;  // loads of rows past m read a valid row
+    const int nbk = (int)(p.K / 16);
+    const int nchunk = (nbk + 15) / 16;
+    const int ks = (int)((p.K + 31) / 32) * 32;  // K rounded up to whole MFMA slices
+    const int nsl = ks / 32;
+    const int nmine = (nsl - wave + kLoraWaves - 1) / kLoraWaves;  // projection slices of this wave
+    const int r16 = lane & 15, kg = lane >> 4;
+    const float gs = p.gs[0];
+    if (t < 128) {
+        const float dec = ue4m3_decode((uint32_t)t);
+        rtab[t] = dec == 0.0f ? 0.0f : gs / dec;
+    }
+    // zero the LDS copy's columns past K up to the last whole slice
+    for (int i = t; i < 16 * (ks - (int)p.K); i += NT) {
+        const int rr = i / (ks - (int)p.K), cc = (int)p.K + i % (ks - (int)p.K);
+        xs[rr * PITCH + cc] = 0;
+    }
+    __syncthreads();
+
+    // projection operands (l2 rows and pqs) of U slices; past this wave's
+    // slices or past K: zeros
+    u32x4 bf[U][RT], pf[U];
+    auto load_group = [&](int g) {
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int col = (wave + kLoraWaves * (g + u)) * 32 + kg * 8;
+            const bool ok = g + u < nmine && col < p.K;
+#pragma unroll
+            for (int i = 0; i < RT; i++)
+                bf[u][i] = ok ? *(const u32x4*)(l2 + (int64_t)(i * 16 + r16) * p.K + col) : u32x4{0u, 0u, 0u, 0u};
+            pf[u] = ok ? *(const u32x4*)(p.pqs + col) : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+
+    // ---- phase 1: quantize, keep the raw rows in LDS
+    {
+        u32x4 raw[kLoraPerThread][2], pqb[kLoraPerThread][2];
+#pragma unroll
+        for (int i = 0; i < kLoraPerThread; i++) {  // every load in flight before any use
+            int cb = (cg + 4 * i) * 16 + bl;
+            cb = cb < nbk ? cb : nbk - 1;
+            const u32x4* src = (const u32x4*)((const uint16_t*)p.x + rrow * p.k_in + (int64_t)cb * 16);
+            raw[i][0] = src[0];
+            raw[i][1] = src[1];
+            load_pqs<V_BF16_SMOOTH>(p, (int64_t)cb * 16, pqb[i]);
+        }
+        load_group(0);  // the first projection operands, behind the rows
+        uint8_t* q = p.out_fp4;
+#pragma unroll
+        for (int i = 0; i < kLoraPerThread; i++) {
+            const int c = cg + 4 * i;
+            if (c >= nchunk) break;  // uniform in the wave
+            const int cb = c * 16 + bl;  // block column
+            const bool blk_ok = row_ok && cb < nbk;
+            float f[16];
+            const float bamax = process_block<V_BF16_SMOOTH>(raw[i], pqb[i], f);
+            const uint32_t sc = blk_ok ? ue4m3_encode((bamax / 6.0f) * gs) : 0u;
+            const float r = rtab[sc];
+            uint32_t w0 = 0, w1 = 0;
+            w0 = NVFP4_PACK_FP4(w0, f[0] * r, f[1] * r, 0);
+            w0 = NVFP4_PACK_FP4(w0, f[2] * r, f[3] * r, 1);
+            w0 = NVFP4_PACK_FP4(w0, f[4] * r, f[5] * r, 2);
+            w0 = NVFP4_PACK_FP4(w0, f[6] * r, f[7] * r, 3);
+            w1 = NVFP4_PACK_FP4(w1, f[8] * r, f[9] * r, 0);
+            w1 = NVFP4_PACK_FP4(w1, f[10] * r, f[11] * r, 1);
+            w1 = NVFP4_PACK_FP4(w1, f[12] * r, f[13] * r, 2);
+            w1 = NVFP4_PACK_FP4(w1, f[14] * r, f[15] * r, 3);
+            if (blk_ok) *(uint2*)(q + row * (p.K / 2) + (int64_t)cb * 8) = uint2{w0, w1};
+            // the 4 scale bytes of a swizzle dword sit in 4 neighbouring lanes
+            uint32_t v = sc << (8 * (bl & 3));
+            v |= __shfl_xor(v, 1);
+            v |= __shfl_xor(v, 2);
+            if ((bl & 3) == 0 && cb < nbk)
+                *(uint32_t*)(p.out_sf + ((row >> 7) * p.nct + (cb >> 2)) * 512 + (row & 31) * 16 +
+                             ((row & 127) >> 5) * 4) = v;
+            // the projection's A operand: the raw rows (the plain product
+            // x * pqs enters the projection, no nan_to_num), 0 past m
+            if (cb < nbk) {
+                u32x4* dst = (u32x4*)(xs + rl * PITCH + cb * 16);
+                dst[0] = row_ok ? raw[i][0] : u32x4{0u, 0u, 0u, 0u};
+                dst[1] = row_ok ? raw[i][1] : u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 2: d = x @ (l2 * pqs)^T over K
+    f32x4 acc[RT];
+#pragma unroll
+    for (int i = 0; i < RT; i++) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int g = 0; g < nmine; g += U) {
+        if (g > 0) load_group(g);
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            if (g + u >= nmine) break;
+            const int col = (wave + kLoraWaves * (g + u)) * 32 + kg * 8;  // this lane's 8 columns of the slice
+            const bf16x8 afr = __builtin_bit_cast(bf16x8, *(const u32x4*)(xs + r16 * PITCH + col));
+#pragma unroll
+            for (int i = 0; i < RT; i++) {
+                uint32_t hi[4], lo[4];
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const f32x2 prod = {bf16_lo(bf[u][i][j]) * bf16_lo(pf[u][j]),
+                                        bf16_hi(bf[u][i][j]) * bf16_hi(pf[u][j])};
+                    const bf16x2 h = __builtin_convertvector(prod, bf16x2);
+                    const f32x2 rest = {prod[0] - (float)h[0], prod[1] - (float)h[1]};
+                    hi[j] = __builtin_bit_cast(uint32_t, h);
+                    lo[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rest, bf16x2));
+                }
+                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, u32x4{hi[0], hi[1], hi[2], hi[3]}), afr, acc[i], 0, 0, 0);
+                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], lo[2], lo[3]}), afr, acc[i], 0, 0, 0);
+            }
+        }
+    }
+    __syncthreads();  // the LDS copy is free: it now holds the waves' partial sums
+    f32x4* const part = (f32x4*)xs;
+    if (wave > 0)
+#pragma unroll
+        for (int i = 0; i < RT; i++) part[((wave - 1) * RT + i) * 64 + lane] = acc[i];
+    __syncthreads();
+    if (wave != 0) return;
+    // lane: row m0 + r16, ranks 16 i + 4 kg .. + 3
+    const int64_t orow = m0 + r16;
+    if (orow >= p.m) return;
+#pragma unroll
+    for (int i = 0; i < RT; i++) {
+        f32x4 v = acc[i];
+        for (int w = 0; w < kLoraWaves - 1; w++) v += part[(w * RT + i) * 64 + lane];
+        *(uint2*)(d_out + orow * rank + i * 16 + kg * 4) =
+            uint2{f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
+                  f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16)};
+    }
+}
+
+hipError_t launch_quantize_lora(const QuantizeArgs& a, const uint16_t* l2, uint16_t* d, int rank,
+                                hipStream_t st) {
+    QParams p{};
+    p.x = a.x;
+    p.pqs = (const uint16_t*)a.pqs;
+    p.gs = a.gs;
+    p.out_fp4 = a.out_fp4;
+    p.out_sf = a.out_sf;
+    p.m = a.m;
+    p.K = a.k_in;
+    p.k_in = a.k_in;
+    p.nct = (int)((p.K + 63) / 64);
+    p.nrt = (int)((p.m + 127) / 128);
+    p.sfsz = (int64_t)p.nrt * 128 * p.nct * 4;
+    p.b = 1;
+    if (a.dynamic) {
+        p.amax_blocks = p.nrt * ((p.nct + 1) / 2);
+        k_amax<V_BF16_SMOOTH, 2><<<dim3(p.amax_blocks, 1), 256, 0, st>>>(p);
+        k_finish_gs<<<1, 256, 0, st>>>(p);
+    }
+    const dim3 grid((unsigned)(p.nrt * 8));  // 16-row bands over the padded rows (their scales are zeroed)
+    constexpr int nt = 64 * kLoraWaves;
+    switch (rank / 16) {
+    case 2: k_quantize_lora<2><<<grid, nt, 0, st>>>(p, l2, d, rank); break;
+    case 4: k_quantize_lora<4><<<grid, nt, 0, st>>>(p, l2, d, rank); break;
+    case 6: k_quantize_lora<6><<<grid, nt, 0, st>>>(p, l2, d, rank); break;
+    default: k_quantize_lora<8><<<grid, nt, 0, st>>>(p, l2, d, rank); break;
+    }
+    return hipGetLastError();
+}
+
 __global__ void k_alpha(const float* ga, const float* gb, float* alpha, int64_t n) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) alpha[i] = 1.0f / (ga[i] * gb[i]);

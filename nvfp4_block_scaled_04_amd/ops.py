@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libnvfp4_amd.so")
 
 EXPORTS = (
     "nvfp4_quantize",
+    "nvfp4_quantize_lora_down",
     "nvfp4_quantize_masked_batched",
     "silu_mul_nvfp4_quantize",
     "nvfp4_gemm",
@@ -43,6 +44,7 @@ def _load():
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     sig = {
         "nvfp4_quantize": [vp, i32, i64, i64, vp, vp, i32, vp, vp, vp],
+        "nvfp4_quantize_lora_down": [vp, i64, i64, vp, vp, i64, vp, i32, vp, vp, vp, vp],
         "nvfp4_quantize_masked_batched": [vp, i64, i64, i64, vp, vp, i32, vp, vp, vp],
         "silu_mul_nvfp4_quantize": [vp, i64, i64, i64, vp, vp, i32, vp, vp, vp],
         "nvfp4_gemm": [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, vp],
@@ -109,6 +111,30 @@ def nvfp4_quantize(x, global_scale=None, gs_mode=GS_DYNAMIC, pre_quant_scale=Non
                              gs_mode, _ptr(out_fp4), _ptr(out_sf), _stream(dev))
     _check(rc, "nvfp4_quantize")
     return out_fp4, out_sf, global_scale
+
+
+def nvfp4_quantize_lora_down(x, pre_quant_scale, l2, global_scale=None, gs_mode=GS_DYNAMIC,
+                             out_fp4=None, out_sf=None, d=None):
+    """Smooth NVFP4 quantize of bf16 x [m, k] (pre_quant_scale [k] bf16) and the
+    SVDQuant LoRA-down d = bf16((x * pqs) @ l2^T), l2 [r, k] bf16, in one read
+    of x.  Returns (fp4 [m, k/2], sf, global_scale [1], d [m, r])."""
+    for t, name in ((x, "x"), (pre_quant_scale, "pre_quant_scale"), (l2, "l2")):
+        _need(t, name)
+    m, k = x.shape
+    r = l2.shape[0]
+    dev_ = x.device
+    if global_scale is None:
+        global_scale = torch.zeros(1, dtype=torch.float32, device=dev_)
+    if out_fp4 is None:
+        out_fp4 = torch.empty(m, k // 2, dtype=torch.uint8, device=dev_)
+    if out_sf is None:
+        out_sf = torch.empty(sf_size(m, k), dtype=torch.uint8, device=dev_)
+    if d is None:
+        d = torch.empty(m, r, dtype=torch.bfloat16, device=dev_)
+    rc = _lib.nvfp4_quantize_lora_down(_ptr(x), m, k, _ptr(pre_quant_scale), _ptr(l2), r, _ptr(global_scale),
+                                       gs_mode, _ptr(out_fp4), _ptr(out_sf), _ptr(d), _stream(dev_))
+    _check(rc, "nvfp4_quantize_lora_down")
+    return out_fp4, out_sf, global_scale, d
 
 
 def nvfp4_quantize_masked_batched(x, mask=None, global_scale=None, gs_mode=GS_DYNAMIC,

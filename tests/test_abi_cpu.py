@@ -34,7 +34,7 @@ def lib():
 def test_header_declares_the_entry_points():
     assert declared() == sorted([
         "nvfp4_alpha", "nvfp4_gemm", "nvfp4_gemm_grouped_masked", "nvfp4_gemm_svdquant",
-        "nvfp4_gemm_w4a16",
+        "nvfp4_gemm_w4a16", "nvfp4_quantize_lora_down",
         "nvfp4_quantize", "nvfp4_quantize_masked_batched", "silu_mul_nvfp4_quantize",
     ])
 
@@ -184,6 +184,24 @@ def test_w4a16_validation(lib):
     assert run(a=P + 8) == MISAL
     assert run(bias=P + 2) == MISAL
     assert run(alpha=P + 1) == MISAL
+
+
+def test_lora_down_validation(lib):
+    f = lib.nvfp4_quantize_lora_down
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                  ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    run = lambda x=P, m=64, k=256, pqs=P, l2=P, r=32, gs=P, mode=1, o4=P, osf=P, d=P: \
+        f(x, m, k, pqs, l2, r, gs, mode, o4, osf, d, None)
+    assert run(pqs=None) == NULLP
+    assert run(l2=None) == NULLP
+    assert run(d=None) == NULLP
+    assert run(r=16) == RANK
+    assert run(r=160) == RANK
+    assert run(k=40) == SHAPE
+    assert run(k=4112) == UNSUP
+    assert run(mode=7) == UNSUP
+    assert run(l2=P + 8) == MISAL
+    assert run(d=P + 8) == MISAL
 
 
 def test_alpha_validation(lib):

@@ -127,6 +127,40 @@ def test_repeat_is_identical(ops):
         assert torch.equal(u, v)
 
 
+@pytest.mark.parametrize("m,k,r,dynamic", [(4096, 3072, 32, False), (100, 400, 64, True), (17, 272, 32, True),
+                                          (300, 4096, 128, True), (130, 96, 96, False)])
+def test_quantize_lora_down(ops, m, k, r, dynamic):
+    """Smooth quantize with the LoRA-down projection fused: the FP4 and scale
+    bytes and gs must equal the oracle's smooth quantization exactly, and
+    d = (x * pqs) @ L2^T must meet the GEMM bar against the oracle's fp64
+    projection (every product is exact in the kernel; only fp32 accumulation
+    and the bf16 output round).  The first case is the SVDQuant workload's
+    activation."""
+    from gpu_util import row_tolerance_check
+    s = synth.svdquant(m=m, n=64, k=k, r=r)
+    l2 = s.l2.to(torch.bfloat16)
+    say("quantize + lora-down", (m, k, r), "dynamic", dynamic)
+    mode = ops.GS_DYNAMIC if dynamic else ops.GS_STATIC
+    gs_static = None if dynamic else np.float32(2688.0 / 7.5)
+    gs_d = torch.tensor([0.0 if gs_static is None else gs_static], dtype=torch.float32, device="cuda")
+    o4 = canary((m, k // 2))
+    osf = canary((ops.sf_size(m, k),))
+    d = torch.full((m, r), 0x7FA5, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    ops.nvfp4_quantize_lora_down(dev(s.x), dev(s.pqs), dev(l2), gs_d, mode, out_fp4=o4, out_sf=osf, d=d)
+    torch.cuda.synchronize()
+    q, sf, g = O.quantize(np_bits(s.x), prologue=O.PRO_SMOOTH, pqs=np_bits(s.pqs),
+                          gs=None if gs_static is None else np.array([gs_static], np.float32), gs_mode=mode)
+    assert np.array_equal(np_bits(gs_d).view(np.uint32), g.view(np.uint32)), (np_bits(gs_d), g)
+    bad = np.argwhere(np_bits(o4) != q)
+    assert len(bad) == 0, f"{len(bad)} FP4 bytes differ, first at {bad[:3].tolist()}"
+    bad = np.argwhere(np_bits(osf) != sf)
+    assert len(bad) == 0, f"{len(bad)} scale bytes differ, first at {bad[:3].tolist()}"
+    ref = O.lora_down(np_bits(s.x), np_bits(s.pqs), np_bits(l2))
+    ratio = row_tolerance_check(d.float().cpu().numpy(), ref)
+    print(f"  d: worst row error / row max = {ratio:.3e}")
+    assert ratio <= 1e-2
+
+
 # ---- batched / masked / silu -------------------------------------------------------
 
 def run_batched(ops, x_cpu, mask, mode, silu=False, gs=None):
