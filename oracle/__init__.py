@@ -65,6 +65,8 @@ def lib():
             ctypes.c_void_p, u8p, u8p, ctypes.c_float, ctypes.c_void_p, ctypes.c_int64,
             ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
         ]
+        L.nvo_f64_to_bf16_via_f32.restype = None
+        L.nvo_f64_to_bf16_via_f32.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
         L.nvo_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -221,3 +223,35 @@ def gemm_w4a16_rows(a_bf16, b, b_sf, alpha, m, n, k, rows=None, bias=None):
     if rc != 0:
         raise ValueError(f"oracle weight-only gemm rejected the arguments (status {rc})")
     return out
+
+
+def f64_to_bf16_via_f32(v):
+    """bf16 bit patterns of fp64 values rounded to fp32, then to bf16 (the
+    bf16 output of an fp32-accumulated GEMM)."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.zeros(v.shape, dtype=np.uint16)
+    lib().nvo_f64_to_bf16_via_f32(_vp(v), _vp(out), v.size)
+    return out
+
+
+def gemm_silu_quantize(a, b, a_sf, b_sf, alpha, gs, mask, m, n2, k):
+    """Front half of a routed-expert SwiGLU ([FI] grouped_gemm_nt_masked over
+    experts, then silu_and_mul_scaled_nvfp4_experts_quantize with a given
+    per-expert global scale), composed from its two steps:
+      h[e] = bf16(fp32(alpha[e] * Adq[e] @ Bdq[e]^T))  on the valid rows, [m, n2]
+      (fp4, sf) = silu_and_mul quantize of h (gate = columns [0, n2/2), up =
+                  the rest), STATIC global scale gs[e], rows >= mask[e] masked.
+    a: [E, m, k/2], b: [E, n2, k/2] packed e2m1; a_sf, b_sf: [E, sf bytes];
+    alpha, gs: [E] float32; mask: [E] int32.  Returns (fp4 [E, m, n2/4] with
+    masked rows zero, sf [E, sf_size(m, n2/2)])."""
+    E = len(alpha)
+    mask = np.asarray(mask, dtype=np.int32).reshape(E)
+    h = np.zeros((E, m, n2), dtype=np.uint16)
+    for e in range(E):
+        valid = int(min(max(mask[e], 0), m))
+        if valid == 0:
+            continue
+        v = gemm_rows(a[e], b[e], a_sf[e], b_sf[e], alpha[e], m, n2, k, rows=np.arange(valid))
+        h[e, :valid] = f64_to_bf16_via_f32(v)
+    fp4, sf, _ = quantize(h, prologue=PRO_SILU, mask=mask, gs=gs, gs_mode=STATIC)
+    return fp4, sf

@@ -51,6 +51,9 @@
  * The weight-only GEMM multiplies the fp64 sum of activation x (e2m1 x
  * block scale) products by 1/global_scale once, where the pages' eager path
  * divides each dequantized weight and rounds it to bf16 first.
+ * The GEMM's bf16 output (where a later step reads it back, as the
+ * routed-expert gate_up output h does) is the exact fp64 value rounded to
+ * fp32, the accumulator type, and then to bf16.
  */
 #include <float.h>
 #include <math.h>
@@ -442,6 +445,18 @@ int nvo_gemm_w4a16_rows(const uint16_t *a, const uint8_t *b, const uint8_t *b_sf
     }
     free(bdq);
     return NVO_OK;
+}
+
+/*
+ * bf16 output of an fp32-accumulated GEMM, from the exact fp64 value: round
+ * to fp32 (nearest even, the C conversion), then to bf16 (nearest even).
+ * [FI] the routed-expert gate_up GEMM writes this bf16 h, which the
+ * silu_and_mul quantize then reads.
+ */
+void nvo_f64_to_bf16_via_f32(const double *v, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = nvo_f32_to_bf16((float)v[i]);
 }
 
 int nvo_num_threads(void)

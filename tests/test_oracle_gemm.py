@@ -223,3 +223,82 @@ def test_lora_down_unit_rows_select_smoothed_columns():
     d = O.lora_down(synth.bits(x), synth.bits(p), synth.bits(l2.to(torch.bfloat16)))
     ref = (x.double() * p.double())[:, cols]
     assert np.array_equal(d, ref.numpy())
+
+
+def unit_scale_operand(rng, E, rows, k, codes=None):
+    """E matrices of random e2m1 codes (all 16) with every block scale 1.0
+    (ue4m3 code 0x38), padding scale bytes 0."""
+    if codes is None:
+        codes = rng.integers(0, 16, size=(E, rows, k))
+    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    sf = np.zeros((E, O.sf_size(rows, k)), dtype=np.uint8)
+    for r in range(rows):
+        for c in range(k // 16):
+            sf[:, swz(r, c, k)] = 0x38
+    return codes, packed, sf
+
+
+def int_products(ca, cb):
+    """2*e2m1 values are the integers 0,1,2,3,4,6,8,12 (signed): exact
+    integer matmul of [E, m, k] and [E, n, k] code arrays, in units of 1/4."""
+    lut = np.array([int(2 * e2m1_frac(c)) for c in range(16)], dtype=np.int64)
+    return np.einsum("emk,enk->emn", lut[ca], lut[cb])
+
+
+def test_gemm_silu_quantize_exact_products():
+    """With unit block scales and a power-of-two alpha every product and every
+    partial sum is exact in fp32, so h is the integer matmul scaled, rounded
+    once to bf16; the composition must equal the silu quantize of that h."""
+    rng = np.random.default_rng(31)
+    E, m, n2, k = 3, 40, 96, 64
+    ca, a, asf = unit_scale_operand(rng, E, m, k)
+    cb, b, bsf = unit_scale_operand(rng, E, n2, k)
+    alpha = np.full(E, 2.0 ** -3, dtype=np.float32)
+    gs = np.array([3.0, 100.0, 7.5], dtype=np.float32)
+    mask = np.array([40, 17, 0], dtype=np.int32)
+    acc = int_products(ca, cb)                       # units of 1/4, |acc| <= 64 * 144
+    hv = (acc.astype(np.float64) / 4.0 * 2.0 ** -3).astype(np.float32)
+    assert np.array_equal(hv.astype(np.float64), acc / 4.0 * 2.0 ** -3)   # exact in fp32
+    h = O.f32_to_bf16(hv).reshape(E, m, n2)
+    for e in range(E):
+        h[e, mask[e]:] = 0
+    want_q, want_sf, _ = O.quantize(h, prologue=O.PRO_SILU, mask=mask, gs=gs, gs_mode=O.STATIC)
+    got_q, got_sf = O.gemm_silu_quantize(a, b, asf, bsf, alpha, gs, mask, m, n2, k)
+    assert np.array_equal(got_q, want_q)
+    assert np.array_equal(got_sf, want_sf)
+    assert not got_q[1, 17:].any() and not got_q[2].any()
+
+
+def test_gemm_silu_quantize_gate_is_first_half():
+    """Up rows that select a column of ones make u = 1, so the result is the
+    plain quantize of bf16(silu(g)); gate and up swapped would give
+    silu(1) * g instead."""
+    rng = np.random.default_rng(32)
+    E, m, H, k = 1, 24, 32, 32
+    ca = rng.integers(0, 16, size=(E, m, k))
+    ca[..., 0] = 2                                   # e2m1 code 2 = 1.0
+    ca, a, asf = unit_scale_operand(rng, E, m, k, ca)
+    cb = rng.integers(0, 16, size=(E, 2 * H, k))
+    cb[:, H:, :] = 0
+    cb[:, H:, 0] = 2                                 # up row = e_0 -> u = 1
+    cb, b, bsf = unit_scale_operand(rng, E, 2 * H, k, cb)
+    alpha = np.ones(E, dtype=np.float32)
+    gs = np.array([50.0], dtype=np.float32)
+    mask = np.array([m], dtype=np.int32)
+    g = (int_products(ca, cb)[0, :, :H] / 4.0).astype(np.float32)
+    sg = np.array([O.silu(v) for v in g.ravel()], dtype=np.float32)
+    hs = O.f32_to_bf16(sg).reshape(m, H)
+    want_q, want_sf, _ = O.quantize(hs, gs=gs, gs_mode=O.STATIC)
+    got_q, got_sf = O.gemm_silu_quantize(a, b, asf, bsf, alpha, gs, mask, m, 2 * H, k)
+    assert np.array_equal(got_q[0], want_q)
+    assert np.array_equal(got_sf[0], want_sf)
+
+
+def test_f64_to_bf16_via_f32_double_rounding():
+    """fp64 -> fp32 -> bf16: ties at each step go to even; a value just above
+    a bf16 tie that fp32 rounds onto the tie then rounds to even."""
+    v = np.array([1.0, 1.0 + 2.0 ** -8, 1.0 + 2.0 ** -8 + 2.0 ** -40, 1.0 + 3 * 2.0 ** -8, -0.0, 2.0 ** 130])
+    got = O.f64_to_bf16_via_f32(v)
+    # 1+2^-8 is the bf16 tie between 1 and 1+2^-7 (even: 1); + 2^-40 is lost in
+    # fp32 (1 + 2^-8 exactly), so the tie again goes to 1; 1+3*2^-8 ties to 1+2^-6
+    assert got.tolist() == [0x3F80, 0x3F80, 0x3F80, 0x3F82, 0x8000, 0x7F80]
