@@ -180,6 +180,34 @@ int nvfp4_gemm_grouped_masked(const uint8_t *a, const uint8_t *b, const uint8_t 
                               void *stream);
 
 /*
+ * Front half of a routed-expert SwiGLU in one launch (flashinfer PR #1774:
+ * the gate_up grouped_gemm_nt_masked whose bf16 output feeds
+ * silu_and_mul_scaled_nvfp4_experts_quantize with a given per-expert global
+ * scale).  For each e and each row i < mask[e] (clamped to [0, m]):
+ *   h[i, :]   = bf16(alpha[e] * (A[e] @ B[e]^T)[i, :])      (n2 = 2H columns)
+ *   out[e, i] = NVFP4 quantize of bf16(silu(h[i, :H]) * h[i, H:]) with the
+ *               static global scale global_scale[e],
+ * bit for bit what nvfp4_gemm_grouped_masked followed by
+ * silu_mul_nvfp4_quantize (STATIC mode) produce, without the bf16 h ever
+ * reaching memory.
+ *   a: [E, m, k/2]; b: [E, n2, k/2], gate rows [0, H) then up rows [H, 2H);
+ *   a_sf: [E, pad_up(m,128)*pad_up(k/16,4)]; b_sf: [E, pad_up(n2,128)*
+ *   pad_up(k/16,4)]; alpha, mask, global_scale: [E] on device (read only);
+ *   out_fp4: [E, m, H/2], rows >= mask[e] not written; out_sf: [E,
+ *   pad_up(m,128)*pad_up(H/16,4)] swizzled, fully written (masked rows and
+ *   padding 0).  All pointers are device pointers owned by the caller.
+ * Requires E, m >= 1, n2 even with H = n2/2 >= 16 and H % 16 == 0, k >= 16,
+ * k % 16 == 0.  Returns NVFP4_NULL_POINTER, NVFP4_BAD_SHAPE,
+ * NVFP4_MISALIGNED or NVFP4_UNSUPPORTED (as nvfp4_gemm) before launching
+ * anything when an argument is invalid.
+ */
+int nvfp4_gemm_grouped_masked_silu_quantize(const uint8_t *a, const uint8_t *b, const uint8_t *a_sf,
+                                            const uint8_t *b_sf, const float *alpha,
+                                            const int32_t *mask, const float *global_scale,
+                                            int64_t E, int64_t m, int64_t n2, int64_t k,
+                                            uint8_t *out_fp4, uint8_t *out_sf, void *stream);
+
+/*
  * SVDQuant fused GEMM (flashinfer docs, flashinfer.gemm.mm_nvfp4_svdquant):
  *   out = bf16(alpha * (A @ B^T + d @ l1^T) (+ bias)), the rank-r term
  *   added to the same fp32 accumulator after the NVFP4 K loop; l1 must be

@@ -136,6 +136,26 @@ int nvfp4_gemm_grouped_masked(const uint8_t* a, const uint8_t* b, const uint8_t*
                        stream);
 }
 
+int nvfp4_gemm_grouped_masked_silu_quantize(const uint8_t* a, const uint8_t* b, const uint8_t* a_sf,
+                                            const uint8_t* b_sf, const float* alpha, const int32_t* mask,
+                                            const float* global_scale, int64_t E, int64_t m, int64_t n2,
+                                            int64_t k, uint8_t* out_fp4, uint8_t* out_sf, void* stream) {
+    if (!a || !b || !a_sf || !b_sf || !alpha || !mask || !global_scale || !out_fp4 || !out_sf)
+        return NVFP4_NULL_POINTER;
+    if (!dim_ok(E) || !dim_ok(m) || !dim_ok(n2) || k < 16 || k % 16 != 0 || k > kMaxDim) return NVFP4_BAD_SHAPE;
+    if (n2 % 2 != 0 || n2 / 2 < 16 || (n2 / 2) % 16 != 0 || !quant_sizes_ok(E, m, n2 / 2)) return NVFP4_BAD_SHAPE;
+    if (E > 65535 || ((m + 127) / 128) * ((n2 / 2 + 63) / 64) > ((int64_t)1 << 31) - 1) return NVFP4_BAD_SHAPE;
+    if (m * (k / 2) > ((int64_t)1 << 32) - 64 || n2 * (k / 2) > ((int64_t)1 << 32) - 64) return NVFP4_UNSUPPORTED;
+    if (!aligned16(a) || !aligned16(b) || !aligned16(a_sf) || !aligned16(b_sf) || !aligned16(out_fp4) ||
+        !aligned16(out_sf) || ((uintptr_t)alpha & 3u) || ((uintptr_t)mask & 3u) || ((uintptr_t)global_scale & 3u))
+        return NVFP4_MISALIGNED;
+    nvfp4::GemmArgs g{};
+    g.a = a; g.b = b; g.a_sf = a_sf; g.b_sf = b_sf; g.alpha = alpha; g.mask = mask;
+    g.E = E; g.m = m; g.n = n2; g.k = k;
+    nvfp4::SiluQuantOut q{out_fp4, out_sf, global_scale};
+    return launch_status(nvfp4::launch_gemm_silu_quantize(g, q, (hipStream_t)stream));
+}
+
 int nvfp4_gemm_svdquant(const uint8_t* a, const uint8_t* b, const uint8_t* a_sf, const uint8_t* b_sf,
                         const float* alpha, const void* d, const void* l1, const void* bias,
                         void* out, int64_t m, int64_t n, int64_t k, int64_t r, void* stream) {

@@ -39,6 +39,7 @@
 // puts 4 consecutive output columns of one output row in each lane.
 #include "device_common.h"
 #include "internal.h"
+#include "quant_block.h"
 
 namespace nvfp4 {
 
@@ -66,7 +67,19 @@ struct GParams {
     int rpa, rpb;        // padded rows of the scale buffers
     int tiles_m, tiles_n;
     int xcd_chunk;       // tiles per XCD when the tile count splits evenly over 8, else 0
+    // quantizing epilogue (silu_and_mul + NVFP4 of the gate | up output)
+    uint8_t* q_fp4;      // [E, M, H/2]
+    uint8_t* q_sf;       // [E, q_sfsz]
+    const float* q_gs;   // [E] static global scales of the quantized output
+    int64_t H;           // gate (= up) width, N = 2H
+    int64_t q_sfsz;      // per-expert scale bytes = pad_up(M,128) * pad_up(H/16,4)
+    int q_cp4;           // pad_up(H/16,4)/4
+    int q_rpad;          // pad_up(M,128)
 };
+
+// Epilogues of k_gemm: bf16 output; bf16 output after the rank-r LoRA-up
+// term; or silu_and_mul of the gate | up output quantized to NVFP4.
+enum Epilogue { EPI_PLAIN = 0, EPI_LORA = 1, EPI_SILUQ = 2 };
 
 // Raw buffer resource (gfx9 word 3: 32-bit untyped records).  Loads past
 // `bytes` return zeros.
@@ -145,10 +158,19 @@ constexpr int kWavesPerEU = WM * WN >= 16384 ? 1 : 2;
 // every SIMD holds two waves (one of each group) when the tile count alone
 // would leave one: one wave's dequantization then overlaps the other's MFMAs.
 // Requires an even number of K steps.
-template <int BM, int BN, int WGM, int WGN, int NST, int KS, bool ALIGNED, bool LORA>
+//
+// EPI_SILUQ (routed-expert SwiGLU front half): B holds 2H rows, gate rows
+// [0, H) then up rows [H, 2H).  A tile covers BN/2 columns j of h, and each
+// wave's WN columns are its WN/2 gate columns followed by the up columns of
+// the same j, so the epilogue finds g and u of one output element in the
+// same wave's staged rows and quantizes silu(g)*u per 16-column block, with
+// the same arithmetic as the silu_and_mul quantize kernel.
+template <int BM, int BN, int WGM, int WGN, int NST, int KS, bool ALIGNED, int EPI>
 __global__ __launch_bounds__(64 * WGM * WGN * KS, (KS == 2 ? 2 : kWavesPerEU<BM / WGM, BN / WGN>)) void k_gemm(GParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
     static_assert(KS == 1 || (KS == 2 && BM / WGM == 64), "the K split swaps 32-row fragment rows of 64-row wave tiles");
+    static_assert(EPI != EPI_SILUQ || KS == 1, "the quantizing epilogue runs on whole-K tiles");
+    constexpr bool LORA = EPI == EPI_LORA;
     constexpr int NW = WGM * WGN;  // waves of one K group, WGM along M x WGN along N
     constexpr int WM = BM / WGM, WN = BN / WGN;
     constexpr int FM = WM / 32, FN = WN / 32;
@@ -173,8 +195,34 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, (KS == 2 ? 2 : kWavesPerEU<BM 
     int tm, tn;
     tile_coords(p, tm, tn);
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+    const int64_t hc0 = (int64_t)tn * (BN / 2);  // first h column of the tile (EPI_SILUQ)
     const int valid = clamp_rows(p.mask, e, (int)p.M);
-    if (m0 >= valid) return;  // whole tile past this expert's valid rows
+    if (m0 >= valid) {  // whole tile past this expert's valid rows
+        if constexpr (EPI == EPI_SILUQ) {
+            // its rows of the output scale buffer are zero
+            constexpr int BC = BN / 32;  // 16-column blocks of the tile
+            uint8_t* sf = p.q_sf + (int64_t)e * p.q_sfsz;
+            for (int i = (int)threadIdx.x; i < BM * BC; i += 64 * WGM * WGN * KS) {
+                const int64_t m = m0 + i / BC, c = hc0 / 16 + i % BC;
+                if (m < p.q_rpad && c < 4 * (int64_t)p.q_cp4) sf[sf_offset(m, c, p.q_cp4)] = 0;
+            }
+        }
+        return;
+    }
+    // B matrix row behind tile column c (0 <= c < BN): row n0 + c, or for
+    // EPI_SILUQ the gate or up row of h column j (clamped rows feed outputs
+    // that are never stored)
+    auto b_row = [&](int c) -> int64_t {
+        if constexpr (EPI == EPI_SILUQ) {
+            constexpr int WNl = BN / WGN, HW = WNl / 2;
+            const int cw = c % WNl;
+            int64_t j = hc0 + (c / WNl) * HW + cw % HW;
+            j = j < p.H ? j : p.H - 1;
+            return cw < HW ? j : p.H + j;
+        } else {
+            return n0 + c < p.N ? n0 + c : p.N - 1;
+        }
+    };
 
     const int64_t rowb = p.K / 2;
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.a + (int64_t)e * p.M * rowb, (uint32_t)(p.M * rowb));
@@ -197,7 +245,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, (KS == 2 ? 2 : kWavesPerEU<BM 
 #pragma unroll
     for (int i = 0; i < NFB; i++) {
         const int r = (i * NW + wave) * 16 + (lane >> 2);
-        const int64_t row = n0 + r < p.N ? n0 + r : p.N - 1;
+        const int64_t row = b_row(r);
         voB[i] = (uint32_t)(row * rowb) + (uint32_t)((((lane & 3) ^ swz(r)) << 4));
     }
 #pragma unroll
@@ -208,7 +256,9 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, (KS == 2 ? 2 : kWavesPerEU<BM 
             const int64_t row = m0 + tr < p.rpa ? m0 + tr : p.rpa - 1;
             voS[i] = scale_dword_off(row, g, p.cpa4);
         } else if (tr < BM + BN) {
-            const int64_t row = n0 + (tr - BM) < p.rpb ? n0 + (tr - BM) : p.rpb - 1;
+            int64_t row;
+            if constexpr (EPI == EPI_SILUQ) row = b_row(tr - BM);
+            else row = n0 + (tr - BM) < p.rpb ? n0 + (tr - BM) : p.rpb - 1;
             voS[i] = scale_dword_off(row, g, p.cpa4);
         } else {
             voS[i] = 0;  // padding dwords: any in-bounds source
@@ -487,6 +537,36 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, (KS == 2 ? 2 : kWavesPerEU<BM 
         }
         __builtin_amdgcn_s_waitcnt((0x3F & 0xF) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));  // lgkmcnt(0)
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (EPI == EPI_SILUQ) {
+            // 32 staged rows x NBW blocks of 16 h columns; lane -> (row, block)
+            constexpr int NBW = WN / 32;
+            const float gs = p.q_gs[e];
+            uint8_t* const Q = p.q_fp4 + (int64_t)e * p.M * (p.H / 2);
+            uint8_t* const SF = p.q_sf + (int64_t)e * p.q_sfsz;
+#pragma unroll
+            for (int it = 0; it < 32 * NBW / 64; it++) {
+                const int bi = it * 64 + lane, rl = bi / NBW, bc = bi % NBW;
+                const lds_u8* rowp = ep + rl * PITCH;
+                u32x4 r[4];
+                r[0] = *(const __attribute__((address_space(3))) u32x4*)(rowp + bc * 32);
+                r[1] = *(const __attribute__((address_space(3))) u32x4*)(rowp + bc * 32 + 16);
+                r[2] = *(const __attribute__((address_space(3))) u32x4*)(rowp + WN + bc * 32);
+                r[3] = *(const __attribute__((address_space(3))) u32x4*)(rowp + WN + bc * 32 + 16);
+                const u32x4 pq[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
+                float f[16];
+                const float bamax = process_block<V_SILU>(r, pq, f);
+                const int64_t m = m0 + wm * WM + im * 32 + rl;
+                const int64_t hc = hc0 + wn * (WN / 2) + bc * 16;
+                const bool active = m < valid && hc < p.H;
+                const uint32_t sc = active ? ue4m3_encode((bamax / 6.0f) * gs) : 0u;
+                const float dec = ue4m3_decode(sc);
+                const float rr = dec == 0.0f ? 0.0f : gs / dec;
+                uint32_t w0, w1;
+                pack_block(f, rr, w0, w1);
+                if (active) *(u32x2*)(Q + m * (p.H / 2) + hc / 2) = u32x2{w0, w1};
+                if (m < p.q_rpad && hc / 16 < 4 * (int64_t)p.q_cp4) SF[sf_offset(m, hc / 16, p.q_cp4)] = (uint8_t)sc;
+            }
+        } else {
 #pragma unroll
         for (int it = 0; it < 32 / RPI; it++) {
             const int rl = it * RPI + lane / CPR, c = lane % CPR;
@@ -501,6 +581,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, (KS == 2 ? 2 : kWavesPerEU<BM 
                 for (int u = 0; u < 8; u++)
                     if (n + u < p.N) O[m * p.N + n + u] = (uint16_t)(v[u >> 1] >> (16 * (u & 1)));
             }
+        }
         }
         __builtin_amdgcn_s_waitcnt((0x3F & 0xF) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));  // reads done before the region is rewritten
         __builtin_amdgcn_sched_barrier(0);
@@ -518,12 +599,27 @@ static hipError_t launch_tile(GParams p, bool lora, hipStream_t st) {
     constexpr int threads = 64 * WGM * WGN * KS;
     const bool aligned = (p.K % 128) == 0;
     if (lora) {
-        if (aligned) k_gemm<BM, BN, WGM, WGN, NST, KS, true, true><<<grid, threads, 0, st>>>(p);
-        else k_gemm<BM, BN, WGM, WGN, NST, KS, false, true><<<grid, threads, 0, st>>>(p);
+        if (aligned) k_gemm<BM, BN, WGM, WGN, NST, KS, true, EPI_LORA><<<grid, threads, 0, st>>>(p);
+        else k_gemm<BM, BN, WGM, WGN, NST, KS, false, EPI_LORA><<<grid, threads, 0, st>>>(p);
     } else {
-        if (aligned) k_gemm<BM, BN, WGM, WGN, NST, KS, true, false><<<grid, threads, 0, st>>>(p);
-        else k_gemm<BM, BN, WGM, WGN, NST, KS, false, false><<<grid, threads, 0, st>>>(p);
+        if (aligned) k_gemm<BM, BN, WGM, WGN, NST, KS, true, EPI_PLAIN><<<grid, threads, 0, st>>>(p);
+        else k_gemm<BM, BN, WGM, WGN, NST, KS, false, EPI_PLAIN><<<grid, threads, 0, st>>>(p);
     }
+    return hipGetLastError();
+}
+
+// Quantizing epilogue: a tile covers BN/2 columns of h (its gate and up
+// columns), so the tile grid runs over H.
+template <int BM, int BN, int WGM, int WGN, int NST>
+static hipError_t launch_tile_siluq(GParams p, hipStream_t st) {
+    p.tiles_m = (int)((p.M + BM - 1) / BM);
+    p.tiles_n = (int)((p.H + BN / 2 - 1) / (BN / 2));
+    const int tiles = p.tiles_m * p.tiles_n;
+    p.xcd_chunk = tiles % 8 == 0 ? tiles / 8 : 0;
+    dim3 grid(tiles, 1, (unsigned)p.E);
+    constexpr int threads = 64 * WGM * WGN;
+    if (p.K % 128 == 0) k_gemm<BM, BN, WGM, WGN, NST, 1, true, EPI_SILUQ><<<grid, threads, 0, st>>>(p);
+    else k_gemm<BM, BN, WGM, WGN, NST, 1, false, EPI_SILUQ><<<grid, threads, 0, st>>>(p);
     return hipGetLastError();
 }
 
@@ -835,6 +931,36 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
     case Tile::Skinny: return launch_skinny(p, lora, st);
     default: return launch_tile<128, 128, 2, 2, 2>(p, lora, st);
     }
+}
+
+// Grouped masked GEMM whose epilogue applies silu_and_mul to the gate | up
+// output and quantizes it to NVFP4 with a static per-expert global scale.
+// Whole-K tiles only (the K-split tile would change the accumulation order
+// and the skinny kernel has no staged epilogue); a tile covers BN/2 columns
+// of h, so the tile counts are those of the plain GEMM over N = 2H.
+hipError_t launch_gemm_silu_quantize(const GemmArgs& g, const SiluQuantOut& q, hipStream_t st) {
+    GParams p{};
+    p.a = g.a; p.b = g.b; p.a_sf = g.a_sf; p.b_sf = g.b_sf;
+    p.alpha = g.alpha; p.mask = g.mask;
+    p.M = g.m; p.N = g.n; p.K = g.k;
+    p.E = g.E;
+    const int64_t cp = ((g.k / 16) + 3) / 4 * 4;
+    p.cpa4 = (int)(cp / 4);
+    p.nblk = (int)(g.k / 16);
+    p.rpa = (int)((g.m + 127) / 128 * 128);
+    p.rpb = (int)((g.n + 127) / 128 * 128);
+    p.sfa = (int64_t)p.rpa * cp;
+    p.sfb = (int64_t)p.rpb * cp;
+    p.H = g.n / 2;
+    const int64_t qcp = ((p.H / 16) + 3) / 4 * 4;
+    p.q_cp4 = (int)(qcp / 4);
+    p.q_rpad = p.rpa;
+    p.q_sfsz = (int64_t)p.q_rpad * qcp;
+    p.q_fp4 = q.fp4; p.q_sf = q.sf; p.q_gs = q.gs;
+    auto tiles = [&](int64_t bm, int64_t bn) { return g.E * ((g.m + bm - 1) / bm) * ((p.H + bn / 2 - 1) / (bn / 2)); };
+    if (tiles(256, 256) >= 2 * 256) return launch_tile_siluq<256, 256, 4, 2, 3>(p, st);
+    if (tiles(128, 256) >= 128) return launch_tile_siluq<128, 256, 2, 2, 2>(p, st);
+    return launch_tile_siluq<128, 128, 2, 2, 2>(p, st);
 }
 
 }  // namespace nvfp4

@@ -46,4 +46,14 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
 // Weight-only form: g.a is the bf16 activation [m, k] (a_sf unused).
 hipError_t launch_gemm_w4a16(const GemmArgs& g, hipStream_t st);
 
+// Grouped masked GEMM (g.n = 2H gate | up rows, g.out unused) whose output
+// h is turned into silu(gate) * up and quantized to NVFP4 with the static
+// per-expert global scales gs.
+struct SiluQuantOut {
+    uint8_t* fp4;     // [E, m, H/2]
+    uint8_t* sf;      // [E, pad_up(m,128) * pad_up(H/16,4)]
+    const float* gs;  // [E]
+};
+hipError_t launch_gemm_silu_quantize(const GemmArgs& g, const SiluQuantOut& q, hipStream_t st);
+
 }  // namespace nvfp4

@@ -30,12 +30,9 @@
 // no device-wide fences are involved.
 #include "device_common.h"
 #include "internal.h"
+#include "quant_block.h"
 
 namespace nvfp4 {
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-enum Variant { V_BF16 = 0, V_F32 = 1, V_BF16_SMOOTH = 2, V_F32_SMOOTH = 3, V_SILU = 4 };
 
 struct QParams {
     const void* x;
@@ -53,60 +50,6 @@ struct QParams {
     int nrt;               // row tiles = ceil(m/128)
     int amax_blocks;       // amax workgroups per item (partials per item)
 };
-
-// silu(g) = g / (1 + e^-g), evaluated in fp64 and rounded once to fp32.
-__device__ __forceinline__ float silu_f32(float g) {
-    double x = (double)g;
-    return (float)(x / (1.0 + exp(-x)));
-}
-
-// h = bf16(fp32(S * u)) with S = silu(g) correctly rounded to fp32, for the
-// two bf16 pairs packed in a gate word and an up word: the fast path and its
-// exactness test.  Returns the two h as a packed bf16 pair; bit i of `bad`
-// (i = 0 low, 1 high) is set where the result must come from the exact path.
-//
-// y = g * rcp(1 + 2^(-g * log2 e)) in fp32.  For |g| < 16 the product
-// -g * log2(e) is off by at most |g| * 2^-23 * log2(e) in absolute terms
-// (two roundings), which moves 2^t by at most |g| * 2^-23 relative; with
-// the hardware exp2 and reciprocal (at most 2 ulp and 1 ulp) and the three
-// fp32 roundings, y is within 21 * 2^-23 of S relative.  So fp32(S * u) and
-// p = fp32(y * u) differ by at most 43 ulp of p (a relative bound is worth at
-// most twice its size in ulp).  bf16 rounding changes its result only where
-// the low 16 bits of the pattern cross 0x8000, which no interval of that
-// width does when they sit more than 64 away from it (a binade change inside
-// the interval puts them next to 0 or 0xFFFF), so then bf16(p) is the exact
-// h.  The test also requires |g| >= 2^-77 (so |y| > 2^-101, far from the
-// subnormals) and |p| in [2^-100, 2^100).  Elements that fail it (about 1 in
-// 500 for N(0,1) data, and every |g| >= 16, inf and NaN) take the exact fp64
-// path.
-__device__ __forceinline__ uint32_t silu_mul_fast2(uint32_t gw, uint32_t uw, uint32_t& bad) {
-    constexpr float kLog2e = 1.44269504088896340736f;
-    const float g0 = bf16_lo(gw), g1 = bf16_hi(gw);
-    const float y0 = g0 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g0 * -kLog2e));
-    const float y1 = g1 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g1 * -kLog2e));
-    const float p0 = y0 * bf16_lo(uw), p1 = y1 * bf16_hi(uw);
-    // (bitwise, not short-circuit, so the test stays branch-free)
-    auto fails = [](float g, float p) -> uint32_t {
-        const uint32_t ga = f_bits(g) & 0x7FFFFFFFu, pb = f_bits(p), pa = pb & 0x7FFFFFFFu;
-        return (uint32_t)(ga - 0x19000000u >= 0x41800000u - 0x19000000u) |  // not 2^-77 <= |g| < 16
-               (uint32_t)(pa - 0x0D800000u >= 0x64000000u) |                 // not 2^-100 <= |p| < 2^100
-               (uint32_t)((pb & 0xFFFFu) - 0x7FC0u <= 0x80u);                // low half within 64 of 0x8000
-    };
-    bad = fails(g0, p0) | (fails(g1, p1) << 1);
-    typedef float f32x2 __attribute__((ext_vector_type(2)));
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0, p1}, bf16x2));  // RNE
-}
-
-__device__ __forceinline__ uint32_t silu_mul_exact(float g, float u) {
-    return f32_to_bf16_rne(silu_f32(g) * u);
-}
-
-// 16-byte loads behind one 16-element block of a row.
-template <int V>
-constexpr int loads_per_block() {
-    return V == V_BF16 || V == V_BF16_SMOOTH ? 2 : 4;  // fp32: 64 bytes; silu: gate 32 + up 32
-}
 
 template <int V>
 __device__ __forceinline__ void load_block(const QParams& p, int64_t e, int64_t row, int64_t col,
@@ -135,97 +78,6 @@ __device__ __forceinline__ void load_pqs(const QParams& p, int64_t col, u32x4 (&
         pq[0] = u32x4{0u, 0u, 0u, 0u};
         pq[1] = u32x4{0u, 0u, 0u, 0u};
     }
-}
-
-// The block's 16 values after the prologue and nan_to_num, and their largest
-// magnitude.
-template <int V>
-__device__ __forceinline__ float process_block(const u32x4 (&r)[loads_per_block<V>()], const u32x4 (&pq)[2],
-                                               float (&f)[16]) {
-    if constexpr (V == V_BF16 || V == V_SILU) {
-        uint32_t w[8];
-        if constexpr (V == V_BF16) {
-#pragma unroll
-            for (int j = 0; j < 4; j++) { w[j] = r[0][j]; w[4 + j] = r[1][j]; }
-        } else {
-            // fast path for all 16 elements, then the exact path for the
-            // flagged ones (rare: one divergent branch per block)
-            uint32_t need = 0;
-#pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const uint32_t gw = j < 4 ? r[0][j] : r[1][j - 4];
-                const uint32_t uw = j < 4 ? r[2][j] : r[3][j - 4];
-                uint32_t bad;
-                w[j] = silu_mul_fast2(gw, uw, bad);
-                need |= bad << (2 * j);
-            }
-            // The flagged elements one at a time through a single inlined
-            // copy of the exact path (a call would make the wave wait for
-            // every load it has in flight).
-            while (need) {
-                const int bit = __builtin_ctz(need);
-                need &= need - 1;
-                const int j = bit >> 1, sh = (bit & 1) * 16;
-                uint32_t gw = 0, uw = 0;
-#pragma unroll
-                for (int jj = 0; jj < 8; jj++) {
-                    if (jj == j) {
-                        gw = jj < 4 ? r[0][jj] : r[1][jj - 4];
-                        uw = jj < 4 ? r[2][jj] : r[3][jj - 4];
-                    }
-                }
-                const uint32_t h = silu_mul_exact(bits_f((gw >> sh) << 16), bits_f((uw >> sh) << 16));
-#pragma unroll
-                for (int jj = 0; jj < 8; jj++)
-                    if (jj == j) w[jj] = (w[jj] & ~(0xFFFFu << sh)) | (h << sh);
-            }
-        }
-        // bf16 magnitudes compare as integers; inf / NaN patterns sort above
-        // every finite one
-        const uint32_t mb = __builtin_elementwise_max(absmax_bits_bf16x8(w), absmax_bits_bf16x8(w + 4));
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            f[2 * j] = bf16_lo(w[j]);
-            f[2 * j + 1] = bf16_hi(w[j]);
-        }
-        if (mb < 0x7F80u) return bits_f(mb << 16);
-    } else {
-        if constexpr (V == V_F32 || V == V_F32_SMOOTH) {
-#pragma unroll
-            for (int j = 0; j < 16; j++) f[j] = bits_f(r[j >> 2][j & 3]);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const uint32_t xw = r[j >> 2][j & 3];
-                f[2 * j] = bf16_lo(xw);
-                f[2 * j + 1] = bf16_hi(xw);
-            }
-        }
-        if constexpr (V == V_BF16_SMOOTH || V == V_F32_SMOOTH) {
-#pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const uint32_t pw = pq[j >> 2][j & 3];
-                f[2 * j] = f[2 * j] * bf16_lo(pw);
-                f[2 * j + 1] = f[2 * j + 1] * bf16_hi(pw);
-            }
-        }
-        float a = 0.0f;
-        uint32_t bad = 0;
-#pragma unroll
-        for (int j = 0; j < 16; j++) {
-            a = __builtin_fmaxf(a, __builtin_fabsf(f[j]));
-            bad |= (f_bits(f[j]) & 0x7FFFFFFFu) >= 0x7F800000u;
-        }
-        if (!bad) return a;
-    }
-    // inf or NaN present: the exact nan_to_num path
-    float a = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 16; j++) {
-        f[j] = nan_to_num(f[j]);
-        a = __builtin_fmaxf(a, __builtin_fabsf(f[j]));
-    }
-    return a;
 }
 
 // Lane layout of a workgroup tile of 128 rows x 64*CT columns: BPR = 4*CT

@@ -21,6 +21,7 @@ EXPORTS = (
     "silu_mul_nvfp4_quantize",
     "nvfp4_gemm",
     "nvfp4_gemm_grouped_masked",
+    "nvfp4_gemm_grouped_masked_silu_quantize",
     "nvfp4_gemm_svdquant",
     "nvfp4_gemm_w4a16",
     "nvfp4_alpha",
@@ -49,6 +50,7 @@ def _load():
         "silu_mul_nvfp4_quantize": [vp, i64, i64, i64, vp, vp, i32, vp, vp, vp],
         "nvfp4_gemm": [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, vp],
         "nvfp4_gemm_grouped_masked": [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp],
+        "nvfp4_gemm_grouped_masked_silu_quantize": [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp],
         "nvfp4_gemm_svdquant": [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp],
         "nvfp4_gemm_w4a16": [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp],
         "nvfp4_alpha": [vp, vp, vp, i64, vp],
@@ -198,6 +200,27 @@ def nvfp4_gemm_grouped_masked(a, b, a_sf, b_sf, alpha, mask, out=None):
                                         _ptr(mask), _ptr(out), E, m, n, kb * 2, _stream(a.device))
     _check(rc, "nvfp4_gemm_grouped_masked")
     return out
+
+
+def nvfp4_gemm_grouped_masked_silu_quantize(a, b, a_sf, b_sf, alpha, mask, global_scale,
+                                            out_fp4=None, out_sf=None):
+    """a: [E, m, k/2], b: [E, 2h, k/2] (gate rows, then up rows), global_scale:
+    [E] static scales of the output -> (fp4 [E, m, h/2], sf [E, sf_size(m, h)])
+    of silu(gate) * up of the grouped masked GEMM; rows >= mask[e] of fp4
+    untouched."""
+    E, m, kb = a.shape
+    n2 = b.shape[1]
+    h = n2 // 2
+    dev = a.device
+    if out_fp4 is None:
+        out_fp4 = torch.empty(E, m, h // 2, dtype=torch.uint8, device=dev)
+    if out_sf is None:
+        out_sf = torch.empty(E, sf_size(m, h), dtype=torch.uint8, device=dev)
+    rc = _lib.nvfp4_gemm_grouped_masked_silu_quantize(
+        _ptr(a), _ptr(b), _ptr(a_sf), _ptr(b_sf), _ptr(alpha), _ptr(mask), _ptr(global_scale),
+        E, m, n2, kb * 2, _ptr(out_fp4), _ptr(out_sf), _stream(dev))
+    _check(rc, "nvfp4_gemm_grouped_masked_silu_quantize")
+    return out_fp4, out_sf
 
 
 def nvfp4_gemm_svdquant(a, b, a_sf, b_sf, alpha, d, l1, bias=None, out=None):

@@ -13,6 +13,10 @@ no dataset or checkpoint is involved):
   * moe       -- Llama4-style routed experts: E=8, gate|up [512,16384] bf16,
                  valid rows per expert uniform in [0,512], down-proj weight
                  [8,5120,8192] ~ N(0,0.02).
+  * moe_swiglu -- the same experts one step earlier: hidden states
+                 [8,512,5120] bf16 ~ N(0,1) against gate|up weights
+                 [8,16384,5120] ~ N(0,0.02) (gate rows, then up rows), valid
+                 rows per expert uniform in [0,512].
   * svdquant  -- video-diffusion linear: bf16 X[4096,3072], pre_quant_scale
                  lognormal(0,0.5), weight [3072,3072], rank-32 LoRA pieces,
                  bias [3072].
@@ -106,6 +110,34 @@ def moe(seed=0, e=8, m=512, h=8192, n=5120, mask_lo=0, mask=None):
     for i in range(e):  # per expert, to bound peak host memory
         w[i] = 0.02 * torch.randn(n, h, generator=g, dtype=torch.float32)
     return MoE(_bf16(x), mk, _bf16(w), e, m, h, n)
+
+
+def expert_mask(seed=0, e=8, m=512, lo=0):
+    """Valid rows per expert, uniform in [lo, m] (inclusive)."""
+    return torch.randint(lo, m + 1, (e,), generator=_gen(seed), dtype=torch.int32)
+
+
+@dataclass
+class MoESwiGLU:
+    x: torch.Tensor          # [E, m, hidden] bf16 expert inputs
+    mask: torch.Tensor       # [E] int32 valid rows
+    w: torch.Tensor          # [E, 2h, hidden] bf16, gate rows then up rows
+    e: int
+    m: int
+    h: int
+    hidden: int
+
+
+def moe_swiglu(seed=0, e=8, m=512, h=8192, hidden=5120, mask=None):
+    """Routed-expert gate_up projection input (the step before the silu_and_mul
+    quantize of the moe workload)."""
+    g = _gen(seed)
+    mk = expert_mask(seed + 1, e, m) if mask is None else torch.as_tensor(mask, dtype=torch.int32)
+    x = _bf16(torch.randn(e, m, hidden, generator=g, dtype=torch.float32))
+    w = torch.empty(e, 2 * h, hidden, dtype=torch.bfloat16)
+    for i in range(e):  # per expert, to bound peak host memory
+        w[i] = _bf16(0.02 * torch.randn(2 * h, hidden, generator=g, dtype=torch.float32))
+    return MoESwiGLU(x, mk, w, e, m, h, hidden)
 
 
 @dataclass

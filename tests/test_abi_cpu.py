@@ -33,7 +33,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared() == sorted([
-        "nvfp4_alpha", "nvfp4_gemm", "nvfp4_gemm_grouped_masked", "nvfp4_gemm_svdquant",
+        "nvfp4_alpha", "nvfp4_gemm", "nvfp4_gemm_grouped_masked",
+        "nvfp4_gemm_grouped_masked_silu_quantize", "nvfp4_gemm_svdquant",
         "nvfp4_gemm_w4a16", "nvfp4_quantize_lora_down",
         "nvfp4_quantize", "nvfp4_quantize_masked_batched", "silu_mul_nvfp4_quantize",
     ])
@@ -221,3 +222,25 @@ def test_product_does_not_touch_oracle():
                 txt = open(os.path.join(dirpath, fn)).read()
                 assert "import oracle" not in txt and "from oracle" not in txt, fn
                 assert "nvfp4_oracle" not in txt and "nvo_" not in txt, fn
+
+
+def test_gemm_silu_quantize_validation(lib):
+    f = lib.nvfp4_gemm_grouped_masked_silu_quantize
+    f.argtypes = [ctypes.c_void_p] * 7 + [ctypes.c_int64] * 4 + [ctypes.c_void_p] * 3
+    run = lambda a=P, b=P, asf=P, bsf=P, alpha=P, mask=P, gs=P, E=2, m=64, n2=128, k=256, o4=P, osf=P: \
+        f(a, b, asf, bsf, alpha, mask, gs, E, m, n2, k, o4, osf, None)
+    assert run(mask=None) == NULLP
+    assert run(gs=None) == NULLP
+    assert run(o4=None) == NULLP
+    assert run(osf=None) == NULLP
+    assert run(n2=127) == SHAPE        # odd
+    assert run(n2=16) == SHAPE         # H = 8 < 16
+    assert run(n2=48) == SHAPE         # H = 24 not a multiple of 16
+    assert run(k=40) == SHAPE
+    assert run(E=0) == SHAPE
+    assert run(m=0) == SHAPE
+    assert run(o4=P + 8) == MISAL
+    assert run(osf=P + 4) == MISAL
+    assert run(gs=P + 2) == MISAL
+    assert run(mask=P + 1) == MISAL
+    assert run(m=1 << 20, k=1 << 13) == UNSUP   # one expert's A spans 2^32 bytes
