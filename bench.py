@@ -61,6 +61,7 @@ def build_workload(name, ops, synth, torch):
     w.hbm_bound = False
     w.w4a16 = None
     w.lora_down = None
+    w.swiglu = None
     dev = "cuda"
     if name in ("prefill", "dense", "decode", "tiny"):
         if name == "prefill":
@@ -163,6 +164,7 @@ def build_workload(name, ops, synth, torch):
         w.m, w.n, w.k = valid, n, h
         w.cfg = {"experts": E, "m_max": m, "valid_rows": mo.mask.tolist(), "n": n, "k": h}
         w.cpu_sample = None
+        w.swiglu = lambda: swiglu_front_half(ops, synth, torch, mo.mask, dev)
         return w
 
     if name == "svdquant":
@@ -211,6 +213,70 @@ def build_workload(name, ops, synth, torch):
         w.cpu_sample = None
         return w
     raise ValueError(name)
+
+
+def swiglu_front_half(ops, synth, torch, mask_cpu, dev):
+    """The experts' step before the moe workload's: hidden states [8,512,5120]
+    (NVFP4, quantized once, untimed) against gate|up weights [8,16384,5120],
+    with silu_and_mul + NVFP4 quantize of the output (static global scale,
+    calibrated by one untimed dynamic pass).  Times the one-launch fused path
+    and the two-launch path (grouped GEMM to bf16 h, then the silu quantize),
+    each back to back in a HIP graph."""
+    sw = synth.moe_swiglu(mask=mask_cpu)
+    E, m, H, hid = sw.e, sw.m, sw.h, sw.hidden
+    mask = sw.mask.to(dev)
+    valid = int(sw.mask.clamp(0, m).sum())
+    fx, sfx, gsx = ops.nvfp4_quantize_masked_batched(sw.x.to(dev), mask)
+    fws, sfws, gsws = [], [], []
+    for e in range(E):
+        f_, s_, g_ = ops.nvfp4_quantize(sw.w[e].to(dev))
+        fws.append(f_); sfws.append(s_); gsws.append(g_)
+    del sw
+    fw = torch.stack(fws); sfw = torch.stack(sfws); gsw = torch.cat(gsws)
+    del fws, sfws
+    alpha = ops.nvfp4_alpha(gsx, gsw)
+    h = ops.nvfp4_gemm_grouped_masked(fx, fw, sfx, sfw, alpha, mask)
+    fq = torch.empty(E, m, H // 2, dtype=torch.uint8, device=dev)
+    sfq = torch.empty(E, sf_size(m, H), dtype=torch.uint8, device=dev)
+    _, _, gsh = ops.silu_mul_nvfp4_quantize(h, mask, out_fp4=fq, out_sf=sfq)   # calibration
+    torch.cuda.synchronize()
+    reps = 4
+
+    def fused():
+        ops.nvfp4_gemm_grouped_masked_silu_quantize(fx, fw, sfx, sfw, alpha, mask, gsh, out_fp4=fq, out_sf=sfq)
+
+    def two_launch():
+        ops.nvfp4_gemm_grouped_masked(fx, fw, sfx, sfw, alpha, mask, out=h)
+        ops.silu_mul_nvfp4_quantize(h, mask, gsh, ops.GS_STATIC, out_fp4=fq, out_sf=sfq)
+
+    def gemm_only():
+        ops.nvfp4_gemm_grouped_masked(fx, fw, sfx, sfw, alpha, mask, out=h)
+
+    for fn in (fused, two_launch):
+        fn()
+    torch.cuda.synchronize()
+    # the three graphs timed in turn, five rounds, best of each (the clock
+    # drifts with the chip's power state over a run)
+    graphs = {name: capture(torch, lambda fn=fn: [fn() for _ in range(reps)])
+              for name, fn in (("fused", fused), ("two_launch", two_launch), ("gemm_only", gemm_only))}
+    times = {name: time_graph(torch, g, reps=1) / reps for name, g in graphs.items()}
+    for _ in range(4):
+        for name, g in graphs.items():
+            times[name] = min(times[name], time_graph(torch, g, reps=1) / reps)
+    del graphs
+    flops = 2.0 * valid * 2 * H * hid
+    tf = flops / (times["fused"] * 1e-3) / 1e12
+    return {
+        "kernel": "k_gemm with the silu_and_mul + NVFP4 quantize epilogue (grouped masked gate_up GEMM)",
+        "shape": f"E={E} x {m} rows (valid {mask_cpu.tolist()}) x gate|up {2 * H} x hidden {hid}",
+        "fused_ms": round(times["fused"], 5),
+        "two_launch_ms": round(times["two_launch"], 5),
+        "gemm_to_bf16_ms": round(times["gemm_only"], 5),
+        "fused_tflops": round(tf, 2),
+        "fused_frac_f16_mfma_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+        "flops_per_launch": flops,
+        "bf16_h_bytes_not_written_or_read": 2 * 2 * valid * 2 * H,
+    }
 
 
 def cpu_baseline_dense(O, np, a_cpu, w_cpu, synth, target_s=12.0):
@@ -432,6 +498,10 @@ def main():
         res["w4a16"] = w4
     if ld is not None:
         res["quantize_lora_down"] = ld
+    if w.swiglu is not None:
+        del acts
+        torch.cuda.empty_cache()
+        res["swiglu_gate_up"] = w.swiglu()
     if not args.no_cpu_baseline and w.cpu_sample is not None:
         import oracle as O
         res["cpu_baseline"] = w.cpu_sample(O, np)

@@ -553,11 +553,20 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, (KS == 2 ? 2 : kWavesPerEU<BM 
                 r[2] = *(const __attribute__((address_space(3))) u32x4*)(rowp + WN + bc * 32);
                 r[3] = *(const __attribute__((address_space(3))) u32x4*)(rowp + WN + bc * 32 + 16);
                 const u32x4 pq[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
-                float f[16];
-                const float bamax = process_block<V_SILU>(r, pq, f);
                 const int64_t m = m0 + wm * WM + im * 32 + rl;
                 const int64_t hc = hc0 + wn * (WN / 2) + bc * 16;
                 const bool active = m < valid && hc < p.H;
+                // rows past the valid ones hold whatever A's padding rows gave
+                // (often zeros, which the silu fast path sends to the exact
+                // path): skip their arithmetic
+                float f[16];
+                float bamax = 0.0f;
+                if (active) {
+                    bamax = process_block<V_SILU>(r, pq, f);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 16; j++) f[j] = 0.0f;
+                }
                 const uint32_t sc = active ? ue4m3_encode((bamax / 6.0f) * gs) : 0u;
                 const float dec = ue4m3_decode(sc);
                 const float rr = dec == 0.0f ? 0.0f : gs / dec;
