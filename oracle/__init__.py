@@ -67,6 +67,19 @@ def lib():
         ]
         L.nvo_f64_to_bf16_via_f32.restype = None
         L.nvo_f64_to_bf16_via_f32.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
+        L.nvo_ue8m0_value.restype = ctypes.c_double
+        L.nvo_ue8m0_value.argtypes = [ctypes.c_uint8]
+        L.nvo_sf_size_mx.restype = ctypes.c_int64
+        L.nvo_sf_size_mx.argtypes = [ctypes.c_int64, ctypes.c_int64]
+        L.nvo_sf_offset_mx.restype = ctypes.c_int64
+        L.nvo_sf_offset_mx.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
+        L.nvo_quantize_mx.restype = ctypes.c_int
+        L.nvo_quantize_mx.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, u8p, u8p]
+        L.nvo_gemm_mx_rows.restype = ctypes.c_int
+        L.nvo_gemm_mx_rows.argtypes = [
+            u8p, u8p, u8p, u8p, ctypes.c_float, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+        ]
         L.nvo_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -255,3 +268,55 @@ def gemm_silu_quantize(a, b, a_sf, b_sf, alpha, gs, mask, m, n2, k):
         h[e, :valid] = f64_to_bf16_via_f32(v)
     fp4, sf, _ = quantize(h, prologue=PRO_SILU, mask=mask, gs=gs, gs_mode=STATIC)
     return fp4, sf
+
+
+# ---- MX variant (ue8m0 scale per 32 elements) ---------------------------------
+
+def ue8m0_value(code):
+    return lib().nvo_ue8m0_value(int(code))
+
+
+def sf_size_mx(rows, k):
+    return lib().nvo_sf_size_mx(rows, k)
+
+
+def sf_offset_mx(r, c, k):
+    return lib().nvo_sf_offset_mx(r, c, k)
+
+
+def quantize_mx(x):
+    """MXFP4 quantization of x (uint16 bf16 bits or float32, [m, k], k % 32
+    == 0): returns (fp4 [m, k/2] uint8, sf [sf_size_mx(m, k)] uint8)."""
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        x_dtype = 0
+    elif x.dtype == np.float32:
+        x_dtype = 1
+    else:
+        raise TypeError("x must be bf16 bits (uint16) or float32")
+    m, k = x.shape
+    out_fp4 = np.zeros((m, k // 2), dtype=np.uint8)
+    out_sf = np.zeros(sf_size_mx(m, k), dtype=np.uint8)
+    rc = lib().nvo_quantize_mx(_vp(x), x_dtype, m, k, _u8(out_fp4), _u8(out_sf))
+    if rc != 0:
+        raise ValueError(f"oracle MX quantize rejected the arguments (status {rc})")
+    return out_fp4, out_sf
+
+
+def gemm_mx_rows(a, b, a_sf, b_sf, alpha, m, n, k, rows=None, bias=None):
+    """fp64 alpha * (Adq @ Bdq^T) + bias for the given A rows, MX operands."""
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    a_sf = np.ascontiguousarray(a_sf, dtype=np.uint8)
+    b_sf = np.ascontiguousarray(b_sf, dtype=np.uint8)
+    if rows is None:
+        rows = np.arange(m, dtype=np.int64)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.uint16)
+    out = np.zeros((len(rows), n), dtype=np.float64)
+    rc = lib().nvo_gemm_mx_rows(_u8(a), _u8(b), _u8(a_sf), _u8(b_sf), float(np.float32(alpha)), _vp(bias),
+                                m, n, k, _vp(rows), len(rows), _vp(out))
+    if rc != 0:
+        raise ValueError(f"oracle MX gemm rejected the arguments (status {rc})")
+    return out

@@ -45,6 +45,9 @@
  *   - pre_quant_scale multiplies x in fp32 with no intermediate rounding.
  *   - nan_to_num (NaN -> 0, +-inf -> +-FLT_MAX) is applied to the prologue
  *     output before everything else.
+ *   - the MX setting of fp4_quantize's flags (32-element blocks, ue8m0
+ *     scales) follows the OCP Microscaling Formats (MX) v1.0 conversion; see
+ *     the MX section below.
  *
  * The GEMM accumulates in fp64 (products of two dequantized NVFP4 values are
  * exact in either precision); the pages leave the accumulation order free.
@@ -441,6 +444,125 @@ int nvo_gemm_w4a16_rows(const uint16_t *a, const uint8_t *b, const uint8_t *b_sf
             if (bias)
                 y += (double)nvo_bf16_to_f32(bias[nn]);
             out[j * n + nn] = y;
+        }
+    }
+    free(bdq);
+    return NVO_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* MX variant: one ue8m0 (power-of-two) scale per 32 elements                 */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * [FI] the single-item fp4_quantize takes the block width (16) and a ue8m0
+ * flag (off) as positional arguments; the pages fix nothing else about the
+ * other setting.  Reading: the OCP Microscaling Formats (MX) v1.0 conversion
+ * for MXFP4 -- 32-element blocks, an e8m0 scale X = 2^(floor(log2 amax) - 2)
+ * (2 is the largest exponent of e2m1), elements e2m1(v / X) nearest-even and
+ * saturating at 6, no global scale.  A block whose amax is 0 gets code 0; the
+ * shared exponent is clamped to e8m0's range [-127, 127].  nan_to_num is
+ * applied first, as on the NVFP4 path.  Scales use the same 128x4 swizzled,
+ * zero-padded layout with k/32 columns.
+ */
+double nvo_ue8m0_value(uint8_t code)
+{
+    return code == 0xFF ? NAN : ldexp(1.0, (int)code - 127);
+}
+
+int64_t nvo_sf_size_mx(int64_t rows, int64_t k)
+{
+    return nvo_pad_up(rows, 128) * nvo_pad_up(k / 32, 4);
+}
+
+int64_t nvo_sf_offset_mx(int64_t r, int64_t c, int64_t k)
+{
+    int64_t cp = nvo_pad_up(k / 32, 4);
+    return ((r / 128) * (cp / 4) + c / 4) * 512 + (r % 32) * 16 + ((r % 128) / 32) * 4 + (c % 4);
+}
+
+/* x: bf16 (x_dtype 0) or fp32 (1) [m, k]; out_fp4 [m, k/2]; out_sf
+ * [sf_size_mx(m, k)], fully written. */
+int nvo_quantize_mx(const void *x, int x_dtype, int64_t m, int64_t k, uint8_t *out_fp4, uint8_t *out_sf)
+{
+    if (m < 0 || k < 32 || k % 32 != 0 || (x_dtype != 0 && x_dtype != 1))
+        return NVO_BAD;
+    memset(out_sf, 0, (size_t)nvo_sf_size_mx(m, k));
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < m; r++) {
+        for (int64_t kb = 0; kb < k / 32; kb++) {
+            float blk[32];
+            float amax = 0.0f;
+            for (int j = 0; j < 32; j++) {
+                int64_t i = r * k + kb * 32 + j;
+                float v = x_dtype == 1 ? ((const float *)x)[i] : nvo_bf16_to_f32(((const uint16_t *)x)[i]);
+                blk[j] = nan_to_num(v);
+                if (fabsf(blk[j]) > amax)
+                    amax = fabsf(blk[j]);
+            }
+            int shared = -127;
+            if (amax > 0.0f) {
+                int ex;
+                frexp((double)amax, &ex);      /* amax = f * 2^ex, 0.5 <= f < 1 */
+                shared = (ex - 1) - 2;         /* floor(log2 amax) - emax(e2m1) */
+                if (shared < -127)
+                    shared = -127;
+                if (shared > 127)
+                    shared = 127;
+            }
+            out_sf[nvo_sf_offset_mx(r, kb, k)] = (uint8_t)(amax > 0.0f ? shared + 127 : 0);
+            uint8_t codes[32];
+            for (int j = 0; j < 32; j++)
+                codes[j] = nvo_e2m1_encode((float)ldexp((double)blk[j], -shared));
+            for (int j = 0; j < 16; j++)
+                out_fp4[r * (k / 2) + kb * 16 + j] = (uint8_t)(codes[2 * j] | (codes[2 * j + 1] << 4));
+        }
+    }
+    return NVO_OK;
+}
+
+static double dq_mx(const uint8_t *p, const uint8_t *sf, int64_t row, int64_t col, int64_t K)
+{
+    uint8_t byte = p[row * (K / 2) + col / 2];
+    uint8_t code = (col & 1) ? (byte >> 4) : (byte & 15);
+    return nvo_e2m1_value(code) * nvo_ue8m0_value(sf[nvo_sf_offset_mx(row, col / 32, K)]);
+}
+
+/* MX GEMM rows: out[j, n] = alpha * sum_k Adq[rows[j],k] * Bdq[n,k] + bias[n]
+ * in fp64 (each product of two dequantized MX values is exact). */
+int nvo_gemm_mx_rows(const uint8_t *a, const uint8_t *b, const uint8_t *a_sf, const uint8_t *b_sf,
+                     float alpha, const uint16_t *bias, int64_t m, int64_t n, int64_t k,
+                     const int64_t *rows, int64_t nrows, double *out)
+{
+    if (k % 32 != 0 || m < 0 || n < 0)
+        return NVO_BAD;
+    for (int64_t j = 0; j < nrows; j++)
+        if (rows[j] < 0 || rows[j] >= m)
+            return NVO_BAD;
+    double *bdq = (double *)malloc(sizeof(double) * (size_t)(n * k > 0 ? n * k : 1));
+    if (!bdq)
+        return NVO_BAD;
+#pragma omp parallel for schedule(static)
+    for (int64_t nn = 0; nn < n; nn++)
+        for (int64_t kk = 0; kk < k; kk++)
+            bdq[nn * k + kk] = dq_mx(b, b_sf, nn, kk, k);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t j = 0; j < nrows; j++) {
+        double *arow = (double *)malloc(sizeof(double) * (size_t)k);
+        if (arow) {
+            for (int64_t kk = 0; kk < k; kk++)
+                arow[kk] = dq_mx(a, a_sf, rows[j], kk, k);
+            for (int64_t nn = 0; nn < n; nn++) {
+                double acc = 0.0;
+                const double *brow = bdq + nn * k;
+                for (int64_t kk = 0; kk < k; kk++)
+                    acc += arow[kk] * brow[kk];
+                double y = (double)alpha * acc;
+                if (bias)
+                    y += (double)nvo_bf16_to_f32(bias[nn]);
+                out[j * n + nn] = y;
+            }
+            free(arow);
         }
     }
     free(bdq);
