@@ -240,6 +240,36 @@ int nvfp4_gemm_w4a16(const void *a, const uint8_t *b, const uint8_t *b_sf, const
                      const void *bias, void *out, int64_t m, int64_t n, int64_t k, void *stream);
 
 /*
+ * MX setting of the quantizer (flashinfer PR #1774: fp4_quantize's block
+ * width and ue8m0 flags, there 16 / off; the other setting read as the OCP
+ * Microscaling Formats v1.0 MXFP4 conversion): per 32 consecutive elements of
+ * a row, after nan_to_num, the ue8m0 scale code 127 + floor(log2 amax) - 2
+ * (clamped to [0, 254]; 0 for an all-zero block) and e2m1 codes of x / X,
+ * X = 2^(code - 127), nearest even, saturating at 6.  No global scale.
+ *   x: [m, k] bf16 or fp32 (x_dtype), row-major, 16-byte aligned.
+ *   out_fp4: [m, k/2] uint8; out_sf: pad_up(m,128) * pad_up(k/32,4) bytes in
+ *   the 128x4 swizzled layout over k/32 columns, fully written (padding 0).
+ * Requires m >= 1, k >= 32, k % 32 == 0.  Returns NVFP4_NULL_POINTER,
+ * NVFP4_BAD_DTYPE, NVFP4_BAD_SHAPE or NVFP4_MISALIGNED before launching
+ * anything when an argument is invalid.
+ */
+int mxfp4_quantize(const void *x, int x_dtype, int64_t m, int64_t k, uint8_t *out_fp4, uint8_t *out_sf,
+                   void *stream);
+
+/*
+ * MXFP4 GEMM: out[m, n] = bf16(alpha * (A @ B^T) (+ bias[n])) with A, B in
+ * the layout mxfp4_quantize writes (dq = e2m1 * 2^(code - 127)), accumulated
+ * in fp32 on gfx950's block-scaled MFMA.
+ *   a: [m, k/2]; b: [n, k/2]; a_sf / b_sf: their MX scales; alpha: NULL
+ *   (1.0) or a device fp32 scalar; bias: NULL or [n] bf16; out: [m, n] bf16.
+ * Requires m, n >= 1, k >= 32, k % 32 == 0; NVFP4_UNSUPPORTED when an
+ * operand spans more than 2^32 - 64 bytes.
+ */
+int mxfp4_gemm(const uint8_t *a, const uint8_t *b, const uint8_t *a_sf, const uint8_t *b_sf,
+               const float *alpha, const void *bias, void *out, int64_t m, int64_t n, int64_t k,
+               void *stream);
+
+/*
  * alpha[i] = 1 / (gs_a[i] * gs_b[i]) in fp32 for i < count, on the device
  * (TensorRT-LLM create_weights, the alpha parameter).  Lets a caller that
  * quantizes activations in DYNAMIC mode form the GEMM's alpha without a host

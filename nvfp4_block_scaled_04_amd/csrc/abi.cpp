@@ -179,6 +179,32 @@ int nvfp4_gemm_w4a16(const void* a, const uint8_t* b, const uint8_t* b_sf, const
     return launch_status(nvfp4::launch_gemm_w4a16(g, (hipStream_t)stream));
 }
 
+int mxfp4_quantize(const void* x, int x_dtype, int64_t m, int64_t k, uint8_t* out_fp4, uint8_t* out_sf,
+                   void* stream) {
+    if (!x || !out_fp4 || !out_sf) return NVFP4_NULL_POINTER;
+    if (x_dtype != NVFP4_BF16 && x_dtype != NVFP4_F32) return NVFP4_BAD_DTYPE;
+    if (k < 32 || k % 32 != 0 || !quant_sizes_ok(1, m, k)) return NVFP4_BAD_SHAPE;
+    if (!aligned16(x) || !aligned16(out_fp4) || !aligned16(out_sf)) return NVFP4_MISALIGNED;
+    nvfp4::MxQuantizeArgs a{x, x_dtype, out_fp4, out_sf, m, k};
+    return launch_status(nvfp4::launch_quantize_mx(a, (hipStream_t)stream));
+}
+
+int mxfp4_gemm(const uint8_t* a, const uint8_t* b, const uint8_t* a_sf, const uint8_t* b_sf, const float* alpha,
+               const void* bias, void* out, int64_t m, int64_t n, int64_t k, void* stream) {
+    if (!a || !b || !a_sf || !b_sf || !out) return NVFP4_NULL_POINTER;
+    if (!dim_ok(m) || !dim_ok(n) || k < 32 || k % 32 != 0 || k > kMaxDim) return NVFP4_BAD_SHAPE;
+    if (((m + 127) / 128) * ((n + 127) / 128) > ((int64_t)1 << 31) - 1) return NVFP4_BAD_SHAPE;
+    if (m * (k / 2) > ((int64_t)1 << 32) - 64 || n * (k / 2) > ((int64_t)1 << 32) - 64) return NVFP4_UNSUPPORTED;
+    if (!aligned16(a) || !aligned16(b) || !aligned16(a_sf) || !aligned16(b_sf) || !aligned16(out) ||
+        ((uintptr_t)alpha & 3u) || (bias && !aligned16(bias)))
+        return NVFP4_MISALIGNED;
+    nvfp4::GemmArgs g{};
+    g.a = a; g.b = b; g.a_sf = a_sf; g.b_sf = b_sf; g.alpha = alpha;
+    g.bias = (const uint16_t*)bias; g.out = (uint16_t*)out;
+    g.E = 1; g.m = m; g.n = n; g.k = k;
+    return launch_status(nvfp4::launch_gemm_mx(g, (hipStream_t)stream));
+}
+
 int nvfp4_alpha(const float* gs_a, const float* gs_b, float* alpha, int64_t count, void* stream) {
     if (!gs_a || !gs_b || !alpha) return NVFP4_NULL_POINTER;
     if (!dim_ok(count)) return NVFP4_BAD_SHAPE;

@@ -56,4 +56,16 @@ struct SiluQuantOut {
 };
 hipError_t launch_gemm_silu_quantize(const GemmArgs& g, const SiluQuantOut& q, hipStream_t st);
 
+// MX setting (32-element blocks, ue8m0 scales, no global scale).
+struct MxQuantizeArgs {
+    const void* x;        // [m, k] bf16 or fp32
+    int x_dtype;          // 0 bf16, 1 fp32
+    uint8_t* out_fp4;     // [m, k/2]
+    uint8_t* out_sf;      // [pad_up(m,128) * pad_up(k/32,4)]
+    int64_t m, k;         // k % 32 == 0
+};
+hipError_t launch_quantize_mx(const MxQuantizeArgs& a, hipStream_t st);
+// g.E = 1; g.alpha may be null (1.0); g.mask, g.d, g.l1 unused.
+hipError_t launch_gemm_mx(const GemmArgs& g, hipStream_t st);
+
 }  // namespace nvfp4

@@ -25,6 +25,8 @@ EXPORTS = (
     "nvfp4_gemm_svdquant",
     "nvfp4_gemm_w4a16",
     "nvfp4_alpha",
+    "mxfp4_quantize",
+    "mxfp4_gemm",
 )
 
 STATUS = {
@@ -54,6 +56,8 @@ def _load():
         "nvfp4_gemm_svdquant": [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp],
         "nvfp4_gemm_w4a16": [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp],
         "nvfp4_alpha": [vp, vp, vp, i64, vp],
+        "mxfp4_quantize": [vp, i32, i64, i64, vp, vp, vp],
+        "mxfp4_gemm": [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -256,4 +260,40 @@ def nvfp4_alpha(gs_a, gs_b, out=None):
         out = torch.empty_like(gs_a)
     rc = _lib.nvfp4_alpha(_ptr(gs_a), _ptr(gs_b), _ptr(out), gs_a.numel(), _stream(gs_a.device))
     _check(rc, "nvfp4_alpha")
+    return out
+
+
+# ---- MX setting (32-element blocks, ue8m0 scales) --------------------------------
+
+def sf_size_mx(rows, k):
+    """pad_up(rows,128) * pad_up(k/32,4): bytes of a swizzled MX scale buffer."""
+    return (rows + 127) // 128 * 128 * ((k // 32 + 3) // 4 * 4)
+
+
+def mxfp4_quantize(x, out_fp4=None, out_sf=None):
+    """x: [m, k] bf16 or fp32 -> (fp4 [m, k/2] uint8, sf [sf_size_mx(m, k)] uint8)."""
+    _need(x, "x")
+    m, k = x.shape
+    dt = {torch.bfloat16: 0, torch.float32: 1}.get(x.dtype)
+    if dt is None:
+        raise ValueError("x must be bf16 or fp32")
+    dev = x.device
+    if out_fp4 is None:
+        out_fp4 = torch.empty(m, k // 2, dtype=torch.uint8, device=dev)
+    if out_sf is None:
+        out_sf = torch.empty(sf_size_mx(m, k), dtype=torch.uint8, device=dev)
+    rc = _lib.mxfp4_quantize(_ptr(x), dt, m, k, _ptr(out_fp4), _ptr(out_sf), _stream(dev))
+    _check(rc, "mxfp4_quantize")
+    return out_fp4, out_sf
+
+
+def mxfp4_gemm(a, b, a_sf, b_sf, alpha=None, bias=None, out=None):
+    """a: [m, k/2], b: [n, k/2] MXFP4 -> out [m, n] bf16 = alpha*(a@b^T) (+bias)."""
+    m, n = a.shape[0], b.shape[0]
+    k = a.shape[1] * 2
+    if out is None:
+        out = torch.empty(m, n, dtype=torch.bfloat16, device=a.device)
+    rc = _lib.mxfp4_gemm(_ptr(a), _ptr(b), _ptr(a_sf), _ptr(b_sf), _ptr(alpha), _ptr(bias), _ptr(out),
+                         m, n, k, _stream(a.device))
+    _check(rc, "mxfp4_gemm")
     return out

@@ -37,6 +37,7 @@ def test_header_declares_the_entry_points():
         "nvfp4_gemm_grouped_masked_silu_quantize", "nvfp4_gemm_svdquant",
         "nvfp4_gemm_w4a16", "nvfp4_quantize_lora_down",
         "nvfp4_quantize", "nvfp4_quantize_masked_batched", "silu_mul_nvfp4_quantize",
+        "mxfp4_quantize", "mxfp4_gemm",
     ])
 
 
@@ -244,3 +245,27 @@ def test_gemm_silu_quantize_validation(lib):
     assert run(gs=P + 2) == MISAL
     assert run(mask=P + 1) == MISAL
     assert run(m=1 << 20, k=1 << 13) == UNSUP   # one expert's A spans 2^32 bytes
+
+
+def test_mx_validation(lib):
+    q = lib.mxfp4_quantize
+    q.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64] + [ctypes.c_void_p] * 3
+    runq = lambda x=P, dt=0, m=64, k=256, o4=P, osf=P: q(x, dt, m, k, o4, osf, None)
+    assert runq(x=None) == NULLP
+    assert runq(osf=None) == NULLP
+    assert runq(dt=3) == DTYPE
+    assert runq(k=48) == SHAPE          # not a multiple of 32
+    assert runq(k=16) == SHAPE
+    assert runq(m=0) == SHAPE
+    assert runq(o4=P + 8) == MISAL
+    g = lib.mxfp4_gemm
+    g.argtypes = [ctypes.c_void_p] * 7 + [ctypes.c_int64] * 3 + [ctypes.c_void_p]
+    rung = lambda a=P, b=P, asf=P, bsf=P, alpha=None, bias=None, out=P, m=64, n=64, k=256: \
+        g(a, b, asf, bsf, alpha, bias, out, m, n, k, None)
+    assert rung(a=None) == NULLP
+    assert rung(out=None) == NULLP
+    assert rung(k=48) == SHAPE
+    assert rung(n=0) == SHAPE
+    assert rung(alpha=P + 2) == MISAL
+    assert rung(bias=P + 2) == MISAL
+    assert rung(m=1 << 20, k=1 << 13) == UNSUP
