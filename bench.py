@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, TFLOP/s
+MFMA_FP4_PEAK_TFLOPS = 10100.0  # MI355X dense fp4 (and fp6) MFMA, TFLOP/s
 
 
 def sf_size(rows, k):
@@ -62,6 +63,7 @@ def build_workload(name, ops, synth, torch):
     w.w4a16 = None
     w.lora_down = None
     w.swiglu = None
+    w.mx = None
     dev = "cuda"
     if name in ("prefill", "dense", "decode", "tiny"):
         if name == "prefill":
@@ -122,6 +124,8 @@ def build_workload(name, ops, synth, torch):
             w.w4a16 = lambda a: ops.nvfp4_gemm_w4a16(a, fw, sfw, alpha_w, out=out_w)
             w.w4a16_bytes = n * k // 2 + sf_size(n, k) + m * k * 2 + 2 * m * n
         w.cpu_sample = lambda O, np: cpu_baseline_dense(O, np, a_cpu, w_cpu, synth)
+        if name in ("prefill", "dense"):
+            w.mx = lambda acts: mx_setting(ops, torch, acts, w_cpu, dev)
         return w
 
     if name == "moe":
@@ -213,6 +217,42 @@ def build_workload(name, ops, synth, torch):
         w.cpu_sample = None
         return w
     raise ValueError(name)
+
+
+def mx_setting(ops, torch, acts, w_cpu, dev):
+    """The same linear in the MX setting (32-element blocks, ue8m0 scales):
+    the weight quantized once (untimed); the activation quantize pass over
+    every activation copy and the GEMM back to back, each in a HIP graph."""
+    m, k = acts[0].shape
+    n = w_cpu.shape[0]
+    fw, sfw = ops.mxfp4_quantize(w_cpu.to(dev))
+    fa = torch.empty(m, k // 2, dtype=torch.uint8, device=dev)
+    sfa = torch.empty(ops.sf_size_mx(m, k), dtype=torch.uint8, device=dev)
+    out = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+    for a in acts:
+        ops.mxfp4_quantize(a, out_fp4=fa, out_sf=sfa)
+    ops.mxfp4_gemm(fa, fw, sfa, sfw, out=out)
+    torch.cuda.synchronize()
+    g_q = capture(torch, lambda: [ops.mxfp4_quantize(a, out_fp4=fa, out_sf=sfa) for a in acts])
+    q_ms = time_graph(torch, g_q) / len(acts)
+    del g_q
+    reps = max(1, len(acts))
+    g_g = capture(torch, lambda: [ops.mxfp4_gemm(fa, fw, sfa, sfw, out=out) for _ in range(reps)])
+    g_ms = time_graph(torch, g_g) / reps
+    del g_g
+    q_bytes = m * k * acts[0].element_size() + m * k // 2 + ops.sf_size_mx(m, k)
+    flops = 2.0 * m * n * k
+    tf = flops / (g_ms * 1e-3) / 1e12
+    q_gbs = q_bytes / (q_ms * 1e-3) / 1e9
+    return {
+        "kernels": "k_quantize_mx (one pass, no global scale) and k_gemm_mx (v_mfma_scale_f32_32x32x64, FP4 operands)",
+        "quantize_pass_ms": round(q_ms, 4), "quantize_gbs": round(q_gbs, 1),
+        "quantize_frac_hbm": round(q_gbs / HBM_PEAK_GBS, 4), "quantize_bytes": q_bytes,
+        "gemm_ms": round(g_ms, 4), "gemm_tflops": round(tf, 2),
+        "gemm_frac_fp4_mfma_peak": round(tf / MFMA_FP4_PEAK_TFLOPS, 4),
+        "step_ms": round(q_ms + g_ms, 4),
+        "step_tflops": round(flops / ((q_ms + g_ms) * 1e-3) / 1e12, 2),
+    }
 
 
 def swiglu_front_half(ops, synth, torch, mask_cpu, dev):
@@ -498,6 +538,8 @@ def main():
         res["w4a16"] = w4
     if ld is not None:
         res["quantize_lora_down"] = ld
+    if w.mx is not None:
+        res["mx"] = w.mx(acts)
     if w.swiglu is not None:
         del acts
         torch.cuda.empty_cache()

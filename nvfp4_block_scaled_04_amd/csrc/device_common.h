@@ -32,6 +32,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return u >> 16;
 }
 
+// Two fp32 values to a packed bf16 pair (a low, b high) with one hardware
+// conversion, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
 // Largest |x| over 8 packed bf16 values, as the bf16 bit pattern of |x|
 // (for non-negative values integer order is value order; NaN and inf patterns
 // compare above every finite one).

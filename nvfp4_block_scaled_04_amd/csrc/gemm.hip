@@ -454,8 +454,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, (KS == 2 ? 2 : kWavesPerEU<BM 
                     if (p.bias && n + u < p.N) y[u] += bf16_lo((uint32_t)p.bias[n + u]);
                 }
                 *(__attribute__((address_space(3))) u32x2*)(ep + l32 * PITCH + cl * 2) =
-                    u32x2{f32_to_bf16_rne(y[0]) | (f32_to_bf16_rne(y[1]) << 16),
-                          f32_to_bf16_rne(y[2]) | (f32_to_bf16_rne(y[3]) << 16)};
+                    u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
             }
         }
         __builtin_amdgcn_s_waitcnt((0x3F & 0xF) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));  // lgkmcnt(0)
@@ -665,13 +664,13 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GParams p) {
     }
     if ((p.N & 3) == 0 && n + 3 < p.N) {
         uint2 o;
-        o.x = f32_to_bf16_rne(y[0]) | (f32_to_bf16_rne(y[1]) << 16);
-        o.y = f32_to_bf16_rne(y[2]) | (f32_to_bf16_rne(y[3]) << 16);
+        o.x = pack_bf16x2(y[0], y[1]);
+        o.y = pack_bf16x2(y[2], y[3]);
         *(uint2*)(O + n) = o;
     } else {
 #pragma unroll
         for (int v = 0; v < 4; v++)
-            if (n + v < p.N) O[n + v] = (uint16_t)f32_to_bf16_rne(y[v]);
+            if (n + v < p.N) O[n + v] = (uint16_t)pack_bf16x2(y[v], 0.0f);
     }
 #endif
 }
@@ -782,13 +781,13 @@ __global__ __launch_bounds__(256) void k_gemm_w4a16(GParams p) {
     }
     if ((p.N & 3) == 0 && n + 3 < p.N) {
         uint2 o;
-        o.x = f32_to_bf16_rne(y[0]) | (f32_to_bf16_rne(y[1]) << 16);
-        o.y = f32_to_bf16_rne(y[2]) | (f32_to_bf16_rne(y[3]) << 16);
+        o.x = pack_bf16x2(y[0], y[1]);
+        o.y = pack_bf16x2(y[2], y[3]);
         *(uint2*)(O + n) = o;
     } else {
 #pragma unroll
         for (int v = 0; v < 4; v++)
-            if (n + v < p.N) O[n + v] = (uint16_t)f32_to_bf16_rne(y[v]);
+            if (n + v < p.N) O[n + v] = (uint16_t)pack_bf16x2(y[v], 0.0f);
     }
 #endif
 }

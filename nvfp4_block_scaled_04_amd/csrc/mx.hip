@@ -243,42 +243,29 @@ __global__ __launch_bounds__(64 * WGM * WGN, (kMxWavesPerEU<BM / WGM, BN / WGN>)
     const int sa_off = OFF_S + (wm * WM + l32) * 4;
     const int sb_off = OFF_S + (BM + wn * WN + l32) * 4;
 
-    // the step's fragments (both half steps) and scale bytes; blocks past K
-    // (only when K % 128 != 0) get zero elements
+    // fragments and scale bytes of half step q (both halves in registers at
+    // once); blocks past K (only when K % 128 != 0) get zero elements
     u32x4 fa[2][FM], fb[2][FN];
     int sa[2][FM], sb[2][FN];
-    auto load_step = [&](const lds_u8* st, int step) {
+    auto load_half = [&](const lds_u8* st, int step, int q) {
+        const int sh = 16 * q + 8 * h;  // byte 2q+h of the row's scale dword
 #pragma unroll
-        for (int i = 0; i < FM; i++) {
-            const uint32_t d = *(const __attribute__((address_space(3))) uint32_t*)(st + sa_off + i * 128);
-            sa[0][i] = (int)((d >> (8 * h)) & 0xFFu);
-            sa[1][i] = (int)((d >> (16 + 8 * h)) & 0xFFu);
-        }
+        for (int i = 0; i < FM; i++)
+            sa[q][i] = (int)((*(const __attribute__((address_space(3))) uint32_t*)(st + sa_off + i * 128) >> sh) & 0xFFu);
 #pragma unroll
-        for (int i = 0; i < FN; i++) {
-            const uint32_t d = *(const __attribute__((address_space(3))) uint32_t*)(st + sb_off + i * 128);
-            sb[0][i] = (int)((d >> (8 * h)) & 0xFFu);
-            sb[1][i] = (int)((d >> (16 + 8 * h)) & 0xFFu);
-        }
+        for (int i = 0; i < FN; i++)
+            sb[q][i] = (int)((*(const __attribute__((address_space(3))) uint32_t*)(st + sb_off + i * 128) >> sh) & 0xFFu);
+        const int cq = q ? cq1 : cq0;
 #pragma unroll
-        for (int i = 0; i < FM; i++) {
-            fa[0][i] = *(const __attribute__((address_space(3))) u32x4*)(st + ra_off + i * 2048 + cq0);
-            fa[1][i] = *(const __attribute__((address_space(3))) u32x4*)(st + ra_off + i * 2048 + cq1);
-        }
+        for (int i = 0; i < FM; i++) fa[q][i] = *(const __attribute__((address_space(3))) u32x4*)(st + ra_off + i * 2048 + cq);
 #pragma unroll
-        for (int i = 0; i < FN; i++) {
-            fb[0][i] = *(const __attribute__((address_space(3))) u32x4*)(st + rb_off + i * 2048 + cq0);
-            fb[1][i] = *(const __attribute__((address_space(3))) u32x4*)(st + rb_off + i * 2048 + cq1);
-        }
+        for (int i = 0; i < FN; i++) fb[q][i] = *(const __attribute__((address_space(3))) u32x4*)(st + rb_off + i * 2048 + cq);
         if constexpr (!ALIGNED) {
+            if (step * 4 + 2 * q + h >= p.nblk) {
 #pragma unroll
-            for (int q = 0; q < 2; q++) {
-                if (step * 4 + 2 * q + h >= p.nblk) {
+                for (int i = 0; i < FM; i++) fa[q][i] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-                    for (int i = 0; i < FM; i++) fa[q][i] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-                    for (int i = 0; i < FN; i++) fb[q][i] = u32x4{0u, 0u, 0u, 0u};
-                }
+                for (int i = 0; i < FN; i++) fb[q][i] = u32x4{0u, 0u, 0u, 0u};
             }
         }
     };
@@ -298,21 +285,27 @@ __global__ __launch_bounds__(64 * WGM * WGN, (kMxWavesPerEU<BM / WGM, BN / WGN>)
 
     // Step kt lives in stage kt % NST; its loads are issued NST-1 steps ahead
     // into the stage step kt-1 used, which every wave has finished reading
-    // (its reads complete before the barrier that ends step kt-1).
+    // (its reads complete before the barrier in the middle of step kt-1's
+    // MFMAs).  The LDS reads of each half step are in flight during the
+    // other half's MFMAs: q = 1 of step kt beside q = 0, and after the
+    // barrier q = 0 of step kt+1 beside q = 1 of step kt.  The last step's
+    // read of the next stage finds a reloaded copy of the final step, unused.
     issue(0, sm);
     if constexpr (NST == 3) issue(1 < nkt ? 1 : 0, sm + STAGE);
     wait_vmcnt<ND * (NST - 2)>();
     barrier();
+    load_half(sm, 0, 0);
     int sc = 0;
     for (int kt = 0; kt < nkt; kt++) {
         const int s1 = sc == NST - 1 ? 0 : sc + 1;
         const int sl = NST == 2 ? s1 : (s1 == 2 ? 0 : s1 + 1);  // stage of step kt+NST-1
-        load_step(sm + sc * STAGE, kt);
         issue(kt + NST - 1 < nkt ? kt + NST - 1 : nkt - 1, sm + sl * STAGE);
+        load_half(sm + sc * STAGE, kt, 1);
         mfma_half(0);
-        mfma_half(1);
         wait_vmcnt<ND * (NST - 2)>();  // step kt+1 has landed (this wave's part)
         barrier();
+        load_half(sm + s1 * STAGE, kt + 1, 0);
+        mfma_half(1);
         sc = s1;
     }
     wait_vmcnt<0>();  // nothing may land in LDS after the workgroup ends
@@ -339,8 +332,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, (kMxWavesPerEU<BM / WGM, BN / WGN>)
                     if (p.bias && n + u < p.N) y[u] += bf16_lo((uint32_t)p.bias[n + u]);
                 }
                 *(__attribute__((address_space(3))) u32x2*)(ep + l32 * PITCH + cl * 2) =
-                    u32x2{f32_to_bf16_rne(y[0]) | (f32_to_bf16_rne(y[1]) << 16),
-                          f32_to_bf16_rne(y[2]) | (f32_to_bf16_rne(y[3]) << 16)};
+                    u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
             }
         }
         __builtin_amdgcn_s_waitcnt((0x3F & 0xF) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));  // lgkmcnt(0)
