@@ -163,7 +163,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, (kMxWavesPerEU<BM / WGM, BN / WGN>)
     constexpr int NFA = BM / (16 * NW), NFB = BN / (16 * NW), NSC = SC_DW / (64 * NW);
     constexpr int ND = NFA + NFB + NSC;
     static_assert(BM % (16 * NW) == 0 && BN % (16 * NW) == 0 && BM % 64 == 0, "whole rows per wave load");
-    static_assert(NST == 2 || NST == 3, "two or three LDS stages");
+    static_assert(NST >= 2 && NST <= 4, "two to four LDS stages");
     __shared__ __align__(16) uint8_t smem[NST * STAGE];
 
     const int t = threadIdx.x;
@@ -243,18 +243,19 @@ __global__ __launch_bounds__(64 * WGM * WGN, (kMxWavesPerEU<BM / WGM, BN / WGN>)
     const int sa_off = OFF_S + (wm * WM + l32) * 4;
     const int sb_off = OFF_S + (BM + wn * WN + l32) * 4;
 
-    // fragments and scale bytes of half step q (both halves in registers at
-    // once); blocks past K (only when K % 128 != 0) get zero elements
+    // fragments of half step q and the scale dwords of a step (shifted so the
+    // lane's block of half step q sits in byte 2q, selected by the MFMA's
+    // opsel); blocks past K (only when K % 128 != 0) get zero elements
     u32x4 fa[2][FM], fb[2][FN];
-    int sa[2][FM], sb[2][FN];
-    auto load_half = [&](const lds_u8* st, int step, int q) {
-        const int sh = 16 * q + 8 * h;  // byte 2q+h of the row's scale dword
+    auto load_scales = [&](const lds_u8* st, int (&sa)[FM], int (&sb)[FN]) {
 #pragma unroll
         for (int i = 0; i < FM; i++)
-            sa[q][i] = (int)((*(const __attribute__((address_space(3))) uint32_t*)(st + sa_off + i * 128) >> sh) & 0xFFu);
+            sa[i] = (int)(*(const __attribute__((address_space(3))) uint32_t*)(st + sa_off + i * 128) >> (8 * h));
 #pragma unroll
         for (int i = 0; i < FN; i++)
-            sb[q][i] = (int)((*(const __attribute__((address_space(3))) uint32_t*)(st + sb_off + i * 128) >> sh) & 0xFFu);
+            sb[i] = (int)(*(const __attribute__((address_space(3))) uint32_t*)(st + sb_off + i * 128) >> (8 * h));
+    };
+    auto load_half = [&](const lds_u8* st, int step, int q) {
         const int cq = q ? cq1 : cq0;
 #pragma unroll
         for (int i = 0; i < FM; i++) fa[q][i] = *(const __attribute__((address_space(3))) u32x4*)(st + ra_off + i * 2048 + cq);
@@ -270,13 +271,21 @@ __global__ __launch_bounds__(64 * WGM * WGN, (kMxWavesPerEU<BM / WGM, BN / WGN>)
         }
     };
     // B is the MFMA's first operand (4 consecutive output columns per lane)
-    auto mfma_half = [&](int q) {
+    auto mfma_half0 = [&](const int (&sa)[FM], const int (&sb)[FN]) {
 #pragma unroll
         for (int in = 0; in < FN; in++)
 #pragma unroll
             for (int im = 0; im < FM; im++)
                 acc[in][im] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    mx_operand(fb[q][in]), mx_operand(fa[q][im]), acc[in][im], 4, 4, 0, sb[q][in], 0, sa[q][im]);
+                    mx_operand(fb[0][in]), mx_operand(fa[0][im]), acc[in][im], 4, 4, 0, sb[in], 0, sa[im]);
+    };
+    auto mfma_half1 = [&](const int (&sa)[FM], const int (&sb)[FN]) {
+#pragma unroll
+        for (int in = 0; in < FN; in++)
+#pragma unroll
+            for (int im = 0; im < FM; im++)
+                acc[in][im] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    mx_operand(fb[1][in]), mx_operand(fa[1][im]), acc[in][im], 4, 4, 2, sb[in], 2, sa[im]);
     };
     auto barrier = [&]() {
         __builtin_amdgcn_s_waitcnt((0x3F & 0xF) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));  // lgkmcnt(0)
@@ -288,24 +297,45 @@ __global__ __launch_bounds__(64 * WGM * WGN, (kMxWavesPerEU<BM / WGM, BN / WGN>)
     // (its reads complete before the barrier in the middle of step kt-1's
     // MFMAs).  The LDS reads of each half step are in flight during the
     // other half's MFMAs: q = 1 of step kt beside q = 0, and after the
-    // barrier q = 0 of step kt+1 beside q = 1 of step kt.  The last step's
-    // read of the next stage finds a reloaded copy of the final step, unused.
-    issue(0, sm);
-    if constexpr (NST == 3) issue(1 < nkt ? 1 : 0, sm + STAGE);
+    // barrier the scales and q = 0 of step kt+1 beside q = 1 of step kt
+    // (measured: 2-3% over letting the compiler place the reads; a fourth
+    // stage, two K steps per barrier and 128 x 128 wave tiles at one wave per
+    // SIMD were no faster).  The last step's read of the next stage finds a
+    // reloaded copy of the final step, unused.
+#pragma unroll
+    for (int j = 0; j < NST - 1; j++) issue(j < nkt ? j : nkt - 1, sm + j * STAGE);
     wait_vmcnt<ND * (NST - 2)>();
     barrier();
+    int sa[FM], sb[FN];
+    load_scales(sm, sa, sb);
     load_half(sm, 0, 0);
     int sc = 0;
     for (int kt = 0; kt < nkt; kt++) {
         const int s1 = sc == NST - 1 ? 0 : sc + 1;
-        const int sl = NST == 2 ? s1 : (s1 == 2 ? 0 : s1 + 1);  // stage of step kt+NST-1
+        const int sl = sc == 0 ? NST - 1 : sc - 1;  // stage of step kt+NST-1 (= that of step kt-1)
         issue(kt + NST - 1 < nkt ? kt + NST - 1 : nkt - 1, sm + sl * STAGE);
         load_half(sm + sc * STAGE, kt, 1);
-        mfma_half(0);
+        mfma_half0(sa, sb);
+        // staging loads, then the q = 1 reads, then the q = 0 MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x020, ND, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
+        __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<ND * (NST - 2)>();  // step kt+1 has landed (this wave's part)
         barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        int na[FM], nb[FN];
+        load_scales(sm + s1 * STAGE, na, nb);
         load_half(sm + s1 * STAGE, kt + 1, 0);
-        mfma_half(1);
+        mfma_half1(sa, sb);
+        // the next step's scale and q = 0 reads, then the q = 1 MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (FM + FN), 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < FM; i++) sa[i] = na[i];
+#pragma unroll
+        for (int i = 0; i < FN; i++) sb[i] = nb[i];
         sc = s1;
     }
     wait_vmcnt<0>();  // nothing may land in LDS after the workgroup ends
