@@ -359,14 +359,19 @@ def cpu_baseline_dense(O, np, a_cpu, w_cpu, synth, target_s=12.0):
 # (--copy-calibration: fetch x2.000, write x1.000).  A record is used only
 # while the kernel sources hash to the value it was measured on.
 MEASURED_TRAFFIC = {
-    "prefill": {"sources_sha256": "dd771d242d42d2ea95666dc4a69faf56a325387be25607b408c665823a67ad4a"
-                                  "32694de9304b75f8ee1cd5af84ca2546d39f0481e139161ecc9e748198c8dfb0",
-                "fetch_kib": 276834.6, "write_kib": 262144.0, "fetch_factor": 2.0, "write_factor": 1.0},
-    "moe": {"sources_sha256": "dd771d242d42d2ea95666dc4a69faf56a325387be25607b408c665823a67ad4a"
-                              "32694de9304b75f8ee1cd5af84ca2546d39f0481e139161ecc9e748198c8dfb0",
-            "fetch_kib": 159820.3, "write_kib": 15350.0, "fetch_factor": 2.0, "write_factor": 1.0},
+    "prefill": {"sources_sha256": "4c38f76689a21cab5a4420095a8271d49a34bdd6848c6b134907006c5cc32195"
+                                  "faf55d4cd243fe2a127d65280e8b95f55a1c37a38f9c6433dcc115ee1fe0f350"
+                                  "b78954052145e2babdd6f327935f70bab87bfb0bca4c38bc415b04c1fd7708b1"
+                                  "1286af577a92b62864a1892dab16fdf95f9c00e73cc4786fcdc44f6510096e56",
+                "fetch_kib": 276691.5, "write_kib": 262144.0, "fetch_factor": 2.0, "write_factor": 1.0},
+    "moe": {"sources_sha256": "4c38f76689a21cab5a4420095a8271d49a34bdd6848c6b134907006c5cc32195"
+                              "faf55d4cd243fe2a127d65280e8b95f55a1c37a38f9c6433dcc115ee1fe0f350"
+                              "b78954052145e2babdd6f327935f70bab87bfb0bca4c38bc415b04c1fd7708b1"
+                              "1286af577a92b62864a1892dab16fdf95f9c00e73cc4786fcdc44f6510096e56",
+            "fetch_kib": 158206.1, "write_kib": 15350.0, "fetch_factor": 2.0, "write_factor": 1.0},
 }
-GEMM_SOURCES = ("nvfp4_block_scaled_04_amd/csrc/gemm.hip", "nvfp4_block_scaled_04_amd/csrc/device_common.h")
+GEMM_SOURCES = ("nvfp4_block_scaled_04_amd/csrc/gemm.hip", "nvfp4_block_scaled_04_amd/csrc/gemm_common.h",
+                "nvfp4_block_scaled_04_amd/csrc/device_common.h", "nvfp4_block_scaled_04_amd/csrc/quant_block.h")
 
 
 def gemm_traffic(workload):
