@@ -141,6 +141,12 @@ __global__ __launch_bounds__(256) void k_amax(QParams p) {
             __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
 }
 
+// gs = 2688 / max(amax, 1e-12) in fp32 (448 * 6 over the clamped amax).
+__device__ __forceinline__ float gs_from_amax(float am) {
+    const float lo = 1e-12f;
+    return 2688.0f / (am < lo ? lo : am);
+}
+
 // gs[e] = 2688 / max(amax_e, 1e-12) from item e's partial maxima.
 __global__ __launch_bounds__(256) void k_finish_gs(QParams p) {
     const int e = blockIdx.x, t = threadIdx.x;
@@ -156,18 +162,15 @@ __global__ __launch_bounds__(256) void k_finish_gs(QParams p) {
     __shared__ float wmax[4];
     if ((t & 63) == 0) wmax[t >> 6] = a;
     __syncthreads();
-    if (t == 0) {
-        const float am = __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
-        const float lo = 1e-12f;
-        p.gs[e] = 2688.0f / (am < lo ? lo : am);
-    }
+    if (t == 0) p.gs[e] = gs_from_amax(__builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3])));
 }
 
-template <int V, int CT>
-__global__ __launch_bounds__(256) void k_quantize(QParams p) {
+// One tile of the quantize pass; gs_of() gives the item's global scale (read
+// while the tile's loads are in flight).
+template <int V, int CT, typename GsFn>
+__device__ __forceinline__ void quantize_tile(const QParams& p, int wct, int rt, int e, GsFn gs_of) {
     using TM = TileMap<CT>;
     constexpr int NL = loads_per_block<V>();
-    const int wct = blockIdx.x, rt = blockIdx.y, e = blockIdx.z;
     const int t = threadIdx.x;
     const int rsub = t / TM::BPR, lb = t % TM::BPR;
     const int c = lb >> 2;   // swizzle tile within the workgroup
@@ -197,7 +200,7 @@ __global__ __launch_bounds__(256) void k_quantize(QParams p) {
     }
     // element factors r = gs / dec(s) for every scale code (0 for code 0),
     // computed while the loads are in flight
-    const float gs = p.gs[e];
+    const float gs = gs_of();
     if (t < 128) {
         const float dec = ue4m3_decode((uint32_t)t);
         rtab[t] = dec == 0.0f ? 0.0f : gs / dec;
@@ -228,93 +231,72 @@ __global__ __launch_bounds__(256) void k_quantize(QParams p) {
     for (int i = t; i < ntile_here * 32; i += 256) *(u32x4*)(sf_dst + i * 16) = *(const u32x4*)(sbuf + i * 16);
 }
 
-// ---------------------------------------------------------------------------
-// Small items (decode-sized activations) in DYNAMIC mode: the whole item in
-// one workgroup of 1024 threads.  Each thread loads up to kSmallBlocks 16-element blocks once
-// and keeps them in registers; the workgroup reduces the global amax, forms
-// gs, and quantizes from the registers, with the item's whole scale buffer
-// (padding included) assembled in LDS and written with 16-byte stores.  One
-// launch and one read of the input instead of the amax pass, the finish and
-// the quantize pass.  Same arithmetic, same results.
-// ---------------------------------------------------------------------------
+template <int V, int CT>
+__global__ __launch_bounds__(256) void k_quantize(QParams p) {
+    const int e = blockIdx.z;
+    quantize_tile<V, CT>(p, blockIdx.x, blockIdx.y, e, [&] { return p.gs[e]; });
+}
 
-constexpr int kSmallThreads = 1024;
-constexpr int kSmallSfBytes = 32768;     // largest padded scale buffer of an item
-// 16-element blocks per thread (the silu prologue needs more registers per
-// block, so it holds fewer)
+// ---------------------------------------------------------------------------
+// Small items (at most 2^16 elements, 2^15 with the silu prologue) in
+// DYNAMIC mode, in one launch: every workgroup of the tiled pass first
+// recomputes the item's global amax over all of its valid blocks -- the item
+// is small, so the redundant reads come from L2 and cost less than the amax
+// and finish launches -- forms gs with the finish kernel's arithmetic, and
+// quantizes its own tile.  The first workgroup of the item writes gs.  Same
+// arithmetic and bytes as the three-kernel path.
+// ---------------------------------------------------------------------------
 template <int V>
-constexpr int small_blocks() { return V == V_SILU ? 2 : 4; }
+constexpr int64_t fused_max_elems() { return V == V_SILU ? 32768 : 65536; }
 
 template <int V>
-__global__ __launch_bounds__(1024) void k_quantize_small(QParams p) {
+__device__ __forceinline__ float item_amax(const QParams& p, int e, int valid) {
     constexpr int NL = loads_per_block<V>();
-    constexpr int kSmallBlocks = small_blocks<V>();
-    const int e = blockIdx.x, t = threadIdx.x;
-    const int valid = clamp_rows(p.mask, e, (int)p.m);
-    const int bpr = (int)(p.K / 16);  // blocks per row
-    const int nb = valid * bpr;       // blocks of the valid rows
-    __shared__ __align__(16) uint8_t sfl[kSmallSfBytes];
-    __shared__ float wmax[kSmallThreads / 64];
-    for (int i = t; i < (int)(p.sfsz / 16); i += kSmallThreads) *(u32x4*)(sfl + i * 16) = u32x4{0u, 0u, 0u, 0u};
-    u32x4 raw[kSmallBlocks][NL];
-    u32x4 pq[kSmallBlocks][2];
+    constexpr int U = V == V_BF16 ? 16 : 8;  // blocks per thread with loads in flight together
+    const int64_t nblk = p.K / 16, nb = (int64_t)valid * nblk;
+    float amax = 0.0f;
+    for (int64_t b0 = threadIdx.x; b0 < nb; b0 += 256 * U) {
+        u32x4 raw[U][NL], pq[U][2];
 #pragma unroll
-    for (int i = 0; i < kSmallBlocks; i++) {  // every load in flight before any use
-        const int b = t + i * kSmallThreads;
-        const int row = b < nb ? b / bpr : 0, cb = b < nb ? b - (b / bpr) * bpr : 0;
-        load_block<V>(p, e, row, (int64_t)cb * 16, raw[i]);
-        load_pqs<V>(p, (int64_t)cb * 16, pq[i]);
-    }
-    float gs;
-    {
-        float amax = 0.0f;
-#pragma unroll
-        for (int i = 0; i < kSmallBlocks; i++) {
-            float f[16];
-            const float a = process_block<V>(raw[i], pq[i], f);
-            if (t + i * kSmallThreads < nb) amax = __builtin_fmaxf(amax, a);
+        for (int u = 0; u < U; u++) {
+            const int64_t b = b0 + 256 * u < nb ? b0 + 256 * u : nb - 1;  // past the end: a repeat, same maximum
+            const int64_t row = b / nblk, col = (b - row * nblk) * 16;
+            load_block<V>(p, e, row, col, raw[u]);
+            load_pqs<V>(p, col, pq[u]);
         }
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, off));
-        if ((t & 63) == 0) wmax[t >> 6] = amax;
-        __syncthreads();
-        float am = wmax[0];
-#pragma unroll
-        for (int w = 1; w < kSmallThreads / 64; w++) am = __builtin_fmaxf(am, wmax[w]);
-        const float lo = 1e-12f;
-        gs = 2688.0f / (am < lo ? lo : am);
-        if (t == 0) p.gs[e] = gs;
+        for (int u = 0; u < U; u++) {
+            float f[16];
+            amax = __builtin_fmaxf(amax, process_block<V>(raw[u], pq[u], f));
+        }
     }
-    uint8_t* q = p.out_fp4 + (int64_t)e * p.m * (p.K / 2);
-    const int cpa4 = p.nct;  // 4-column scale groups per row
-#pragma unroll
-    for (int i = 0; i < kSmallBlocks; i++) {
-        const int b = t + i * kSmallThreads;
-        if (b >= nb) continue;
-        const int row = b / bpr, cb = b - (b / bpr) * bpr;
-        float f[16];
-        const float bamax = process_block<V>(raw[i], pq[i], f);
-        const uint32_t sc = ue4m3_encode((bamax / 6.0f) * gs);
-        const float dec = ue4m3_decode(sc);
-        const float r = dec == 0.0f ? 0.0f : gs / dec;
-        uint32_t w0 = 0, w1 = 0;
-        w0 = NVFP4_PACK_FP4(w0, f[0] * r, f[1] * r, 0);
-        w0 = NVFP4_PACK_FP4(w0, f[2] * r, f[3] * r, 1);
-        w0 = NVFP4_PACK_FP4(w0, f[4] * r, f[5] * r, 2);
-        w0 = NVFP4_PACK_FP4(w0, f[6] * r, f[7] * r, 3);
-        w1 = NVFP4_PACK_FP4(w1, f[8] * r, f[9] * r, 0);
-        w1 = NVFP4_PACK_FP4(w1, f[10] * r, f[11] * r, 1);
-        w1 = NVFP4_PACK_FP4(w1, f[12] * r, f[13] * r, 2);
-        w1 = NVFP4_PACK_FP4(w1, f[14] * r, f[15] * r, 3);
-        *(uint2*)(q + (int64_t)row * (p.K / 2) + cb * 8) = uint2{w0, w1};
-        sfl[((row >> 7) * cpa4 + (cb >> 2)) * 512 + (row & 31) * 16 + ((row & 127) >> 5) * 4 + (cb & 3)] =
-            (uint8_t)sc;
-    }
-    __syncthreads();
-    uint8_t* sf_dst = p.out_sf + (int64_t)e * p.sfsz;
-    for (int i = t; i < (int)(p.sfsz / 16); i += kSmallThreads)
-        *(u32x4*)(sf_dst + i * 16) = *(const u32x4*)(sfl + i * 16);
+    return amax;
 }
+
+template <int V, int CT>
+__global__ __launch_bounds__(256) void k_quantize_fused(QParams p) {
+    const int wct = blockIdx.x, rt = blockIdx.y, e = blockIdx.z;
+    const int t = threadIdx.x;
+    const int valid = clamp_rows(p.mask, e, (int)p.m);
+    const bool first = wct == 0 && rt == 0;
+    __shared__ float wmax[4];
+    // no valid rows: every tile only zeroes its scales, and gs comes from amax 0
+    if (valid == 0 && first && t == 0) p.gs[e] = gs_from_amax(0.0f);
+    // The amax pass runs where the tile asks for gs, after its own loads are
+    // issued, so they land meanwhile (tiles past the valid rows never ask).
+    quantize_tile<V, CT>(p, wct, rt, e, [&] {
+        float a = item_amax<V>(p, e, valid);
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) a = __builtin_fmaxf(a, __shfl_xor(a, off));
+        if ((t & 63) == 0) wmax[t >> 6] = a;
+        __syncthreads();
+        const float gs = gs_from_amax(__builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]),
+                                                      __builtin_fmaxf(wmax[2], wmax[3])));
+        if (first && t == 0) p.gs[e] = gs;
+        return gs;
+    });
+}
+
 
 // ---------------------------------------------------------------------------
 // Smooth quantize with the SVDQuant LoRA-down projection fused (flashinfer
@@ -555,8 +537,12 @@ static hipError_t launch_variant(QParams p, bool dynamic, hipStream_t st) {
     constexpr int CTA = V == V_SILU ? 1 : 2;
     // DYNAMIC mode on small items: one launch instead of three (a STATIC pass
     // is one launch anyway, and spreads over more compute units)
-    if (dynamic && p.m * p.K <= (int64_t)kSmallThreads * small_blocks<V>() * 16 && p.sfsz <= kSmallSfBytes) {
-        k_quantize_small<V><<<p.b, kSmallThreads, 0, st>>>(p);
+    if (dynamic && p.m * p.K <= fused_max_elems<V>()) {
+        if constexpr (V == V_SILU) {
+            k_quantize_fused<V, 1><<<dim3(p.nct, p.nrt, p.b), 256, 0, st>>>(p);
+        } else {
+            k_quantize_fused<V, 2><<<dim3((p.nct + 1) / 2, p.nrt, p.b), 256, 0, st>>>(p);
+        }
         return hipGetLastError();
     }
     if (dynamic) {

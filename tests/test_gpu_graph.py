@@ -38,7 +38,7 @@ def _capture(fn):
 
 @pytest.mark.parametrize("shape", [(16, 4096, 4096), (512, 1024, 2048), (2048, 4096, 4096)])
 def test_dynamic_pipeline_replays(ops, shape):
-    """Dynamic quantize (one-workgroup and tiled paths), alpha, GEMM (skinny,
+    """Dynamic quantize (one-launch small-item and three-kernel paths), alpha, GEMM (skinny,
     K-split and tiled kernels) captured once, replayed three times."""
     m, n, k = shape
     say("graph pipeline", shape)
