@@ -3,10 +3,10 @@ and global scales must be bit-identical.  Outputs start filled with a canary
 byte so that unwritten padding and masked rows are caught.
 
 In DYNAMIC mode, items of at most 65536 elements (32768 with the silu
-prologue) whose padded scale buffer fits 32 KB are quantized by one
-workgroup per item; larger ones, and STATIC mode, by the tiled passes.  The
-cases below cover each prologue and masking form on both sides of that
-line."""
+prologue) are quantized in one launch (each workgroup of the tiled pass
+recomputes the item's amax); larger ones take the amax pass, the finish and
+the quantize pass.  The cases below cover each prologue and masking form on
+both sides of that line."""
 import numpy as np
 import pytest
 import torch
