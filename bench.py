@@ -372,6 +372,21 @@ MEASURED_TRAFFIC = {
                               "b78954052145e2babdd6f327935f70bab87bfb0bca4c38bc415b04c1fd7708b1"
                               "1286af577a92b62864a1892dab16fdf95f9c00e73cc4786fcdc44f6510096e56",
             "fetch_kib": 158206.1, "write_kib": 15350.0, "fetch_factor": 2.0, "write_factor": 1.0},
+    "dense": {"sources_sha256": "4c38f76689a21cab5a4420095a8271d49a34bdd6848c6b134907006c5cc32195"
+                                "faf55d4cd243fe2a127d65280e8b95f55a1c37a38f9c6433dcc115ee1fe0f350"
+                                "b78954052145e2babdd6f327935f70bab87bfb0bca4c38bc415b04c1fd7708b1"
+                                "1286af577a92b62864a1892dab16fdf95f9c00e73cc4786fcdc44f6510096e56",
+              "fetch_kib": 18638.0, "write_kib": 16384.0, "fetch_factor": 2.0, "write_factor": 1.0},
+    "svdquant": {"sources_sha256": "4c38f76689a21cab5a4420095a8271d49a34bdd6848c6b134907006c5cc32195"
+                                   "faf55d4cd243fe2a127d65280e8b95f55a1c37a38f9c6433dcc115ee1fe0f350"
+                                   "b78954052145e2babdd6f327935f70bab87bfb0bca4c38bc415b04c1fd7708b1"
+                                   "1286af577a92b62864a1892dab16fdf95f9c00e73cc4786fcdc44f6510096e56",
+                 "fetch_kib": 18474.0, "write_kib": 24576.0, "fetch_factor": 2.0, "write_factor": 1.0},
+    "decode": {"sources_sha256": "4c38f76689a21cab5a4420095a8271d49a34bdd6848c6b134907006c5cc32195"
+                                 "faf55d4cd243fe2a127d65280e8b95f55a1c37a38f9c6433dcc115ee1fe0f350"
+                                 "b78954052145e2babdd6f327935f70bab87bfb0bca4c38bc415b04c1fd7708b1"
+                                 "1286af577a92b62864a1892dab16fdf95f9c00e73cc4786fcdc44f6510096e56",
+               "fetch_kib": 6404.0, "write_kib": 128.0, "fetch_factor": 2.0, "write_factor": 1.0},
 }
 GEMM_SOURCES = ("nvfp4_block_scaled_04_amd/csrc/gemm.hip", "nvfp4_block_scaled_04_amd/csrc/gemm_common.h",
                 "nvfp4_block_scaled_04_amd/csrc/device_common.h", "nvfp4_block_scaled_04_amd/csrc/quant_block.h")
@@ -554,7 +569,7 @@ def main():
         # HBM, over the back-to-back kernel time
         gbs = w.gemm_bytes / (gemm_graph_ms * 1e-3) / 1e9
         res["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                           "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": gemm_traffic(args.workload),
                            "kernel": "k_gemm_skinny (block-scaled NVFP4 GEMM, 16 rows)",
                            "algorithmic_bytes_per_launch": w.gemm_bytes}
     if w4 is not None:
