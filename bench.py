@@ -48,6 +48,8 @@ def parse():
     p.add_argument("--workload", default="prefill",
                    choices=["prefill", "dense", "decode", "moe", "svdquant", "tiny"])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-library", action="store_true",
+                   help="skip the comparison with the vendor library's GEMMs (prefill and dense only)")
     p.add_argument("--rotate", type=int, default=0,
                    help="activation copies cycled per step (0: enough to exceed 512 MB)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -67,6 +69,7 @@ def build_workload(name, ops, synth, torch):
     w.lora_down = None
     w.swiglu = None
     w.mx = None
+    w.library = None
     dev = "cuda"
     if name in ("prefill", "dense", "decode", "tiny"):
         if name == "prefill":
@@ -129,6 +132,7 @@ def build_workload(name, ops, synth, torch):
         w.cpu_sample = lambda O, np: cpu_baseline_dense(O, np, a_cpu, w_cpu, synth)
         if name in ("prefill", "dense"):
             w.mx = lambda acts: mx_setting(ops, torch, acts, w_cpu, dev)
+            w.library = lambda acts: library_comparison(ops, torch, w, acts[0], w_cpu, dev)
         return w
 
     if name == "moe":
@@ -392,6 +396,69 @@ GEMM_SOURCES = ("nvfp4_block_scaled_04_amd/csrc/gemm.hip", "nvfp4_block_scaled_0
                 "nvfp4_block_scaled_04_amd/csrc/device_common.h", "nvfp4_block_scaled_04_amd/csrc/quant_block.h")
 
 
+def library_comparison(ops, torch, w, a16, w_cpu, dev, rounds=3):
+    """For comparison only: the vendor library's GEMMs (hipBLASLt through
+    torch) on the same shape and the same data, timed beside this library's
+    two GEMMs by the same method (reps launches back to back between HIP
+    events on the current stream, best of `rounds` interleaved rounds):
+      * bf16 x bf16 with the weight [n, k] (both operands K-contiguous, as in
+        the NVFP4 GEMM) -- the unquantized linear, on the same fp16/bf16
+        MFMA pipe the exact NVFP4 path runs on;
+      * fp8 e4m3 with per-tensor scales;
+      * MXFP4 (torch._scaled_mm with e2m1 operands and e8m0 block scales) on
+        this library's MX-quantized operands; the scale bytes are handed over
+        in this library's swizzled order, so this leg is timed only and its
+        output is not checked."""
+    m, k = a16.shape
+    n = w_cpu.shape[0]
+    flops = 2.0 * m * n * k
+    w16 = w_cpu.to(dev)
+    out16 = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+    legs = {"k_gemm (NVFP4, this library)": (w.gemm, MFMA_F16_PEAK_TFLOPS),
+            "hipblaslt bf16": (lambda: torch.matmul(a16, w16.t(), out=out16), MFMA_F16_PEAK_TFLOPS)}
+    fa, sfa = ops.mxfp4_quantize(a16)
+    fw, sfw = ops.mxfp4_quantize(w16)
+    out_mx = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+    legs["k_gemm_mx (MXFP4, this library)"] = (lambda: ops.mxfp4_gemm(fa, fw, sfa, sfw, out=out_mx),
+                                                MFMA_FP4_PEAK_TFLOPS)
+    one = torch.ones((), dtype=torch.float32, device=dev)
+    a8, w8 = a16.to(torch.float8_e4m3fn), w16.to(torch.float8_e4m3fn)
+    legs["hipblaslt fp8 e4m3"] = (lambda: torch._scaled_mm(a8, w8.t(), one, one, out_dtype=torch.bfloat16),
+                                  2 * MFMA_F16_PEAK_TFLOPS)
+    fa4, fw4 = fa.view(torch.float4_e2m1fn_x2), fw.view(torch.float4_e2m1fn_x2)
+    sa8, sw8 = sfa.view(torch.float8_e8m0fnu), sfw.view(torch.float8_e8m0fnu)
+    legs["hipblaslt mxfp4"] = (lambda: torch._scaled_mm(fa4, fw4.t(), sa8, sw8, out_dtype=torch.bfloat16),
+                               MFMA_FP4_PEAK_TFLOPS)
+    res, ok = {}, {}
+    for name, (fn, peak) in legs.items():
+        try:
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            ok[name] = (fn, peak)
+        except Exception as ex:  # a library leg this torch build does not support
+            res[name] = {"error": repr(ex)[:200]}
+    est_ms = flops / 1.0e12   # the launch time at 1 PFLOP/s
+    reps = max(5, min(200, int(30.0 / est_ms)))
+    best = {}
+    for _ in range(rounds):
+        for name, (fn, _) in ok.items():
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) / reps
+            best[name] = min(best.get(name, t), t)
+    for name, (_, peak) in ok.items():
+        tf = flops / (best[name] * 1e-3) / 1e12
+        res[name] = {"ms": round(best[name], 5), "tflops": round(tf, 1), "frac_of_dtype_peak": round(tf / peak, 4),
+                     "dtype_peak_tflops": peak}
+    return {"note": "comparison only: vendor GEMMs on the same shape and data, timed by the same method "
+                    f"({reps} launches back to back, best of {rounds} interleaved rounds)", "legs": res}
+
+
 def gemm_traffic(workload):
     import hashlib
 
@@ -578,6 +645,8 @@ def main():
         res["quantize_lora_down"] = ld
     if w.mx is not None:
         res["mx"] = w.mx(acts)
+    if w.library is not None and not args.no_library:
+        res["library"] = w.library(acts)
     if w.swiglu is not None:
         del acts
         torch.cuda.empty_cache()
