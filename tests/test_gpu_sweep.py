@@ -23,21 +23,21 @@ def draw(n, fn):
     return [fn(RNG) for _ in range(n)]
 
 
-QUANT = draw(10, lambda r: (int(r.integers(1, 400)), 16 * int(r.integers(1, 160)), bool(r.integers(0, 2)),
+QUANT = draw(60, lambda r: (int(r.integers(1, 400)), 16 * int(r.integers(1, 160)), bool(r.integers(0, 2)),
                             bool(r.integers(0, 2)), bool(r.integers(0, 2))))
-BATCHED = draw(6, lambda r: (int(r.integers(1, 5)), int(r.integers(1, 260)), 16 * int(r.integers(1, 48)),
+BATCHED = draw(30, lambda r: (int(r.integers(1, 5)), int(r.integers(1, 260)), 16 * int(r.integers(1, 48)),
                              bool(r.integers(0, 2)), bool(r.integers(0, 2))))
-GEMM = draw(12, lambda r: (int(r.integers(1, 520)), int(r.integers(1, 700)), 16 * int(r.integers(1, 80)),
+GEMM = draw(60, lambda r: (int(r.integers(1, 520)), int(r.integers(1, 700)), 16 * int(r.integers(1, 80)),
                            bool(r.integers(0, 2))))
-GROUPED = draw(4, lambda r: (int(r.integers(1, 5)), int(r.integers(1, 300)), int(r.integers(1, 300)),
+GROUPED = draw(20, lambda r: (int(r.integers(1, 5)), int(r.integers(1, 300)), int(r.integers(1, 300)),
                              16 * int(r.integers(1, 40))))
-SVD = draw(4, lambda r: (int(r.integers(1, 300)), int(r.integers(1, 300)), 16 * int(r.integers(1, 40)),
+SVD = draw(20, lambda r: (int(r.integers(1, 300)), int(r.integers(1, 300)), 16 * int(r.integers(1, 40)),
                          32 * int(r.integers(1, 5))))
-W4 = draw(6, lambda r: (int(r.integers(1, 100)), int(r.integers(1, 500)), 16 * int(r.integers(1, 100)),
+W4 = draw(30, lambda r: (int(r.integers(1, 100)), int(r.integers(1, 500)), 16 * int(r.integers(1, 100)),
                         bool(r.integers(0, 2))))
-SWIGLU = draw(4, lambda r: (int(r.integers(1, 4)), int(r.integers(1, 300)), 16 * int(r.integers(1, 30)),
+SWIGLU = draw(16, lambda r: (int(r.integers(1, 4)), int(r.integers(1, 300)), 16 * int(r.integers(1, 30)),
                             16 * int(r.integers(1, 40))))
-MX = draw(8, lambda r: (int(r.integers(1, 400)), int(r.integers(1, 600)), 32 * int(r.integers(1, 60))))
+MX = draw(40, lambda r: (int(r.integers(1, 400)), int(r.integers(1, 600)), 32 * int(r.integers(1, 60))))
 
 
 @pytest.fixture(scope="module")
