@@ -338,12 +338,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, (kMxWavesPerEU<BM / WGM, BN / WGN>)
         for (int i = 0; i < FN; i++) sb[i] = nb[i];
         sc = s1;
     }
-    wait_vmcnt<0>();  // nothing may land in LDS after the workgroup ends
+    wait_vmcnt<0>();  // this wave's staging loads have landed
 
     // ---- epilogue: alpha, bias, bf16, staged through LDS one 32-row
-    // fragment row at a time so every output row leaves as 16-byte pieces
+    // fragment row at a time so every output row leaves as 16-byte pieces.
+    // The staging region overlaps the pipeline stages: the barrier holds it
+    // until every wave's last staging loads have landed.
     constexpr int PITCH = WN * 2 + 16;
     static_assert(NW * 32 * PITCH <= NST * STAGE, "epilogue staging fits in the pipeline's LDS");
+    barrier();
     lds_u8* const ep = sm + wave * 32 * PITCH;
     const float alpha = p.alpha ? p.alpha[0] : 1.0f;
     constexpr int CPR = WN / 8, RPI = 64 / CPR;
