@@ -20,7 +20,9 @@ step / step time); the quantize and GEMM kernels are also reported on their
 own (the quantize pass and the whole dynamic call timed back to back over
 every activation copy, next to a plain device copy for reference), and
 `roofline` covers the dominant kernel (the GEMM), timed with HIP events on
-the stream it runs on.
+the stream it runs on.  For the prefill and dense workloads, `library` times
+the vendor library's GEMMs (hipBLASLt through torch: bf16, fp8, MXFP4) beside
+this library's on the same shape and data, for comparison only.
 """
 import argparse
 import json
