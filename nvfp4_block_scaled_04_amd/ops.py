@@ -92,8 +92,39 @@ def sf_size(rows, k):
 
 
 def _need(t, name):
-    if not (t.is_cuda and t.is_contiguous()):
+    if not (isinstance(t, torch.Tensor) and t.is_cuda and t.is_contiguous()):
         raise ValueError(f"{name} must be a contiguous device tensor")
+
+
+BYTES = "bytes"  # any one-byte dtype (uint8, float4_e2m1fn_x2, float8 scale types)
+
+
+def _dev(t, name, dtype, numel, device):
+    """t must be a contiguous tensor on `device` of `dtype` (a dtype, a tuple
+    of them, or BYTES) holding at least `numel` elements: the library reads
+    or writes that many through the raw pointer, so anything else raises here,
+    before any launch."""
+    _need(t, name)
+    if dtype is BYTES:
+        if t.element_size() != 1:
+            raise ValueError(f"{name} must have a one-byte dtype, got {t.dtype}")
+    elif t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, the call needs {numel}")
+    return t
+
+
+def _opt(t, name, dtype, numel, device):
+    return None if t is None else _dev(t, name, dtype, numel, device)
+
+
+def _dims(t, name, nd):
+    _need(t, name)
+    if t.dim() != nd:
+        raise ValueError(f"{name} must have {nd} dimensions, got shape {tuple(t.shape)}")
 
 
 # ---- quantization -------------------------------------------------------------
@@ -101,7 +132,7 @@ def _need(t, name):
 def nvfp4_quantize(x, global_scale=None, gs_mode=GS_DYNAMIC, pre_quant_scale=None,
                    out_fp4=None, out_sf=None):
     """x: [m, k] bf16 or fp32 -> (fp4 [m, k/2] uint8, sf [sf_size] uint8, gs [1] fp32)."""
-    _need(x, "x")
+    _dims(x, "x", 2)
     m, k = x.shape
     dt = {torch.bfloat16: 0, torch.float32: 1}.get(x.dtype)
     if dt is None:
@@ -113,6 +144,10 @@ def nvfp4_quantize(x, global_scale=None, gs_mode=GS_DYNAMIC, pre_quant_scale=Non
         out_fp4 = torch.empty(m, k // 2, dtype=torch.uint8, device=dev)
     if out_sf is None:
         out_sf = torch.empty(sf_size(m, k), dtype=torch.uint8, device=dev)
+    _opt(pre_quant_scale, "pre_quant_scale", torch.bfloat16, k, dev)
+    _dev(global_scale, "global_scale", torch.float32, 1, dev)
+    _dev(out_fp4, "out_fp4", BYTES, m * (k // 2), dev)
+    _dev(out_sf, "out_sf", BYTES, sf_size(m, k), dev)
     rc = _lib.nvfp4_quantize(_ptr(x), dt, m, k, _ptr(pre_quant_scale), _ptr(global_scale),
                              gs_mode, _ptr(out_fp4), _ptr(out_sf), _stream(dev))
     _check(rc, "nvfp4_quantize")
@@ -124,11 +159,16 @@ def nvfp4_quantize_lora_down(x, pre_quant_scale, l2, global_scale=None, gs_mode=
     """Smooth NVFP4 quantize of bf16 x [m, k] (pre_quant_scale [k] bf16) and the
     SVDQuant LoRA-down d = bf16((x * pqs) @ l2^T), l2 [r, k] bf16, in one read
     of x.  Returns (fp4 [m, k/2], sf, global_scale [1], d [m, r])."""
-    for t, name in ((x, "x"), (pre_quant_scale, "pre_quant_scale"), (l2, "l2")):
-        _need(t, name)
+    _dims(x, "x", 2)
+    _dims(l2, "l2", 2)
     m, k = x.shape
     r = l2.shape[0]
     dev_ = x.device
+    _dev(x, "x", torch.bfloat16, m * k, dev_)
+    _dev(pre_quant_scale, "pre_quant_scale", torch.bfloat16, k, dev_)
+    if l2.shape[1] != k:
+        raise ValueError(f"l2 must be [r, {k}], got {tuple(l2.shape)}")
+    _dev(l2, "l2", torch.bfloat16, r * k, dev_)
     if global_scale is None:
         global_scale = torch.zeros(1, dtype=torch.float32, device=dev_)
     if out_fp4 is None:
@@ -137,6 +177,10 @@ def nvfp4_quantize_lora_down(x, pre_quant_scale, l2, global_scale=None, gs_mode=
         out_sf = torch.empty(sf_size(m, k), dtype=torch.uint8, device=dev_)
     if d is None:
         d = torch.empty(m, r, dtype=torch.bfloat16, device=dev_)
+    _dev(global_scale, "global_scale", torch.float32, 1, dev_)
+    _dev(out_fp4, "out_fp4", BYTES, m * (k // 2), dev_)
+    _dev(out_sf, "out_sf", BYTES, sf_size(m, k), dev_)
+    _dev(d, "d", torch.bfloat16, m * r, dev_)
     rc = _lib.nvfp4_quantize_lora_down(_ptr(x), m, k, _ptr(pre_quant_scale), _ptr(l2), r, _ptr(global_scale),
                                        gs_mode, _ptr(out_fp4), _ptr(out_sf), _ptr(d), _stream(dev_))
     _check(rc, "nvfp4_quantize_lora_down")
@@ -146,15 +190,20 @@ def nvfp4_quantize_lora_down(x, pre_quant_scale, l2, global_scale=None, gs_mode=
 def nvfp4_quantize_masked_batched(x, mask=None, global_scale=None, gs_mode=GS_DYNAMIC,
                                   out_fp4=None, out_sf=None):
     """x: [b, m, k] bf16 -> (fp4 [b, m, k/2], sf [b, sf_size], gs [b])."""
-    _need(x, "x")
+    _dims(x, "x", 3)
     b, m, k = x.shape
     dev = x.device
+    _dev(x, "x", torch.bfloat16, b * m * k, dev)
     if global_scale is None:
         global_scale = torch.zeros(b, dtype=torch.float32, device=dev)
     if out_fp4 is None:
         out_fp4 = torch.empty(b, m, k // 2, dtype=torch.uint8, device=dev)
     if out_sf is None:
         out_sf = torch.empty(b, sf_size(m, k), dtype=torch.uint8, device=dev)
+    _opt(mask, "mask", torch.int32, b, dev)
+    _dev(global_scale, "global_scale", torch.float32, b, dev)
+    _dev(out_fp4, "out_fp4", BYTES, b * m * (k // 2), dev)
+    _dev(out_sf, "out_sf", BYTES, b * sf_size(m, k), dev)
     rc = _lib.nvfp4_quantize_masked_batched(_ptr(x), b, m, k, _ptr(mask), _ptr(global_scale),
                                             gs_mode, _ptr(out_fp4), _ptr(out_sf), _stream(dev))
     _check(rc, "nvfp4_quantize_masked_batched")
@@ -164,16 +213,21 @@ def nvfp4_quantize_masked_batched(x, mask=None, global_scale=None, gs_mode=GS_DY
 def silu_mul_nvfp4_quantize(x, mask=None, global_scale=None, gs_mode=GS_DYNAMIC,
                             out_fp4=None, out_sf=None):
     """x: [b, m, 2h] bf16 (gate | up) -> (fp4 [b, m, h/2], sf [b, sf_size(m, h)], gs [b])."""
-    _need(x, "x")
+    _dims(x, "x", 3)
     b, m, k2 = x.shape
     h = k2 // 2
     dev = x.device
+    _dev(x, "x", torch.bfloat16, b * m * k2, dev)
     if global_scale is None:
         global_scale = torch.zeros(b, dtype=torch.float32, device=dev)
     if out_fp4 is None:
         out_fp4 = torch.empty(b, m, h // 2, dtype=torch.uint8, device=dev)
     if out_sf is None:
         out_sf = torch.empty(b, sf_size(m, h), dtype=torch.uint8, device=dev)
+    _opt(mask, "mask", torch.int32, b, dev)
+    _dev(global_scale, "global_scale", torch.float32, b, dev)
+    _dev(out_fp4, "out_fp4", BYTES, b * m * (h // 2), dev)
+    _dev(out_sf, "out_sf", BYTES, b * sf_size(m, h), dev)
     rc = _lib.silu_mul_nvfp4_quantize(_ptr(x), b, m, k2, _ptr(mask), _ptr(global_scale), gs_mode,
                                       _ptr(out_fp4), _ptr(out_sf), _stream(dev))
     _check(rc, "silu_mul_nvfp4_quantize")
@@ -182,12 +236,31 @@ def silu_mul_nvfp4_quantize(x, mask=None, global_scale=None, gs_mode=GS_DYNAMIC,
 
 # ---- GEMM -----------------------------------------------------------------------
 
+def _operands(a, b, a_sf, b_sf, E, m, n, k, dev, sfsz):
+    """Packed FP4 operands (E items of [m|n, k/2]) and their scale buffers."""
+    if b.shape[-1] != a.shape[-1]:
+        raise ValueError(f"a and b must have the same bytes per row, got {a.shape[-1]} and {b.shape[-1]}")
+    _dev(a, "a", BYTES, E * m * (k // 2), dev)
+    _dev(b, "b", BYTES, E * n * (k // 2), dev)
+    _dev(a_sf, "a_sf", BYTES, E * sfsz(m, k), dev)
+    _dev(b_sf, "b_sf", BYTES, E * sfsz(n, k), dev)
+
+
 def nvfp4_gemm(a, b, a_sf, b_sf, alpha, bias=None, out=None, k=None):
     """a: [m, k/2], b: [n, k/2] packed FP4 -> out [m, n] bf16 = alpha*(a@b^T) (+bias)."""
+    _dims(a, "a", 2)
+    _dims(b, "b", 2)
     m, n = a.shape[0], b.shape[0]
-    k = a.shape[1] * 2 if k is None else k
+    if k is not None and k != a.shape[1] * 2:
+        raise ValueError(f"k = {k} does not match a's {a.shape[1]} bytes per row")
+    k = a.shape[1] * 2
+    dev = a.device
     if out is None:
-        out = torch.empty(m, n, dtype=torch.bfloat16, device=a.device)
+        out = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+    _operands(a, b, a_sf, b_sf, 1, m, n, k, dev, sf_size)
+    _dev(alpha, "alpha", torch.float32, 1, dev)
+    _opt(bias, "bias", torch.bfloat16, n, dev)
+    _dev(out, "out", torch.bfloat16, m * n, dev)
     rc = _lib.nvfp4_gemm(_ptr(a), _ptr(b), _ptr(a_sf), _ptr(b_sf), _ptr(alpha), _ptr(bias),
                          _ptr(out), m, n, k, _stream(a.device))
     _check(rc, "nvfp4_gemm")
@@ -196,10 +269,19 @@ def nvfp4_gemm(a, b, a_sf, b_sf, alpha, bias=None, out=None, k=None):
 
 def nvfp4_gemm_grouped_masked(a, b, a_sf, b_sf, alpha, mask, out=None):
     """a: [E, m, k/2], b: [E, n, k/2] -> out [E, m, n] bf16, rows >= mask[e] untouched."""
+    _dims(a, "a", 3)
+    _dims(b, "b", 3)
     E, m, kb = a.shape
     n = b.shape[1]
+    dev = a.device
+    if b.shape[0] != E:
+        raise ValueError(f"b must hold {E} experts, got {b.shape[0]}")
     if out is None:
-        out = torch.empty(E, m, n, dtype=torch.bfloat16, device=a.device)
+        out = torch.empty(E, m, n, dtype=torch.bfloat16, device=dev)
+    _operands(a, b, a_sf, b_sf, E, m, n, kb * 2, dev, sf_size)
+    _dev(alpha, "alpha", torch.float32, E, dev)
+    _dev(mask, "mask", torch.int32, E, dev)
+    _dev(out, "out", torch.bfloat16, E * m * n, dev)
     rc = _lib.nvfp4_gemm_grouped_masked(_ptr(a), _ptr(b), _ptr(a_sf), _ptr(b_sf), _ptr(alpha),
                                         _ptr(mask), _ptr(out), E, m, n, kb * 2, _stream(a.device))
     _check(rc, "nvfp4_gemm_grouped_masked")
@@ -212,14 +294,24 @@ def nvfp4_gemm_grouped_masked_silu_quantize(a, b, a_sf, b_sf, alpha, mask, globa
     [E] static scales of the output -> (fp4 [E, m, h/2], sf [E, sf_size(m, h)])
     of silu(gate) * up of the grouped masked GEMM; rows >= mask[e] of fp4
     untouched."""
+    _dims(a, "a", 3)
+    _dims(b, "b", 3)
     E, m, kb = a.shape
     n2 = b.shape[1]
     h = n2 // 2
     dev = a.device
+    if b.shape[0] != E:
+        raise ValueError(f"b must hold {E} experts, got {b.shape[0]}")
+    _operands(a, b, a_sf, b_sf, E, m, n2, kb * 2, dev, sf_size)
+    _dev(alpha, "alpha", torch.float32, E, dev)
+    _dev(mask, "mask", torch.int32, E, dev)
+    _dev(global_scale, "global_scale", torch.float32, E, dev)
     if out_fp4 is None:
         out_fp4 = torch.empty(E, m, h // 2, dtype=torch.uint8, device=dev)
     if out_sf is None:
         out_sf = torch.empty(E, sf_size(m, h), dtype=torch.uint8, device=dev)
+    _dev(out_fp4, "out_fp4", BYTES, E * m * (h // 2), dev)
+    _dev(out_sf, "out_sf", BYTES, E * sf_size(m, h), dev)
     rc = _lib.nvfp4_gemm_grouped_masked_silu_quantize(
         _ptr(a), _ptr(b), _ptr(a_sf), _ptr(b_sf), _ptr(alpha), _ptr(mask), _ptr(global_scale),
         E, m, n2, kb * 2, _ptr(out_fp4), _ptr(out_sf), _stream(dev))
@@ -229,11 +321,21 @@ def nvfp4_gemm_grouped_masked_silu_quantize(a, b, a_sf, b_sf, alpha, mask, globa
 
 def nvfp4_gemm_svdquant(a, b, a_sf, b_sf, alpha, d, l1, bias=None, out=None):
     """out = alpha*(a@b^T + d@l1^T) (+bias); l1 pre-divided by alpha by the caller."""
+    _dims(a, "a", 2)
+    _dims(b, "b", 2)
+    _dims(d, "d", 2)
     m, n = a.shape[0], b.shape[0]
     k = a.shape[1] * 2
     r = d.shape[1]
+    dev = a.device
     if out is None:
-        out = torch.empty(m, n, dtype=torch.bfloat16, device=a.device)
+        out = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+    _operands(a, b, a_sf, b_sf, 1, m, n, k, dev, sf_size)
+    _dev(alpha, "alpha", torch.float32, 1, dev)
+    _dev(d, "d", torch.bfloat16, m * r, dev)
+    _dev(l1, "l1", torch.bfloat16, n * r, dev)
+    _opt(bias, "bias", torch.bfloat16, n, dev)
+    _dev(out, "out", torch.bfloat16, m * n, dev)
     rc = _lib.nvfp4_gemm_svdquant(_ptr(a), _ptr(b), _ptr(a_sf), _ptr(b_sf), _ptr(alpha), _ptr(d),
                                   _ptr(l1), _ptr(bias), _ptr(out), m, n, k, r, _stream(a.device))
     _check(rc, "nvfp4_gemm_svdquant")
@@ -243,11 +345,21 @@ def nvfp4_gemm_svdquant(a, b, a_sf, b_sf, alpha, d, l1, bias=None, out=None):
 def nvfp4_gemm_w4a16(a, b, b_sf, alpha, bias=None, out=None):
     """a: [m, k] bf16 activation, b: [n, k/2] packed FP4 weight ->
     out [m, n] bf16 = alpha*(a @ dequant(b)^T) (+bias), alpha = 1/weight gs."""
-    _need(a, "a")
+    _dims(a, "a", 2)
+    _dims(b, "b", 2)
     m, k = a.shape
     n = b.shape[0]
+    dev = a.device
+    if b.shape[1] * 2 != k:
+        raise ValueError(f"b must be [n, {k // 2}] packed FP4, got {tuple(b.shape)}")
     if out is None:
-        out = torch.empty(m, n, dtype=torch.bfloat16, device=a.device)
+        out = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+    _dev(a, "a", torch.bfloat16, m * k, dev)
+    _dev(b, "b", BYTES, n * (k // 2), dev)
+    _dev(b_sf, "b_sf", BYTES, sf_size(n, k), dev)
+    _dev(alpha, "alpha", torch.float32, 1, dev)
+    _opt(bias, "bias", torch.bfloat16, n, dev)
+    _dev(out, "out", torch.bfloat16, m * n, dev)
     rc = _lib.nvfp4_gemm_w4a16(_ptr(a), _ptr(b), _ptr(b_sf), _ptr(alpha), _ptr(bias), _ptr(out), m, n, k,
                                _stream(a.device))
     _check(rc, "nvfp4_gemm_w4a16")
@@ -256,8 +368,13 @@ def nvfp4_gemm_w4a16(a, b, b_sf, alpha, bias=None, out=None):
 
 def nvfp4_alpha(gs_a, gs_b, out=None):
     """alpha = 1 / (gs_a * gs_b) elementwise on the device."""
+    _need(gs_a, "gs_a")
+    dev = gs_a.device
     if out is None:
         out = torch.empty_like(gs_a)
+    _dev(gs_a, "gs_a", torch.float32, 1, dev)
+    _dev(gs_b, "gs_b", torch.float32, gs_a.numel(), dev)
+    _dev(out, "out", torch.float32, gs_a.numel(), dev)
     rc = _lib.nvfp4_alpha(_ptr(gs_a), _ptr(gs_b), _ptr(out), gs_a.numel(), _stream(gs_a.device))
     _check(rc, "nvfp4_alpha")
     return out
@@ -272,7 +389,7 @@ def sf_size_mx(rows, k):
 
 def mxfp4_quantize(x, out_fp4=None, out_sf=None):
     """x: [m, k] bf16 or fp32 -> (fp4 [m, k/2] uint8, sf [sf_size_mx(m, k)] uint8)."""
-    _need(x, "x")
+    _dims(x, "x", 2)
     m, k = x.shape
     dt = {torch.bfloat16: 0, torch.float32: 1}.get(x.dtype)
     if dt is None:
@@ -282,6 +399,8 @@ def mxfp4_quantize(x, out_fp4=None, out_sf=None):
         out_fp4 = torch.empty(m, k // 2, dtype=torch.uint8, device=dev)
     if out_sf is None:
         out_sf = torch.empty(sf_size_mx(m, k), dtype=torch.uint8, device=dev)
+    _dev(out_fp4, "out_fp4", BYTES, m * (k // 2), dev)
+    _dev(out_sf, "out_sf", BYTES, sf_size_mx(m, k), dev)
     rc = _lib.mxfp4_quantize(_ptr(x), dt, m, k, _ptr(out_fp4), _ptr(out_sf), _stream(dev))
     _check(rc, "mxfp4_quantize")
     return out_fp4, out_sf
@@ -289,10 +408,17 @@ def mxfp4_quantize(x, out_fp4=None, out_sf=None):
 
 def mxfp4_gemm(a, b, a_sf, b_sf, alpha=None, bias=None, out=None):
     """a: [m, k/2], b: [n, k/2] MXFP4 -> out [m, n] bf16 = alpha*(a@b^T) (+bias)."""
+    _dims(a, "a", 2)
+    _dims(b, "b", 2)
     m, n = a.shape[0], b.shape[0]
     k = a.shape[1] * 2
+    dev = a.device
     if out is None:
-        out = torch.empty(m, n, dtype=torch.bfloat16, device=a.device)
+        out = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+    _operands(a, b, a_sf, b_sf, 1, m, n, k, dev, sf_size_mx)
+    _opt(alpha, "alpha", torch.float32, 1, dev)
+    _opt(bias, "bias", torch.bfloat16, n, dev)
+    _dev(out, "out", torch.bfloat16, m * n, dev)
     rc = _lib.mxfp4_gemm(_ptr(a), _ptr(b), _ptr(a_sf), _ptr(b_sf), _ptr(alpha), _ptr(bias), _ptr(out),
                          m, n, k, _stream(a.device))
     _check(rc, "mxfp4_gemm")

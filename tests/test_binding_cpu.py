@@ -1,0 +1,52 @@
+"""The Python binding refuses host tensors before anything reaches the C ABI:
+every entry point raises ValueError for CPU inputs (the library only takes
+device pointers, and a host pointer handed to a kernel would fault)."""
+import pytest
+import torch
+
+from nvfp4_block_scaled_04_amd import ops
+
+
+def u8(*shape):
+    return torch.zeros(*shape, dtype=torch.uint8)
+
+
+def bf(*shape):
+    return torch.zeros(*shape, dtype=torch.bfloat16)
+
+
+def f32(*shape):
+    return torch.zeros(*shape, dtype=torch.float32)
+
+
+CALLS = {
+    "nvfp4_quantize": lambda: ops.nvfp4_quantize(bf(128, 64)),
+    "nvfp4_quantize_lora_down": lambda: ops.nvfp4_quantize_lora_down(bf(128, 64), bf(64), bf(32, 64)),
+    "nvfp4_quantize_masked_batched": lambda: ops.nvfp4_quantize_masked_batched(bf(2, 128, 64)),
+    "silu_mul_nvfp4_quantize": lambda: ops.silu_mul_nvfp4_quantize(bf(2, 128, 64)),
+    "nvfp4_gemm": lambda: ops.nvfp4_gemm(u8(128, 32), u8(64, 32), u8(ops.sf_size(128, 64)),
+                                         u8(ops.sf_size(64, 64)), f32(1)),
+    "nvfp4_gemm_grouped_masked": lambda: ops.nvfp4_gemm_grouped_masked(
+        u8(2, 128, 32), u8(2, 64, 32), u8(2, ops.sf_size(128, 64)), u8(2, ops.sf_size(64, 64)), f32(2),
+        torch.zeros(2, dtype=torch.int32)),
+    "nvfp4_gemm_grouped_masked_silu_quantize": lambda: ops.nvfp4_gemm_grouped_masked_silu_quantize(
+        u8(2, 128, 32), u8(2, 64, 32), u8(2, ops.sf_size(128, 64)), u8(2, ops.sf_size(64, 64)), f32(2),
+        torch.zeros(2, dtype=torch.int32), f32(2)),
+    "nvfp4_gemm_svdquant": lambda: ops.nvfp4_gemm_svdquant(
+        u8(128, 32), u8(64, 32), u8(ops.sf_size(128, 64)), u8(ops.sf_size(64, 64)), f32(1), bf(128, 32), bf(64, 32)),
+    "nvfp4_gemm_w4a16": lambda: ops.nvfp4_gemm_w4a16(bf(16, 64), u8(64, 32), u8(ops.sf_size(64, 64)), f32(1)),
+    "nvfp4_alpha": lambda: ops.nvfp4_alpha(f32(1), f32(1)),
+    "mxfp4_quantize": lambda: ops.mxfp4_quantize(bf(128, 64)),
+    "mxfp4_gemm": lambda: ops.mxfp4_gemm(u8(128, 32), u8(64, 32), u8(ops.sf_size_mx(128, 64)),
+                                         u8(ops.sf_size_mx(64, 64))),
+}
+
+
+def test_every_entry_point_is_covered():
+    assert sorted(CALLS) == sorted(ops.EXPORTS)
+
+
+@pytest.mark.parametrize("name", sorted(CALLS))
+def test_host_tensors_are_refused(name):
+    with pytest.raises(ValueError, match="device tensor"):
+        CALLS[name]()
