@@ -97,24 +97,29 @@ def _need(t, name):
 
 
 BYTES = "bytes"  # any one-byte dtype (uint8, float4_e2m1fn_x2, float8 scale types)
+F32, BF16, I32 = (torch.float32,), (torch.bfloat16,), (torch.int32,)
 
 
 def _dev(t, name, dtype, numel, device):
-    """t must be a contiguous tensor on `device` of `dtype` (a dtype, a tuple
-    of them, or BYTES) holding at least `numel` elements: the library reads
+    """t must be a contiguous tensor on `device` of a dtype in `dtype` (or of
+    one byte, for BYTES) holding at least `numel` elements: the library reads
     or writes that many through the raw pointer, so anything else raises here,
-    before any launch."""
+    before any launch.  One short-circuit test on the common path (these
+    checks run on every eager call); the slow path only words the error."""
+    try:
+        if (t.is_cuda and t.is_contiguous() and t.numel() >= numel and t.get_device() == device.index
+                and (t.element_size() == 1 if dtype is BYTES else t.dtype in dtype)):
+            return t
+    except AttributeError:
+        pass
     _need(t, name)
-    if dtype is BYTES:
-        if t.element_size() != 1:
-            raise ValueError(f"{name} must have a one-byte dtype, got {t.dtype}")
-    elif t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
-        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if dtype is BYTES and t.element_size() != 1:
+        raise ValueError(f"{name} must have a one-byte dtype, got {t.dtype}")
+    if dtype is not BYTES and t.dtype not in dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtype}")
     if t.device != device:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
-    if t.numel() < numel:
-        raise ValueError(f"{name} holds {t.numel()} elements, the call needs {numel}")
-    return t
+    raise ValueError(f"{name} holds {t.numel()} elements, the call needs {numel}")
 
 
 def _opt(t, name, dtype, numel, device):
@@ -144,8 +149,8 @@ def nvfp4_quantize(x, global_scale=None, gs_mode=GS_DYNAMIC, pre_quant_scale=Non
         out_fp4 = torch.empty(m, k // 2, dtype=torch.uint8, device=dev)
     if out_sf is None:
         out_sf = torch.empty(sf_size(m, k), dtype=torch.uint8, device=dev)
-    _opt(pre_quant_scale, "pre_quant_scale", torch.bfloat16, k, dev)
-    _dev(global_scale, "global_scale", torch.float32, 1, dev)
+    _opt(pre_quant_scale, "pre_quant_scale", BF16, k, dev)
+    _dev(global_scale, "global_scale", F32, 1, dev)
     _dev(out_fp4, "out_fp4", BYTES, m * (k // 2), dev)
     _dev(out_sf, "out_sf", BYTES, sf_size(m, k), dev)
     rc = _lib.nvfp4_quantize(_ptr(x), dt, m, k, _ptr(pre_quant_scale), _ptr(global_scale),
@@ -164,11 +169,11 @@ def nvfp4_quantize_lora_down(x, pre_quant_scale, l2, global_scale=None, gs_mode=
     m, k = x.shape
     r = l2.shape[0]
     dev_ = x.device
-    _dev(x, "x", torch.bfloat16, m * k, dev_)
-    _dev(pre_quant_scale, "pre_quant_scale", torch.bfloat16, k, dev_)
+    _dev(x, "x", BF16, m * k, dev_)
+    _dev(pre_quant_scale, "pre_quant_scale", BF16, k, dev_)
     if l2.shape[1] != k:
         raise ValueError(f"l2 must be [r, {k}], got {tuple(l2.shape)}")
-    _dev(l2, "l2", torch.bfloat16, r * k, dev_)
+    _dev(l2, "l2", BF16, r * k, dev_)
     if global_scale is None:
         global_scale = torch.zeros(1, dtype=torch.float32, device=dev_)
     if out_fp4 is None:
@@ -177,10 +182,10 @@ def nvfp4_quantize_lora_down(x, pre_quant_scale, l2, global_scale=None, gs_mode=
         out_sf = torch.empty(sf_size(m, k), dtype=torch.uint8, device=dev_)
     if d is None:
         d = torch.empty(m, r, dtype=torch.bfloat16, device=dev_)
-    _dev(global_scale, "global_scale", torch.float32, 1, dev_)
+    _dev(global_scale, "global_scale", F32, 1, dev_)
     _dev(out_fp4, "out_fp4", BYTES, m * (k // 2), dev_)
     _dev(out_sf, "out_sf", BYTES, sf_size(m, k), dev_)
-    _dev(d, "d", torch.bfloat16, m * r, dev_)
+    _dev(d, "d", BF16, m * r, dev_)
     rc = _lib.nvfp4_quantize_lora_down(_ptr(x), m, k, _ptr(pre_quant_scale), _ptr(l2), r, _ptr(global_scale),
                                        gs_mode, _ptr(out_fp4), _ptr(out_sf), _ptr(d), _stream(dev_))
     _check(rc, "nvfp4_quantize_lora_down")
@@ -193,15 +198,15 @@ def nvfp4_quantize_masked_batched(x, mask=None, global_scale=None, gs_mode=GS_DY
     _dims(x, "x", 3)
     b, m, k = x.shape
     dev = x.device
-    _dev(x, "x", torch.bfloat16, b * m * k, dev)
+    _dev(x, "x", BF16, b * m * k, dev)
     if global_scale is None:
         global_scale = torch.zeros(b, dtype=torch.float32, device=dev)
     if out_fp4 is None:
         out_fp4 = torch.empty(b, m, k // 2, dtype=torch.uint8, device=dev)
     if out_sf is None:
         out_sf = torch.empty(b, sf_size(m, k), dtype=torch.uint8, device=dev)
-    _opt(mask, "mask", torch.int32, b, dev)
-    _dev(global_scale, "global_scale", torch.float32, b, dev)
+    _opt(mask, "mask", I32, b, dev)
+    _dev(global_scale, "global_scale", F32, b, dev)
     _dev(out_fp4, "out_fp4", BYTES, b * m * (k // 2), dev)
     _dev(out_sf, "out_sf", BYTES, b * sf_size(m, k), dev)
     rc = _lib.nvfp4_quantize_masked_batched(_ptr(x), b, m, k, _ptr(mask), _ptr(global_scale),
@@ -217,15 +222,15 @@ def silu_mul_nvfp4_quantize(x, mask=None, global_scale=None, gs_mode=GS_DYNAMIC,
     b, m, k2 = x.shape
     h = k2 // 2
     dev = x.device
-    _dev(x, "x", torch.bfloat16, b * m * k2, dev)
+    _dev(x, "x", BF16, b * m * k2, dev)
     if global_scale is None:
         global_scale = torch.zeros(b, dtype=torch.float32, device=dev)
     if out_fp4 is None:
         out_fp4 = torch.empty(b, m, h // 2, dtype=torch.uint8, device=dev)
     if out_sf is None:
         out_sf = torch.empty(b, sf_size(m, h), dtype=torch.uint8, device=dev)
-    _opt(mask, "mask", torch.int32, b, dev)
-    _dev(global_scale, "global_scale", torch.float32, b, dev)
+    _opt(mask, "mask", I32, b, dev)
+    _dev(global_scale, "global_scale", F32, b, dev)
     _dev(out_fp4, "out_fp4", BYTES, b * m * (h // 2), dev)
     _dev(out_sf, "out_sf", BYTES, b * sf_size(m, h), dev)
     rc = _lib.silu_mul_nvfp4_quantize(_ptr(x), b, m, k2, _ptr(mask), _ptr(global_scale), gs_mode,
@@ -258,9 +263,9 @@ def nvfp4_gemm(a, b, a_sf, b_sf, alpha, bias=None, out=None, k=None):
     if out is None:
         out = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
     _operands(a, b, a_sf, b_sf, 1, m, n, k, dev, sf_size)
-    _dev(alpha, "alpha", torch.float32, 1, dev)
-    _opt(bias, "bias", torch.bfloat16, n, dev)
-    _dev(out, "out", torch.bfloat16, m * n, dev)
+    _dev(alpha, "alpha", F32, 1, dev)
+    _opt(bias, "bias", BF16, n, dev)
+    _dev(out, "out", BF16, m * n, dev)
     rc = _lib.nvfp4_gemm(_ptr(a), _ptr(b), _ptr(a_sf), _ptr(b_sf), _ptr(alpha), _ptr(bias),
                          _ptr(out), m, n, k, _stream(a.device))
     _check(rc, "nvfp4_gemm")
@@ -279,9 +284,9 @@ def nvfp4_gemm_grouped_masked(a, b, a_sf, b_sf, alpha, mask, out=None):
     if out is None:
         out = torch.empty(E, m, n, dtype=torch.bfloat16, device=dev)
     _operands(a, b, a_sf, b_sf, E, m, n, kb * 2, dev, sf_size)
-    _dev(alpha, "alpha", torch.float32, E, dev)
-    _dev(mask, "mask", torch.int32, E, dev)
-    _dev(out, "out", torch.bfloat16, E * m * n, dev)
+    _dev(alpha, "alpha", F32, E, dev)
+    _dev(mask, "mask", I32, E, dev)
+    _dev(out, "out", BF16, E * m * n, dev)
     rc = _lib.nvfp4_gemm_grouped_masked(_ptr(a), _ptr(b), _ptr(a_sf), _ptr(b_sf), _ptr(alpha),
                                         _ptr(mask), _ptr(out), E, m, n, kb * 2, _stream(a.device))
     _check(rc, "nvfp4_gemm_grouped_masked")
@@ -303,9 +308,9 @@ def nvfp4_gemm_grouped_masked_silu_quantize(a, b, a_sf, b_sf, alpha, mask, globa
     if b.shape[0] != E:
         raise ValueError(f"b must hold {E} experts, got {b.shape[0]}")
     _operands(a, b, a_sf, b_sf, E, m, n2, kb * 2, dev, sf_size)
-    _dev(alpha, "alpha", torch.float32, E, dev)
-    _dev(mask, "mask", torch.int32, E, dev)
-    _dev(global_scale, "global_scale", torch.float32, E, dev)
+    _dev(alpha, "alpha", F32, E, dev)
+    _dev(mask, "mask", I32, E, dev)
+    _dev(global_scale, "global_scale", F32, E, dev)
     if out_fp4 is None:
         out_fp4 = torch.empty(E, m, h // 2, dtype=torch.uint8, device=dev)
     if out_sf is None:
@@ -331,11 +336,11 @@ def nvfp4_gemm_svdquant(a, b, a_sf, b_sf, alpha, d, l1, bias=None, out=None):
     if out is None:
         out = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
     _operands(a, b, a_sf, b_sf, 1, m, n, k, dev, sf_size)
-    _dev(alpha, "alpha", torch.float32, 1, dev)
-    _dev(d, "d", torch.bfloat16, m * r, dev)
-    _dev(l1, "l1", torch.bfloat16, n * r, dev)
-    _opt(bias, "bias", torch.bfloat16, n, dev)
-    _dev(out, "out", torch.bfloat16, m * n, dev)
+    _dev(alpha, "alpha", F32, 1, dev)
+    _dev(d, "d", BF16, m * r, dev)
+    _dev(l1, "l1", BF16, n * r, dev)
+    _opt(bias, "bias", BF16, n, dev)
+    _dev(out, "out", BF16, m * n, dev)
     rc = _lib.nvfp4_gemm_svdquant(_ptr(a), _ptr(b), _ptr(a_sf), _ptr(b_sf), _ptr(alpha), _ptr(d),
                                   _ptr(l1), _ptr(bias), _ptr(out), m, n, k, r, _stream(a.device))
     _check(rc, "nvfp4_gemm_svdquant")
@@ -354,12 +359,12 @@ def nvfp4_gemm_w4a16(a, b, b_sf, alpha, bias=None, out=None):
         raise ValueError(f"b must be [n, {k // 2}] packed FP4, got {tuple(b.shape)}")
     if out is None:
         out = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
-    _dev(a, "a", torch.bfloat16, m * k, dev)
+    _dev(a, "a", BF16, m * k, dev)
     _dev(b, "b", BYTES, n * (k // 2), dev)
     _dev(b_sf, "b_sf", BYTES, sf_size(n, k), dev)
-    _dev(alpha, "alpha", torch.float32, 1, dev)
-    _opt(bias, "bias", torch.bfloat16, n, dev)
-    _dev(out, "out", torch.bfloat16, m * n, dev)
+    _dev(alpha, "alpha", F32, 1, dev)
+    _opt(bias, "bias", BF16, n, dev)
+    _dev(out, "out", BF16, m * n, dev)
     rc = _lib.nvfp4_gemm_w4a16(_ptr(a), _ptr(b), _ptr(b_sf), _ptr(alpha), _ptr(bias), _ptr(out), m, n, k,
                                _stream(a.device))
     _check(rc, "nvfp4_gemm_w4a16")
@@ -372,9 +377,9 @@ def nvfp4_alpha(gs_a, gs_b, out=None):
     dev = gs_a.device
     if out is None:
         out = torch.empty_like(gs_a)
-    _dev(gs_a, "gs_a", torch.float32, 1, dev)
-    _dev(gs_b, "gs_b", torch.float32, gs_a.numel(), dev)
-    _dev(out, "out", torch.float32, gs_a.numel(), dev)
+    _dev(gs_a, "gs_a", F32, 1, dev)
+    _dev(gs_b, "gs_b", F32, gs_a.numel(), dev)
+    _dev(out, "out", F32, gs_a.numel(), dev)
     rc = _lib.nvfp4_alpha(_ptr(gs_a), _ptr(gs_b), _ptr(out), gs_a.numel(), _stream(gs_a.device))
     _check(rc, "nvfp4_alpha")
     return out
@@ -416,9 +421,9 @@ def mxfp4_gemm(a, b, a_sf, b_sf, alpha=None, bias=None, out=None):
     if out is None:
         out = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
     _operands(a, b, a_sf, b_sf, 1, m, n, k, dev, sf_size_mx)
-    _opt(alpha, "alpha", torch.float32, 1, dev)
-    _opt(bias, "bias", torch.bfloat16, n, dev)
-    _dev(out, "out", torch.bfloat16, m * n, dev)
+    _opt(alpha, "alpha", F32, 1, dev)
+    _opt(bias, "bias", BF16, n, dev)
+    _dev(out, "out", BF16, m * n, dev)
     rc = _lib.mxfp4_gemm(_ptr(a), _ptr(b), _ptr(a_sf), _ptr(b_sf), _ptr(alpha), _ptr(bias), _ptr(out),
                          m, n, k, _stream(a.device))
     _check(rc, "mxfp4_gemm")
