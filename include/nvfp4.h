@@ -100,6 +100,24 @@ int nvfp4_quantize(const void *x, int x_dtype, int64_t m, int64_t k,
                    uint8_t *out_fp4, uint8_t *out_sf, void *stream);
 
 /*
+ * nvfp4_quantize, plus the GEMM's alpha written by the same launch: once
+ * this call's global scale is final, alpha[0] = 1 / (global_scale[0] *
+ * gs_other[0]) in fp32, the value nvfp4_alpha(global_scale, gs_other)
+ * writes (TensorRT-LLM create_weights, the alpha parameter: the product of
+ * the two operands' dequantization scales).  For a dynamically quantized
+ * activation, this saves the separate alpha launch before the GEMM.
+ *   gs_other: [1] fp32 device pointer, read (the weight's global scale).
+ *   alpha:    [1] fp32 device pointer, written.
+ * Everything else, the bytes written and the errors are as nvfp4_quantize;
+ * NVFP4_NULL_POINTER also for a NULL gs_other or alpha, NVFP4_MISALIGNED
+ * when either is not 4-byte aligned.
+ */
+int nvfp4_quantize_alpha(const void *x, int x_dtype, int64_t m, int64_t k,
+                         const void *pre_quant_scale, float *global_scale, int gs_mode,
+                         const float *gs_other, float *alpha,
+                         uint8_t *out_fp4, uint8_t *out_sf, void *stream);
+
+/*
  * Smooth quantization with the SVDQuant LoRA-down projection fused
  * (flashinfer docs, flashinfer.gemm.mm_nvfp4_svdquant: parameter a is x with
  * pre_quant_scale folded into its quantization, and d = x @ (pqs[:, None] *

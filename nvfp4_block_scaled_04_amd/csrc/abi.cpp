@@ -31,21 +31,38 @@ bool quant_sizes_ok(int64_t b, int64_t m, int64_t K) {
 
 extern "C" {
 
-int nvfp4_quantize(const void* x, int x_dtype, int64_t m, int64_t k, const void* pre_quant_scale,
-                   float* global_scale, int gs_mode, uint8_t* out_fp4, uint8_t* out_sf,
-                   void* stream) {
+static int quantize_common(const void* x, int x_dtype, int64_t m, int64_t k, const void* pre_quant_scale,
+                           float* global_scale, int gs_mode, const float* gs_other, float* alpha,
+                           uint8_t* out_fp4, uint8_t* out_sf, void* stream) {
     if (!x || !global_scale || !out_fp4 || !out_sf) return NVFP4_NULL_POINTER;
     if (x_dtype != NVFP4_BF16 && x_dtype != NVFP4_F32) return NVFP4_BAD_DTYPE;
     if (gs_mode != NVFP4_GS_STATIC && gs_mode != NVFP4_GS_DYNAMIC) return NVFP4_UNSUPPORTED;
     if (k < 16 || k % 16 != 0 || !quant_sizes_ok(1, m, k)) return NVFP4_BAD_SHAPE;
     if (!aligned16(x) || !aligned16(out_fp4) || !aligned16(out_sf) ||
-        (pre_quant_scale && !aligned16(pre_quant_scale)) || ((uintptr_t)global_scale & 3u))
+        (pre_quant_scale && !aligned16(pre_quant_scale)) || ((uintptr_t)global_scale & 3u) ||
+        ((uintptr_t)gs_other & 3u) || ((uintptr_t)alpha & 3u))
         return NVFP4_MISALIGNED;
     nvfp4::QuantizeArgs a{};
     a.x = x; a.x_dtype = x_dtype; a.pqs = pre_quant_scale; a.mask = nullptr;
     a.gs = global_scale; a.out_fp4 = out_fp4; a.out_sf = out_sf;
     a.b = 1; a.m = m; a.k_in = k; a.silu = false; a.dynamic = gs_mode == NVFP4_GS_DYNAMIC;
+    a.gs_other = gs_other; a.alpha_out = alpha;
     return launch_status(nvfp4::launch_quantize(a, (hipStream_t)stream));
+}
+
+int nvfp4_quantize(const void* x, int x_dtype, int64_t m, int64_t k, const void* pre_quant_scale,
+                   float* global_scale, int gs_mode, uint8_t* out_fp4, uint8_t* out_sf,
+                   void* stream) {
+    return quantize_common(x, x_dtype, m, k, pre_quant_scale, global_scale, gs_mode, nullptr, nullptr,
+                           out_fp4, out_sf, stream);
+}
+
+int nvfp4_quantize_alpha(const void* x, int x_dtype, int64_t m, int64_t k, const void* pre_quant_scale,
+                         float* global_scale, int gs_mode, const float* gs_other, float* alpha,
+                         uint8_t* out_fp4, uint8_t* out_sf, void* stream) {
+    if (!gs_other || !alpha) return NVFP4_NULL_POINTER;
+    return quantize_common(x, x_dtype, m, k, pre_quant_scale, global_scale, gs_mode, gs_other, alpha,
+                           out_fp4, out_sf, stream);
 }
 
 int nvfp4_quantize_lora_down(const void* x, int64_t m, int64_t k, const void* pre_quant_scale,

@@ -18,6 +18,8 @@ struct QuantizeArgs {
     int64_t b, m, k_in;   // k_in: input row width (2*K for silu)
     bool silu;
     bool dynamic;
+    const float* gs_other = nullptr;  // with alpha_out: [b] the other operand's global scales
+    float* alpha_out = nullptr;       // [b] alpha = 1 / (gs * gs_other), or null
 };
 
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t st);

@@ -49,7 +49,14 @@ struct QParams {
     int nct;               // 64-column tiles = ceil(K/64) = Cp/4
     int nrt;               // row tiles = ceil(m/128)
     int amax_blocks;       // amax workgroups per item (partials per item)
+    const float* gs_other; // [b] the GEMM partner's global scales, when alpha_out is set
+    float* alpha_out;      // [b] or null: alpha = 1 / (gs * gs_other)
 };
+
+// alpha of item e from its final global scale, with the arithmetic of k_alpha
+__device__ __forceinline__ void write_alpha(const QParams& p, int e, float gs) {
+    if (p.alpha_out) p.alpha_out[e] = 1.0f / (gs * p.gs_other[e]);
+}
 
 template <int V>
 __device__ __forceinline__ void load_block(const QParams& p, int64_t e, int64_t row, int64_t col,
@@ -234,6 +241,8 @@ __device__ __forceinline__ void quantize_tile(const QParams& p, int wct, int rt,
 template <int V, int CT>
 __global__ __launch_bounds__(256) void k_quantize(QParams p) {
     const int e = blockIdx.z;
+    // gs[e] is final here (given, or written by the finish kernel before this pass)
+    if (p.alpha_out && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) write_alpha(p, e, p.gs[e]);
     quantize_tile<V, CT>(p, blockIdx.x, blockIdx.y, e, [&] { return p.gs[e]; });
 }
 
@@ -281,7 +290,10 @@ __global__ __launch_bounds__(256) void k_quantize_fused(QParams p) {
     const bool first = wct == 0 && rt == 0;
     __shared__ float wmax[4];
     // no valid rows: every tile only zeroes its scales, and gs comes from amax 0
-    if (valid == 0 && first && t == 0) p.gs[e] = gs_from_amax(0.0f);
+    if (valid == 0 && first && t == 0) {
+        p.gs[e] = gs_from_amax(0.0f);
+        write_alpha(p, e, p.gs[e]);
+    }
     // The amax pass runs where the tile asks for gs, after its own loads are
     // issued, so they land meanwhile (tiles past the valid rows never ask).
     quantize_tile<V, CT>(p, wct, rt, e, [&] {
@@ -292,7 +304,10 @@ __global__ __launch_bounds__(256) void k_quantize_fused(QParams p) {
         __syncthreads();
         const float gs = gs_from_amax(__builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]),
                                                       __builtin_fmaxf(wmax[2], wmax[3])));
-        if (first && t == 0) p.gs[e] = gs;
+        if (first && t == 0) {
+            p.gs[e] = gs;
+            write_alpha(p, e, gs);
+        }
         return gs;
     });
 }
@@ -575,6 +590,8 @@ hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t st) {
     p.nrt = (int)((p.m + 127) / 128);
     p.sfsz = (int64_t)p.nrt * 128 * p.nct * 4;
     p.b = (int)a.b;
+    p.gs_other = a.gs_other;
+    p.alpha_out = a.alpha_out;
     const bool dyn = a.dynamic;
     if (a.silu) return launch_variant<V_SILU>(p, dyn, st);
     if (a.x_dtype == 0) {

@@ -36,7 +36,7 @@ def test_header_declares_the_entry_points():
         "nvfp4_alpha", "nvfp4_gemm", "nvfp4_gemm_grouped_masked",
         "nvfp4_gemm_grouped_masked_silu_quantize", "nvfp4_gemm_svdquant",
         "nvfp4_gemm_w4a16", "nvfp4_quantize_lora_down",
-        "nvfp4_quantize", "nvfp4_quantize_masked_batched", "silu_mul_nvfp4_quantize",
+        "nvfp4_quantize", "nvfp4_quantize_alpha", "nvfp4_quantize_masked_batched", "silu_mul_nvfp4_quantize",
         "mxfp4_quantize", "mxfp4_gemm",
     ])
 
@@ -154,6 +154,24 @@ def test_grouped_validation(lib):
     assert f(*args(E=0)) == SHAPE
     assert f(*args(k=17)) == SHAPE
     assert f(*args(mask=P + 2)) == MISAL
+
+
+def test_quantize_alpha_validation(lib):
+    """nvfp4_quantize's checks, plus the two alpha pointers."""
+    f = lib.nvfp4_quantize_alpha
+    f.restype = ctypes.c_int
+
+    def run(x=P, dtype=0, k=64, gs_other=P, alpha=P):
+        return f(ctypes.c_void_p(x), ctypes.c_int(dtype), ctypes.c_int64(32), ctypes.c_int64(k), ctypes.c_void_p(None),
+                 ctypes.c_void_p(P), ctypes.c_int(1), ctypes.c_void_p(gs_other), ctypes.c_void_p(alpha),
+                 ctypes.c_void_p(P), ctypes.c_void_p(P), ctypes.c_void_p(None))
+    assert run(gs_other=None) == NULLP
+    assert run(alpha=None) == NULLP
+    assert run(x=None) == NULLP
+    assert run(dtype=3) == DTYPE
+    assert run(k=40) == SHAPE
+    assert run(gs_other=P + 2) == MISAL
+    assert run(alpha=P + 1) == MISAL
 
 
 def test_svdquant_rank_and_alignment(lib):

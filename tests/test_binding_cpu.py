@@ -21,6 +21,7 @@ def f32(*shape):
 
 CALLS = {
     "nvfp4_quantize": lambda: ops.nvfp4_quantize(bf(128, 64)),
+    "nvfp4_quantize_alpha": lambda: ops.nvfp4_quantize_alpha(bf(128, 64), f32(1)),
     "nvfp4_quantize_lora_down": lambda: ops.nvfp4_quantize_lora_down(bf(128, 64), bf(64), bf(32, 64)),
     "nvfp4_quantize_masked_batched": lambda: ops.nvfp4_quantize_masked_batched(bf(2, 128, 64)),
     "silu_mul_nvfp4_quantize": lambda: ops.silu_mul_nvfp4_quantize(bf(2, 128, 64)),

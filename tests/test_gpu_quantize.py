@@ -279,3 +279,31 @@ def test_svdquant_workload_full(ops):
 def test_moe_workload_full(ops):
     mo = synth.moe(h=8192, n=64)   # the down-proj weights are exercised in the GEMM tests
     run_batched(ops, mo.x, mo.mask, ops.GS_DYNAMIC, silu=True)
+
+
+@pytest.mark.parametrize("m,k,dtype,dynamic,smooth", [
+    (16, 4096, torch.bfloat16, True, False),     # one-launch dynamic path
+    (37, 96, torch.float32, True, True),         # one-launch, fp32 input, smooth prologue
+    (1024, 4096, torch.bfloat16, True, False),   # amax, finish, quantize pass
+    (300, 512, torch.bfloat16, False, True),     # static gs
+])
+def test_quantize_alpha(ops, m, k, dtype, dynamic, smooth):
+    """nvfp4_quantize_alpha writes the bytes nvfp4_quantize writes, and alpha =
+    1 / (gs * gs_other) bit for bit as nvfp4_alpha and fp32 arithmetic give it."""
+    say("quantize_alpha", (m, k), dtype, "dynamic" if dynamic else "static", "smooth" if smooth else "")
+    g = torch.Generator().manual_seed(m + k)
+    x = (torch.randn(m, k, generator=g) * 3).to(dtype).cuda()
+    pqs = torch.exp(0.3 * torch.randn(k, generator=g)).to(torch.bfloat16).cuda() if smooth else None
+    mode = ops.GS_DYNAMIC if dynamic else ops.GS_STATIC
+    gs0 = torch.full((1,), 2688.0 / 11.0, dtype=torch.float32, device="cuda")
+    gs_w = torch.full((1,), 2688.0 / 0.137, dtype=torch.float32, device="cuda")
+    q1, sf1, gs1 = ops.nvfp4_quantize(x, gs0.clone(), mode, pre_quant_scale=pqs)
+    q2, sf2, gs2, alpha = ops.nvfp4_quantize_alpha(x, gs_w, gs0.clone(), mode, pre_quant_scale=pqs)
+    want = ops.nvfp4_alpha(gs2, gs_w)
+    torch.cuda.synchronize()
+    assert torch.equal(q1, q2) and torch.equal(sf1, sf2)
+    assert np_bits(gs1).view(np.uint32)[0] == np_bits(gs2).view(np.uint32)[0]
+    a = np_bits(alpha).view(np.uint32)[0]
+    assert a == np_bits(want).view(np.uint32)[0]
+    host = np.float32(1.0) / (np_bits(gs2)[0] * np_bits(gs_w)[0])
+    assert a == np.array([host], dtype=np.float32).view(np.uint32)[0]
