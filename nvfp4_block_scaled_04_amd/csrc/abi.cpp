@@ -27,6 +27,14 @@ bool quant_sizes_ok(int64_t b, int64_t m, int64_t K) {
     return true;
 }
 
+// Bytes of a swizzled scale buffer for `rows` rows of `nblk` blocks:
+// pad_up(rows,128) * pad_up(nblk,4).  The GEMM kernels address a scale
+// buffer through a 32-bit buffer descriptor with 32-bit signed per-step
+// offsets, so each one must stay below 2^31 bytes.
+bool gemm_sf_ok(int64_t rows, int64_t nblk) {
+    return ((rows + 127) / 128 * 128) * ((nblk + 3) / 4 * 4) < ((int64_t)1 << 31);
+}
+
 }  // namespace
 
 extern "C" {
@@ -127,6 +135,7 @@ static int gemm_common(const uint8_t* a, const uint8_t* b, const uint8_t* a_sf, 
     if (E > 65535 || ((m + 63) / 64) * ((n + 63) / 64) > ((int64_t)1 << 31) - 1) return NVFP4_BAD_SHAPE;
     // the GEMM kernels address one FP4 matrix with 32-bit byte offsets
     if (m * (k / 2) > ((int64_t)1 << 32) - 64 || n * (k / 2) > ((int64_t)1 << 32) - 64) return NVFP4_UNSUPPORTED;
+    if (!gemm_sf_ok(m, k / 16) || !gemm_sf_ok(n, k / 16)) return NVFP4_UNSUPPORTED;
     if (!aligned16(a) || !aligned16(b) || !aligned16(a_sf) || !aligned16(b_sf) || !aligned16(out) ||
         ((uintptr_t)alpha & 3u) || (bias && !aligned16(bias)) || (d && !aligned16(d)) ||
         (l1 && !aligned16(l1)) || ((uintptr_t)mask & 3u))
@@ -163,6 +172,7 @@ int nvfp4_gemm_grouped_masked_silu_quantize(const uint8_t* a, const uint8_t* b, 
     if (n2 % 2 != 0 || n2 / 2 < 16 || (n2 / 2) % 16 != 0 || !quant_sizes_ok(E, m, n2 / 2)) return NVFP4_BAD_SHAPE;
     if (E > 65535 || ((m + 127) / 128) * ((n2 / 2 + 63) / 64) > ((int64_t)1 << 31) - 1) return NVFP4_BAD_SHAPE;
     if (m * (k / 2) > ((int64_t)1 << 32) - 64 || n2 * (k / 2) > ((int64_t)1 << 32) - 64) return NVFP4_UNSUPPORTED;
+    if (!gemm_sf_ok(m, k / 16) || !gemm_sf_ok(n2, k / 16)) return NVFP4_UNSUPPORTED;
     if (!aligned16(a) || !aligned16(b) || !aligned16(a_sf) || !aligned16(b_sf) || !aligned16(out_fp4) ||
         !aligned16(out_sf) || ((uintptr_t)alpha & 3u) || ((uintptr_t)mask & 3u) || ((uintptr_t)global_scale & 3u))
         return NVFP4_MISALIGNED;
@@ -212,6 +222,7 @@ int mxfp4_gemm(const uint8_t* a, const uint8_t* b, const uint8_t* a_sf, const ui
     if (!dim_ok(m) || !dim_ok(n) || k < 32 || k % 32 != 0 || k > kMaxDim) return NVFP4_BAD_SHAPE;
     if (((m + 127) / 128) * ((n + 127) / 128) > ((int64_t)1 << 31) - 1) return NVFP4_BAD_SHAPE;
     if (m * (k / 2) > ((int64_t)1 << 32) - 64 || n * (k / 2) > ((int64_t)1 << 32) - 64) return NVFP4_UNSUPPORTED;
+    if (!gemm_sf_ok(m, k / 32) || !gemm_sf_ok(n, k / 32)) return NVFP4_UNSUPPORTED;
     if (!aligned16(a) || !aligned16(b) || !aligned16(a_sf) || !aligned16(b_sf) || !aligned16(out) ||
         ((uintptr_t)alpha & 3u) || (bias && !aligned16(bias)))
         return NVFP4_MISALIGNED;

@@ -5,6 +5,7 @@ import numpy as np
 import torch
 
 CANARY = 0xA5
+OUT_CANARY = 0x7FA5  # a bf16 NaN pattern the GEMM kernels never write
 
 
 def say(*a):
@@ -44,3 +45,25 @@ def row_tolerance_check(gpu, ref, tol=1e-2):
     scale = np.where(scale == 0, 1.0, scale)
     ratio = err / scale
     return float(ratio.max())
+
+
+def assert_all_written(out_bits):
+    """No element of an (all valid) GEMM output may still hold OUT_CANARY;
+    out_bits is the output viewed as int16, checked on its device."""
+    left = int((out_bits == OUT_CANARY).sum().item())
+    if left:
+        idx = torch.nonzero(out_bits == OUT_CANARY)[:4].tolist()
+        raise AssertionError(f"{left} outputs never written, first at {idx}")
+
+
+def tile_rows(m, bm, per_tile, seed):
+    """Rows stratified over the M-tiles of height bm: per tile its first and
+    last row and per_tile - 2 others drawn from a seeded generator."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for t0 in range(0, m, bm):
+        t1 = min(m, t0 + bm)
+        inner = np.arange(t0 + 1, t1 - 1)
+        k = min(len(inner), per_tile - 2)
+        rows += [t0, t1 - 1] + (rng.choice(inner, k, replace=False).tolist() if k > 0 else [])
+    return np.array(sorted(set(rows)))

@@ -143,6 +143,9 @@ def test_gemm_validation(lib):
     # 32-bit offsets inside one FP4 matrix: 2^32 - 64 bytes is the limit
     assert g(lib, m=(1 << 20), k=8192) == UNSUP      # 4 GiB of A
     assert g(lib, n=(1 << 20) + 1, k=8192) == UNSUP
+    # scale buffers (32-bit descriptors, signed per-step offsets): below 2^31 bytes
+    assert g(lib, m=7, n=7, k=1 << 30) == UNSUP       # 128 rows x 2^26 blocks = 2^33 bytes
+    assert g(lib, m=7, n=7, k=1 << 28) == UNSUP       # 128 x 2^24 = 2^31 bytes: the first size refused
 
 
 def test_grouped_validation(lib):
@@ -287,3 +290,8 @@ def test_mx_validation(lib):
     assert rung(alpha=P + 2) == MISAL
     assert rung(bias=P + 2) == MISAL
     assert rung(m=1 << 20, k=1 << 13) == UNSUP
+    # a 2^30-wide K with 7 rows: 128 x 2^25 scale bytes = 2^32, past the
+    # 32-bit descriptor the kernel would address them with
+    assert rung(m=7, n=7, k=1 << 30) == UNSUP
+    assert rung(m=7, n=7, k=1 << 29) == UNSUP        # 128 x 2^24 = 2^31 bytes: the first size refused
+

@@ -2,10 +2,17 @@
 
 Bar: for every compared row, max |gpu - oracle| <= 1e-2 * max |oracle row|
 (bf16 output against the fp64-accumulated oracle).  Both sides consume the
-same NVFP4 bytes, produced by the oracle.  Full workload sizes compare a
-seeded sample of rows (the oracle computes rows one by one); smaller shapes
-compare every row.  Output buffers start filled with a canary so rows that
-must not be written (masked experts) are checked too.
+same NVFP4 bytes, produced by the oracle.
+
+Every output buffer starts filled with a bf16 NaN pattern the kernels never
+write (0x7FA5).  After each call the whole buffer is checked on the device:
+no element of a valid row may still hold it (so a tile that the launch never
+wrote fails, wherever it is), and rows that must not be written (masked
+experts) must hold nothing else.  Rows compared with the oracle: every row
+up to the dense workload's 2048; for the prefill and SVDQuant workloads 512
+rows stratified over the M-tiles of the launch (16 per 256-row tile, 16 per
+128-row tile), each tile's first and last row included; every valid row of
+every expert for the routed-expert workload.
 """
 import numpy as np
 import pytest
@@ -13,11 +20,10 @@ import torch
 
 import oracle as O
 from nvfp4_block_scaled_04_amd import synth
-from gpu_util import dev, np_bits, row_tolerance_check, say
+from gpu_util import OUT_CANARY, assert_all_written, dev, np_bits, row_tolerance_check, say, tile_rows
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-2
-OUT_CANARY = 0x7FA5  # a bf16 NaN pattern the kernels never produce
 
 
 @pytest.fixture(scope="module")
@@ -52,11 +58,13 @@ def gemm_case(ops, a_cpu, w_cpu, bias=None, rows=None, label=""):
     qa, sa, ga = oq(a_cpu)
     qb, sb, gb = oq(w_cpu)
     alpha = np.float32(1.0) / (ga[0] * gb[0])
-    out = torch.full((m, n), 0, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    out_bits = torch.full((m, n), OUT_CANARY, dtype=torch.int16, device="cuda")
+    out = out_bits.view(torch.bfloat16)
     ops.nvfp4_gemm(t_u8(qa), t_u8(qb), t_u8(sa), t_u8(sb),
                    torch.tensor([alpha], dtype=torch.float32, device="cuda"),
                    bias=None if bias is None else dev(bias), out=out, k=k)
     torch.cuda.synchronize()
+    assert_all_written(out_bits)
     if rows is None:
         rows = np.arange(m)
     ref = O.gemm_rows(qa, qb, sa, sb, alpha, m, n, k, rows=rows,
@@ -112,23 +120,29 @@ def test_tiny_workload(ops):
     gemm_case(ops, t.a, t.w, label="tiny fp32 workload")
 
 
-def test_large_tile_path_full_rows(ops):
-    # big enough for the largest tile configuration, every row compared
+def test_256x256_tile_order_every_row(ops):
+    """4096 x 8192 gives 16 x 32 = 512 tiles of 256 x 256, the launch the
+    prefill shape takes: the XCD remap hands each XCD 64 consecutive tiles and
+    the order walks bands of 8 tile rows.  Every row is compared."""
     g = torch.Generator().manual_seed(9)
     a = torch.randn(4096, 1024, generator=g).to(torch.bfloat16)
-    w = (torch.randn(4096, 1024, generator=g) * 0.02).to(torch.bfloat16)
-    gemm_case(ops, a, w, rows=sample_rows(4096, 256, 1), label="large tiles")
+    w = (torch.randn(8192, 1024, generator=g) * 0.02).to(torch.bfloat16)
+    gemm_case(ops, a, w, label="256x256 tiles, 512 of them, every row")
 
 
 def test_dense_workload(ops):
     d, a16 = synth.dense()
-    gemm_case(ops, d.a, d.w, rows=sample_rows(d.m, 48, 2), label="dense 2048x4096x4096")
+    gemm_case(ops, d.a, d.w, label="dense 2048x4096x4096, every row")
     gemm_case(ops, a16, d.w, label="decode 16x4096x4096")
 
 
 def test_prefill_workload(ops):
+    """8192 x 16384 x 5120 (32 x 64 tiles of 256 x 256): 16 rows of each of
+    the 32 M-tiles, every column, and the canary check over all outputs."""
     p = synth.prefill()
-    gemm_case(ops, p.a, p.w, rows=sample_rows(p.m, 24, 3), label="prefill 8192x16384x5120")
+    rows = tile_rows(p.m, 256, 16, 3)
+    assert len(rows) == 512
+    gemm_case(ops, p.a, p.w, rows=rows, label="prefill 8192x16384x5120, 512 rows over 32 M-tiles")
 
 
 def test_svdquant_workload(ops):
@@ -139,12 +153,15 @@ def test_svdquant_workload(ops):
     alpha = np.float32(1.0) / (ga[0] * gb[0])
     d = synth.lora_down(s)
     l1 = synth.lora_up(s, alpha)
-    out = torch.empty(s.m, s.n, dtype=torch.bfloat16, device="cuda")
+    out_bits = torch.full((s.m, s.n), OUT_CANARY, dtype=torch.int16, device="cuda")
+    out = out_bits.view(torch.bfloat16)
     ops.nvfp4_gemm_svdquant(t_u8(qa), t_u8(qb), t_u8(sa), t_u8(sb),
                             torch.tensor([alpha], dtype=torch.float32, device="cuda"),
                             dev(d), dev(l1), bias=dev(s.bias), out=out)
     torch.cuda.synchronize()
-    rows = sample_rows(s.m, 48, 4)
+    assert_all_written(out_bits)
+    rows = tile_rows(s.m, 128, 16, 4)   # 32 M-tiles of the 128 x 128 launch
+    assert len(rows) == 512
     ref = O.gemm_rows(qa, qb, sa, sb, alpha, s.m, s.n, s.k, rows=rows, bias=np_bits(s.bias),
                       d=np_bits(d), l1=np_bits(l1))
     ratio = row_tolerance_check(out.float().cpu().numpy()[rows], ref)
@@ -213,6 +230,7 @@ def grouped_case(ops, E, m, n, h, mask, rows_per_expert=None, seed=0):
     for e in range(E):
         v = int(min(max(mk[e], 0), m))
         assert bool((got_all[e, v:] == OUT_CANARY).all()), f"expert {e}: rows >= {v} were written"
+        assert not bool((got_all[e, :v] == OUT_CANARY).any()), f"expert {e}: valid rows left unwritten"
         if v == 0:
             continue
         rows = np.arange(v) if rows_per_expert is None else sample_rows(v, rows_per_expert, e)
@@ -302,7 +320,8 @@ def test_moe_workload(ops):
         assert bool((got_all[e, v:] == OUT_CANARY).all()), f"expert {e}: rows >= {v} were written"
         if v == 0:
             continue
-        rows = sample_rows(v, 6, e)
+        assert not bool((got_all[e, :v] == OUT_CANARY).any()), f"expert {e}: valid rows left unwritten"
+        rows = np.arange(v)   # every valid row
         ref = O.gemm_rows(qa[e], qb[e], sa[e], sb[e], alpha[e], mo.m, mo.n, mo.h, rows=rows)
         got = got_all[e].view(torch.bfloat16).float().numpy()[rows]
         assert row_tolerance_check(got, ref) <= TOL, e

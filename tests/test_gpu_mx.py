@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import oracle as O
-from gpu_util import np_bits, row_tolerance_check, say
+from gpu_util import OUT_CANARY, assert_all_written, np_bits, row_tolerance_check, say, tile_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -89,10 +89,12 @@ def gemm_case(ops, m, n, k, bias=False, rows=None, seed=0, alpha=0.5):
     b16 = (torch.randn(n, generator=g) * 0.1).to(torch.bfloat16) if bias else None
     qa, sa = O.quantize_mx(np_bits(a))
     qb, sb = O.quantize_mx(np_bits(w))
-    out = torch.full((m, n), 0x7FA5, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    out_bits = torch.full((m, n), OUT_CANARY, dtype=torch.int16, device="cuda")
+    out = out_bits.view(torch.bfloat16)
     al = torch.tensor([alpha], dtype=torch.float32, device="cuda") if alpha is not None else None
     ops.mxfp4_gemm(t(qa), t(qb), t(sa), t(sb), alpha=al, bias=None if b16 is None else b16.to("cuda"), out=out)
     torch.cuda.synchronize()
+    assert_all_written(out_bits)
     if rows is None:
         rows = np.arange(m)
     ref = O.gemm_mx_rows(qa, qb, sa, sb, 1.0 if alpha is None else alpha, m, n, k, rows=rows,
@@ -121,16 +123,19 @@ def test_gemm_large_tile(ops):
 
 
 def test_gemm_prefill_shape(ops):
-    """The prefill linear 8192 x 16384 x 5120 (the bench's launch), sampled
-    rows against the oracle; operands quantized by the oracle."""
+    """The prefill linear 8192 x 16384 x 5120 (the bench's launch): every
+    output written (canary), 512 rows stratified over the 32 M-tiles of 256
+    against the oracle; operands quantized by the oracle."""
     from nvfp4_block_scaled_04_amd import synth
     d = synth.prefill()
     say("mx gemm prefill", (d.m, d.n, d.k))
     qa, sa = O.quantize_mx(np_bits(d.a))
     qb, sb = O.quantize_mx(np_bits(d.w))
-    out = ops.mxfp4_gemm(t(qa), t(qb), t(sa), t(sb))
+    out_bits = torch.full((d.m, d.n), OUT_CANARY, dtype=torch.int16, device="cuda")
+    out = ops.mxfp4_gemm(t(qa), t(qb), t(sa), t(sb), out=out_bits.view(torch.bfloat16))
     torch.cuda.synchronize()
-    rows = np.array([0, 1, 4095, 8191])
+    assert_all_written(out_bits)
+    rows = tile_rows(d.m, 256, 16, 6)
     ref = O.gemm_mx_rows(qa, qb, sa, sb, 1.0, d.m, d.n, d.k, rows=rows)
     ratio = row_tolerance_check(out.float().cpu().numpy()[rows], ref)
     print(f"  worst row error / row max = {ratio:.3e}")
