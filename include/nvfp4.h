@@ -38,9 +38,9 @@
  *     synchronisation, as for any HIP call.
  *   - Calls that overlap on the same buffers race like any kernels.
  *   - In DYNAMIC mode the call uses the first bytes of each item's out_sf
- *     region as scratch for partial maxima before it writes the scales; out_sf
- *     and global_scale hold their final values when the call's work
- *     completes.
+ *     region as scratch for partial maxima before it writes the scales
+ *     (nvfp4_quantize_ws takes a workspace for them instead); out_sf and
+ *     global_scale hold their final values when the call's work completes.
  */
 #ifndef NVFP4_AMD_H
 #define NVFP4_AMD_H
@@ -116,6 +116,35 @@ int nvfp4_quantize_alpha(const void *x, int x_dtype, int64_t m, int64_t k,
                          const void *pre_quant_scale, float *global_scale, int gs_mode,
                          const float *gs_other, float *alpha,
                          uint8_t *out_fp4, uint8_t *out_sf, void *stream);
+
+/*
+ * nvfp4_quantize / nvfp4_quantize_alpha with a caller workspace for the
+ * DYNAMIC mode's partial maxima (FastVideo PR #1350 review thread,
+ * _global_sf: the per-call global-amax step whose cost this reduces).
+ * Without a workspace a dynamic call is three launches: the amax pass, a
+ * one-workgroup reduction of its partial maxima (kept in out_sf) to the
+ * global scale, and the quantize pass.  With one, the partials go to the
+ * workspace and every quantize workgroup reduces them itself: two launches,
+ * the same bytes.
+ *   gs_other, alpha: both NULL (no alpha), or as nvfp4_quantize_alpha.
+ *   workspace:       DYNAMIC mode: a device buffer of workspace_bytes >=
+ *                    NVFP4_QUANTIZE_WS_BYTES, 16-byte aligned, owned by the
+ *                    caller; its contents on entry are ignored and on exit
+ *                    undefined.  Calls sharing a workspace must not overlap
+ *                    (same stream, or ordered by events).  STATIC mode does
+ *                    not touch it (it may be NULL).
+ * Everything else, the bytes written and the errors are as
+ * nvfp4_quantize_alpha; in DYNAMIC mode NVFP4_NULL_POINTER also for a NULL
+ * workspace, NVFP4_BAD_SHAPE for workspace_bytes below
+ * NVFP4_QUANTIZE_WS_BYTES, NVFP4_MISALIGNED for a workspace not 16-byte
+ * aligned; NVFP4_NULL_POINTER when exactly one of gs_other and alpha is NULL.
+ */
+#define NVFP4_QUANTIZE_WS_BYTES 4096
+int nvfp4_quantize_ws(const void *x, int x_dtype, int64_t m, int64_t k,
+                      const void *pre_quant_scale, float *global_scale, int gs_mode,
+                      const float *gs_other, float *alpha,
+                      uint8_t *out_fp4, uint8_t *out_sf,
+                      void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
  * Smooth quantization with the SVDQuant LoRA-down projection fused

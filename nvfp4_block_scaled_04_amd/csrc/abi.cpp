@@ -41,7 +41,7 @@ extern "C" {
 
 static int quantize_common(const void* x, int x_dtype, int64_t m, int64_t k, const void* pre_quant_scale,
                            float* global_scale, int gs_mode, const float* gs_other, float* alpha,
-                           uint8_t* out_fp4, uint8_t* out_sf, void* stream) {
+                           uint8_t* out_fp4, uint8_t* out_sf, float* ws, void* stream) {
     if (!x || !global_scale || !out_fp4 || !out_sf) return NVFP4_NULL_POINTER;
     if (x_dtype != NVFP4_BF16 && x_dtype != NVFP4_F32) return NVFP4_BAD_DTYPE;
     if (gs_mode != NVFP4_GS_STATIC && gs_mode != NVFP4_GS_DYNAMIC) return NVFP4_UNSUPPORTED;
@@ -55,6 +55,7 @@ static int quantize_common(const void* x, int x_dtype, int64_t m, int64_t k, con
     a.gs = global_scale; a.out_fp4 = out_fp4; a.out_sf = out_sf;
     a.b = 1; a.m = m; a.k_in = k; a.silu = false; a.dynamic = gs_mode == NVFP4_GS_DYNAMIC;
     a.gs_other = gs_other; a.alpha_out = alpha;
+    a.ws = a.dynamic ? ws : nullptr;
     return launch_status(nvfp4::launch_quantize(a, (hipStream_t)stream));
 }
 
@@ -62,7 +63,7 @@ int nvfp4_quantize(const void* x, int x_dtype, int64_t m, int64_t k, const void*
                    float* global_scale, int gs_mode, uint8_t* out_fp4, uint8_t* out_sf,
                    void* stream) {
     return quantize_common(x, x_dtype, m, k, pre_quant_scale, global_scale, gs_mode, nullptr, nullptr,
-                           out_fp4, out_sf, stream);
+                           out_fp4, out_sf, nullptr, stream);
 }
 
 int nvfp4_quantize_alpha(const void* x, int x_dtype, int64_t m, int64_t k, const void* pre_quant_scale,
@@ -70,7 +71,22 @@ int nvfp4_quantize_alpha(const void* x, int x_dtype, int64_t m, int64_t k, const
                          uint8_t* out_fp4, uint8_t* out_sf, void* stream) {
     if (!gs_other || !alpha) return NVFP4_NULL_POINTER;
     return quantize_common(x, x_dtype, m, k, pre_quant_scale, global_scale, gs_mode, gs_other, alpha,
-                           out_fp4, out_sf, stream);
+                           out_fp4, out_sf, nullptr, stream);
+}
+
+int nvfp4_quantize_ws(const void* x, int x_dtype, int64_t m, int64_t k, const void* pre_quant_scale,
+                      float* global_scale, int gs_mode, const float* gs_other, float* alpha,
+                      uint8_t* out_fp4, uint8_t* out_sf, void* workspace, int64_t workspace_bytes,
+                      void* stream) {
+    if (!gs_other != !alpha) return NVFP4_NULL_POINTER;
+    if (gs_mode == NVFP4_GS_DYNAMIC) {
+        if (!workspace) return NVFP4_NULL_POINTER;
+        if (workspace_bytes < NVFP4_QUANTIZE_WS_BYTES) return NVFP4_BAD_SHAPE;
+        if (!aligned16(workspace)) return NVFP4_MISALIGNED;
+    }
+    static_assert(NVFP4_QUANTIZE_WS_BYTES >= nvfp4::kQuantizeWsFloats * 4, "workspace holds the partials");
+    return quantize_common(x, x_dtype, m, k, pre_quant_scale, global_scale, gs_mode, gs_other, alpha,
+                           out_fp4, out_sf, (float*)workspace, stream);
 }
 
 int nvfp4_quantize_lora_down(const void* x, int64_t m, int64_t k, const void* pre_quant_scale,

@@ -65,6 +65,20 @@ __device__ __forceinline__ float xor1(float v) {
     return bits_f((uint32_t)__builtin_amdgcn_mov_dpp((int)f_bits(v), 0xB1, 0xF, 0xF, true));
 }
 
+// fp32(x / 6) for x >= 0, correctly rounded, without the division sequence:
+// q0 = x * RN(1/6), then one correction step with the exact FMA residual
+// r = x - q0 * 6 (Markstein's correction for division by a constant).
+// Compared with the IEEE quotient over every non-negative finite fp32: equal
+// for all x >= 2^-120; below that, where the quotient is subnormal, the
+// division itself is used.
+__device__ __forceinline__ float div6(float x) {
+    const float c = 0.16666667163372039794921875f;  // RN(1/6)
+    const float q0 = x * c;
+    const float q1 = __builtin_fmaf(__builtin_fmaf(-q0, 6.0f, x), c, q0);
+    if (__builtin_expect(x < 0x1p-120f, 0)) return x / 6.0f;
+    return q1;
+}
+
 // ue4m3 code of a non-negative fp32 value: round to nearest even, saturating
 // at 448.  The hardware e4m3 conversion rounds to nearest even but overflows
 // to NaN above 464, so the value is clamped to 448 first.

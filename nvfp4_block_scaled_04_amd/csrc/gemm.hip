@@ -489,7 +489,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, (KS == 2 ? 2 : kWavesPerEU<BM 
 #pragma unroll
                     for (int j = 0; j < 16; j++) f[j] = 0.0f;
                 }
-                const uint32_t sc = active ? ue4m3_encode((bamax / 6.0f) * gs) : 0u;
+                const uint32_t sc = active ? ue4m3_encode(div6(bamax) * gs) : 0u;
                 const float dec = ue4m3_decode(sc);
                 const float rr = dec == 0.0f ? 0.0f : gs / dec;
                 uint32_t w0, w1;

@@ -20,7 +20,13 @@ struct QuantizeArgs {
     bool dynamic;
     const float* gs_other = nullptr;  // with alpha_out: [b] the other operand's global scales
     float* alpha_out = nullptr;       // [b] alpha = 1 / (gs * gs_other), or null
+    float* ws = nullptr;              // DYNAMIC, b == 1, no mask: >= kQuantizeWsFloats floats for the
+                                      // partial maxima (two launches instead of three), or null
 };
+
+// Floats of workspace a DYNAMIC single-tensor quantization uses for its
+// partial maxima (the flat amax pass's largest grid).
+constexpr int kQuantizeWsFloats = 1024;
 
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t st);
 // Smooth quantize of a bf16 [m, k] (a.pqs set, a.b = 1) with the LoRA-down

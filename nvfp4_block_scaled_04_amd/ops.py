@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libnvfp4_amd.so")
 EXPORTS = (
     "nvfp4_quantize",
     "nvfp4_quantize_alpha",
+    "nvfp4_quantize_ws",
     "nvfp4_quantize_lora_down",
     "nvfp4_quantize_masked_batched",
     "silu_mul_nvfp4_quantize",
@@ -49,6 +50,7 @@ def _load():
     sig = {
         "nvfp4_quantize": [vp, i32, i64, i64, vp, vp, i32, vp, vp, vp],
         "nvfp4_quantize_alpha": [vp, i32, i64, i64, vp, vp, i32, vp, vp, vp, vp, vp],
+        "nvfp4_quantize_ws": [vp, i32, i64, i64, vp, vp, i32, vp, vp, vp, vp, vp, i64, vp],
         "nvfp4_quantize_lora_down": [vp, i64, i64, vp, vp, i64, vp, i32, vp, vp, vp, vp],
         "nvfp4_quantize_masked_batched": [vp, i64, i64, i64, vp, vp, i32, vp, vp, vp],
         "silu_mul_nvfp4_quantize": [vp, i64, i64, i64, vp, vp, i32, vp, vp, vp],
@@ -189,6 +191,51 @@ def nvfp4_quantize_alpha(x, gs_other, global_scale=None, gs_mode=GS_DYNAMIC, pre
     rc = _lib.nvfp4_quantize_alpha(_ptr(x), dt, m, k, _ptr(pre_quant_scale), _ptr(global_scale), gs_mode,
                                    _ptr(gs_other), _ptr(alpha), _ptr(out_fp4), _ptr(out_sf), _stream(dev))
     _check(rc, "nvfp4_quantize_alpha")
+    return out_fp4, out_sf, global_scale, alpha
+
+
+QUANTIZE_WS_BYTES = 4096   # NVFP4_QUANTIZE_WS_BYTES
+
+
+def quantize_workspace(device):
+    """A workspace for nvfp4_quantize_ws (caller-owned device memory)."""
+    return torch.empty(QUANTIZE_WS_BYTES, dtype=torch.uint8, device=device)
+
+
+def nvfp4_quantize_ws(x, workspace, global_scale=None, gs_mode=GS_DYNAMIC, pre_quant_scale=None,
+                      gs_other=None, alpha=None, out_fp4=None, out_sf=None):
+    """nvfp4_quantize with a caller workspace ([QUANTIZE_WS_BYTES] bytes on the
+    device) for the DYNAMIC mode's partial maxima: two launches instead of
+    three.  With gs_other ([1] fp32, the weight's global scale) it also writes
+    alpha = 1 / (gs * gs_other[0]) (allocated when None).  Returns (fp4, sf,
+    gs, alpha or None)."""
+    _dims(x, "x", 2)
+    m, k = x.shape
+    dt = {torch.bfloat16: 0, torch.float32: 1}.get(x.dtype)
+    if dt is None:
+        raise ValueError("x must be bf16 or fp32")
+    dev = x.device
+    if global_scale is None:
+        global_scale = torch.zeros(1, dtype=torch.float32, device=dev)
+    if out_fp4 is None:
+        out_fp4 = torch.empty(m, k // 2, dtype=torch.uint8, device=dev)
+    if out_sf is None:
+        out_sf = torch.empty(sf_size(m, k), dtype=torch.uint8, device=dev)
+    if gs_other is not None and alpha is None:
+        alpha = torch.empty(1, dtype=torch.float32, device=dev)
+    if (gs_other is None) != (alpha is None):
+        raise ValueError("gs_other and alpha go together")
+    _opt(pre_quant_scale, "pre_quant_scale", BF16, k, dev)
+    _dev(global_scale, "global_scale", F32, 1, dev)
+    _opt(gs_other, "gs_other", F32, 1, dev)
+    _opt(alpha, "alpha", F32, 1, dev)
+    _dev(out_fp4, "out_fp4", BYTES, m * (k // 2), dev)
+    _dev(out_sf, "out_sf", BYTES, sf_size(m, k), dev)
+    _dev(workspace, "workspace", BYTES, QUANTIZE_WS_BYTES, dev)
+    rc = _lib.nvfp4_quantize_ws(_ptr(x), dt, m, k, _ptr(pre_quant_scale), _ptr(global_scale), gs_mode,
+                                _ptr(gs_other), _ptr(alpha), _ptr(out_fp4), _ptr(out_sf), _ptr(workspace),
+                                workspace.numel(), _stream(dev))
+    _check(rc, "nvfp4_quantize_ws")
     return out_fp4, out_sf, global_scale, alpha
 
 

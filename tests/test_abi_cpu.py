@@ -36,7 +36,8 @@ def test_header_declares_the_entry_points():
         "nvfp4_alpha", "nvfp4_gemm", "nvfp4_gemm_grouped_masked",
         "nvfp4_gemm_grouped_masked_silu_quantize", "nvfp4_gemm_svdquant",
         "nvfp4_gemm_w4a16", "nvfp4_quantize_lora_down",
-        "nvfp4_quantize", "nvfp4_quantize_alpha", "nvfp4_quantize_masked_batched", "silu_mul_nvfp4_quantize",
+        "nvfp4_quantize", "nvfp4_quantize_alpha", "nvfp4_quantize_ws", "nvfp4_quantize_masked_batched",
+        "silu_mul_nvfp4_quantize",
         "mxfp4_quantize", "mxfp4_gemm",
     ])
 
@@ -175,6 +176,28 @@ def test_quantize_alpha_validation(lib):
     assert run(k=40) == SHAPE
     assert run(gs_other=P + 2) == MISAL
     assert run(alpha=P + 1) == MISAL
+
+
+def test_quantize_ws_validation(lib):
+    """nvfp4_quantize's checks, plus the optional alpha pair and, in DYNAMIC
+    mode, the workspace (present, large enough, 16-byte aligned)."""
+    f = lib.nvfp4_quantize_ws
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    run = lambda x=P, dt=0, m=128, k=256, pqs=None, gs=P, mode=1, go=None, al=None, o=P, s=P, ws=P, wsb=4096: \
+        f(x, dt, m, k, pqs, gs, mode, go, al, o, s, ws, wsb, None)
+    assert run(go=P) == NULLP            # gs_other without alpha
+    assert run(al=P) == NULLP            # alpha without gs_other
+    assert run(ws=None) == NULLP         # DYNAMIC needs the workspace
+    assert run(wsb=4095) == SHAPE        # smaller than NVFP4_QUANTIZE_WS_BYTES
+    assert run(ws=P + 4) == MISAL
+    assert run(x=None) == NULLP
+    assert run(k=40) == SHAPE
+    assert run(dt=2) == DTYPE
+    assert run(mode=2) == UNSUP
+    assert run(o=P + 8) == MISAL
+    assert run(go=P + 2, al=P) == MISAL
 
 
 def test_svdquant_rank_and_alignment(lib):

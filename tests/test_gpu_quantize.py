@@ -307,3 +307,76 @@ def test_quantize_alpha(ops, m, k, dtype, dynamic, smooth):
     assert a == np_bits(want).view(np.uint32)[0]
     host = np.float32(1.0) / (np_bits(gs2)[0] * np_bits(gs_w)[0])
     assert a == np.array([host], dtype=np.float32).view(np.uint32)[0]
+
+
+def _nonfinite(x):
+    x[0, 5] = float("nan")
+    x[1, 17] = float("inf")
+    x[2, 33] = float("-inf")
+    x[4, 16:32] = -0.0
+    return x
+
+
+@pytest.mark.parametrize("m,k,dtype,case", [
+    (640, 256, torch.float32, "nonfinite"),
+    (640, 256, torch.bfloat16, "nonfinite"),
+    (300, 1040, torch.bfloat16, "plain"),
+    (8200, 4112, torch.bfloat16, "plain"),      # ragged both ways, more than one amax chunk per workgroup
+    (300, 320, torch.bfloat16, "smooth"),
+    (300, 320, torch.float32, "smooth"),
+    (16, 4096, torch.bfloat16, "plain"),        # small: the one-launch path (workspace unused)
+    (300, 512, torch.bfloat16, "static"),
+])
+def test_quantize_ws(ops, m, k, dtype, case):
+    """nvfp4_quantize_ws: the partial maxima in the caller's workspace (filled
+    with a NaN pattern beforehand), the quantize pass reducing them itself.
+    FP4 and scale bytes and gs equal to the oracle's, alpha = 1 / (gs *
+    gs_other) bit for bit; the same bytes without alpha."""
+    say("quantize_ws", (m, k), dtype, case)
+    g = torch.Generator().manual_seed(m * 3 + k)
+    x = torch.randn(m, k, generator=g) * 3
+    if case == "nonfinite":
+        x = _nonfinite(x)
+    x = x.to(dtype)
+    pqs = torch.exp(0.4 * torch.randn(k, generator=g)).to(torch.bfloat16) if case == "smooth" else None
+    static = case == "static"
+    mode = ops.GS_STATIC if static else ops.GS_DYNAMIC
+    gs_in = 2688.0 / 9.5
+    ws = torch.full((ops.QUANTIZE_WS_BYTES,), 0xFF, dtype=torch.uint8, device="cuda")
+    gs_w = torch.full((1,), 2688.0 / 0.137, dtype=torch.float32, device="cuda")
+    o4, osf = canary((m, k // 2)), canary((ops.sf_size(m, k),))
+    gs_d = torch.tensor([gs_in], dtype=torch.float32, device="cuda")
+    _, _, _, alpha = ops.nvfp4_quantize_ws(dev(x), ws, gs_d, mode, pre_quant_scale=None if pqs is None else dev(pqs),
+                                           gs_other=gs_w, out_fp4=o4, out_sf=osf)
+    o4b, osfb = canary((m, k // 2)), canary((ops.sf_size(m, k),))
+    gs_b = torch.tensor([gs_in], dtype=torch.float32, device="cuda")
+    ops.nvfp4_quantize_ws(dev(x), ws, gs_b, mode, pre_quant_scale=None if pqs is None else dev(pqs),
+                          out_fp4=o4b, out_sf=osfb)
+    torch.cuda.synchronize()
+    q, sf, gsv = O.quantize(np_bits(x), prologue=O.PRO_SMOOTH if pqs is not None else O.PRO_NONE,
+                            pqs=None if pqs is None else np_bits(pqs),
+                            gs=np.array([gs_in], np.float32) if static else None,
+                            gs_mode=O.STATIC if static else O.DYNAMIC)
+    for a4, asf, ag in ((o4, osf, gs_d), (o4b, osfb, gs_b)):
+        assert np_bits(ag).view(np.uint32)[0] == gsv.view(np.uint32)[0]
+        assert np.array_equal(np_bits(a4), q), int((np_bits(a4) != q).sum())
+        assert np.array_equal(np_bits(asf), sf), int((np_bits(asf) != sf).sum())
+    want = np.float32(1.0) / (gsv[0] * np_bits(gs_w)[0])
+    assert np_bits(alpha).view(np.uint32)[0] == np.array([want], np.float32).view(np.uint32)[0]
+
+
+def test_quantize_ws_prefill_and_reuse(ops):
+    """The prefill activation through the workspace path, then a smaller
+    tensor through the same workspace: both bit-exact with the oracle."""
+    p = synth.prefill()
+    ws = torch.full((ops.QUANTIZE_WS_BYTES,), 0xFF, dtype=torch.uint8, device="cuda")
+    for x in (p.a, p.a[:1000, :2048].contiguous()):
+        m, k = x.shape
+        say("quantize_ws reuse", (m, k))
+        o4, osf = canary((m, k // 2)), canary((ops.sf_size(m, k),))
+        _, _, gs, _ = ops.nvfp4_quantize_ws(dev(x), ws, out_fp4=o4, out_sf=osf)
+        torch.cuda.synchronize()
+        q, sf, gv = O.quantize(np_bits(x))
+        assert np_bits(gs).view(np.uint32)[0] == gv.view(np.uint32)[0]
+        assert np.array_equal(np_bits(o4), q)
+        assert np.array_equal(np_bits(osf), sf)
