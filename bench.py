@@ -2,14 +2,16 @@
 
 A step is one pass of the whole path over one batch of synthetic input that
 is already resident in HBM: NVFP4 quantization of the bf16 activation with a
-dynamic global scale (amax pass, finish, quantize pass; one launch for small
-activations) whose last launch also writes alpha = 1/(gs_a*gs_w), and the
-block-scaled GEMM to bf16.  Weights are
-quantized once before timing (same kernels, untimed).  The K timed steps
-are launched as one HIP graph (captured after the W warm-up steps, launched
-once untimed to upload it); the same K steps launched eagerly, with HIP
-events between the quantize part and the GEMM, give the two parts' times and
-`eager_ms_per_step`.
+dynamic global scale (the amax pass with its partial maxima in a workspace,
+then the quantize pass, which also writes gs and alpha = 1/(gs_a*gs_w); one
+launch for small activations), and the block-scaled GEMM to bf16.  Weights
+are quantized once before timing (same kernels, untimed).  Each step owns
+its quantized outputs.  The K timed steps run as two HIP graphs replayed
+back to back -- the K quantizations, then the K GEMMs -- between three HIP
+events on the kernels' stream, after a cache flush; the step time, the
+quantize share and the GEMM's average duration all come from those events.
+The same steps interleaved in one graph, and launched eagerly, are reported
+for reference.
 
 Default workload: the large prefill linear, activation [8192, 5120] bf16
 (0.5% outlier channels x30) against a [16384, 5120] weight, output [8192,
@@ -62,7 +64,19 @@ def parse():
 
 
 class Workload:
-    """Device-resident inputs plus the step closure and its algorithmic work."""
+    """Device-resident inputs, the step closures and their algorithmic work.
+
+    make_steps(acts, K) gives K (quantize, gemm) closure pairs; step i reads
+    activation copy i % len(acts) and owns its quantized outputs, which its
+    GEMM consumes (so the K quantizations and the K GEMMs can run as two
+    graphs and every GEMM still reads its own step's operands).  quant(a,
+    mode) quantizes into one shared output set (the pass measurements)."""
+
+
+def _rotation(nbytes):
+    """Copies of an nbytes buffer needed to exceed 512 MiB (twice the 256 MB
+    Infinity Cache), so reads cycling through them come from HBM."""
+    return max(1, -(-512 * 2 ** 20 // nbytes))
 
 
 def build_workload(name, ops, synth, torch):
@@ -73,6 +87,7 @@ def build_workload(name, ops, synth, torch):
     w.swiglu = None
     w.mx = None
     w.library = None
+    w.quant_3launch = None
     dev = "cuda"
     if name in ("prefill", "dense", "decode", "tiny"):
         if name == "prefill":
@@ -86,51 +101,73 @@ def build_workload(name, ops, synth, torch):
         elif name == "decode":
             d, a16 = synth.dense()
             a_cpu, w_cpu = a16, d.w
-            w.desc = "decode linear 16x4096x4096: bf16 activation -> dynamic NVFP4 quantize -> block-scaled GEMM -> bf16"
+            w.desc = ("decode linear 16x4096x4096: bf16 activation -> dynamic NVFP4 quantize -> block-scaled GEMM "
+                      "-> bf16; every step reads its own weight copy (cold)")
         else:
             d = synth.tiny()
             a_cpu, w_cpu = d.a, d.w
             w.desc = "tiny 128x256x256: fp32 activation -> dynamic NVFP4 quantize -> block-scaled GEMM -> bf16"
         m, k = a_cpu.shape
         n = w_cpu.shape[0]
-        fw, sfw, gsw = ops.nvfp4_quantize(w_cpu.to(dev))
+        fw0, sfw0, gsw = ops.nvfp4_quantize(w_cpu.to(dev))
+        w.hbm_bound = name == "decode"   # 16 rows: the weight read bounds the GEMM
+        w_bytes = n * k // 2 + sf_size(n, k)
+        # decode: enough weight copies that the steps' weight reads come from HBM
+        w.n_wcopies = _rotation(w_bytes) if w.hbm_bound else 1
+        weights = [(fw0, sfw0)] + [(fw0.clone(), sfw0.clone()) for _ in range(w.n_wcopies - 1)]
         esz = a_cpu.element_size()
-        act_bytes = m * k * esz
-        copies = w.rotate_hint = max(1, -(-512 * 2 ** 20 // act_bytes))
-        w.acts = None
+        w.rotate_hint = _rotation(m * k * esz)
         w.a_cpu, w.w_cpu = a_cpu, w_cpu
         w.m, w.n, w.k = m, n, k
         w.flops = 2.0 * m * n * k
         w.q_bytes = m * k * esz + m * k // 2 + sf_size(m, k)     # quantize pass
         w.amax_bytes = m * k * esz                                 # amax pass
-        w.gemm_bytes = m * k // 2 + sf_size(m, k) + n * k // 2 + sf_size(n, k) + 2 * m * n
+        w.gemm_bytes = m * k // 2 + sf_size(m, k) + w_bytes + 2 * m * n
+        out = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+        ws = ops.quantize_workspace(dev)
         fa = torch.empty(m, k // 2, dtype=torch.uint8, device=dev)
         sfa = torch.empty(sf_size(m, k), dtype=torch.uint8, device=dev)
         gsa = torch.zeros(1, dtype=torch.float32, device=dev)
         alpha = torch.empty(1, dtype=torch.float32, device=dev)
-        out = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
 
         def quant(a, mode=ops.GS_DYNAMIC):
-            ops.nvfp4_quantize(a, gsa, mode, out_fp4=fa, out_sf=sfa)
+            # the step's call: with the workspace; DYNAMIC also writes alpha
+            ops.nvfp4_quantize_ws(a, ws, gsa, mode, gs_other=gsw, alpha=alpha, out_fp4=fa, out_sf=sfa)
 
-        def gemm():
-            ops.nvfp4_gemm(fa, fw, sfa, sfw, alpha, out=out)
-
-        def pre(a):  # dynamic quantize; the same launch writes alpha = 1/(gs_a*gs_w)
+        def quant_3launch(a):
             ops.nvfp4_quantize_alpha(a, gsw, gsa, ops.GS_DYNAMIC, out_fp4=fa, out_sf=sfa, alpha=alpha)
 
+        def make_steps(acts, K):
+            steps = []
+            for i in range(K):
+                o = (torch.empty(m, k // 2, dtype=torch.uint8, device=dev),
+                     torch.empty(sf_size(m, k), dtype=torch.uint8, device=dev),
+                     torch.zeros(1, dtype=torch.float32, device=dev), torch.empty(1, dtype=torch.float32, device=dev))
+                fw, sfw = weights[i % len(weights)]
+                a = acts[i % len(acts)]
+
+                def pre(a=a, o=o):
+                    ops.nvfp4_quantize_ws(a, ws, o[2], ops.GS_DYNAMIC, gs_other=gsw, alpha=o[3],
+                                          out_fp4=o[0], out_sf=o[1])
+
+                def gemm(o=o, fw=fw, sfw=sfw):
+                    ops.nvfp4_gemm(o[0], fw, o[1], sfw, o[3], out=out)
+                steps.append((pre, gemm))
+            return steps
+
         w.make_acts = lambda n_copies: [a_cpu.to(dev) for _ in range(n_copies)]
-        w.pre, w.quant, w.gemm = pre, quant, gemm
-        w.outputs = (fa, sfa, gsa, alpha, out)
+        w.make_steps, w.quant, w.quant_3launch = make_steps, quant, quant_3launch
+        w.gemm0 = lambda: ops.nvfp4_gemm(fa, fw0, sfa, sfw0, alpha, out=out)
         w.cfg = {"m": m, "n": n, "k": k}
-        w.hbm_bound = name == "decode"   # 16 rows: the weight read bounds the GEMM
         if name == "decode":
             # weight-only form: the bf16 activation against the NVFP4 weight,
-            # no activation quantization (alpha = 1 / the weight's gs)
+            # no activation quantization (alpha = 1 / the weight's gs); step i
+            # reads weight copy i
             alpha_w = ops.nvfp4_alpha(torch.ones(1, dtype=torch.float32, device=dev), gsw)
             out_w = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
-            w.w4a16 = lambda a: ops.nvfp4_gemm_w4a16(a, fw, sfw, alpha_w, out=out_w)
-            w.w4a16_bytes = n * k // 2 + sf_size(n, k) + m * k * 2 + 2 * m * n
+            w.w4a16 = lambda a, i: ops.nvfp4_gemm_w4a16(a, weights[i % len(weights)][0], weights[i % len(weights)][1],
+                                                        alpha_w, out=out_w)
+            w.w4a16_bytes = w_bytes + m * k * 2 + 2 * m * n
         w.cpu_sample = lambda O, np: cpu_baseline_dense(O, np, a_cpu, w_cpu, synth)
         if name in ("prefill", "dense"):
             w.mx = lambda acts: mx_setting(ops, torch, acts, w_cpu, dev)
@@ -145,6 +182,7 @@ def build_workload(name, ops, synth, torch):
             f_, s_, g_ = ops.nvfp4_quantize(mo.w[e].to(dev))
             fws.append(f_); sfws.append(s_); gsws.append(g_)
         fw = torch.stack(fws); sfw = torch.stack(sfws); gsw = torch.cat(gsws)
+        del fws, sfws
         mask = mo.mask.to(dev)
         valid = int(mo.mask.clamp(0, m).sum())
         fa = torch.empty(E, m, h // 2, dtype=torch.uint8, device=dev)
@@ -156,20 +194,30 @@ def build_workload(name, ops, synth, torch):
         def quant(x, mode=ops.GS_DYNAMIC):
             ops.silu_mul_nvfp4_quantize(x, mask, gsa, mode, out_fp4=fa, out_sf=sfa)
 
-        def gemm():
-            ops.nvfp4_gemm_grouped_masked(fa, fw, sfa, sfw, alpha, mask, out=out)
+        def make_steps(acts, K):
+            steps = []
+            for i in range(K):
+                o = (torch.empty(E, m, h // 2, dtype=torch.uint8, device=dev),
+                     torch.empty(E, sf_size(m, h), dtype=torch.uint8, device=dev),
+                     torch.zeros(E, dtype=torch.float32, device=dev), torch.empty(E, dtype=torch.float32, device=dev))
+                x = acts[i % len(acts)]
 
-        def pre(x):
-            quant(x)
-            ops.nvfp4_alpha(gsa, gsw, out=alpha)
+                def pre(x=x, o=o):
+                    ops.silu_mul_nvfp4_quantize(x, mask, o[2], ops.GS_DYNAMIC, out_fp4=o[0], out_sf=o[1])
+                    ops.nvfp4_alpha(o[2], gsw, out=o[3])
+
+                def gemm(o=o):
+                    ops.nvfp4_gemm_grouped_masked(o[0], fw, o[1], sfw, o[3], mask, out=out)
+                steps.append((pre, gemm))
+            return steps
 
         w.desc = ("Llama4-style routed experts: E=8 gate|up [512,16384] bf16, valid rows "
                   f"{mo.mask.tolist()} -> fused silu_and_mul + NVFP4 quantize -> grouped masked GEMM vs [8,5120,8192]")
-        act_bytes = mo.x.numel() * 2
-        w.rotate_hint = max(1, -(-512 * 2 ** 20 // act_bytes))
+        w.rotate_hint = _rotation(mo.x.numel() * 2)
         w.make_acts = lambda n_copies: [mo.x.to(dev) for _ in range(n_copies)]
-        w.pre, w.quant, w.gemm = pre, quant, gemm
-        w.outputs = (fa, sfa, gsa, alpha, out)
+        w.make_steps, w.quant = make_steps, quant
+        w.gemm0 = lambda: ops.nvfp4_gemm_grouped_masked(fa, fw, sfa, sfw, alpha, mask, out=out)
+        w.n_wcopies = 1
         w.flops = 2.0 * n * h * valid
         w.q_bytes = valid * 2 * h * 2 + E * m * h // 2 + E * sf_size(m, h)
         w.amax_bytes = valid * 2 * h * 2
@@ -192,31 +240,45 @@ def build_workload(name, ops, synth, torch):
         alpha = ops.nvfp4_alpha(gsa, gsw)
         al = float(alpha.item())
         l2 = s.l2.to(torch.bfloat16).to(dev)
-        d = torch.empty(m, r, dtype=torch.bfloat16, device=dev)   # formed inside the step
         l1 = synth.lora_up(s, al).to(dev)
         bias = s.bias.to(dev)
         fa = torch.empty(m, k // 2, dtype=torch.uint8, device=dev)
         sfa = torch.empty(sf_size(m, k), dtype=torch.uint8, device=dev)
+        d = torch.empty(m, r, dtype=torch.bfloat16, device=dev)
         out = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
 
         def quant(x, mode=ops.GS_STATIC):
             ops.nvfp4_quantize(x, gsa, mode, pre_quant_scale=pqs, out_fp4=fa, out_sf=sfa)
 
-        def gemm():
-            ops.nvfp4_gemm_svdquant(fa, fw, sfa, sfw, alpha, d, l1, bias=bias, out=out)
-
-        def pre(x):
+        def lora_down(x):
             # smooth quantize and the LoRA-down projection d, one read of x
             ops.nvfp4_quantize_lora_down(x, pqs, l2, gsa, ops.GS_STATIC, out_fp4=fa, out_sf=sfa, d=d)
 
-        w.lora_down = pre
+        def make_steps(acts, K):
+            steps = []
+            for i in range(K):
+                o = (torch.empty(m, k // 2, dtype=torch.uint8, device=dev),
+                     torch.empty(sf_size(m, k), dtype=torch.uint8, device=dev),
+                     torch.empty(m, r, dtype=torch.bfloat16, device=dev))
+                x = acts[i % len(acts)]
+
+                def pre(x=x, o=o):
+                    ops.nvfp4_quantize_lora_down(x, pqs, l2, gsa, ops.GS_STATIC, out_fp4=o[0], out_sf=o[1], d=o[2])
+
+                def gemm(o=o):
+                    ops.nvfp4_gemm_svdquant(o[0], fw, o[1], sfw, alpha, o[2], l1, bias=bias, out=out)
+                steps.append((pre, gemm))
+            return steps
+
+        w.lora_down = lora_down
         w.lora_down_bytes = m * k * 2 + k * 2 + r * k * 2 + m * k // 2 + sf_size(m, k) + 2 * m * r
         w.desc = ("SVDQuant linear 4096x3072x3072, r=32: smooth NVFP4 quantize (static gs) with the LoRA-down "
                   "projection fused -> fused GEMM + LoRA-up + bias")
-        w.rotate_hint = max(1, -(-512 * 2 ** 20 // (m * k * 2)))
+        w.rotate_hint = _rotation(m * k * 2)
         w.make_acts = lambda n_copies: [s.x.to(dev) for _ in range(n_copies)]
-        w.pre, w.quant, w.gemm = pre, quant, gemm
-        w.outputs = (fa, sfa, out)
+        w.make_steps, w.quant = make_steps, quant
+        w.gemm0 = lambda: ops.nvfp4_gemm_svdquant(fa, fw, sfa, sfw, alpha, d, l1, bias=bias, out=out)
+        w.n_wcopies = 1
         w.flops = 2.0 * m * n * k + 2.0 * m * n * r
         w.q_bytes = m * k * 2 + k * 2 + m * k // 2 + sf_size(m, k)
         w.amax_bytes = 0
@@ -416,7 +478,8 @@ def library_comparison(ops, torch, w, a16, w_cpu, dev, rounds=3):
     flops = 2.0 * m * n * k
     w16 = w_cpu.to(dev)
     out16 = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
-    legs = {"k_gemm (NVFP4, this library)": (w.gemm, MFMA_F16_PEAK_TFLOPS),
+    w.quant(a16)   # the shared output set the GEMM leg reads
+    legs = {"k_gemm (NVFP4, this library)": (w.gemm0, MFMA_F16_PEAK_TFLOPS),
             "hipblaslt bf16": (lambda: torch.matmul(a16, w16.t(), out=out16), MFMA_F16_PEAK_TFLOPS)}
     fa, sfa = ops.mxfp4_quantize(a16)
     fw, sfw = ops.mxfp4_quantize(w16)
@@ -497,6 +560,14 @@ def time_graph(torch, g, reps=3):
     return best
 
 
+def flush_caches(torch):
+    """Stream 1 GiB of writes through the caches (L2 and the 256 MB Infinity
+    Cache), so the next kernel finds none of its inputs there."""
+    buf = torch.empty(2 ** 28, dtype=torch.float32, device="cuda")
+    buf.zero_()
+    del buf
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -509,14 +580,17 @@ def main():
     from nvfp4_block_scaled_04_amd import ops, synth
 
     torch.cuda.set_device(0)
+    K = args.steps
     w = build_workload(args.workload, ops, synth, torch)
     n_copies = min(args.rotate or w.rotate_hint, 64)
     acts = w.make_acts(n_copies)
+    steps = w.make_steps(acts, K)
     torch.cuda.synchronize()
 
     for i in range(args.warmup):
-        w.pre(acts[i % n_copies])
-        w.gemm()
+        pre, gemm = steps[i % K]
+        pre()
+        gemm()
     torch.cuda.synchronize()
 
     if args.copy_calibration:
@@ -527,59 +601,79 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # ---- the K steps launched eagerly on the current stream, with HIP events
-    # between the quantize part and the GEMM (the per-phase times)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # ---- the timed K steps: the K quantizations as one HIP graph, then the K
+    # GEMMs (each reading its own step's quantized activation) as another,
+    # replayed back to back between three HIP events on the stream the
+    # kernels run on; the caches are flushed first, so the steps start cold.
+    # ms_per_step, the quantize share and the GEMM's average duration (the
+    # roofline's) all come from these events.
+    g_q = capture(torch, lambda: [pre() for pre, _ in steps])
+    g_g = capture(torch, lambda: [gemm() for _, gemm in steps])
+    g_q.replay()
+    g_g.replay()
+    torch.cuda.synchronize()
+    flush_caches(torch)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        evs[i][0].record()
-        w.pre(acts[i % n_copies])
-        evs[i][1].record()
-        w.gemm()
-        evs[i][2].record()
+    ev[0].record()
+    g_q.replay()
+    ev[1].record()
+    g_g.replay()
+    ev[2].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    eager_step_ms = (t1 - t0) * 1e3 / args.steps
-    quant_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    gemm_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    step_ms = ev[0].elapsed_time(ev[2]) / K
+    quant_ms = ev[0].elapsed_time(ev[1]) / K
+    gemm_ms = ev[1].elapsed_time(ev[2]) / K
+    wall_step_ms = (t1 - t0) * 1e3 / K
+    del g_q, g_g
 
-    # ---- the timed K steps: the same launches captured as one HIP graph (a
-    # launch-bound step such as decode spends most of its eager time in host
-    # launches), launched once untimed so that the timed launch finds it
-    # uploaded, then timed between two synchronizations
-    g_steps = capture(torch, lambda: [(w.pre(acts[i % n_copies]), w.gemm()) for i in range(args.steps)])
-    g_steps.replay()
+    # ---- for reference: the same steps interleaved (quantize, GEMM, quantize,
+    # ...) in one graph, and launched eagerly
+    g_i = capture(torch, lambda: [f() for pair in steps for f in pair])
+    g_i.replay()
+    torch.cuda.synchronize()
+    flush_caches(torch)
+    torch.cuda.synchronize()
+    inter_ms = time_graph(torch, g_i, reps=1) / K
+    del g_i
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    g_steps.replay()
+    for pre, gemm in steps:
+        pre()
+        gemm()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    step_ms = (t1 - t0) * 1e3 / args.steps
-    del g_steps
+    eager_step_ms = (time.perf_counter() - t0) * 1e3 / K
 
     # ---- kernel passes back to back, over every activation copy (cold inputs),
     # as HIP graphs so the host's launch latency stays out of the kernel times
     g_pass = capture(torch, lambda: [w.quant(a, ops.GS_STATIC) for a in acts])
     qpass_ms = time_graph(torch, g_pass) / n_copies
+    del g_pass
+    qdyn_ms = qdyn3_ms = None
     if w.amax_bytes:
         g_dyn = capture(torch, lambda: [w.quant(a, ops.GS_DYNAMIC) for a in acts])
         qdyn_ms = time_graph(torch, g_dyn) / n_copies
-    else:
-        qdyn_ms = qpass_ms
-    # the GEMM alone, back to back (for the weight-bound decode shape, whose
-    # eager launches cost more than the kernel)
-    g_gemm = capture(torch, lambda: [w.gemm() for _ in range(n_copies)])
-    gemm_graph_ms = time_graph(torch, g_gemm) / n_copies
-    del g_gemm
+        del g_dyn
+        if w.quant_3launch is not None:
+            g_dyn3 = capture(torch, lambda: [w.quant_3launch(a) for a in acts])
+            qdyn3_ms = time_graph(torch, g_dyn3) / n_copies
+            del g_dyn3
     w4 = None
     if w.w4a16 is not None:
-        g_w4 = capture(torch, lambda: [w.w4a16(a) for a in acts])
-        w4_ms = time_graph(torch, g_w4) / n_copies
+        # step i reads weight copy i (cold after the flush)
+        g_w4 = capture(torch, lambda: [w.w4a16(acts[i % n_copies], i) for i in range(K)])
+        g_w4.replay()
+        torch.cuda.synchronize()
+        flush_caches(torch)
+        torch.cuda.synchronize()
+        w4_ms = time_graph(torch, g_w4, reps=1) / K
         del g_w4
         w4_gbs = w.w4a16_bytes / (w4_ms * 1e-3) / 1e9
         w4 = {"ms": round(w4_ms, 5), "gbs": round(w4_gbs, 1), "frac_hbm": round(w4_gbs / HBM_PEAK_GBS, 4),
-              "bytes": w.w4a16_bytes, "kernel": "k_gemm_w4a16 (bf16 activation x NVFP4 weight, no activation quantize)"}
+              "bytes": w.w4a16_bytes, "weights": "cold (one weight copy per launch, caches flushed first)",
+              "kernel": "k_gemm_w4a16 (bf16 activation x NVFP4 weight, no activation quantize)"}
     ld = None
     if w.lora_down is not None:
         g_ld = capture(torch, lambda: [w.lora_down(a) for a in acts])
@@ -589,57 +683,83 @@ def main():
         ld = {"ms": round(ld_ms, 5), "gbs": round(ld_gbs, 1), "frac_hbm": round(ld_gbs / HBM_PEAK_GBS, 4),
               "bytes": w.lora_down_bytes,
               "kernel": "k_quantize_lora (smooth quantize + LoRA-down projection, one read of x)"}
+    # ceilings of the memory system on this machine, timed the same way: a plain
+    # elementwise copy (read + write) and a read-only reduction (torch)
     src = torch.ones(64 * 2 ** 20, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     g_copy = capture(torch, lambda: [torch.neg(src, out=dst) for _ in range(4)])
     copy_gbs = 2 * src.numel() * 4 / (time_graph(torch, g_copy) / 4 * 1e-3) / 1e9
-    del src, dst, g_copy
+    del g_copy
+    # (launched eagerly: a reduction may record memset nodes, which stay out
+    # of graphs here; each launch reads 256 MiB, so launch gaps are small)
+    red = torch.empty((), dtype=torch.float32, device="cuda")
+    torch.sum(src, dim=0, out=red)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(4):
+        torch.sum(src, dim=0, out=red)
+    e1.record()
+    torch.cuda.synchronize()
+    read_gbs = src.numel() * 4 / (e0.elapsed_time(e1) / 4 * 1e-3) / 1e9
+    del src, dst
 
     gemm_tflops = w.flops / (gemm_ms * 1e-3) / 1e12
     value = w.flops / (step_ms * 1e-3) / 1e12
     q_gbs = w.q_bytes / (qpass_ms * 1e-3) / 1e9
-    amax_ms = qdyn_ms - qpass_ms
     e2e_bytes = w.q_bytes + w.amax_bytes
+    quant = {"pass_ms": round(qpass_ms, 5), "pass_gbs": round(q_gbs, 1),
+             "pass_frac_hbm": round(q_gbs / HBM_PEAK_GBS, 4),
+             "pass_frac_copy": round(q_gbs / copy_gbs, 4),
+             "in_step_ms": round(quant_ms, 5),
+             "pass_bytes": w.q_bytes, "amax_pass_bytes": w.amax_bytes,
+             "copy_kernel_gbs": round(copy_gbs, 1), "read_only_reduction_gbs": round(read_gbs, 1)}
+    if qdyn_ms is not None:
+        quant["dynamic_call_ms"] = round(qdyn_ms, 5)
+        quant["dynamic_call_gbs"] = round(e2e_bytes / (qdyn_ms * 1e-3) / 1e9, 1)
+        quant["dynamic_call"] = ("the step's call: amax pass with partials in a workspace, then the quantize "
+                                 "pass (which reduces them and writes gs and alpha); bytes = amax pass + "
+                                 "quantize pass")
+    if qdyn3_ms is not None:
+        quant["dynamic_call_3launch_ms"] = round(qdyn3_ms, 5)
+        quant["dynamic_call_3launch_gbs"] = round(e2e_bytes / (qdyn3_ms * 1e-3) / 1e9, 1)
     res = {
         "metric": "NVFP4 GEMM TFLOP/s (+% peak) and quantize GB/s (+% HBM peak), 1xMI355X",
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": K,
         "warmup": args.warmup,
-        "ms_per_step": round(step_ms, 4),
-        "eager_ms_per_step": round(eager_step_ms, 4),
+        "ms_per_step": round(step_ms, 5),
+        "wall_ms_per_step": round(wall_step_ms, 5),
+        "interleaved_graph_ms_per_step": round(inter_ms, 5),
+        "eager_ms_per_step": round(eager_step_ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic (seeded N(0,1) activations with outlier channels, N(0,0.02) weights)",
         "config": {"workload": w.desc, **w.cfg, "operands": "NVFP4 (e2m1 + ue4m3 per 16, 128x4 swizzled)",
-                   "parallelism": "none (1 GPU)", "activation_copies_rotated": n_copies},
-        "gemm": {"ms": round(gemm_ms, 4), "tflops": round(gemm_tflops, 2),
-                 "frac_f16_mfma_peak": round(gemm_tflops / MFMA_F16_PEAK_TFLOPS, 4),
-                 "back_to_back_ms": round(gemm_graph_ms, 5)},
-        "quantize": {"pass_ms": round(qpass_ms, 4), "pass_gbs": round(q_gbs, 1),
-                     "pass_frac_hbm": round(q_gbs / HBM_PEAK_GBS, 4),
-                     "amax_and_finish_ms": round(amax_ms, 4),
-                     "amax_gbs": round(w.amax_bytes / (amax_ms * 1e-3) / 1e9, 1) if w.amax_bytes else None,
-                     "dynamic_call_ms": round(qdyn_ms, 4),
-                     "dynamic_call_gbs": round(e2e_bytes / (qdyn_ms * 1e-3) / 1e9, 1),
-                     "in_step_ms": round(quant_ms, 4),
-                     "pass_bytes": w.q_bytes, "amax_pass_bytes": w.amax_bytes,
-                     "copy_kernel_gbs": round(copy_gbs, 1)},
+                   "parallelism": "none (1 GPU)", "activation_copies_rotated": n_copies,
+                   "weight_copies_rotated": w.n_wcopies},
+        "gemm": {"ms": round(gemm_ms, 5), "tflops": round(gemm_tflops, 2),
+                 "frac_f16_mfma_peak": round(gemm_tflops / MFMA_F16_PEAK_TFLOPS, 4)},
+        "quantize": quant,
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / MFMA_F16_PEAK_TFLOPS, 4),
                      "traffic": gemm_traffic(args.workload), "kernel": "k_gemm (block-scaled NVFP4 GEMM)",
                      "flops_per_launch": w.flops, "algorithmic_bytes_per_launch": w.gemm_bytes},
+        "timing": ("one timed region: the K steps' quantizations as one HIP graph, then their K GEMMs as "
+                   "another, between HIP events on the kernels' stream, caches flushed first; ms_per_step, "
+                   "quantize.in_step_ms, gemm.ms and roofline.achieved all come from those events"),
     }
     if w.hbm_bound:
         # 16 activation rows: the GEMM streams the weight once; its roofline is
-        # HBM, over the back-to-back kernel time
-        gbs = w.gemm_bytes / (gemm_graph_ms * 1e-3) / 1e9
+        # HBM, over the same event-timed GEMM duration, cold weights
+        gbs = w.gemm_bytes / (gemm_ms * 1e-3) / 1e9
         res["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": gemm_traffic(args.workload),
-                           "kernel": "k_gemm_skinny (block-scaled NVFP4 GEMM, 16 rows)",
+                           "kernel": "k_gemm_skinny (block-scaled NVFP4 GEMM, 16 rows, cold weight copies)",
                            "algorithmic_bytes_per_launch": w.gemm_bytes}
     if w4 is not None:
         res["w4a16"] = w4
@@ -650,7 +770,7 @@ def main():
     if w.library is not None and not args.no_library:
         res["library"] = w.library(acts)
     if w.swiglu is not None:
-        del acts
+        del acts, steps
         torch.cuda.empty_cache()
         res["swiglu_gate_up"] = w.swiglu()
     if not args.no_cpu_baseline and w.cpu_sample is not None:
