@@ -436,7 +436,6 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, (KS == 2 ? 2 : kWavesPerEU<BM 
     const float alpha = p.alpha[e];
     uint16_t* O = p.out + (int64_t)e * p.M * p.N;
     constexpr int CPR = WN / 8;        // 16-byte pieces per staged row
-    constexpr int RPI = 64 / CPR;      // rows per wave store instruction
 #pragma unroll
     for (int im = 0; im < FM; im++) {
         if (KS == 2 && im != grp) continue;  // the other K group stores this fragment row
@@ -498,9 +497,12 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, (KS == 2 ? 2 : kWavesPerEU<BM 
                 if (m < p.q_rpad && hc / 16 < 4 * (int64_t)p.q_cp4) SF[sf_offset(m, hc / 16, p.q_cp4)] = (uint8_t)sc;
             }
         } else {
+        // 32 staged rows x CPR pieces, 64 pieces per wave store instruction
 #pragma unroll
-        for (int it = 0; it < 32 / RPI; it++) {
-            const int rl = it * RPI + lane / CPR, c = lane % CPR;
+        for (int it = 0; it < (32 * CPR + 63) / 64; it++) {
+            const int pc = it * 64 + lane;
+            if ((32 * CPR) % 64 != 0 && pc >= 32 * CPR) break;
+            const int rl = pc / CPR, c = pc % CPR;
             const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(ep + rl * PITCH + c * 16);
             const int64_t m = m0 + wm * WM + im * 32 + rl;
             const int64_t n = n0 + wn * WN + c * 8;
@@ -828,8 +830,8 @@ enum class Tile { T256x256, T128x256, T128x256K2, T128x128, Skinny };
 // spread evenly over the 256 CUs (measured on the workload shapes: the
 // 256x256 tile needs at least two tiles per CU; the 128x128 tile wins when
 // it gives three per CU; with at most one 128x256 tile per CU the K loop is
-// split over two wave groups so each SIMD still holds two waves; grouped
-// problems, whose masked tiles exit at once, do best with plain 128x256).
+// split over two wave groups so each SIMD still holds two waves).
+
 static Tile pick_tile(int64_t m, int64_t n, int64_t k, int64_t E) {
     auto tiles = [&](int64_t bm, int64_t bn) { return E * ((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
     const bool even_steps = ((k + 127) / 128) % 2 == 0;

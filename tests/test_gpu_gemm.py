@@ -245,6 +245,17 @@ def test_grouped_masked_small(ops, mask):
     grouped_case(ops, 4, 256, 96, 128, mask, seed=sum(mask))
 
 
+@pytest.mark.parametrize("n,h,mask", [
+    (5000, 400, [0, 1, 129, 255, 256, 300, 512, 7]),   # ragged N, K % 128 != 0
+    (5120, 512, [512, 384, 100, 0, 64, 65, 511, 200]),
+])
+def test_grouped_masked_eight_experts(ops, n, h, mask):
+    """Eight experts of 512 rows (the routed-expert launch, 128 x 256 tiles),
+    masks from 0 to full: every valid row of every expert against the oracle,
+    masked rows untouched."""
+    grouped_case(ops, 8, 512, n, h, mask, seed=n + h)
+
+
 @pytest.mark.parametrize("mask", [[0, 17, 48], [48, 48, 5]])
 def test_grouped_masked_few_rows(ops, mask):
     """m <= 64 per expert: the skinny kernel, masks inside and at the edge."""
