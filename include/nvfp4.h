@@ -147,6 +147,25 @@ int nvfp4_quantize_ws(const void *x, int x_dtype, int64_t m, int64_t k,
                       void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
+ * nvfp4_quantize_ws without the workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the DYNAMIC mode's partial maxima go to
+ * a static device array inside the library (NVFP4_QUANTIZE_WS_BYTES = 4 KiB
+ * per GPU, held until the process ends; it holds the at most 1024 partials
+ * of any call, so no size is refused for it).  Its address is looked up on
+ * the first DYNAMIC call on each device, with that device current -- the
+ * one piece of host state the library keeps.  The call allocates nothing.
+ * Calls that overlap on one GPU (other streams, other threads) share the
+ * array and race; serialise them.  Arguments, bytes written and errors are
+ * those of nvfp4_quantize_ws (without the workspace checks);
+ * NVFP4_LAUNCH_FAILED also when the array's address cannot be obtained.
+ */
+int nvfp4_quantize_noalloc(const void *x, int x_dtype, int64_t m, int64_t k,
+                           const void *pre_quant_scale, float *global_scale, int gs_mode,
+                           const float *gs_other, float *alpha,
+                           uint8_t *out_fp4, uint8_t *out_sf, void *stream);
+
+/*
  * Smooth quantization with the SVDQuant LoRA-down projection fused
  * (flashinfer docs, flashinfer.gemm.mm_nvfp4_svdquant: parameter a is x with
  * pre_quant_scale folded into its quantization, and d = x @ (pqs[:, None] *

@@ -39,9 +39,9 @@ bool gemm_sf_ok(int64_t rows, int64_t nblk) {
 
 extern "C" {
 
-static int quantize_common(const void* x, int x_dtype, int64_t m, int64_t k, const void* pre_quant_scale,
-                           float* global_scale, int gs_mode, const float* gs_other, float* alpha,
-                           uint8_t* out_fp4, uint8_t* out_sf, float* ws, void* stream) {
+static int quantize_check(const void* x, int x_dtype, int64_t m, int64_t k, const void* pre_quant_scale,
+                          float* global_scale, int gs_mode, const float* gs_other, float* alpha,
+                          uint8_t* out_fp4, uint8_t* out_sf) {
     if (!x || !global_scale || !out_fp4 || !out_sf) return NVFP4_NULL_POINTER;
     if (x_dtype != NVFP4_BF16 && x_dtype != NVFP4_F32) return NVFP4_BAD_DTYPE;
     if (gs_mode != NVFP4_GS_STATIC && gs_mode != NVFP4_GS_DYNAMIC) return NVFP4_UNSUPPORTED;
@@ -50,6 +50,13 @@ static int quantize_common(const void* x, int x_dtype, int64_t m, int64_t k, con
         (pre_quant_scale && !aligned16(pre_quant_scale)) || ((uintptr_t)global_scale & 3u) ||
         ((uintptr_t)gs_other & 3u) || ((uintptr_t)alpha & 3u))
         return NVFP4_MISALIGNED;
+    return NVFP4_OK;
+}
+
+// Arguments already checked by quantize_check.
+static int quantize_launch(const void* x, int x_dtype, int64_t m, int64_t k, const void* pre_quant_scale,
+                           float* global_scale, int gs_mode, const float* gs_other, float* alpha,
+                           uint8_t* out_fp4, uint8_t* out_sf, float* ws, void* stream) {
     nvfp4::QuantizeArgs a{};
     a.x = x; a.x_dtype = x_dtype; a.pqs = pre_quant_scale; a.mask = nullptr;
     a.gs = global_scale; a.out_fp4 = out_fp4; a.out_sf = out_sf;
@@ -57,6 +64,16 @@ static int quantize_common(const void* x, int x_dtype, int64_t m, int64_t k, con
     a.gs_other = gs_other; a.alpha_out = alpha;
     a.ws = a.dynamic ? ws : nullptr;
     return launch_status(nvfp4::launch_quantize(a, (hipStream_t)stream));
+}
+
+static int quantize_common(const void* x, int x_dtype, int64_t m, int64_t k, const void* pre_quant_scale,
+                           float* global_scale, int gs_mode, const float* gs_other, float* alpha,
+                           uint8_t* out_fp4, uint8_t* out_sf, float* ws, void* stream) {
+    const int st = quantize_check(x, x_dtype, m, k, pre_quant_scale, global_scale, gs_mode, gs_other, alpha,
+                                  out_fp4, out_sf);
+    if (st != NVFP4_OK) return st;
+    return quantize_launch(x, x_dtype, m, k, pre_quant_scale, global_scale, gs_mode, gs_other, alpha, out_fp4,
+                           out_sf, ws, stream);
 }
 
 int nvfp4_quantize(const void* x, int x_dtype, int64_t m, int64_t k, const void* pre_quant_scale,
@@ -87,6 +104,21 @@ int nvfp4_quantize_ws(const void* x, int x_dtype, int64_t m, int64_t k, const vo
     static_assert(NVFP4_QUANTIZE_WS_BYTES >= nvfp4::kQuantizeWsFloats * 4, "workspace holds the partials");
     return quantize_common(x, x_dtype, m, k, pre_quant_scale, global_scale, gs_mode, gs_other, alpha,
                            out_fp4, out_sf, (float*)workspace, stream);
+}
+
+int nvfp4_quantize_noalloc(const void* x, int x_dtype, int64_t m, int64_t k, const void* pre_quant_scale,
+                           float* global_scale, int gs_mode, const float* gs_other, float* alpha,
+                           uint8_t* out_fp4, uint8_t* out_sf, void* stream) {
+    if (!gs_other != !alpha) return NVFP4_NULL_POINTER;
+    // every argument is checked before the device is touched (symbol lookup)
+    const int st = quantize_check(x, x_dtype, m, k, pre_quant_scale, global_scale, gs_mode, gs_other, alpha,
+                                  out_fp4, out_sf);
+    if (st != NVFP4_OK) return st;
+    float* ws = nullptr;
+    if (gs_mode == NVFP4_GS_DYNAMIC && nvfp4::scratch_for_current_device(&ws) != hipSuccess)
+        return NVFP4_LAUNCH_FAILED;
+    return quantize_launch(x, x_dtype, m, k, pre_quant_scale, global_scale, gs_mode, gs_other, alpha, out_fp4,
+                           out_sf, ws, stream);
 }
 
 int nvfp4_quantize_lora_down(const void* x, int64_t m, int64_t k, const void* pre_quant_scale,

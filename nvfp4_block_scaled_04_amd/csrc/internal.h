@@ -29,6 +29,10 @@ struct QuantizeArgs {
 constexpr int kQuantizeWsFloats = 1024;
 
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t st);
+// Device address of the library's static scratch array for the partial
+// maxima (kQuantizeWsFloats floats) on the current device, looked up on the
+// first call per device.
+hipError_t scratch_for_current_device(float** ptr);
 // Smooth quantize of a bf16 [m, k] (a.pqs set, a.b = 1) with the LoRA-down
 // projection d = bf16((x * pqs) @ l2^T), l2 bf16 [rank, k]; rank in
 // {32, 64, 96, 128}, k <= 4096.

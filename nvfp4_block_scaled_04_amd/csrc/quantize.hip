@@ -36,6 +36,8 @@
 //     (three launches).
 // No atomics and no device-wide fences are involved: the kernel boundaries
 // order every step.
+#include <mutex>
+
 #include "device_common.h"
 #include "internal.h"
 #include "quant_block.h"
@@ -764,6 +766,38 @@ hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t st) {
     }
     if (a.pqs) return launch_variant<V_F32_SMOOTH>(p, dyn, ws, st);
     return launch_variant<V_F32>(p, dyn, ws, st);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free DYNAMIC quantization: the partial maxima that
+// nvfp4_quantize_ws keeps in a caller workspace live in this file-scope
+// device array instead, one copy per GPU, held until the process ends.  Its
+// device address is looked up once per device (first call with that device
+// current) and only that address is handed to kernels.  Every partial is
+// written by the amax pass before the quantize pass reads it, so nothing
+// needs clearing; calls that overlap on one GPU share the array and race.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) float scratch[kQuantizeWsFloats];
+
+constexpr int kMaxDevices = 64;
+static float* g_scratch_ptr[kMaxDevices];
+static hipError_t g_scratch_err[kMaxDevices];
+static std::once_flag g_scratch_once[kMaxDevices];
+
+hipError_t scratch_for_current_device(float** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = (float*)p;
+    });
+    if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+    if (!g_scratch_ptr[dev]) return hipErrorInvalidSymbol;
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_alpha(const float* ga, const float* gb, float* alpha, int64_t n, hipStream_t st) {

@@ -18,6 +18,7 @@ EXPORTS = (
     "nvfp4_quantize",
     "nvfp4_quantize_alpha",
     "nvfp4_quantize_ws",
+    "nvfp4_quantize_noalloc",
     "nvfp4_quantize_lora_down",
     "nvfp4_quantize_masked_batched",
     "silu_mul_nvfp4_quantize",
@@ -51,6 +52,7 @@ def _load():
         "nvfp4_quantize": [vp, i32, i64, i64, vp, vp, i32, vp, vp, vp],
         "nvfp4_quantize_alpha": [vp, i32, i64, i64, vp, vp, i32, vp, vp, vp, vp, vp],
         "nvfp4_quantize_ws": [vp, i32, i64, i64, vp, vp, i32, vp, vp, vp, vp, vp, i64, vp],
+        "nvfp4_quantize_noalloc": [vp, i32, i64, i64, vp, vp, i32, vp, vp, vp, vp, vp],
         "nvfp4_quantize_lora_down": [vp, i64, i64, vp, vp, i64, vp, i32, vp, vp, vp, vp],
         "nvfp4_quantize_masked_batched": [vp, i64, i64, i64, vp, vp, i32, vp, vp, vp],
         "silu_mul_nvfp4_quantize": [vp, i64, i64, i64, vp, vp, i32, vp, vp, vp],
@@ -236,6 +238,33 @@ def nvfp4_quantize_ws(x, workspace, global_scale=None, gs_mode=GS_DYNAMIC, pre_q
                                 _ptr(gs_other), _ptr(alpha), _ptr(out_fp4), _ptr(out_sf), _ptr(workspace),
                                 workspace.numel(), _stream(dev))
     _check(rc, "nvfp4_quantize_ws")
+    return out_fp4, out_sf, global_scale, alpha
+
+
+def nvfp4_quantize_noalloc(x, global_scale, gs_other=None, alpha=None, gs_mode=GS_DYNAMIC, pre_quant_scale=None,
+                           out_fp4=None, out_sf=None):
+    """nvfp4_quantize_ws with the library's static scratch array in place of
+    a workspace: every output must be given (nothing is allocated here).
+    Returns (fp4, sf, gs, alpha)."""
+    _dims(x, "x", 2)
+    m, k = x.shape
+    dt = {torch.bfloat16: 0, torch.float32: 1}.get(x.dtype)
+    if dt is None:
+        raise ValueError("x must be bf16 or fp32")
+    if out_fp4 is None or out_sf is None:
+        raise ValueError("nvfp4_quantize_noalloc allocates nothing: pass out_fp4 and out_sf")
+    if (gs_other is None) != (alpha is None):
+        raise ValueError("gs_other and alpha go together")
+    dev = x.device
+    _opt(pre_quant_scale, "pre_quant_scale", BF16, k, dev)
+    _dev(global_scale, "global_scale", F32, 1, dev)
+    _opt(gs_other, "gs_other", F32, 1, dev)
+    _opt(alpha, "alpha", F32, 1, dev)
+    _dev(out_fp4, "out_fp4", BYTES, m * (k // 2), dev)
+    _dev(out_sf, "out_sf", BYTES, sf_size(m, k), dev)
+    rc = _lib.nvfp4_quantize_noalloc(_ptr(x), dt, m, k, _ptr(pre_quant_scale), _ptr(global_scale), gs_mode,
+                                     _ptr(gs_other), _ptr(alpha), _ptr(out_fp4), _ptr(out_sf), _stream(dev))
+    _check(rc, "nvfp4_quantize_noalloc")
     return out_fp4, out_sf, global_scale, alpha
 
 

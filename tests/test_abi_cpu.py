@@ -36,7 +36,8 @@ def test_header_declares_the_entry_points():
         "nvfp4_alpha", "nvfp4_gemm", "nvfp4_gemm_grouped_masked",
         "nvfp4_gemm_grouped_masked_silu_quantize", "nvfp4_gemm_svdquant",
         "nvfp4_gemm_w4a16", "nvfp4_quantize_lora_down",
-        "nvfp4_quantize", "nvfp4_quantize_alpha", "nvfp4_quantize_ws", "nvfp4_quantize_masked_batched",
+        "nvfp4_quantize", "nvfp4_quantize_alpha", "nvfp4_quantize_ws", "nvfp4_quantize_noalloc",
+        "nvfp4_quantize_masked_batched",
         "silu_mul_nvfp4_quantize",
         "mxfp4_quantize", "mxfp4_gemm",
     ])
@@ -200,6 +201,25 @@ def test_quantize_ws_validation(lib):
     assert run(go=P + 2, al=P) == MISAL
 
 
+def test_quantize_noalloc_validation(lib):
+    """nvfp4_quantize's checks and the optional alpha pair, all refused before
+    the library touches the device (no symbol lookup on a refused call)."""
+    f = lib.nvfp4_quantize_noalloc
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    run = lambda x=P, dt=0, m=128, k=256, pqs=None, gs=P, mode=1, go=None, al=None, o=P, s=P: \
+        f(x, dt, m, k, pqs, gs, mode, go, al, o, s, None)
+    assert run(go=P) == NULLP
+    assert run(al=P) == NULLP
+    assert run(x=None) == NULLP
+    assert run(s=None) == NULLP
+    assert run(k=40) == SHAPE
+    assert run(m=0) == SHAPE
+    assert run(dt=2) == DTYPE
+    assert run(mode=2) == UNSUP
+
+
 def test_svdquant_rank_and_alignment(lib):
     f = lib.nvfp4_gemm_svdquant
 
@@ -318,3 +338,13 @@ def test_mx_validation(lib):
     assert rung(m=7, n=7, k=1 << 30) == UNSUP
     assert rung(m=7, n=7, k=1 << 29) == UNSUP        # 128 x 2^24 = 2^31 bytes: the first size refused
 
+
+
+def test_quantize_noalloc_alignment_refused(lib):
+    f = lib.nvfp4_quantize_noalloc
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    assert f(P + 8, 0, 128, 256, None, P, 1, None, None, P, P, None) == MISAL
+    assert f(P, 0, 128, 256, P + 4, P, 1, None, None, P, P, None) == MISAL
+    assert f(P, 0, 128, 256, None, P, 1, P + 2, P, P, P, None) == MISAL
