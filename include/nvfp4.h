@@ -178,8 +178,8 @@ int nvfp4_quantize_noalloc(const void *x, int x_dtype, int64_t m, int64_t k,
  *   weight, row-major); d: [m, r] bf16 (16-byte aligned, ready for
  *   nvfp4_gemm_svdquant).  The product x * pqs enters the projection as is
  *   (non-finite values propagate; only the quantization applies nan_to_num).
- * Requires r in {32, 64, 96, 128} (NVFP4_BAD_RANK otherwise), 16 <= k <=
- * 4096 (larger k: NVFP4_UNSUPPORTED), k % 16 == 0.  Device pointers owned by
+ * Requires r in {32, 64, 96, 128} (NVFP4_BAD_RANK otherwise), k >= 16,
+ * k % 16 == 0.  Device pointers owned by
  * the caller; nothing is allocated.
  */
 int nvfp4_quantize_lora_down(const void *x, int64_t m, int64_t k, const void *pre_quant_scale,

@@ -128,7 +128,6 @@ int nvfp4_quantize_lora_down(const void* x, int64_t m, int64_t k, const void* pr
     if (gs_mode != NVFP4_GS_STATIC && gs_mode != NVFP4_GS_DYNAMIC) return NVFP4_UNSUPPORTED;
     if (r <= 0 || r % 32 != 0 || r > 128) return NVFP4_BAD_RANK;
     if (k < 16 || k % 16 != 0 || !quant_sizes_ok(1, m, k)) return NVFP4_BAD_SHAPE;
-    if (k > 4096) return NVFP4_UNSUPPORTED;  // the workgroup's LDS copy of its rows holds 4096 columns
     if (!aligned16(x) || !aligned16(pre_quant_scale) || !aligned16(l2) || !aligned16(out_fp4) ||
         !aligned16(out_sf) || !aligned16(d) || ((uintptr_t)global_scale & 3u))
         return NVFP4_MISALIGNED;

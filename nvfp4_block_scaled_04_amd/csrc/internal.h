@@ -35,7 +35,7 @@ hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t st);
 hipError_t scratch_for_current_device(float** ptr);
 // Smooth quantize of a bf16 [m, k] (a.pqs set, a.b = 1) with the LoRA-down
 // projection d = bf16((x * pqs) @ l2^T), l2 bf16 [rank, k]; rank in
-// {32, 64, 96, 128}, k <= 4096.
+// {32, 64, 96, 128}, any k % 16 == 0.
 hipError_t launch_quantize_lora(const QuantizeArgs& a, const uint16_t* l2, uint16_t* d, int rank,
                                 hipStream_t st);
 hipError_t launch_alpha(const float* ga, const float* gb, float* alpha, int64_t n, hipStream_t st);

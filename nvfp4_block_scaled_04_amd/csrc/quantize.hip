@@ -446,151 +446,142 @@ __global__ __launch_bounds__(256) void k_quantize_fused(QParams p) {
 // Smooth quantize with the SVDQuant LoRA-down projection fused (flashinfer
 // mm_nvfp4_svdquant: a is the NVFP4 quantization of x * pqs, and d = x @
 // (pqs[:, None] * L2^T) is its rank-r projection): one read of x feeds both.
-// A workgroup of 16 waves owns 16 rows across the whole K.  Phase 1: each
-// thread takes one 16-element block per 256-column chunk of a row, for up
-// to four chunks (all its loads in flight before any use), quantizes them
-// exactly as the smooth pass does, and parks the raw bf16 rows in LDS.
-// Phase 2 runs v_mfma_f32_16x16x32_bf16 over K with x from LDS as the A
-// operand and l2 * pqs as the B operand, read through the caches (every
-// workgroup reads the same L2 and pqs) and split exactly into two bf16
-// halves: the product of two bf16 values has at most 16 significant bits,
-// its bf16 rounding hi takes the top 8 and the remainder lo = product - hi
-// at most 8 more, so x * hi + x * lo is x * l2 * pqs with every product
-// exact and only fp32 accumulation rounding.  The waves take interleaved
-// 32-column slices; their partial projections are added through LDS and
-// stored as bf16.
+// A workgroup of 16 waves owns a 16-row band and walks K in chunks of
+// kLoraChunk columns.  In a chunk, wave w holds row w of the band and lane l
+// its 16-element block l (two 16-byte loads; the wave reads 2 KB of the row
+// contiguously): the block is quantized with the smooth pass's arithmetic
+// and its raw bf16 values are parked in one of two LDS buffers.  After one
+// barrier each wave projects its 32-column slices of the chunk with
+// v_mfma_f32_16x16x32_bf16, x from LDS as the B operand and l2 * pqs as the
+// A operand, read through the caches (every workgroup reads the same L2 and
+// pqs) and split exactly into two bf16 halves: the product of two bf16
+// values has at most 16 significant bits, its bf16 rounding hi takes the top
+// 8 and the remainder lo = product - hi at most 8 more, so x * hi + x * lo
+// is x * l2 * pqs with every product exact and only fp32 accumulation
+// rounding.  The accumulators carry across chunks.  The next chunk's row
+// loads are issued before the current chunk is quantized, so HBM reads
+// overlap the arithmetic; the two LDS buffers alternate, so one barrier per
+// chunk orders parking and projection (a wave parks chunk c only after the
+// barrier of chunk c - 1, which every wave passes after projecting chunk
+// c - 2 from the same buffer).  At the end the waves' partial projections
+// are added through LDS and stored as bf16.  Any K with K % 16 == 0.
 // ---------------------------------------------------------------------------
 
-constexpr int kLoraMaxK = 4096;   // columns of the LDS copy
-constexpr int kLoraWaves = 16;
-constexpr int kLoraPerThread = kLoraMaxK / 256 / (kLoraWaves / 4);  // chunks per thread
+constexpr int kLoraChunk = 1024;  // columns per chunk (64 blocks: one per lane)
+constexpr int kLoraWaves = 16;    // = rows per band
 
 template <int RT>  // rank tiles of 16
 __global__ __launch_bounds__(64 * kLoraWaves) void k_quantize_lora(QParams p, const uint16_t* l2, uint16_t* d_out,
                                                                   int rank) {
-    constexpr int NT = 64 * kLoraWaves;
-    constexpr int PITCH = kLoraMaxK + 8;  // bf16 per LDS row (16 bytes of pad spread the banks)
-    constexpr int U = RT <= 4 ? 2 : 1;    // projection slices whose operands load together
-    static_assert((kLoraWaves - 1) * RT * 64 * 16 <= 16 * PITCH * 2, "partial sums fit in the LDS copy");
+    constexpr int PITCH = kLoraChunk + 8;  // bf16 per LDS row (16 bytes of pad spread the banks)
+    constexpr int BUF = 16 * PITCH;        // bf16 per buffer
+    constexpr int SPW = kLoraChunk / 32 / kLoraWaves;  // projection slices per wave per chunk
+    // rank 32: the projection operands of the next chunk load with its rows;
+    // larger ranks load each slice's operands just before its MFMAs (the
+    // register file of a 16-wave workgroup holds no more)
+    constexpr bool PREFETCH = RT <= 2;
+    constexpr int PART = (kLoraWaves - 1) * RT * 64 * 8;  // bf16-sized slots of the waves' partial sums
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    __shared__ __align__(16) uint16_t xs[16 * PITCH];
+    __shared__ __align__(16) uint16_t xs[2 * BUF > PART ? 2 * BUF : PART];
     __shared__ float rtab[128];
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int64_t m0 = (int64_t)blockIdx.x * 16;
-    const int cg = __builtin_amdgcn_readfirstlane(t >> 8);  // chunk group: chunks cg, cg + 4, ...
-    const int rl = (t >> 4) & 15, bl = t & 15;             // row within the band, block within a chunk
-    const int64_t row = m0 + rl;
+    const int64_t row = m0 + wave;                 // this wave's row of the band
     const bool row_ok = row < p.m;
-    const int64_t rrow = row_ok ? row : p.m - 1;  // loads of rows past m read a valid row
+    const uint16_t* xrow = (const uint16_t*)p.x + (row_ok ? row : p.m - 1) * p.k_in;
     const int nbk = (int)(p.K / 16);
-    const int nchunk = (nbk + 15) / 16;
-    const int ks = (int)((p.K + 31) / 32) * 32;  // K rounded up to whole MFMA slices
-    const int nsl = ks / 32;
-    const int nmine = (nsl - wave + kLoraWaves - 1) / kLoraWaves;  // projection slices of this wave
+    const int nch = (int)((p.K + kLoraChunk - 1) / kLoraChunk);
     const int r16 = lane & 15, kg = lane >> 4;
     const float gs = p.gs[0];
     if (t < 128) {
         const float dec = ue4m3_decode((uint32_t)t);
         rtab[t] = dec == 0.0f ? 0.0f : gs / dec;
     }
-    // zero the LDS copy's columns past K up to the last whole slice
-    for (int i = t; i < 16 * (ks - (int)p.K); i += NT) {
-        const int rr = i / (ks - (int)p.K), cc = (int)p.K + i % (ks - (int)p.K);
-        xs[rr * PITCH + cc] = 0;
-    }
-    __syncthreads();
 
-    // projection operands (l2 rows and pqs) of U slices; past this wave's
-    // slices or past K: zeros
-    u32x4 bf[U][RT], pf[U];
-    auto load_group = [&](int g) {
+    // this lane's block of chunk c (past K: the last block, never stored)
+    auto load_rows = [&](int c, u32x4 (&raw)[2], u32x4 (&pq)[2]) {
+        int cb = c * 64 + lane;
+        cb = cb < nbk ? cb : nbk - 1;
+        const u32x4* src = (const u32x4*)(xrow + (int64_t)cb * 16);
+        raw[0] = src[0];
+        raw[1] = src[1];
+        load_pqs<V_BF16_SMOOTH>(p, (int64_t)cb * 16, pq);
+    };
+    // projection operands of this wave's slice j of chunk c: l2 rows and pqs
+    // at this lane's 8 columns; zeros past K
+    auto load_slice = [&](int c, int j, u32x4 (&b)[RT], u32x4& pv) {
+        const int64_t col = (int64_t)c * kLoraChunk + (wave + kLoraWaves * j) * 32 + kg * 8;
+        const bool ok = col < p.K;
 #pragma unroll
-        for (int u = 0; u < U; u++) {
-            const int col = (wave + kLoraWaves * (g + u)) * 32 + kg * 8;
-            const bool ok = g + u < nmine && col < p.K;
+        for (int i = 0; i < RT; i++)
+            b[i] = ok ? *(const u32x4*)(l2 + (int64_t)(i * 16 + r16) * p.K + col) : u32x4{0u, 0u, 0u, 0u};
+        pv = ok ? *(const u32x4*)(p.pqs + col) : u32x4{0u, 0u, 0u, 0u};
+    };
+    auto load_proj = [&](int c, u32x4 (&b)[PREFETCH ? SPW : 1][RT], u32x4 (&pv)[PREFETCH ? SPW : 1]) {
 #pragma unroll
-            for (int i = 0; i < RT; i++)
-                bf[u][i] = ok ? *(const u32x4*)(l2 + (int64_t)(i * 16 + r16) * p.K + col) : u32x4{0u, 0u, 0u, 0u};
-            pf[u] = ok ? *(const u32x4*)(p.pqs + col) : u32x4{0u, 0u, 0u, 0u};
-        }
+        for (int j = 0; j < SPW; j++) load_slice(c, j, b[j], pv[j]);
     };
 
-    // ---- phase 1: quantize, keep the raw rows in LDS
-    {
-        u32x4 raw[kLoraPerThread][2], pqb[kLoraPerThread][2];
-#pragma unroll
-        for (int i = 0; i < kLoraPerThread; i++) {  // every load in flight before any use
-            int cb = (cg + 4 * i) * 16 + bl;
-            cb = cb < nbk ? cb : nbk - 1;
-            const u32x4* src = (const u32x4*)((const uint16_t*)p.x + rrow * p.k_in + (int64_t)cb * 16);
-            raw[i][0] = src[0];
-            raw[i][1] = src[1];
-            load_pqs<V_BF16_SMOOTH>(p, (int64_t)cb * 16, pqb[i]);
-        }
-        load_group(0);  // the first projection operands, behind the rows
-        uint8_t* q = p.out_fp4;
-#pragma unroll
-        for (int i = 0; i < kLoraPerThread; i++) {
-            const int c = cg + 4 * i;
-            if (c >= nchunk) break;  // uniform in the wave
-            const int cb = c * 16 + bl;  // block column
-            const bool blk_ok = row_ok && cb < nbk;
-            float f[16];
-            const float bamax = process_block<V_BF16_SMOOTH>(raw[i], pqb[i], f);
-            const uint32_t sc = blk_ok ? ue4m3_encode(div6(bamax) * gs) : 0u;
-            const float r = rtab[sc];
-            uint32_t w0 = 0, w1 = 0;
-            w0 = NVFP4_PACK_FP4(w0, f[0] * r, f[1] * r, 0);
-            w0 = NVFP4_PACK_FP4(w0, f[2] * r, f[3] * r, 1);
-            w0 = NVFP4_PACK_FP4(w0, f[4] * r, f[5] * r, 2);
-            w0 = NVFP4_PACK_FP4(w0, f[6] * r, f[7] * r, 3);
-            w1 = NVFP4_PACK_FP4(w1, f[8] * r, f[9] * r, 0);
-            w1 = NVFP4_PACK_FP4(w1, f[10] * r, f[11] * r, 1);
-            w1 = NVFP4_PACK_FP4(w1, f[12] * r, f[13] * r, 2);
-            w1 = NVFP4_PACK_FP4(w1, f[14] * r, f[15] * r, 3);
-            if (blk_ok) *(uint2*)(q + row * (p.K / 2) + (int64_t)cb * 8) = uint2{w0, w1};
-            // the 4 scale bytes of a swizzle dword sit in 4 neighbouring lanes
-            uint32_t v = sc << (8 * (bl & 3));
-            v |= __shfl_xor(v, 1);
-            v |= __shfl_xor(v, 2);
-            if ((bl & 3) == 0 && cb < nbk)
-                *(uint32_t*)(p.out_sf + ((row >> 7) * p.nct + (cb >> 2)) * 512 + (row & 31) * 16 +
-                             ((row & 127) >> 5) * 4) = v;
-            // the projection's A operand: the raw rows (the plain product
-            // x * pqs enters the projection, no nan_to_num), 0 past m
-            if (cb < nbk) {
-                u32x4* dst = (u32x4*)(xs + rl * PITCH + cb * 16);
-                dst[0] = row_ok ? raw[i][0] : u32x4{0u, 0u, 0u, 0u};
-                dst[1] = row_ok ? raw[i][1] : u32x4{0u, 0u, 0u, 0u};
-            }
-        }
-    }
-    __syncthreads();
-
-    // ---- phase 2: d = x @ (l2 * pqs)^T over K
     f32x4 acc[RT];
 #pragma unroll
     for (int i = 0; i < RT; i++) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int g = 0; g < nmine; g += U) {
-        if (g > 0) load_group(g);
+    u32x4 raw[2], pqb[2], nraw[2], npqb[2];
+    u32x4 bf[PREFETCH ? SPW : 1][RT], pf[PREFETCH ? SPW : 1];
+    load_rows(0, raw, pqb);
+    if constexpr (PREFETCH) load_proj(0, bf, pf);
+    __syncthreads();  // rtab
+
+    uint8_t* const q = p.out_fp4;
+    for (int c = 0; c < nch; c++) {
+        uint16_t* const buf = xs + (c & 1) * BUF;
+        if (c + 1 < nch) load_rows(c + 1, nraw, npqb);  // in flight while this chunk is worked on
+
+        // ---- quantize this lane's block, park its raw values
+        const int cb = c * 64 + lane;  // block column
+        const bool in_k = cb < nbk;
+        const bool blk_ok = row_ok && in_k;
+        float f[16];
+        const float bamax = process_block<V_BF16_SMOOTH>(raw, pqb, f);
+        const uint32_t sc = blk_ok ? ue4m3_encode(div6(bamax) * gs) : 0u;
+        uint32_t w0, w1;
+        pack_block(f, rtab[sc], w0, w1);
+        if (blk_ok) *(uint2*)(q + row * (p.K / 2) + (int64_t)cb * 8) = uint2{w0, w1};
+        // the 4 scale bytes of a swizzle dword sit in 4 neighbouring lanes;
+        // rows past m (up to the padded 128) and blocks past K write 0
+        uint32_t v = sc << (8 * (lane & 3));
+        v |= __shfl_xor(v, 1);
+        v |= __shfl_xor(v, 2);
+        if ((lane & 3) == 0 && in_k)
+            *(uint32_t*)(p.out_sf + ((row >> 7) * p.nct + (cb >> 2)) * 512 + (row & 31) * 16 +
+                         ((row & 127) >> 5) * 4) = v;
+        // the projection's input is the raw row (x * pqs enters as is, no
+        // nan_to_num); rows past m and columns past K are 0
+        u32x4* dst = (u32x4*)(buf + wave * PITCH + lane * 16);
+        dst[0] = row_ok && in_k ? raw[0] : u32x4{0u, 0u, 0u, 0u};
+        dst[1] = row_ok && in_k ? raw[1] : u32x4{0u, 0u, 0u, 0u};
+        __syncthreads();
+
+        // ---- project this wave's slices of the chunk
 #pragma unroll
-        for (int u = 0; u < U; u++) {
-            if (g + u >= nmine) break;
-            const int col = (wave + kLoraWaves * (g + u)) * 32 + kg * 8;  // this lane's 8 columns of the slice
-            const bf16x8 afr = __builtin_bit_cast(bf16x8, *(const u32x4*)(xs + r16 * PITCH + col));
+        for (int j = 0; j < SPW; j++) {
+            const int sl = wave + kLoraWaves * j;
+            if ((int64_t)c * kLoraChunk + sl * 32 >= p.K) break;  // uniform in the wave
+            const int js = PREFETCH ? j : 0;
+            if constexpr (!PREFETCH) load_slice(c, j, bf[0], pf[0]);
+            const bf16x8 afr = __builtin_bit_cast(bf16x8, *(const u32x4*)(buf + r16 * PITCH + sl * 32 + kg * 8));
 #pragma unroll
             for (int i = 0; i < RT; i++) {
                 uint32_t hi[4], lo[4];
 #pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const f32x2 prod = {bf16_lo(bf[u][i][j]) * bf16_lo(pf[u][j]),
-                                        bf16_hi(bf[u][i][j]) * bf16_hi(pf[u][j])};
+                for (int jj = 0; jj < 4; jj++) {
+                    const f32x2 prod = {bf16_lo(bf[js][i][jj]) * bf16_lo(pf[js][jj]),
+                                        bf16_hi(bf[js][i][jj]) * bf16_hi(pf[js][jj])};
                     const bf16x2 h = __builtin_convertvector(prod, bf16x2);
                     const f32x2 rest = {prod[0] - (float)h[0], prod[1] - (float)h[1]};
-                    hi[j] = __builtin_bit_cast(uint32_t, h);
-                    lo[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rest, bf16x2));
+                    hi[jj] = __builtin_bit_cast(uint32_t, h);
+                    lo[jj] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rest, bf16x2));
                 }
                 acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                     __builtin_bit_cast(bf16x8, u32x4{hi[0], hi[1], hi[2], hi[3]}), afr, acc[i], 0, 0, 0);
@@ -598,8 +589,13 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_quantize_lora(QParams p, co
                     __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], lo[2], lo[3]}), afr, acc[i], 0, 0, 0);
             }
         }
+        if constexpr (PREFETCH) {
+            if (c + 1 < nch) load_proj(c + 1, bf, pf);
+        }
+        raw[0] = nraw[0]; raw[1] = nraw[1];
+        pqb[0] = npqb[0]; pqb[1] = npqb[1];
     }
-    __syncthreads();  // the LDS copy is free: it now holds the waves' partial sums
+    __syncthreads();  // the LDS is free: it now holds the waves' partial sums
     f32x4* const part = (f32x4*)xs;
     if (wave > 0)
 #pragma unroll

@@ -264,7 +264,7 @@ def test_lora_down_validation(lib):
     assert run(r=16) == RANK
     assert run(r=160) == RANK
     assert run(k=40) == SHAPE
-    assert run(k=4112) == UNSUP
+    assert run(k=4112, d=P + 8) == MISAL   # any K % 16 == 0 is accepted (here refused for d's alignment)
     assert run(mode=7) == UNSUP
     assert run(l2=P + 8) == MISAL
     assert run(d=P + 8) == MISAL

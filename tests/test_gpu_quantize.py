@@ -128,7 +128,10 @@ def test_repeat_is_identical(ops):
 
 
 @pytest.mark.parametrize("m,k,r,dynamic", [(4096, 3072, 32, False), (100, 400, 64, True), (17, 272, 32, True),
-                                          (300, 4096, 128, True), (130, 96, 96, False)])
+                                          (300, 4096, 128, True), (130, 96, 96, False),
+                                          (200, 8192, 32, True),     # K past the old 4096 limit: 8 chunks
+                                          (130, 5136, 64, False),    # 5 chunks and one block
+                                          (64, 1024, 96, True), (40, 1040, 128, False)])
 def test_quantize_lora_down(ops, m, k, r, dynamic):
     """Smooth quantize with the LoRA-down projection fused: the FP4 and scale
     bytes and gs must equal the oracle's smooth quantization exactly, and
