@@ -240,7 +240,9 @@ def build_workload(name, ops, synth, torch):
         alpha = ops.nvfp4_alpha(gsa, gsw)
         al = float(alpha.item())
         l2 = s.l2.to(torch.bfloat16).to(dev)
-        l1 = synth.lora_up(s, al).to(dev)
+        # the caller's LoRA-up weight with 1/alpha folded in (the fused
+        # epilogue's alpha * acc restores the unscaled term)
+        l1 = (s.l1_raw / al).to(torch.bfloat16).to(dev)
         bias = s.bias.to(dev)
         fa = torch.empty(m, k // 2, dtype=torch.uint8, device=dev)
         sfa = torch.empty(sf_size(m, k), dtype=torch.uint8, device=dev)
@@ -430,31 +432,31 @@ def cpu_baseline_dense(O, np, a_cpu, w_cpu, synth, target_s=12.0):
 # (--copy-calibration: fetch x2.000, write x1.000).  A record is used only
 # while the kernel sources hash to the value it was measured on.
 MEASURED_TRAFFIC = {
-    "prefill": {"sources_sha256": "4c38f76689a21cab5a4420095a8271d49a34bdd6848c6b134907006c5cc32195"
-                                  "faf55d4cd243fe2a127d65280e8b95f55a1c37a38f9c6433dcc115ee1fe0f350"
-                                  "b78954052145e2babdd6f327935f70bab87bfb0bca4c38bc415b04c1fd7708b1"
-                                  "1286af577a92b62864a1892dab16fdf95f9c00e73cc4786fcdc44f6510096e56",
-                "fetch_kib": 276691.5, "write_kib": 262144.0, "fetch_factor": 2.0, "write_factor": 1.0},
-    "moe": {"sources_sha256": "4c38f76689a21cab5a4420095a8271d49a34bdd6848c6b134907006c5cc32195"
-                              "faf55d4cd243fe2a127d65280e8b95f55a1c37a38f9c6433dcc115ee1fe0f350"
-                              "b78954052145e2babdd6f327935f70bab87bfb0bca4c38bc415b04c1fd7708b1"
-                              "1286af577a92b62864a1892dab16fdf95f9c00e73cc4786fcdc44f6510096e56",
-            "fetch_kib": 158206.1, "write_kib": 15350.0, "fetch_factor": 2.0, "write_factor": 1.0},
-    "dense": {"sources_sha256": "4c38f76689a21cab5a4420095a8271d49a34bdd6848c6b134907006c5cc32195"
-                                "faf55d4cd243fe2a127d65280e8b95f55a1c37a38f9c6433dcc115ee1fe0f350"
-                                "b78954052145e2babdd6f327935f70bab87bfb0bca4c38bc415b04c1fd7708b1"
-                                "1286af577a92b62864a1892dab16fdf95f9c00e73cc4786fcdc44f6510096e56",
-              "fetch_kib": 18638.0, "write_kib": 16384.0, "fetch_factor": 2.0, "write_factor": 1.0},
-    "svdquant": {"sources_sha256": "4c38f76689a21cab5a4420095a8271d49a34bdd6848c6b134907006c5cc32195"
-                                   "faf55d4cd243fe2a127d65280e8b95f55a1c37a38f9c6433dcc115ee1fe0f350"
-                                   "b78954052145e2babdd6f327935f70bab87bfb0bca4c38bc415b04c1fd7708b1"
-                                   "1286af577a92b62864a1892dab16fdf95f9c00e73cc4786fcdc44f6510096e56",
-                 "fetch_kib": 18474.0, "write_kib": 24576.0, "fetch_factor": 2.0, "write_factor": 1.0},
-    "decode": {"sources_sha256": "4c38f76689a21cab5a4420095a8271d49a34bdd6848c6b134907006c5cc32195"
-                                 "faf55d4cd243fe2a127d65280e8b95f55a1c37a38f9c6433dcc115ee1fe0f350"
-                                 "b78954052145e2babdd6f327935f70bab87bfb0bca4c38bc415b04c1fd7708b1"
-                                 "1286af577a92b62864a1892dab16fdf95f9c00e73cc4786fcdc44f6510096e56",
-               "fetch_kib": 6404.0, "write_kib": 128.0, "fetch_factor": 2.0, "write_factor": 1.0},
+    "prefill": {"sources_sha256": "f592982e2f6204edb2e64390275773ab557c99dfa26fe36df48824f7b6a9e1b9"
+                          "faf55d4cd243fe2a127d65280e8b95f55a1c37a38f9c6433dcc115ee1fe0f350"
+                          "0b8ab37c346d4290d1fdb25793ffb74b674eb91941278aed19a6fa7e4e266b6a"
+                          "1286af577a92b62864a1892dab16fdf95f9c00e73cc4786fcdc44f6510096e56",
+             "fetch_kib": 276681.2, "write_kib": 262144.0, "fetch_factor": 2.0, "write_factor": 1.0},
+    "moe": {"sources_sha256": "f592982e2f6204edb2e64390275773ab557c99dfa26fe36df48824f7b6a9e1b9"
+                          "faf55d4cd243fe2a127d65280e8b95f55a1c37a38f9c6433dcc115ee1fe0f350"
+                          "0b8ab37c346d4290d1fdb25793ffb74b674eb91941278aed19a6fa7e4e266b6a"
+                          "1286af577a92b62864a1892dab16fdf95f9c00e73cc4786fcdc44f6510096e56",
+             "fetch_kib": 158099.0, "write_kib": 15350.0, "fetch_factor": 2.0, "write_factor": 1.0},
+    "dense": {"sources_sha256": "f592982e2f6204edb2e64390275773ab557c99dfa26fe36df48824f7b6a9e1b9"
+                          "faf55d4cd243fe2a127d65280e8b95f55a1c37a38f9c6433dcc115ee1fe0f350"
+                          "0b8ab37c346d4290d1fdb25793ffb74b674eb91941278aed19a6fa7e4e266b6a"
+                          "1286af577a92b62864a1892dab16fdf95f9c00e73cc4786fcdc44f6510096e56",
+             "fetch_kib": 18638.4, "write_kib": 16384.0, "fetch_factor": 2.0, "write_factor": 1.0},
+    "svdquant": {"sources_sha256": "f592982e2f6204edb2e64390275773ab557c99dfa26fe36df48824f7b6a9e1b9"
+                          "faf55d4cd243fe2a127d65280e8b95f55a1c37a38f9c6433dcc115ee1fe0f350"
+                          "0b8ab37c346d4290d1fdb25793ffb74b674eb91941278aed19a6fa7e4e266b6a"
+                          "1286af577a92b62864a1892dab16fdf95f9c00e73cc4786fcdc44f6510096e56",
+             "fetch_kib": 18513.0, "write_kib": 24576.0, "fetch_factor": 2.0, "write_factor": 1.0},
+    "decode": {"sources_sha256": "f592982e2f6204edb2e64390275773ab557c99dfa26fe36df48824f7b6a9e1b9"
+                          "faf55d4cd243fe2a127d65280e8b95f55a1c37a38f9c6433dcc115ee1fe0f350"
+                          "0b8ab37c346d4290d1fdb25793ffb74b674eb91941278aed19a6fa7e4e266b6a"
+                          "1286af577a92b62864a1892dab16fdf95f9c00e73cc4786fcdc44f6510096e56",
+             "fetch_kib": 6404.7, "write_kib": 128.0, "fetch_factor": 2.0, "write_factor": 1.0},
 }
 GEMM_SOURCES = ("nvfp4_block_scaled_04_amd/csrc/gemm.hip", "nvfp4_block_scaled_04_amd/csrc/gemm_common.h",
                 "nvfp4_block_scaled_04_amd/csrc/device_common.h", "nvfp4_block_scaled_04_amd/csrc/quant_block.h")

@@ -165,19 +165,6 @@ def svdquant(seed=0, m=4096, n=3072, k=3072, r=32):
     return SVDQ(_bf16(x), _bf16(pqs), _bf16(w), l2, l1_raw, _bf16(bias), m, n, k, r)
 
 
-def lora_down(s: SVDQ):
-    """d = bf16((x * pqs) @ L2^T): the LoRA-down projection that the caller
-    forms before the fused GEMM (plain torch CPU fp32 matmul, then bf16)."""
-    xs = s.x.float() * s.pqs.float()
-    return _bf16(xs @ s.l2.t())
-
-
-def lora_up(s: SVDQ, alpha):
-    """l1 = bf16(l1_raw / alpha): the caller folds 1/alpha into the LoRA-up
-    weight so the fused epilogue alpha*acc restores the unscaled term."""
-    return _bf16(s.l1_raw / float(alpha))
-
-
 def bits(t: torch.Tensor):
     """numpy view of a CPU tensor's raw bits (bf16 -> uint16, fp32 -> float32)."""
     t = t.contiguous()

@@ -67,3 +67,15 @@ def tile_rows(m, bm, per_tile, seed):
         k = min(len(inner), per_tile - 2)
         rows += [t0, t1 - 1] + (rng.choice(inner, k, replace=False).tolist() if k > 0 else [])
     return np.array(sorted(set(rows)))
+
+
+def svdquant_lora_pieces(s, alpha):
+    """The caller-side pieces of the SVDQuant GEMM for a synth.svdquant()
+    draw (flashinfer mm_nvfp4_svdquant puts them on the caller):
+    d = bf16((x * pqs) @ L2^T), the LoRA-down output (plain torch CPU fp32
+    matmul, then bf16), and l1 = bf16(l1_raw / alpha), the LoRA-up weight
+    with 1/alpha folded in so that the epilogue's alpha * acc restores it."""
+    xs = s.x.float() * s.pqs.float()
+    d = (xs @ s.l2.t()).to(torch.bfloat16)
+    l1 = (s.l1_raw / float(alpha)).to(torch.bfloat16)
+    return d, l1

@@ -20,7 +20,8 @@ import torch
 
 import oracle as O
 from nvfp4_block_scaled_04_amd import synth
-from gpu_util import OUT_CANARY, assert_all_written, dev, np_bits, row_tolerance_check, say, tile_rows
+from gpu_util import (OUT_CANARY, assert_all_written, dev, np_bits, row_tolerance_check, say,
+                      svdquant_lora_pieces, tile_rows)
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-2
@@ -151,8 +152,7 @@ def test_svdquant_workload(ops):
     qa, sa, ga = oq(s.x, prologue=O.PRO_SMOOTH, pqs=np_bits(s.pqs))
     qb, sb, gb = oq(s.w)
     alpha = np.float32(1.0) / (ga[0] * gb[0])
-    d = synth.lora_down(s)
-    l1 = synth.lora_up(s, alpha)
+    d, l1 = svdquant_lora_pieces(s, alpha)
     out_bits = torch.full((s.m, s.n), OUT_CANARY, dtype=torch.int16, device="cuda")
     out = out_bits.view(torch.bfloat16)
     ops.nvfp4_gemm_svdquant(t_u8(qa), t_u8(qb), t_u8(sa), t_u8(sb),
