@@ -81,6 +81,7 @@ def _rotation(nbytes):
 
 def build_workload(name, ops, synth, torch):
     w = Workload()
+    w.gemm_kernel = "k_gemm (block-scaled NVFP4 GEMM)"
     w.hbm_bound = False
     w.w4a16 = None
     w.lora_down = None
@@ -190,6 +191,7 @@ def build_workload(name, ops, synth, torch):
         gsa = torch.zeros(E, dtype=torch.float32, device=dev)
         alpha = torch.empty(E, dtype=torch.float32, device=dev)
         out = torch.empty(E, m, n, dtype=torch.bfloat16, device=dev)
+        gws = ops.gemm_workspace(dev)   # partial tiles of the split-tail schedule
 
         def quant(x, mode=ops.GS_DYNAMIC):
             ops.silu_mul_nvfp4_quantize(x, mask, gsa, mode, out_fp4=fa, out_sf=sfa)
@@ -207,16 +209,19 @@ def build_workload(name, ops, synth, torch):
                     ops.nvfp4_alpha(o[2], gsw, out=o[3])
 
                 def gemm(o=o):
-                    ops.nvfp4_gemm_grouped_masked(o[0], fw, o[1], sfw, o[3], mask, out=out)
+                    ops.nvfp4_gemm_grouped_masked(o[0], fw, o[1], sfw, o[3], mask, out=out, workspace=gws)
                 steps.append((pre, gemm))
             return steps
 
         w.desc = ("Llama4-style routed experts: E=8 gate|up [512,16384] bf16, valid rows "
-                  f"{mo.mask.tolist()} -> fused silu_and_mul + NVFP4 quantize -> grouped masked GEMM vs [8,5120,8192]")
+                  f"{mo.mask.tolist()} -> fused silu_and_mul + NVFP4 quantize -> grouped masked GEMM vs [8,5120,8192] "
+                  "(split-tail schedule with a workspace)")
         w.rotate_hint = _rotation(mo.x.numel() * 2)
         w.make_acts = lambda n_copies: [mo.x.to(dev) for _ in range(n_copies)]
         w.make_steps, w.quant = make_steps, quant
-        w.gemm0 = lambda: ops.nvfp4_gemm_grouped_masked(fa, fw, sfa, sfw, alpha, mask, out=out)
+        w.gemm0 = lambda: ops.nvfp4_gemm_grouped_masked(fa, fw, sfa, sfw, alpha, mask, out=out, workspace=gws)
+        w.gemm_kernel = ("k_gemm split-tail schedule + k_gemm_fixup (block-scaled NVFP4 grouped GEMM; the two "
+                         "launches together)")
         w.n_wcopies = 1
         w.flops = 2.0 * n * h * valid
         w.q_bytes = valid * 2 * h * 2 + E * m * h // 2 + E * sf_size(m, h)
@@ -749,7 +754,7 @@ def main():
         "quantize": quant,
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / MFMA_F16_PEAK_TFLOPS, 4),
-                     "traffic": gemm_traffic(args.workload), "kernel": "k_gemm (block-scaled NVFP4 GEMM)",
+                     "traffic": gemm_traffic(args.workload), "kernel": w.gemm_kernel,
                      "flops_per_launch": w.flops, "algorithmic_bytes_per_launch": w.gemm_bytes},
         "timing": ("one timed region: the K steps' quantizations as one HIP graph, then their K GEMMs as "
                    "another, between HIP events on the kernels' stream, caches flushed first; ms_per_step, "

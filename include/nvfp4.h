@@ -41,6 +41,8 @@
  *     region as scratch for partial maxima before it writes the scales
  *     (nvfp4_quantize_ws takes a workspace for them instead); out_sf and
  *     global_scale hold their final values when the call's work completes.
+ *   - The *_ws GEMM calls take a caller-owned workspace for the partial sums
+ *     of a split-tail schedule.
  */
 #ifndef NVFP4_AMD_H
 #define NVFP4_AMD_H
@@ -285,6 +287,41 @@ int nvfp4_gemm_svdquant(const uint8_t *a, const uint8_t *b, const uint8_t *a_sf,
                         const uint8_t *b_sf, const float *alpha, const void *d, const void *l1,
                         const void *bias, void *out, int64_t m, int64_t n, int64_t k, int64_t r,
                         void *stream);
+
+/*
+ * nvfp4_gemm, nvfp4_gemm_grouped_masked and nvfp4_gemm_svdquant with a
+ * workspace for a split-tail schedule: when the output tiles do not divide
+ * evenly over the CUs, the last tiles' K loops are split over all CUs and
+ * their fp32 partial sums pass through the workspace (a second launch adds
+ * them in a fixed order, so results are deterministic).  The results equal
+ * the plain calls' up to the order of the fp32 accumulation (the sums of
+ * split tiles are formed in a different order); every bar that holds for
+ * the plain calls holds for these.  Without a workspace (NULL) the calls
+ * behave as the plain ones.
+ *   workspace: NULL, or a device buffer of workspace_bytes >=
+ *              NVFP4_GEMM_WS_BYTES (32 MiB: one fp32 128x256 partial tile
+ *              for each of up to 256 CUs), 16-byte aligned, owned by the
+ *              caller; its contents on entry are ignored and on exit
+ *              undefined.  Calls sharing a workspace must not overlap (same
+ *              stream, or ordered by events).
+ * Every other argument, the bytes written and the errors are those of the
+ * plain call; NVFP4_BAD_SHAPE also for workspace_bytes below
+ * NVFP4_GEMM_WS_BYTES and NVFP4_MISALIGNED for a workspace not 16-byte
+ * aligned.
+ */
+#define NVFP4_GEMM_WS_BYTES 33554432
+int nvfp4_gemm_ws(const uint8_t *a, const uint8_t *b, const uint8_t *a_sf, const uint8_t *b_sf,
+                  const float *alpha, const void *bias, void *out,
+                  int64_t m, int64_t n, int64_t k, void *workspace, int64_t workspace_bytes,
+                  void *stream);
+int nvfp4_gemm_grouped_masked_ws(const uint8_t *a, const uint8_t *b, const uint8_t *a_sf,
+                                 const uint8_t *b_sf, const float *alpha, const int32_t *mask,
+                                 void *out, int64_t E, int64_t m, int64_t n, int64_t k,
+                                 void *workspace, int64_t workspace_bytes, void *stream);
+int nvfp4_gemm_svdquant_ws(const uint8_t *a, const uint8_t *b, const uint8_t *a_sf,
+                           const uint8_t *b_sf, const float *alpha, const void *d, const void *l1,
+                           const void *bias, void *out, int64_t m, int64_t n, int64_t k, int64_t r,
+                           void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
  * Weight-only GEMM (NVIDIA/Fuser PR #5737: f16a_nvfp4weight_scaled_mm, whose

@@ -172,10 +172,12 @@ int silu_mul_nvfp4_quantize(const void* x, int64_t b, int64_t m, int64_t k2, con
     return launch_status(nvfp4::launch_quantize(a, (hipStream_t)stream));
 }
 
+static_assert(NVFP4_GEMM_WS_BYTES == nvfp4::kGemmWsBytes, "GEMM workspace size");
+
 static int gemm_common(const uint8_t* a, const uint8_t* b, const uint8_t* a_sf, const uint8_t* b_sf,
                        const float* alpha, const int32_t* mask, const void* bias, const void* d,
                        const void* l1, void* out, int64_t E, int64_t m, int64_t n, int64_t k,
-                       int64_t r, void* stream) {
+                       int64_t r, void* ws, int64_t ws_bytes, void* stream) {
     if (!a || !b || !a_sf || !b_sf || !alpha || !out) return NVFP4_NULL_POINTER;
     if (!dim_ok(E) || !dim_ok(m) || !dim_ok(n) || k < 16 || k % 16 != 0 || k > kMaxDim)
         return NVFP4_BAD_SHAPE;
@@ -187,10 +189,13 @@ static int gemm_common(const uint8_t* a, const uint8_t* b, const uint8_t* a_sf, 
         ((uintptr_t)alpha & 3u) || (bias && !aligned16(bias)) || (d && !aligned16(d)) ||
         (l1 && !aligned16(l1)) || ((uintptr_t)mask & 3u))
         return NVFP4_MISALIGNED;
+    if (ws && ws_bytes < NVFP4_GEMM_WS_BYTES) return NVFP4_BAD_SHAPE;
+    if (ws && !aligned16(ws)) return NVFP4_MISALIGNED;
     nvfp4::GemmArgs g{};
     g.a = a; g.b = b; g.a_sf = a_sf; g.b_sf = b_sf; g.alpha = alpha; g.mask = mask;
     g.bias = (const uint16_t*)bias; g.d = (const uint16_t*)d; g.l1 = (const uint16_t*)l1;
     g.out = (uint16_t*)out; g.E = E; g.m = m; g.n = n; g.k = k; g.r = r;
+    g.ws = (float*)ws;
     return launch_status(nvfp4::launch_gemm(g, (hipStream_t)stream));
 }
 
@@ -198,7 +203,14 @@ int nvfp4_gemm(const uint8_t* a, const uint8_t* b, const uint8_t* a_sf, const ui
                const float* alpha, const void* bias, void* out, int64_t m, int64_t n, int64_t k,
                void* stream) {
     return gemm_common(a, b, a_sf, b_sf, alpha, nullptr, bias, nullptr, nullptr, out, 1, m, n, k, 0,
-                       stream);
+                       nullptr, 0, stream);
+}
+
+int nvfp4_gemm_ws(const uint8_t* a, const uint8_t* b, const uint8_t* a_sf, const uint8_t* b_sf,
+                  const float* alpha, const void* bias, void* out, int64_t m, int64_t n, int64_t k,
+                  void* workspace, int64_t workspace_bytes, void* stream) {
+    return gemm_common(a, b, a_sf, b_sf, alpha, nullptr, bias, nullptr, nullptr, out, 1, m, n, k, 0,
+                       workspace, workspace_bytes, stream);
 }
 
 int nvfp4_gemm_grouped_masked(const uint8_t* a, const uint8_t* b, const uint8_t* a_sf,
@@ -206,7 +218,16 @@ int nvfp4_gemm_grouped_masked(const uint8_t* a, const uint8_t* b, const uint8_t*
                               void* out, int64_t E, int64_t m, int64_t n, int64_t k, void* stream) {
     if (!mask) return NVFP4_NULL_POINTER;
     return gemm_common(a, b, a_sf, b_sf, alpha, mask, nullptr, nullptr, nullptr, out, E, m, n, k, 0,
-                       stream);
+                       nullptr, 0, stream);
+}
+
+int nvfp4_gemm_grouped_masked_ws(const uint8_t* a, const uint8_t* b, const uint8_t* a_sf,
+                                 const uint8_t* b_sf, const float* alpha, const int32_t* mask,
+                                 void* out, int64_t E, int64_t m, int64_t n, int64_t k,
+                                 void* workspace, int64_t workspace_bytes, void* stream) {
+    if (!mask) return NVFP4_NULL_POINTER;
+    return gemm_common(a, b, a_sf, b_sf, alpha, mask, nullptr, nullptr, nullptr, out, E, m, n, k, 0,
+                       workspace, workspace_bytes, stream);
 }
 
 int nvfp4_gemm_grouped_masked_silu_quantize(const uint8_t* a, const uint8_t* b, const uint8_t* a_sf,
@@ -235,7 +256,17 @@ int nvfp4_gemm_svdquant(const uint8_t* a, const uint8_t* b, const uint8_t* a_sf,
                         void* out, int64_t m, int64_t n, int64_t k, int64_t r, void* stream) {
     if (!d || !l1) return NVFP4_NULL_POINTER;
     if (r <= 0 || r % 32 != 0 || r > 4096) return NVFP4_BAD_RANK;
-    return gemm_common(a, b, a_sf, b_sf, alpha, nullptr, bias, d, l1, out, 1, m, n, k, r, stream);
+    return gemm_common(a, b, a_sf, b_sf, alpha, nullptr, bias, d, l1, out, 1, m, n, k, r, nullptr, 0, stream);
+}
+
+int nvfp4_gemm_svdquant_ws(const uint8_t* a, const uint8_t* b, const uint8_t* a_sf, const uint8_t* b_sf,
+                           const float* alpha, const void* d, const void* l1, const void* bias,
+                           void* out, int64_t m, int64_t n, int64_t k, int64_t r, void* workspace,
+                           int64_t workspace_bytes, void* stream) {
+    if (!d || !l1) return NVFP4_NULL_POINTER;
+    if (r <= 0 || r % 32 != 0 || r > 4096) return NVFP4_BAD_RANK;
+    return gemm_common(a, b, a_sf, b_sf, alpha, nullptr, bias, d, l1, out, 1, m, n, k, r, workspace,
+                       workspace_bytes, stream);
 }
 
 int nvfp4_gemm_w4a16(const void* a, const uint8_t* b, const uint8_t* b_sf, const float* alpha,

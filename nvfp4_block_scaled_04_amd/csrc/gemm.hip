@@ -75,6 +75,63 @@ __device__ __forceinline__ int64_t scale_byte_off(int64_t row, int c, int cpa4) 
 template <int WM, int WN>
 constexpr int kWavesPerEU = WM * WN >= 16384 ? 1 : 2;
 
+// Split-tail schedule over rounds of G = p.sk_grid workgroups (one per CU;
+// the workgroups of a round start as those of the previous one finish).  The
+// T live tiles (experts in order; within an expert, bands
+// of 8 tile rows walked column by column, as tile_coords does) are cut into
+// D = floor(T/G)*G whole tiles, dealt G per round (XCD x taking the x-th
+// eighth of a round, so tiles that share panels share an L2), and R = T - D
+// tail tiles.  The K steps of a tail tile are split into S = min(G/R, steps
+// per K group / 4) parts of whole groups of KS steps, one part per
+// workgroup, so every CU receives the same work to within one part.  With
+// S > 1 each part leaves an fp32 partial tile in workspace slot (r*S + j)
+// and a second launch (k_gemm_fixup) adds a tail tile's S partials in part
+// order: deterministic, and no workgroup ever waits for another.  Without a
+// workspace, S = 1 (the tail tiles run whole).  Every workgroup of both
+// launches derives the schedule from the mask itself.
+struct SkPlan {
+    int T, D, R, S;
+};
+
+__device__ __forceinline__ int sk_rows(const GParams& p, int e, int bm) {
+    return (clamp_rows(p.mask, e, (int)p.M) + bm - 1) / bm;
+}
+
+__device__ __forceinline__ SkPlan sk_plan(const GParams& p, int bm, int nkt, int ks) {
+    int T = 0;
+    for (int e = 0; e < (int)p.E; e++) T += sk_rows(p, e, bm) * p.tiles_n;
+    const int G = p.sk_grid;
+    SkPlan s;
+    s.T = T;
+    s.D = T / G * G;
+    s.R = T - s.D;
+    // parts of at least 4 K-step pairs (of KS steps): shorter ones cost
+    // more in pipeline fill and partial-tile traffic than they balance
+    int S = s.R ? G / s.R : 0;
+    const int smax = nkt / ks / 4 > 1 ? nkt / ks / 4 : 1;
+    if (S > smax) S = smax;
+    if (!p.part && S > 1) S = 1;
+    s.S = S;
+    return s;
+}
+
+// Expert and tile coordinates of live tile idx (0 <= idx < T).
+__device__ __forceinline__ void sk_tile(const GParams& p, int bm, int idx, int& e, int& tm, int& tn) {
+    for (e = 0; e < (int)p.E - 1; e++) {
+        const int cnt = sk_rows(p, e, bm) * p.tiles_n;
+        if (idx < cnt) break;
+        idx -= cnt;
+    }
+    constexpr int G8 = 8;
+    const int tme = sk_rows(p, e, bm);
+    const int per = G8 * p.tiles_n;
+    const int band = idx / per, first = band * G8;
+    const int rows = tme - first < G8 ? tme - first : G8;
+    const int in = idx - band * per;
+    tm = first + in % rows;
+    tn = in / rows;
+}
+
 // KS = 2 splits the K loop inside the workgroup: two groups of WGM x WGN
 // waves each run half of the K steps through their own LDS pipeline over the
 // same tile, then swap halves of their partial sums through LDS, so that
@@ -88,7 +145,12 @@ constexpr int kWavesPerEU = WM * WN >= 16384 ? 1 : 2;
 // the same j, so the epilogue finds g and u of one output element in the
 // same wave's staged rows and quantizes silu(g)*u per 16-column block, with
 // the same arithmetic as the silu_and_mul quantize kernel.
-template <int BM, int BN, int WGM, int WGN, int NST, int KS, bool ALIGNED, int EPI>
+//
+// SK (split-tail schedule, plain and LoRA epilogues): rounds of p.sk_grid
+// workgroups, one per CU, find their work from the mask (see sk_plan): a
+// whole tile, or one K range of a tail tile, whose fp32 partial sums go to
+// the workspace when the tile is split.
+template <int BM, int BN, int WGM, int WGN, int NST, int KS, bool ALIGNED, int EPI, bool SK = false>
 __global__ __launch_bounds__(64 * WGM * WGN * KS, (KS == 2 ? 2 : kWavesPerEU<BM / WGM, BN / WGN>)) void k_gemm(GParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
     static_assert(KS == 1 || (KS == 2 && BM / WGM == 64), "the K split swaps 32-row fragment rows of 64-row wave tiles");
@@ -114,9 +176,13 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, (KS == 2 ? 2 : kWavesPerEU<BM 
     const int grp = KS == 1 ? 0 : wave_wg / NW;          // K group
     const int wave = KS == 1 ? wave_wg : wave_wg % NW;   // wave within the group
     const int wm = wave % WGM, wn = wave / WGM;
-    const int e = blockIdx.z;
-    int tm, tn;
-    tile_coords(p, tm, tn);
+    const int nkt = (int)((p.K + 127) / 128);  // K steps of a whole tile
+
+    // One tile (expert e, tile row tm, tile column tn) over K steps
+    // [ks0, ks1): stored as bf16, or with slot >= 0 left as an fp32 partial
+    // tile in workspace slot `slot`.  lora: add the rank-r term (EPI_LORA).
+    auto tile = [&](const int e, const int tm, const int tn, const int ks0, const int ks1, const int slot,
+                    const bool lora) {
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
     const int64_t hc0 = (int64_t)tn * (BN / 2);  // first h column of the tile (EPI_SILUQ)
     const int valid = clamp_rows(p.mask, e, (int)p.M);
@@ -214,8 +280,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, (KS == 2 ? 2 : kWavesPerEU<BM 
 #pragma unroll
             for (int v = 0; v < 16; v++) acc[i][j][v] = 0.0f;
 
-    const int nkt = (int)((p.K + 127) / 128);
-    const int kb = grp * (nkt / KS), ke = KS == 1 ? nkt : kb + nkt / KS;  // this group's K steps
+    const int kb = ks0 + grp * ((ks1 - ks0) / KS), ke = KS == 1 ? ks1 : kb + (ks1 - ks0) / KS;  // this group's K steps
     const int h = lane >> 5, l32 = lane & 31;
     // per-lane LDS offsets, fixed for the whole K loop (fragment i adds i*32 rows)
     const int ra_off = (wm * WM + l32) * 64, rb_off = OFF_B + (wn * WN + l32) * 64;
@@ -397,7 +462,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, (KS == 2 ? 2 : kWavesPerEU<BM 
         }
     }
 
-    if constexpr (LORA) {
+    if (LORA && lora) {
         // rank-r bf16 correction into the same accumulator
         for (int kr = 0; kr < p.r; kr += 16) {
             bf16x8 od[FM], ol[FN];
@@ -422,6 +487,26 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, (KS == 2 ? 2 : kWavesPerEU<BM 
                     if (KS == 1 || im == grp)
                     acc[in][im] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ol[in], od[im], acc[in][im], 0, 0, 0);
         }
+    }
+
+    if (SK && slot >= 0) {
+        // fp32 partial tile, fragment-major: the v-th 4 floats of every lane
+        // of fragment f (32-row block f / (BN/32), 32-column block f % (BN/32))
+        // form one contiguous 1 KB piece at float offset (4f + v) * 256
+        float* const P = p.part + (int64_t)slot * (BM * BN);
+#pragma unroll
+        for (int im = 0; im < FM; im++) {
+            if (KS == 2 && im != grp) continue;  // the other K group holds this fragment row
+#pragma unroll
+            for (int in = 0; in < FN; in++) {
+                const int f = (wm * FM + im) * (BN / 32) + wn * FN + in;
+#pragma unroll
+                for (int v = 0; v < 4; v++)
+                    *(f32x4*)(P + ((f * 4 + v) * 64 + lane) * 4) =
+                        f32x4{acc[in][im][4 * v], acc[in][im][4 * v + 1], acc[in][im][4 * v + 2], acc[in][im][4 * v + 3]};
+            }
+        }
+        return;
     }
 
     // ---- epilogue: alpha, bias, bf16; staged through LDS (each wave its own
@@ -519,7 +604,98 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, (KS == 2 ? 2 : kWavesPerEU<BM 
         __builtin_amdgcn_s_waitcnt((0x3F & 0xF) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));  // reads done before the region is rewritten
         __builtin_amdgcn_sched_barrier(0);
     }
+    };  // tile
+
+    if constexpr (!SK) {
+        int tm, tn;
+        tile_coords(p, tm, tn);
+        tile(blockIdx.z, tm, tn, 0, nkt, -1, true);
+    } else {
+        // workgroup w: round w / G, position b = w % G within the round (the
+        // grid holds enough rounds for every live tile; workgroups past the
+        // schedule exit at once)
+        static_assert(EPI != EPI_SILUQ, "the split schedule stores plain or LoRA tiles");
+        const int G = p.sk_grid, w = blockIdx.x, round = w / G, b = w % G;
+        const SkPlan pl = sk_plan(p, BM, nkt, KS);
+        const int rounds = pl.D / G;
+        int idx, ks0 = 0, ks1 = nkt, slot = -1, lora = 1;
+        if (round < rounds) {
+            idx = round * G + ((G & 7) == 0 ? (b & 7) * (G >> 3) + (b >> 3) : b);
+        } else if (round == rounds && b < pl.R * pl.S) {
+            const int r = b / pl.S, j = b % pl.S, np = nkt / KS;
+            idx = pl.D + r;
+            ks0 = KS * (j * np / pl.S);
+            ks1 = KS * ((j + 1) * np / pl.S);
+            if (pl.S > 1) {
+                slot = b;
+                lora = j == 0;
+            }
+        } else {
+            return;
+        }
+        int e, tm, tn;
+        sk_tile(p, BM, idx, e, tm, tn);
+        tile(__builtin_amdgcn_readfirstlane(e), __builtin_amdgcn_readfirstlane(tm),
+             __builtin_amdgcn_readfirstlane(tn), __builtin_amdgcn_readfirstlane(ks0),
+             __builtin_amdgcn_readfirstlane(ks1), __builtin_amdgcn_readfirstlane(slot),
+             __builtin_amdgcn_readfirstlane(lora) != 0);
+    }
 #endif
+}
+
+// Second launch of a split-tail schedule: adds the S fp32 partial tiles of
+// each tail tile r in part order (slots r*S .. r*S+S-1), applies alpha and
+// bias and stores bf16, rows >= mask[e] untouched.  One item is 4 outputs
+// (one float4 of every partial); a grid of one 1024-thread workgroup per CU
+// walks the R * BM*BN/4 items, 1024 consecutive items (one tile) per
+// workgroup and step, the loads of up to 8 parts of an item in flight
+// together.  Exits at once when nothing was split.
+constexpr int kFixupThreads = 1024;
+
+template <int BM, int BN, int KS>
+__global__ __launch_bounds__(kFixupThreads) void k_gemm_fixup(GParams p) {
+    constexpr int ITEMS = BM * BN / 4;  // float4 items of one partial tile
+    static_assert(ITEMS % kFixupThreads == 0, "a workgroup's items lie in one tile");
+    const int nkt = (int)((p.K + 127) / 128);
+    const SkPlan pl = sk_plan(p, BM, nkt, KS);
+    if (pl.S <= 1) return;
+    const int total = pl.R * ITEMS;
+    for (int g0 = blockIdx.x * kFixupThreads; g0 < total; g0 += gridDim.x * kFixupThreads) {
+        const int r = g0 / ITEMS, i = g0 % ITEMS + (int)threadIdx.x;
+        int e, tm, tn;
+        sk_tile(p, BM, pl.D + r, e, tm, tn);
+        const int valid = clamp_rows(p.mask, e, (int)p.M);
+        const int lane = i & 63, v = (i >> 6) & 3, f = i >> 8;
+        const int64_t m = (int64_t)tm * BM + (f / (BN / 32)) * 32 + (lane & 31);
+        const int64_t n = (int64_t)tn * BN + (f % (BN / 32)) * 32 + v * 8 + (lane >> 5) * 4;
+        if (m >= valid) continue;
+        const float* const P = p.part + (int64_t)r * pl.S * (BM * BN) + (int64_t)i * 4;
+        f32x4 s = *(const f32x4*)P;
+        for (int j0 = 1; j0 < pl.S; j0 += 8) {
+            f32x4 t[8];
+#pragma unroll
+            for (int u = 0; u < 8; u++)
+                if (j0 + u < pl.S) t[u] = *(const f32x4*)(P + (int64_t)(j0 + u) * (BM * BN));
+#pragma unroll
+            for (int u = 0; u < 8; u++)
+                if (j0 + u < pl.S) s += t[u];
+        }
+        const float alpha = p.alpha[e];
+        uint16_t* const O = p.out + (int64_t)e * p.M * p.N;
+        float y[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            y[u] = alpha * s[u];
+            if (p.bias && n + u < p.N) y[u] += bf16_lo((uint32_t)p.bias[n + u]);
+        }
+        if ((p.N & 3) == 0 && n + 3 < p.N) {
+            *(u32x2*)(O + m * p.N + n) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; u++)
+                if (n + u < p.N) O[m * p.N + n + u] = (uint16_t)pack_bf16x2(y[u], 0.0f);
+        }
+    }
 }
 
 template <int BM, int BN, int WGM, int WGN, int NST, int KS = 1>
@@ -538,6 +714,31 @@ static hipError_t launch_tile(GParams p, bool lora, hipStream_t st) {
         if (aligned) k_gemm<BM, BN, WGM, WGN, NST, KS, true, EPI_PLAIN><<<grid, threads, 0, st>>>(p);
         else k_gemm<BM, BN, WGM, WGN, NST, KS, false, EPI_PLAIN><<<grid, threads, 0, st>>>(p);
     }
+    return hipGetLastError();
+}
+
+// Split-tail launch (see sk_plan) and, with a workspace, the launch that
+// adds the split tiles' partial sums.
+template <int BM, int BN, int WGM, int WGN, int NST, int KS>
+static hipError_t launch_tile_sk(GParams p, bool lora, float* ws, int G, hipStream_t st) {
+    p.tiles_m = (int)((p.M + BM - 1) / BM);
+    p.tiles_n = (int)((p.N + BN - 1) / BN);
+    p.xcd_chunk = 0;
+    p.part = ws;
+    p.sk_grid = G;
+    constexpr int threads = 64 * WGM * WGN * KS;
+    const bool aligned = (p.K % 128) == 0;
+    // rounds for every tile of every expert, plus the tail round
+    const int64_t tmax = p.E * p.tiles_m * p.tiles_n;
+    const dim3 grid((unsigned)(G * (tmax / G + 1)), 1, 1);
+    if (lora) {
+        if (aligned) k_gemm<BM, BN, WGM, WGN, NST, KS, true, EPI_LORA, true><<<grid, threads, 0, st>>>(p);
+        else k_gemm<BM, BN, WGM, WGN, NST, KS, false, EPI_LORA, true><<<grid, threads, 0, st>>>(p);
+    } else {
+        if (aligned) k_gemm<BM, BN, WGM, WGN, NST, KS, true, EPI_PLAIN, true><<<grid, threads, 0, st>>>(p);
+        else k_gemm<BM, BN, WGM, WGN, NST, KS, false, EPI_PLAIN, true><<<grid, threads, 0, st>>>(p);
+    }
+    if (ws) k_gemm_fixup<BM, BN, KS><<<dim3((unsigned)G), kFixupThreads, 0, st>>>(p);
     return hipGetLastError();
 }
 
@@ -842,6 +1043,28 @@ static Tile pick_tile(int64_t m, int64_t n, int64_t k, int64_t E) {
     return Tile::T128x128;
 }
 
+// Workgroups of a persistent launch: one per CU, at most the workspace's
+// slot count.
+static int sk_grid_size() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        return 0;
+    return cus < kGemmWsSlots ? cus : kGemmWsSlots;
+}
+
+// The split-tail schedule on the K-split 128x256 tile replaces a 128x256
+// tile choice that would leave one wave per SIMD or a mostly idle second
+// round: for the grouped form (live tiles unknown on the host) always, and
+// for a single problem (then more 128x256 tiles than CUs, but fewer than
+// two 256x256 or three 128x128 tiles per CU) given a workspace.  K must make
+// an even number of steps (the two K groups of the tile).
+static bool use_split_schedule(const GemmArgs& g, Tile t) {
+    if (((g.k + 127) / 128) % 2 != 0) return false;
+    if (g.E > 1) return g.E <= kSkMaxExperts && (t == Tile::T128x256 || t == Tile::T128x256K2);
+    return g.ws && t == Tile::T128x256;
+}
+
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
     GParams p{};
     p.a = g.a; p.b = g.b; p.a_sf = g.a_sf; p.b_sf = g.b_sf;
@@ -857,7 +1080,13 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
     p.sfa = (int64_t)p.rpa * cp;
     p.sfb = (int64_t)p.rpb * cp;
     const bool lora = g.d != nullptr;
-    switch (pick_tile(g.m, g.n, g.k, g.E)) {
+    const Tile t = pick_tile(g.m, g.n, g.k, g.E);
+    if (use_split_schedule(g, t)) {
+        const int G = sk_grid_size();
+        if (G <= 0) return hipErrorInvalidDevice;
+        return launch_tile_sk<128, 256, 2, 2, 2, 2>(p, lora, g.ws, G, st);
+    }
+    switch (t) {
     case Tile::T256x256: return launch_tile<256, 256, 4, 2, 3>(p, lora, st);
     case Tile::T128x256: return launch_tile<128, 256, 2, 2, 2>(p, lora, st);
     case Tile::T128x256K2: return launch_tile<128, 256, 2, 2, 2, 2>(p, lora, st);

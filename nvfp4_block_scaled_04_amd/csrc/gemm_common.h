@@ -39,6 +39,9 @@ struct GParams {
     int64_t q_sfsz;      // per-expert scale bytes = pad_up(M,128) * pad_up(H/16,4)
     int q_cp4;           // pad_up(H/16,4)/4
     int q_rpad;          // pad_up(M,128)
+    // split-tail schedule (persistent K-split launch)
+    float* part;         // fp32 partial tiles of the split tail tiles, or null (no split)
+    int sk_grid;         // workgroups of the persistent launch
 };
 
 // Raw buffer resource (gfx9 word 3: 32-bit untyped records).  Loads past

@@ -52,7 +52,16 @@ struct GemmArgs {
     const uint16_t* l1;    // [n, r] or null
     uint16_t* out;         // [E, m, n]
     int64_t E, m, n, k, r;
+    float* ws = nullptr;   // kGemmWsSlots partial 128x256 fp32 tiles for the split-tail schedule, or null
 };
+
+// Workspace of the split-tail GEMM schedule: one fp32 128x256 partial tile
+// per workgroup of the persistent launch (one workgroup per CU).
+constexpr int kGemmWsSlots = 256;
+constexpr int64_t kGemmWsBytes = (int64_t)kGemmWsSlots * 128 * 256 * 4;
+// Experts up to which the grouped form takes the split-tail schedule (each
+// workgroup walks the mask to find its tiles).
+constexpr int kSkMaxExperts = 64;
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
 // Weight-only form: g.a is the bf16 activation [m, k] (a_sf unused).

@@ -26,6 +26,9 @@ EXPORTS = (
     "nvfp4_gemm_grouped_masked",
     "nvfp4_gemm_grouped_masked_silu_quantize",
     "nvfp4_gemm_svdquant",
+    "nvfp4_gemm_ws",
+    "nvfp4_gemm_grouped_masked_ws",
+    "nvfp4_gemm_svdquant_ws",
     "nvfp4_gemm_w4a16",
     "nvfp4_alpha",
     "mxfp4_quantize",
@@ -60,6 +63,9 @@ def _load():
         "nvfp4_gemm_grouped_masked": [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp],
         "nvfp4_gemm_grouped_masked_silu_quantize": [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp],
         "nvfp4_gemm_svdquant": [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp],
+        "nvfp4_gemm_ws": [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, vp, i64, vp],
+        "nvfp4_gemm_grouped_masked_ws": [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, i64, vp],
+        "nvfp4_gemm_svdquant_ws": [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, i64, vp],
         "nvfp4_gemm_w4a16": [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp],
         "nvfp4_alpha": [vp, vp, vp, i64, vp],
         "mxfp4_quantize": [vp, i32, i64, i64, vp, vp, vp],
@@ -360,8 +366,24 @@ def _operands(a, b, a_sf, b_sf, E, m, n, k, dev, sfsz):
     _dev(b_sf, "b_sf", BYTES, E * sfsz(n, k), dev)
 
 
-def nvfp4_gemm(a, b, a_sf, b_sf, alpha, bias=None, out=None, k=None):
-    """a: [m, k/2], b: [n, k/2] packed FP4 -> out [m, n] bf16 = alpha*(a@b^T) (+bias)."""
+GEMM_WS_BYTES = 33554432   # NVFP4_GEMM_WS_BYTES
+
+
+def gemm_workspace(device):
+    """A workspace for the split-tail GEMM schedule (caller-owned device memory)."""
+    return torch.empty(GEMM_WS_BYTES, dtype=torch.uint8, device=device)
+
+
+def _ws_args(workspace, dev):
+    if workspace is None:
+        return []
+    _dev(workspace, "workspace", BYTES, GEMM_WS_BYTES, dev)
+    return [_ptr(workspace), workspace.numel()]
+
+
+def nvfp4_gemm(a, b, a_sf, b_sf, alpha, bias=None, out=None, k=None, workspace=None):
+    """a: [m, k/2], b: [n, k/2] packed FP4 -> out [m, n] bf16 = alpha*(a@b^T) (+bias).
+    With a workspace ([GEMM_WS_BYTES] bytes) the call is nvfp4_gemm_ws."""
     _dims(a, "a", 2)
     _dims(b, "b", 2)
     m, n = a.shape[0], b.shape[0]
@@ -375,14 +397,17 @@ def nvfp4_gemm(a, b, a_sf, b_sf, alpha, bias=None, out=None, k=None):
     _dev(alpha, "alpha", F32, 1, dev)
     _opt(bias, "bias", BF16, n, dev)
     _dev(out, "out", BF16, m * n, dev)
-    rc = _lib.nvfp4_gemm(_ptr(a), _ptr(b), _ptr(a_sf), _ptr(b_sf), _ptr(alpha), _ptr(bias),
-                         _ptr(out), m, n, k, _stream(a.device))
-    _check(rc, "nvfp4_gemm")
+    ws = _ws_args(workspace, dev)
+    f = _lib.nvfp4_gemm_ws if ws else _lib.nvfp4_gemm
+    rc = f(_ptr(a), _ptr(b), _ptr(a_sf), _ptr(b_sf), _ptr(alpha), _ptr(bias),
+           _ptr(out), m, n, k, *ws, _stream(a.device))
+    _check(rc, "nvfp4_gemm_ws" if ws else "nvfp4_gemm")
     return out
 
 
-def nvfp4_gemm_grouped_masked(a, b, a_sf, b_sf, alpha, mask, out=None):
-    """a: [E, m, k/2], b: [E, n, k/2] -> out [E, m, n] bf16, rows >= mask[e] untouched."""
+def nvfp4_gemm_grouped_masked(a, b, a_sf, b_sf, alpha, mask, out=None, workspace=None):
+    """a: [E, m, k/2], b: [E, n, k/2] -> out [E, m, n] bf16, rows >= mask[e] untouched.
+    With a workspace ([GEMM_WS_BYTES] bytes) the call is nvfp4_gemm_grouped_masked_ws."""
     _dims(a, "a", 3)
     _dims(b, "b", 3)
     E, m, kb = a.shape
@@ -396,9 +421,11 @@ def nvfp4_gemm_grouped_masked(a, b, a_sf, b_sf, alpha, mask, out=None):
     _dev(alpha, "alpha", F32, E, dev)
     _dev(mask, "mask", I32, E, dev)
     _dev(out, "out", BF16, E * m * n, dev)
-    rc = _lib.nvfp4_gemm_grouped_masked(_ptr(a), _ptr(b), _ptr(a_sf), _ptr(b_sf), _ptr(alpha),
-                                        _ptr(mask), _ptr(out), E, m, n, kb * 2, _stream(a.device))
-    _check(rc, "nvfp4_gemm_grouped_masked")
+    ws = _ws_args(workspace, dev)
+    f = _lib.nvfp4_gemm_grouped_masked_ws if ws else _lib.nvfp4_gemm_grouped_masked
+    rc = f(_ptr(a), _ptr(b), _ptr(a_sf), _ptr(b_sf), _ptr(alpha),
+           _ptr(mask), _ptr(out), E, m, n, kb * 2, *ws, _stream(a.device))
+    _check(rc, "nvfp4_gemm_grouped_masked_ws" if ws else "nvfp4_gemm_grouped_masked")
     return out
 
 
@@ -433,8 +460,9 @@ def nvfp4_gemm_grouped_masked_silu_quantize(a, b, a_sf, b_sf, alpha, mask, globa
     return out_fp4, out_sf
 
 
-def nvfp4_gemm_svdquant(a, b, a_sf, b_sf, alpha, d, l1, bias=None, out=None):
-    """out = alpha*(a@b^T + d@l1^T) (+bias); l1 pre-divided by alpha by the caller."""
+def nvfp4_gemm_svdquant(a, b, a_sf, b_sf, alpha, d, l1, bias=None, out=None, workspace=None):
+    """out = alpha*(a@b^T + d@l1^T) (+bias); l1 pre-divided by alpha by the caller.
+    With a workspace ([GEMM_WS_BYTES] bytes) the call is nvfp4_gemm_svdquant_ws."""
     _dims(a, "a", 2)
     _dims(b, "b", 2)
     _dims(d, "d", 2)
@@ -450,9 +478,11 @@ def nvfp4_gemm_svdquant(a, b, a_sf, b_sf, alpha, d, l1, bias=None, out=None):
     _dev(l1, "l1", BF16, n * r, dev)
     _opt(bias, "bias", BF16, n, dev)
     _dev(out, "out", BF16, m * n, dev)
-    rc = _lib.nvfp4_gemm_svdquant(_ptr(a), _ptr(b), _ptr(a_sf), _ptr(b_sf), _ptr(alpha), _ptr(d),
-                                  _ptr(l1), _ptr(bias), _ptr(out), m, n, k, r, _stream(a.device))
-    _check(rc, "nvfp4_gemm_svdquant")
+    ws = _ws_args(workspace, dev)
+    f = _lib.nvfp4_gemm_svdquant_ws if ws else _lib.nvfp4_gemm_svdquant
+    rc = f(_ptr(a), _ptr(b), _ptr(a_sf), _ptr(b_sf), _ptr(alpha), _ptr(d),
+           _ptr(l1), _ptr(bias), _ptr(out), m, n, k, r, *ws, _stream(a.device))
+    _check(rc, "nvfp4_gemm_svdquant_ws" if ws else "nvfp4_gemm_svdquant")
     return out
 
 

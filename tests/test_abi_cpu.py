@@ -35,6 +35,7 @@ def test_header_declares_the_entry_points():
     assert declared() == sorted([
         "nvfp4_alpha", "nvfp4_gemm", "nvfp4_gemm_grouped_masked",
         "nvfp4_gemm_grouped_masked_silu_quantize", "nvfp4_gemm_svdquant",
+        "nvfp4_gemm_ws", "nvfp4_gemm_grouped_masked_ws", "nvfp4_gemm_svdquant_ws",
         "nvfp4_gemm_w4a16", "nvfp4_quantize_lora_down",
         "nvfp4_quantize", "nvfp4_quantize_alpha", "nvfp4_quantize_ws", "nvfp4_quantize_noalloc",
         "nvfp4_quantize_masked_batched",
@@ -159,6 +160,45 @@ def test_grouped_validation(lib):
     assert f(*args(E=0)) == SHAPE
     assert f(*args(k=17)) == SHAPE
     assert f(*args(mask=P + 2)) == MISAL
+
+
+GEMM_WS = 33554432  # NVFP4_GEMM_WS_BYTES
+
+
+def test_gemm_ws_validation(lib):
+    """The workspace forms keep every check of the plain calls, and refuse a
+    workspace that is too small or misaligned; NULL selects the plain
+    schedule (here refused for another argument, so nothing launches)."""
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    f = lib.nvfp4_gemm_ws
+    f.argtypes = [vp] * 7 + [i64] * 3 + [vp, i64, vp]
+    run = lambda a=P, out=P, m=128, k=256, ws=P, wsb=GEMM_WS: f(a, P, P, P, P, None, out, m, 128, k, ws, wsb, None)
+    assert run(a=None) == NULLP
+    assert run(k=40) == SHAPE
+    assert run(m=0) == SHAPE
+    assert run(out=P + 2) == MISAL
+    assert run(wsb=GEMM_WS - 1) == SHAPE
+    assert run(ws=P + 8) == MISAL
+    assert run(ws=None, k=40) == SHAPE
+    assert run(m=(1 << 20), k=8192) == UNSUP
+    fg = lib.nvfp4_gemm_grouped_masked_ws
+    fg.argtypes = [vp] * 7 + [i64] * 4 + [vp, i64, vp]
+    rung = lambda mask=P, E=4, k=256, ws=P, wsb=GEMM_WS: fg(P, P, P, P, P, mask, P, E, 64, 64, k, ws, wsb, None)
+    assert rung(mask=None) == NULLP
+    assert rung(E=0) == SHAPE
+    assert rung(k=17) == SHAPE
+    assert rung(mask=P + 2) == MISAL
+    assert rung(wsb=1 << 20) == SHAPE
+    assert rung(ws=P + 4) == MISAL
+    fs = lib.nvfp4_gemm_svdquant_ws
+    fs.argtypes = [vp] * 9 + [i64] * 4 + [vp, i64, vp]
+    runs = lambda r=32, d=P, k=256, ws=P, wsb=GEMM_WS: fs(P, P, P, P, P, d, P, None, P, 64, 64, k, r, ws, wsb, None)
+    assert runs(r=16) == RANK
+    assert runs(d=None) == NULLP
+    assert runs(d=P + 8) == MISAL
+    assert runs(k=40) == SHAPE
+    assert runs(wsb=0) == SHAPE
+    assert runs(ws=P + 2) == MISAL
 
 
 def test_quantize_alpha_validation(lib):

@@ -38,6 +38,14 @@ CALLS = {
         torch.zeros(2, dtype=torch.int32), f32(2)),
     "nvfp4_gemm_svdquant": lambda: ops.nvfp4_gemm_svdquant(
         u8(128, 32), u8(64, 32), u8(ops.sf_size(128, 64)), u8(ops.sf_size(64, 64)), f32(1), bf(128, 32), bf(64, 32)),
+    "nvfp4_gemm_ws": lambda: ops.nvfp4_gemm(u8(128, 32), u8(64, 32), u8(ops.sf_size(128, 64)),
+                                            u8(ops.sf_size(64, 64)), f32(1), workspace=u8(16)),
+    "nvfp4_gemm_grouped_masked_ws": lambda: ops.nvfp4_gemm_grouped_masked(
+        u8(2, 128, 32), u8(2, 64, 32), u8(2, ops.sf_size(128, 64)), u8(2, ops.sf_size(64, 64)), f32(2),
+        torch.zeros(2, dtype=torch.int32), workspace=u8(16)),
+    "nvfp4_gemm_svdquant_ws": lambda: ops.nvfp4_gemm_svdquant(
+        u8(128, 32), u8(64, 32), u8(ops.sf_size(128, 64)), u8(ops.sf_size(64, 64)), f32(1), bf(128, 32), bf(64, 32),
+        workspace=u8(16)),
     "nvfp4_gemm_w4a16": lambda: ops.nvfp4_gemm_w4a16(bf(16, 64), u8(64, 32), u8(ops.sf_size(64, 64)), f32(1)),
     "nvfp4_alpha": lambda: ops.nvfp4_alpha(f32(1), f32(1)),
     "mxfp4_quantize": lambda: ops.mxfp4_quantize(bf(128, 64)),
