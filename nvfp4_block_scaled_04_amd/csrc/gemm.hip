@@ -23,12 +23,15 @@
 // (BM/WGM) x (BN/WGN), each wave a grid of 32 x 32 MFMA fragments: 4 x 2
 // waves of 64 x 128 for the 256 x 256 tile (two waves per SIMD, so one
 // wave's dequantization and LDS waits overlap the other's MFMAs; measured
-// 9% faster than 2 x 2 waves of 128 x 128 with one wave per SIMD), 2 x 2
+// 2% faster than 2 x 2 waves of 128 x 128 with one wave per SIMD), 2 x 2
 // waves for the smaller tiles.  K advances
 // 128 elements (64 bytes of a row) per step.  A step's FP4 rows and raw scale
 // bytes go from global memory straight into LDS (buffer loads with the LDS
-// bit: no registers), three stages deep, so a step's loads are issued two
-// steps before it is consumed.  Within a 64-element half step q, lane l of a
+// bit: no registers), two or three stages deep, so a step's loads are issued
+// one or two steps before it is consumed (the 256 x 256 tile runs a step of
+// about 3 us, which covers the load latency with two stages: measured 1.5%
+// faster than three; the quantizing epilogue's launch keeps three, measured
+// faster there).  Within a 64-element half step q, lane l of a
 // fragment (row l%32, half h = l/32) owns the 32 consecutive elements
 // 64q+32h.. of its row: one 16-byte LDS read, two block scales, four MFMA
 // K-slices.  The same K permutation is used for both operands, so the
@@ -1087,7 +1090,7 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
         return launch_tile_sk<128, 256, 2, 2, 2, 2>(p, lora, g.ws, G, st);
     }
     switch (t) {
-    case Tile::T256x256: return launch_tile<256, 256, 4, 2, 3>(p, lora, st);
+    case Tile::T256x256: return launch_tile<256, 256, 4, 2, 2>(p, lora, st);
     case Tile::T128x256: return launch_tile<128, 256, 2, 2, 2>(p, lora, st);
     case Tile::T128x256K2: return launch_tile<128, 256, 2, 2, 2, 2>(p, lora, st);
     case Tile::Skinny: return launch_skinny(p, lora, st);
