@@ -763,7 +763,7 @@ static hipError_t launch_tile_siluq(GParams p, hipStream_t st) {
 
 // ---------------------------------------------------------------------------
 // Skinny GEMM for small M (decode-shaped: M <= 64).  A workgroup computes a
-// 16 x 16 output tile; its 4 waves split K into four contiguous ranges and
+// 16 x 16 output tile; its kSkinnyWaves waves split K into contiguous ranges and
 // their fp32 partial tiles are summed through LDS.  Each lane loads its
 // operand fragments straight from global memory (no reuse to stage for):
 // lane (row r = l%16, group g = l/16) holds, per 128-element K chunk, the 32
@@ -772,8 +772,10 @@ static hipError_t launch_tile_siluq(GParams p, hipStream_t st) {
 // (the same K permutation on both operands).  With N/16 x M/16 workgroups the
 // weight is streamed once, spread over every CU.
 // ---------------------------------------------------------------------------
+constexpr int kSkinnyWaves = 8;  // K ranges of a workgroup (two waves per SIMD)
+
 template <bool ALIGNED, bool LORA>
-__global__ __launch_bounds__(256) void k_gemm_skinny(GParams p) {
+__global__ __launch_bounds__(64 * kSkinnyWaves) void k_gemm_skinny(GParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -791,10 +793,10 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GParams p) {
     const uint8_t* SB = p.b_sf + (int64_t)e * p.sfb;
 
     const int nch = (int)((p.K + 127) / 128);
-    const int per = (nch + 3) / 4;
+    const int per = (nch + kSkinnyWaves - 1) / kSkinnyWaves;
     const int c0 = wave * per, c1 = c0 + per < nch ? c0 + per : nch;
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    constexpr int U = 8;  // chunks whose loads are in flight together
+    constexpr int U = 4;  // chunks whose loads are in flight together
     for (int cb = c0; cb < c1; cb += U) {
         u32x4 fa[U], fb[U];
         uint32_t sa[U], sb[U];
@@ -850,12 +852,13 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GParams p) {
             }
         }
     }
-    // sum the four waves' partial tiles
-    __shared__ f32x4 part[3][64];
+    // sum the waves' partial tiles (in wave order)
+    __shared__ f32x4 part[kSkinnyWaves - 1][64];
     if (wave > 0) part[wave - 1][lane] = acc;
     __syncthreads();
     if (wave != 0) return;
-    acc += part[0][lane] + part[1][lane] + part[2][lane];
+#pragma unroll
+    for (int w = 0; w < kSkinnyWaves - 1; w++) acc += part[w][lane];
     // lane: output row m0 + r, columns n0 + 4g .. n0 + 4g + 3
     const int64_t m = m0 + r;
     if (m >= valid) return;
@@ -887,7 +890,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GParams p) {
 // (A @ Bdq^T) (+ bias)) with A bf16 [M, K] and alpha = 1 / the weight's
 // global scale.  Built for decode, where the weight read bounds the time:
 // the skinny kernel's layout (a 16 x 16 output tile per workgroup, the K
-// loop split over its 4 waves, partial tiles added through LDS, 16-byte
+// loop split over its waves, partial tiles added through LDS, 16-byte
 // weight loads covering 32 elements of a row per lane), with the weight
 // dequantized exactly to bf16 (e2m1 times the block scale has at most 6
 // significant bits) for v_mfma_f32_16x16x32_bf16.  The activation needs no
@@ -911,7 +914,7 @@ __device__ __forceinline__ bf16x8 dequant8_bf16(uint32_t w, float s) {
 }
 
 template <bool ALIGNED>
-__global__ __launch_bounds__(256) void k_gemm_w4a16(GParams p) {
+__global__ __launch_bounds__(64 * kSkinnyWaves) void k_gemm_w4a16(GParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -924,7 +927,7 @@ __global__ __launch_bounds__(256) void k_gemm_w4a16(GParams p) {
     const uint8_t* B = p.b + brow * rowb;
 
     const int nch = (int)((p.K + 127) / 128);
-    const int per = (nch + 3) / 4;
+    const int per = (nch + kSkinnyWaves - 1) / kSkinnyWaves;
     const int c0 = wave * per, c1 = c0 + per < nch ? c0 + per : nch;
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     constexpr int U = 4;  // chunks whose loads are in flight together
@@ -967,12 +970,13 @@ __global__ __launch_bounds__(256) void k_gemm_w4a16(GParams p) {
             }
         }
     }
-    // sum the four waves' partial tiles
-    __shared__ f32x4 part[3][64];
+    // sum the waves' partial tiles (in wave order)
+    __shared__ f32x4 part[kSkinnyWaves - 1][64];
     if (wave > 0) part[wave - 1][lane] = acc;
     __syncthreads();
     if (wave != 0) return;
-    acc += part[0][lane] + part[1][lane] + part[2][lane];
+#pragma unroll
+    for (int w = 0; w < kSkinnyWaves - 1; w++) acc += part[w][lane];
     // lane: output row m0 + r, columns n0 + 4g .. n0 + 4g + 3
     const int64_t m = m0 + r;
     if (m >= p.M) return;
@@ -1007,8 +1011,8 @@ hipError_t launch_gemm_w4a16(const GemmArgs& g, hipStream_t st) {
     p.cpa4 = (int)(cp / 4);
     p.nblk = (int)(g.k / 16);
     dim3 grid((unsigned)((p.N + 15) / 16), (unsigned)((p.M + 15) / 16), 1u);
-    if (p.K % 128 == 0) k_gemm_w4a16<true><<<grid, 256, 0, st>>>(p);
-    else k_gemm_w4a16<false><<<grid, 256, 0, st>>>(p);
+    if (p.K % 128 == 0) k_gemm_w4a16<true><<<grid, 64 * kSkinnyWaves, 0, st>>>(p);
+    else k_gemm_w4a16<false><<<grid, 64 * kSkinnyWaves, 0, st>>>(p);
     return hipGetLastError();
 }
 
@@ -1016,11 +1020,11 @@ static hipError_t launch_skinny(GParams p, bool lora, hipStream_t st) {
     dim3 grid((unsigned)((p.N + 15) / 16), (unsigned)((p.M + 15) / 16), (unsigned)p.E);
     const bool aligned = (p.K % 128) == 0;
     if (lora) {
-        if (aligned) k_gemm_skinny<true, true><<<grid, 256, 0, st>>>(p);
-        else k_gemm_skinny<false, true><<<grid, 256, 0, st>>>(p);
+        if (aligned) k_gemm_skinny<true, true><<<grid, 64 * kSkinnyWaves, 0, st>>>(p);
+        else k_gemm_skinny<false, true><<<grid, 64 * kSkinnyWaves, 0, st>>>(p);
     } else {
-        if (aligned) k_gemm_skinny<true, false><<<grid, 256, 0, st>>>(p);
-        else k_gemm_skinny<false, false><<<grid, 256, 0, st>>>(p);
+        if (aligned) k_gemm_skinny<true, false><<<grid, 64 * kSkinnyWaves, 0, st>>>(p);
+        else k_gemm_skinny<false, false><<<grid, 64 * kSkinnyWaves, 0, st>>>(p);
     }
     return hipGetLastError();
 }

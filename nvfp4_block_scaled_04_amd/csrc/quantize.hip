@@ -160,6 +160,24 @@ __global__ __launch_bounds__(256) void k_amax(QParams p) {
             __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
 }
 
+// Running maximum of the bf16 magnitudes of 8 elements (one 16-byte load),
+// compared as integers: NaN patterns are skipped and an infinity is noted
+// (the caller takes it as FLT_MAX), which is max |nan_to_num(x)|.
+__device__ __forceinline__ void bf16_amax8(const u32x4& v, uint32_t& mb, bool& inf) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    const uint32_t b = absmax_bits_bf16x8(w);
+    if (b < 0x7F80u) {
+        mb = b > mb ? b : mb;
+    } else {  // inf or NaN in these 8: one at a time
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const uint32_t h = (w[j >> 1] >> (16 * (j & 1))) & 0x7FFFu;
+            if (h == 0x7F80u) inf = true;
+            else if (h < 0x7F80u) mb = h > mb ? h : mb;
+        }
+    }
+}
+
 // Amax pass over one item as a flat stream (b == 1, no row mask, no silu:
 // the valid elements are x[0, m*K) in order).  Each workgroup walks chunks
 // of 256 * U 16-byte loads (U in flight per thread), grid-strided; its
@@ -189,25 +207,7 @@ __global__ __launch_bounds__(256) void k_amax_flat(QParams p) {
         }
         if constexpr (V == V_BF16) {
 #pragma unroll
-            for (int u = 0; u < U; u++) {
-                const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-                u16x2 m2 = __builtin_elementwise_max(
-                    __builtin_elementwise_max(__builtin_bit_cast(u16x2, w[0] & 0x7FFF7FFFu),
-                                              __builtin_bit_cast(u16x2, w[1] & 0x7FFF7FFFu)),
-                    __builtin_elementwise_max(__builtin_bit_cast(u16x2, w[2] & 0x7FFF7FFFu),
-                                              __builtin_bit_cast(u16x2, w[3] & 0x7FFF7FFFu)));
-                const uint32_t b = m2[0] > m2[1] ? m2[0] : m2[1];
-                if (b < 0x7F80u) {
-                    mb = b > mb ? b : mb;
-                } else {  // inf or NaN in these 8: one at a time
-#pragma unroll
-                    for (int j = 0; j < 8; j++) {
-                        const uint32_t h = (w[j >> 1] >> (16 * (j & 1))) & 0x7FFFu;
-                        if (h == 0x7F80u) inf = true;
-                        else if (h < 0x7F80u) mb = h > mb ? h : mb;
-                    }
-                }
-            }
+            for (int u = 0; u < U; u++) bf16_amax8(v[u], mb, inf);
         } else {
 #pragma unroll
             for (int u = 0; u < U; u++) {
@@ -389,6 +389,26 @@ constexpr int64_t fused_max_elems() { return V == V_SILU ? 32768 : 65536; }
 
 template <int V>
 __device__ __forceinline__ float item_amax(const QParams& p, int e, int valid) {
+    if constexpr (V == V_BF16) {
+        // plain bf16: the item's valid rows as one flat stream of 16-byte
+        // loads, magnitudes compared as integers
+        constexpr int UL = 32;  // loads per thread in flight together
+        const u32x4* src = (const u32x4*)((const uint16_t*)p.x + (int64_t)e * p.m * p.k_in);
+        const int64_t nl = (int64_t)valid * p.K / 8;
+        uint32_t mb = 0;
+        bool inf = false;
+        for (int64_t b0 = threadIdx.x; b0 < nl; b0 += 256 * UL) {
+            u32x4 v[UL];
+#pragma unroll
+            for (int u = 0; u < UL; u++) {
+                const int64_t i = b0 + 256 * u;
+                v[u] = i < nl ? src[i] : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int u = 0; u < UL; u++) bf16_amax8(v[u], mb, inf);
+        }
+        return inf ? kFp32Max : bits_f(mb << 16);
+    }
     constexpr int NL = loads_per_block<V>();
     constexpr int U = V == V_BF16 ? 16 : 8;  // blocks per thread with loads in flight together
     const int64_t nblk = p.K / 16, nb = (int64_t)valid * nblk;
