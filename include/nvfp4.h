@@ -219,6 +219,40 @@ int silu_mul_nvfp4_quantize(const void *x, int64_t b, int64_t m, int64_t k2,
                             uint8_t *out_fp4, uint8_t *out_sf, void *stream);
 
 /*
+ * nvfp4_quantize_masked_batched and silu_mul_nvfp4_quantize with the two
+ * additions of nvfp4_quantize_ws, per item:
+ *   gs_other, alpha: both NULL, or [b] fp32 each: the GEMM partner's global
+ *                    scales (read) and alpha[e] = 1 / (gs[e] * gs_other[e])
+ *                    (written by the same call, from the final gs[e]).
+ *   workspace:       DYNAMIC mode: a device buffer of workspace_bytes >=
+ *                    NVFP4_BATCHED_WS_BYTES(b, m, k) (k: the quantized
+ *                    width, k2/2 for the silu form), 16-byte aligned, owned
+ *                    by the caller, contents ignored on entry and undefined
+ *                    on exit; it receives the items' partial maxima, so the
+ *                    amax pass and the quantize pass are the whole call (no
+ *                    finishing launch, no separate alpha launch).  Calls
+ *                    sharing a workspace must not overlap.  STATIC mode does
+ *                    not touch it (it may be NULL).
+ * The bytes written and the errors are those of the plain calls;
+ * NVFP4_NULL_POINTER also when exactly one of gs_other and alpha is NULL or
+ * when the workspace is NULL in DYNAMIC mode, NVFP4_BAD_SHAPE for a
+ * workspace below the size above, NVFP4_MISALIGNED for a workspace not
+ * 16-byte aligned or gs_other / alpha not 4-byte aligned.
+ */
+#define NVFP4_BATCHED_WS_BYTES(b, m, k) \
+    (4096 + 4 * (int64_t)(b) * (((int64_t)(m) + 127) / 128) * (((int64_t)(k) + 63) / 64))
+int nvfp4_quantize_masked_batched_ws(const void *x, int64_t b, int64_t m, int64_t k,
+                                     const int32_t *mask, float *global_scale, int gs_mode,
+                                     const float *gs_other, float *alpha,
+                                     uint8_t *out_fp4, uint8_t *out_sf,
+                                     void *workspace, int64_t workspace_bytes, void *stream);
+int silu_mul_nvfp4_quantize_ws(const void *x, int64_t b, int64_t m, int64_t k2,
+                               const int32_t *mask, float *global_scale, int gs_mode,
+                               const float *gs_other, float *alpha,
+                               uint8_t *out_fp4, uint8_t *out_sf,
+                               void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
  * out[m, n] = bf16(alpha * (A @ B^T) (+ bias[n])) with A [m, k] and B [n, k]
  * in NVFP4 (flashinfer mm_nvfp4_svdquant without the LoRA term; the FP4
  * linear of FastVideo PR #1350 and the scaled_mm of NVIDIA/Fuser PR #5737).

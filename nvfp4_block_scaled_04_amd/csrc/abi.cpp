@@ -139,37 +139,70 @@ int nvfp4_quantize_lora_down(const void* x, int64_t m, int64_t k, const void* pr
                                                       (hipStream_t)stream));
 }
 
-int nvfp4_quantize_masked_batched(const void* x, int64_t b, int64_t m, int64_t k,
-                                  const int32_t* mask, float* global_scale, int gs_mode,
-                                  uint8_t* out_fp4, uint8_t* out_sf, void* stream) {
+// The batched forms (k_in: the input row width, 2K for silu): every check of
+// the call, then the launch; with_ws: the *_ws forms (gs_other / alpha and,
+// in DYNAMIC mode, the workspace).
+static int batched_common(const void* x, int64_t b, int64_t m, int64_t k_in, bool silu, const int32_t* mask,
+                          float* global_scale, int gs_mode, const float* gs_other, float* alpha,
+                          uint8_t* out_fp4, uint8_t* out_sf, bool with_ws, void* workspace,
+                          int64_t workspace_bytes, void* stream) {
     if (!x || !global_scale || !out_fp4 || !out_sf) return NVFP4_NULL_POINTER;
+    if (!gs_other != !alpha) return NVFP4_NULL_POINTER;
     if (gs_mode != NVFP4_GS_STATIC && gs_mode != NVFP4_GS_DYNAMIC) return NVFP4_UNSUPPORTED;
+    int64_t k = k_in;
+    if (silu) {
+        if (k_in < 32 || k_in % 2 != 0 || (k_in / 2) % 16 != 0) return NVFP4_BAD_SHAPE;
+        k = k_in / 2;
+    }
     if (k < 16 || k % 16 != 0 || !quant_sizes_ok(b, m, k)) return NVFP4_BAD_SHAPE;
+    const bool use_ws = with_ws && gs_mode == NVFP4_GS_DYNAMIC;
+    if (use_ws) {
+        if (!workspace) return NVFP4_NULL_POINTER;
+        if (workspace_bytes < NVFP4_BATCHED_WS_BYTES(b, m, k)) return NVFP4_BAD_SHAPE;
+    }
     if (!aligned16(x) || !aligned16(out_fp4) || !aligned16(out_sf) || ((uintptr_t)global_scale & 3u) ||
-        ((uintptr_t)mask & 3u))
+        ((uintptr_t)mask & 3u) || ((uintptr_t)gs_other & 3u) || ((uintptr_t)alpha & 3u) ||
+        (use_ws && !aligned16(workspace)))
         return NVFP4_MISALIGNED;
     nvfp4::QuantizeArgs a{};
     a.x = x; a.x_dtype = NVFP4_BF16; a.pqs = nullptr; a.mask = mask;
     a.gs = global_scale; a.out_fp4 = out_fp4; a.out_sf = out_sf;
-    a.b = b; a.m = m; a.k_in = k; a.silu = false; a.dynamic = gs_mode == NVFP4_GS_DYNAMIC;
+    a.b = b; a.m = m; a.k_in = k_in; a.silu = silu; a.dynamic = gs_mode == NVFP4_GS_DYNAMIC;
+    a.gs_other = gs_other; a.alpha_out = alpha;
+    a.ws = use_ws ? (float*)workspace : nullptr;
     return launch_status(nvfp4::launch_quantize(a, (hipStream_t)stream));
+}
+
+static_assert(NVFP4_BATCHED_WS_BYTES(1, 1, 16) >= nvfp4::kQuantizeWsFloats * 4, "the flat amax pass's partials fit");
+
+int nvfp4_quantize_masked_batched(const void* x, int64_t b, int64_t m, int64_t k,
+                                  const int32_t* mask, float* global_scale, int gs_mode,
+                                  uint8_t* out_fp4, uint8_t* out_sf, void* stream) {
+    return batched_common(x, b, m, k, false, mask, global_scale, gs_mode, nullptr, nullptr, out_fp4, out_sf,
+                          false, nullptr, 0, stream);
+}
+
+int nvfp4_quantize_masked_batched_ws(const void* x, int64_t b, int64_t m, int64_t k, const int32_t* mask,
+                                     float* global_scale, int gs_mode, const float* gs_other, float* alpha,
+                                     uint8_t* out_fp4, uint8_t* out_sf, void* workspace,
+                                     int64_t workspace_bytes, void* stream) {
+    return batched_common(x, b, m, k, false, mask, global_scale, gs_mode, gs_other, alpha, out_fp4, out_sf,
+                          true, workspace, workspace_bytes, stream);
 }
 
 int silu_mul_nvfp4_quantize(const void* x, int64_t b, int64_t m, int64_t k2, const int32_t* mask,
                             float* global_scale, int gs_mode, uint8_t* out_fp4, uint8_t* out_sf,
                             void* stream) {
-    if (!x || !global_scale || !out_fp4 || !out_sf) return NVFP4_NULL_POINTER;
-    if (gs_mode != NVFP4_GS_STATIC && gs_mode != NVFP4_GS_DYNAMIC) return NVFP4_UNSUPPORTED;
-    if (k2 < 32 || k2 % 2 != 0 || (k2 / 2) % 16 != 0 || !quant_sizes_ok(b, m, k2 / 2))
-        return NVFP4_BAD_SHAPE;
-    if (!aligned16(x) || !aligned16(out_fp4) || !aligned16(out_sf) || ((uintptr_t)global_scale & 3u) ||
-        ((uintptr_t)mask & 3u))
-        return NVFP4_MISALIGNED;
-    nvfp4::QuantizeArgs a{};
-    a.x = x; a.x_dtype = NVFP4_BF16; a.pqs = nullptr; a.mask = mask;
-    a.gs = global_scale; a.out_fp4 = out_fp4; a.out_sf = out_sf;
-    a.b = b; a.m = m; a.k_in = k2; a.silu = true; a.dynamic = gs_mode == NVFP4_GS_DYNAMIC;
-    return launch_status(nvfp4::launch_quantize(a, (hipStream_t)stream));
+    return batched_common(x, b, m, k2, true, mask, global_scale, gs_mode, nullptr, nullptr, out_fp4, out_sf,
+                          false, nullptr, 0, stream);
+}
+
+int silu_mul_nvfp4_quantize_ws(const void* x, int64_t b, int64_t m, int64_t k2, const int32_t* mask,
+                               float* global_scale, int gs_mode, const float* gs_other, float* alpha,
+                               uint8_t* out_fp4, uint8_t* out_sf, void* workspace, int64_t workspace_bytes,
+                               void* stream) {
+    return batched_common(x, b, m, k2, true, mask, global_scale, gs_mode, gs_other, alpha, out_fp4, out_sf,
+                          true, workspace, workspace_bytes, stream);
 }
 
 static_assert(NVFP4_GEMM_WS_BYTES == nvfp4::kGemmWsBytes, "GEMM workspace size");

@@ -20,8 +20,9 @@ struct QuantizeArgs {
     bool dynamic;
     const float* gs_other = nullptr;  // with alpha_out: [b] the other operand's global scales
     float* alpha_out = nullptr;       // [b] alpha = 1 / (gs * gs_other), or null
-    float* ws = nullptr;              // DYNAMIC, b == 1, no mask: >= kQuantizeWsFloats floats for the
-                                      // partial maxima (two launches instead of three), or null
+    float* ws = nullptr;              // DYNAMIC: the partial maxima (two launches instead of three), or
+                                      // null; b == 1 without mask and silu: >= kQuantizeWsFloats floats,
+                                      // otherwise >= b * ceil(m/128) * ceil(K/64) floats
 };
 
 // Floats of workspace a DYNAMIC single-tensor quantization uses for its

@@ -37,27 +37,62 @@ __device__ __forceinline__ float silu_f32(float g) {
 // subnormals) and |p| in [2^-100, 2^100).  Elements that fail it (about 1 in
 // 500 for N(0,1) data, and every |g| >= 16, inf and NaN) take the exact fp64
 // path.
-__device__ __forceinline__ uint32_t silu_mul_fast2(uint32_t gw, uint32_t uw, uint32_t& bad) {
+//
+// The two failure kinds are reported apart: `rng` (an operand or the product
+// outside the ranges above, inf, NaN: nothing is known of h) and `win` (in
+// range, but the low half of p within 64 of 0x8000: h is bf16(p) or its
+// neighbour on the other side of p, i.e. |h| is at most the magnitude bits
+// of bf16(p) plus one).
+__device__ __forceinline__ uint32_t silu_mul_fast2s(uint32_t gw, uint32_t uw, uint32_t& rng, uint32_t& win) {
     constexpr float kLog2e = 1.44269504088896340736f;
     const float g0 = bf16_lo(gw), g1 = bf16_hi(gw);
     const float y0 = g0 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g0 * -kLog2e));
     const float y1 = g1 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g1 * -kLog2e));
     const float p0 = y0 * bf16_lo(uw), p1 = y1 * bf16_hi(uw);
     // (bitwise, not short-circuit, so the test stays branch-free)
-    auto fails = [](float g, float p) -> uint32_t {
-        const uint32_t ga = f_bits(g) & 0x7FFFFFFFu, pb = f_bits(p), pa = pb & 0x7FFFFFFFu;
+    auto out_of_range = [](float g, float p) -> uint32_t {
+        const uint32_t ga = f_bits(g) & 0x7FFFFFFFu, pa = f_bits(p) & 0x7FFFFFFFu;
         return (uint32_t)(ga - 0x19000000u >= 0x41800000u - 0x19000000u) |  // not 2^-77 <= |g| < 16
-               (uint32_t)(pa - 0x0D800000u >= 0x64000000u) |                 // not 2^-100 <= |p| < 2^100
-               (uint32_t)((pb & 0xFFFFu) - 0x7FC0u <= 0x80u);                // low half within 64 of 0x8000
+               (uint32_t)(pa - 0x0D800000u >= 0x64000000u);                  // not 2^-100 <= |p| < 2^100
     };
-    bad = fails(g0, p0) | (fails(g1, p1) << 1);
+    auto near_tie = [](float p) -> uint32_t {
+        return (uint32_t)((f_bits(p) & 0xFFFFu) - 0x7FC0u <= 0x80u);  // low half within 64 of 0x8000
+    };
+    rng = out_of_range(g0, p0) | (out_of_range(g1, p1) << 1);
+    win = near_tie(p0) | (near_tie(p1) << 1);
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0, p1}, bf16x2));  // RNE
 }
 
+__device__ __forceinline__ uint32_t silu_mul_fast2(uint32_t gw, uint32_t uw, uint32_t& bad) {
+    uint32_t rng, win;
+    const uint32_t h = silu_mul_fast2s(gw, uw, rng, win);
+    bad = rng | win;
+    return h;
+}
+
 __device__ __forceinline__ uint32_t silu_mul_exact(float g, float u) {
     return f32_to_bf16_rne(silu_f32(g) * u);
+}
+
+// Element `bit` (2j + half) of a silu block's gate / up words r[0..3] through
+// the exact path, written into its bf16 half of w[j]: a single inlined copy
+// of the exact path for every flagged element of the block, one at a time.
+__device__ __forceinline__ void silu_exact_into(const u32x4 (&r)[4], int bit, uint32_t (&w)[8]) {
+    const int j = bit >> 1, sh = (bit & 1) * 16;
+    uint32_t gw = 0, uw = 0;
+#pragma unroll
+    for (int jj = 0; jj < 8; jj++) {
+        if (jj == j) {
+            gw = jj < 4 ? r[0][jj] : r[1][jj - 4];
+            uw = jj < 4 ? r[2][jj] : r[3][jj - 4];
+        }
+    }
+    const uint32_t h = silu_mul_exact(bits_f((gw >> sh) << 16), bits_f((uw >> sh) << 16));
+#pragma unroll
+    for (int jj = 0; jj < 8; jj++)
+        if (jj == j) w[jj] = (w[jj] & ~(0xFFFFu << sh)) | (h << sh);
 }
 
 // 16-byte loads behind one 16-element block of a row.
@@ -94,19 +129,7 @@ __device__ __forceinline__ float process_block(const u32x4 (&r)[loads_per_block<
             while (need) {
                 const int bit = __builtin_ctz(need);
                 need &= need - 1;
-                const int j = bit >> 1, sh = (bit & 1) * 16;
-                uint32_t gw = 0, uw = 0;
-#pragma unroll
-                for (int jj = 0; jj < 8; jj++) {
-                    if (jj == j) {
-                        gw = jj < 4 ? r[0][jj] : r[1][jj - 4];
-                        uw = jj < 4 ? r[2][jj] : r[3][jj - 4];
-                    }
-                }
-                const uint32_t h = silu_mul_exact(bits_f((gw >> sh) << 16), bits_f((uw >> sh) << 16));
-#pragma unroll
-                for (int jj = 0; jj < 8; jj++)
-                    if (jj == j) w[jj] = (w[jj] & ~(0xFFFFu << sh)) | (h << sh);
+                silu_exact_into(r, bit, w);
             }
         }
         // bf16 magnitudes compare as integers; inf / NaN patterns sort above
@@ -153,6 +176,62 @@ __device__ __forceinline__ float process_block(const u32x4 (&r)[loads_per_block<
     for (int j = 0; j < 16; j++) {
         f[j] = nan_to_num(f[j]);
         a = __builtin_fmaxf(a, __builtin_fabsf(f[j]));
+    }
+    return a;
+}
+
+// Largest |h| of a silu block (nan_to_num applied), given that `thr` (>= 0,
+// a value already attained) is a lower bound of the result: as
+// process_block<V_SILU> for the maximum, except that an element flagged only
+// for being near a bf16 tie skips the exact path when even the larger of its
+// two possible values, |bf16(p)| + 1 ulp, cannot exceed max(thr, the block's
+// unflagged magnitudes) -- it cannot change the maximum then.
+__device__ __forceinline__ float silu_block_amax(const u32x4 (&r)[4], float thr) {
+    uint32_t w[8];
+    uint32_t rng = 0, win = 0;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const uint32_t gw = j < 4 ? r[0][j] : r[1][j - 4];
+        const uint32_t uw = j < 4 ? r[2][j] : r[3][j - 4];
+        uint32_t rb, wb;
+        w[j] = silu_mul_fast2s(gw, uw, rb, wb);
+        rng |= rb << (2 * j);
+        win |= wb << (2 * j);
+    }
+    uint32_t need = rng;
+    uint32_t tie = win & ~rng;
+    if (tie) {
+        // bound from thr and the unflagged elements (their bf16 h is exact)
+        uint32_t tb = f_bits(thr) >> 16;
+        const uint32_t flagged = rng | win;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const uint32_t m0 = (flagged >> (2 * j)) & 1u ? 0u : w[j] & 0x7FFFu;
+            const uint32_t m1 = (flagged >> (2 * j + 1)) & 1u ? 0u : (w[j] >> 16) & 0x7FFFu;
+            tb = __builtin_elementwise_max(tb, __builtin_elementwise_max(m0, m1));
+        }
+        while (tie) {
+            const int bit = __builtin_ctz(tie);
+            tie &= tie - 1;
+            uint32_t hw = 0;
+#pragma unroll
+            for (int jj = 0; jj < 8; jj++)
+                if (jj == (bit >> 1)) hw = w[jj];
+            if (((hw >> ((bit & 1) * 16)) & 0x7FFFu) + 1u > tb) need |= 1u << bit;
+        }
+    }
+    while (need) {
+        const int bit = __builtin_ctz(need);
+        need &= need - 1;
+        silu_exact_into(r, bit, w);
+    }
+    const uint32_t mb = __builtin_elementwise_max(absmax_bits_bf16x8(w), absmax_bits_bf16x8(w + 4));
+    if (mb < 0x7F80u) return bits_f(mb << 16);
+    float a = 0.0f;  // inf or NaN present: nan_to_num
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+        const float v = nan_to_num((j & 1) ? bf16_hi(w[j >> 1]) : bf16_lo(w[j >> 1]));
+        a = __builtin_fmaxf(a, __builtin_fabsf(v));
     }
     return a;
 }

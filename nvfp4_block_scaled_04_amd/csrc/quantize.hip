@@ -137,16 +137,26 @@ __global__ __launch_bounds__(256) void k_amax(QParams p) {
         load_pqs<V>(p, col, pq);
         u32x4 raw[TM::NP][NL];
 #pragma unroll
-        for (int i = 0; i < TM::NP; i++) {  // every load in flight before any use
+        for (int i = 0; i < TM::NP; i++) {  // every load in flight before any use; rows past the valid ones are not read
             const int64_t row = (int64_t)rt * 128 + rsub + TM::RPP * i;
-            load_block<V>(p, e, row < p.m ? row : p.m - 1, col, raw[i]);
+            if (row < valid) {
+                load_block<V>(p, e, row, col, raw[i]);
+            } else {
+#pragma unroll
+                for (int l = 0; l < NL; l++) raw[i][l] = u32x4{0u, 0u, 0u, 0u};
+            }
         }
 #pragma unroll
         for (int i = 0; i < TM::NP; i++) {
             const int64_t row = (int64_t)rt * 128 + rsub + TM::RPP * i;
-            float f[16];
-            const float a = process_block<V>(raw[i], pq, f);
-            if (col_ok && row < valid) amax = __builtin_fmaxf(amax, a);
+            if (col_ok && row < valid) {
+                if constexpr (V == V_SILU) {
+                    amax = __builtin_fmaxf(amax, silu_block_amax(raw[i], amax));
+                } else {
+                    float f[16];
+                    amax = __builtin_fmaxf(amax, process_block<V>(raw[i], pq, f));
+                }
+            }
         }
     }
     // workgroup max: wave reduction through shuffles, then LDS across waves
@@ -315,7 +325,16 @@ __device__ __forceinline__ void quantize_tile(const QParams& p, int wct, int rt,
 #pragma unroll
     for (int i = 0; i < TM::NP; i++) {  // every load in flight before any use
         const int64_t row = (int64_t)rt * 128 + rsub + TM::RPP * i;
-        load_block<V>(p, e, row < p.m ? row : p.m - 1, col, raw[i]);
+        if constexpr (V == V_SILU) {  // rows past the valid ones are not read (nor processed, below)
+            if (row < valid) {
+                load_block<V>(p, e, row, col, raw[i]);
+            } else {
+#pragma unroll
+                for (int l = 0; l < NL; l++) raw[i][l] = u32x4{0u, 0u, 0u, 0u};
+            }
+        } else {
+            load_block<V>(p, e, row < p.m ? row : p.m - 1, col, raw[i]);
+        }
     }
     // element factors r = gs / dec(s) for every scale code (0 for code 0),
     // computed while the loads are in flight
@@ -330,20 +349,23 @@ __device__ __forceinline__ void quantize_tile(const QParams& p, int wct, int rt,
         const int rl = rsub + TM::RPP * i;  // row within the 128-row tile
         const int64_t row = (int64_t)rt * 128 + rl;
         const bool active = col_ok && row < valid;
-        float f[16];
-        const float bamax = process_block<V>(raw[i], pq, f);
-        const uint32_t sc = active ? ue4m3_encode(div6(bamax) * gs) : 0u;
-        const float r = rtab[sc];
-        uint32_t w0 = 0, w1 = 0;
-        w0 = NVFP4_PACK_FP4(w0, f[0] * r, f[1] * r, 0);
-        w0 = NVFP4_PACK_FP4(w0, f[2] * r, f[3] * r, 1);
-        w0 = NVFP4_PACK_FP4(w0, f[4] * r, f[5] * r, 2);
-        w0 = NVFP4_PACK_FP4(w0, f[6] * r, f[7] * r, 3);
-        w1 = NVFP4_PACK_FP4(w1, f[8] * r, f[9] * r, 0);
-        w1 = NVFP4_PACK_FP4(w1, f[10] * r, f[11] * r, 1);
-        w1 = NVFP4_PACK_FP4(w1, f[12] * r, f[13] * r, 2);
-        w1 = NVFP4_PACK_FP4(w1, f[14] * r, f[15] * r, 3);
-        if (active) *(uint2*)(q + row * (p.K / 2) + col / 2) = uint2{w0, w1};
+        uint32_t sc = 0u;  // rows past the valid ones (and blocks past K): zero scale, no FP4 written
+        if (V != V_SILU || active) {  // (the silu work of padding rows is skipped; elsewhere it is cheap)
+            float f[16];
+            const float bamax = process_block<V>(raw[i], pq, f);
+            sc = active ? ue4m3_encode(div6(bamax) * gs) : 0u;
+            const float r = rtab[sc];
+            uint32_t w0 = 0, w1 = 0;
+            w0 = NVFP4_PACK_FP4(w0, f[0] * r, f[1] * r, 0);
+            w0 = NVFP4_PACK_FP4(w0, f[2] * r, f[3] * r, 1);
+            w0 = NVFP4_PACK_FP4(w0, f[4] * r, f[5] * r, 2);
+            w0 = NVFP4_PACK_FP4(w0, f[6] * r, f[7] * r, 3);
+            w1 = NVFP4_PACK_FP4(w1, f[8] * r, f[9] * r, 0);
+            w1 = NVFP4_PACK_FP4(w1, f[10] * r, f[11] * r, 1);
+            w1 = NVFP4_PACK_FP4(w1, f[12] * r, f[13] * r, 2);
+            w1 = NVFP4_PACK_FP4(w1, f[14] * r, f[15] * r, 3);
+            if (active) *(uint2*)(q + row * (p.K / 2) + col / 2) = uint2{w0, w1};
+        }
         sbuf[c * 512 + (rl & 31) * 16 + (rl >> 5) * 4 + blk] = (uint8_t)sc;
     }
     __syncthreads();
@@ -360,6 +382,12 @@ __global__ __launch_bounds__(256) void k_quantize(QParams p) {
     const int e = blockIdx.z;
     const bool first = blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0;
     if constexpr (FROM_PART) {
+        // an item without valid rows has only tiles that never ask for gs:
+        // its amax is 0 (all its partials are)
+        if (first && clamp_rows(p.mask, e, (int)p.m) == 0) {
+            p.gs[e] = gs_from_amax(0.0f);
+            write_alpha(p, e, p.gs[e]);
+        }
         __shared__ float wmax[4];
         quantize_tile<V, CT>(p, blockIdx.x, blockIdx.y, e, [&] {
             const float gs = gs_from_amax(reduce_partials(p, e, wmax));
@@ -734,10 +762,18 @@ static hipError_t launch_variant(QParams p, bool dynamic, float* ws, hipStream_t
             launch_amax_flat<V>(p, ws, st);
             from_part = ws != nullptr;
         } else {
-            // one amax workgroup, and one partial maximum, per amax tile
+            // one amax workgroup, and one partial maximum, per amax tile:
+            // into the workspace (the quantize pass then reduces an item's
+            // partials itself) or into each item's own scale buffer
             p.nparts = p.nrt * ((p.nct + CTA - 1) / CTA);
-            p.part = (float*)p.out_sf;
-            p.part_stride = p.sfsz / 4;
+            if (ws) {
+                p.part = ws;
+                p.part_stride = p.nparts;
+                from_part = true;
+            } else {
+                p.part = (float*)p.out_sf;
+                p.part_stride = p.sfsz / 4;
+            }
             k_amax<V, CTA><<<dim3(p.nparts, p.b), 256, 0, st>>>(p);
         }
         if (!from_part) k_finish_gs<<<p.b, 256, 0, st>>>(p);
@@ -774,8 +810,8 @@ hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t st) {
     p.gs_other = a.gs_other;
     p.alpha_out = a.alpha_out;
     const bool dyn = a.dynamic;
-    float* ws = a.b == 1 && !a.mask ? a.ws : nullptr;
-    if (a.silu) return launch_variant<V_SILU>(p, dyn, nullptr, st);
+    float* ws = a.ws;
+    if (a.silu) return launch_variant<V_SILU>(p, dyn, ws, st);
     if (a.x_dtype == 0) {
         if (a.pqs) return launch_variant<V_BF16_SMOOTH>(p, dyn, ws, st);
         return launch_variant<V_BF16>(p, dyn, ws, st);

@@ -21,7 +21,9 @@ EXPORTS = (
     "nvfp4_quantize_noalloc",
     "nvfp4_quantize_lora_down",
     "nvfp4_quantize_masked_batched",
+    "nvfp4_quantize_masked_batched_ws",
     "silu_mul_nvfp4_quantize",
+    "silu_mul_nvfp4_quantize_ws",
     "nvfp4_gemm",
     "nvfp4_gemm_grouped_masked",
     "nvfp4_gemm_grouped_masked_silu_quantize",
@@ -59,6 +61,8 @@ def _load():
         "nvfp4_quantize_lora_down": [vp, i64, i64, vp, vp, i64, vp, i32, vp, vp, vp, vp],
         "nvfp4_quantize_masked_batched": [vp, i64, i64, i64, vp, vp, i32, vp, vp, vp],
         "silu_mul_nvfp4_quantize": [vp, i64, i64, i64, vp, vp, i32, vp, vp, vp],
+        "nvfp4_quantize_masked_batched_ws": [vp, i64, i64, i64, vp, vp, i32, vp, vp, vp, vp, vp, i64, vp],
+        "silu_mul_nvfp4_quantize_ws": [vp, i64, i64, i64, vp, vp, i32, vp, vp, vp, vp, vp, i64, vp],
         "nvfp4_gemm": [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, vp],
         "nvfp4_gemm_grouped_masked": [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp],
         "nvfp4_gemm_grouped_masked_silu_quantize": [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp],
@@ -352,6 +356,68 @@ def silu_mul_nvfp4_quantize(x, mask=None, global_scale=None, gs_mode=GS_DYNAMIC,
                                       _ptr(out_fp4), _ptr(out_sf), _stream(dev))
     _check(rc, "silu_mul_nvfp4_quantize")
     return out_fp4, out_sf, global_scale
+
+
+def batched_ws_bytes(b, m, k):
+    """NVFP4_BATCHED_WS_BYTES(b, m, k): workspace of the batched *_ws quantizers
+    (k: the quantized width)."""
+    return 4096 + 4 * b * ((m + 127) // 128) * ((k + 63) // 64)
+
+
+def batched_workspace(b, m, k, device):
+    """A workspace for nvfp4_quantize_masked_batched_ws / silu_mul_nvfp4_quantize_ws
+    (caller-owned device memory)."""
+    return torch.empty(batched_ws_bytes(b, m, k), dtype=torch.uint8, device=device)
+
+
+def _batched_ws(fn, x, b, m, k_in, k, workspace, mask, global_scale, gs_mode, gs_other, alpha, out_fp4, out_sf):
+    dev = x.device
+    _dev(x, "x", BF16, b * m * k_in, dev)
+    if global_scale is None:
+        global_scale = torch.zeros(b, dtype=torch.float32, device=dev)
+    if out_fp4 is None:
+        out_fp4 = torch.empty(b, m, k // 2, dtype=torch.uint8, device=dev)
+    if out_sf is None:
+        out_sf = torch.empty(b, sf_size(m, k), dtype=torch.uint8, device=dev)
+    if alpha is not None and gs_other is None:
+        raise ValueError("alpha needs gs_other")
+    if gs_other is not None and alpha is None:
+        alpha = torch.empty(b, dtype=torch.float32, device=dev)
+    _opt(mask, "mask", I32, b, dev)
+    _dev(global_scale, "global_scale", F32, b, dev)
+    _opt(gs_other, "gs_other", F32, b, dev)
+    _opt(alpha, "alpha", F32, b, dev)
+    _dev(out_fp4, "out_fp4", BYTES, b * m * (k // 2), dev)
+    _dev(out_sf, "out_sf", BYTES, b * sf_size(m, k), dev)
+    if gs_mode == GS_DYNAMIC:
+        _dev(workspace, "workspace", BYTES, batched_ws_bytes(b, m, k), dev)
+    wsb = workspace.numel() if workspace is not None else 0
+    rc = getattr(_lib, fn)(_ptr(x), b, m, k_in, _ptr(mask), _ptr(global_scale), gs_mode, _ptr(gs_other),
+                           _ptr(alpha), _ptr(out_fp4), _ptr(out_sf), _ptr(workspace), wsb, _stream(dev))
+    _check(rc, fn)
+    return out_fp4, out_sf, global_scale, alpha
+
+
+def nvfp4_quantize_masked_batched_ws(x, workspace, mask=None, global_scale=None, gs_mode=GS_DYNAMIC,
+                                     gs_other=None, alpha=None, out_fp4=None, out_sf=None):
+    """nvfp4_quantize_masked_batched with a workspace ([batched_ws_bytes(b, m, k)]
+    bytes) and, given gs_other [b], alpha [b] = 1 / (gs * gs_other) from the same
+    call -> (fp4, sf, gs, alpha or None)."""
+    _dims(x, "x", 3)
+    b, m, k = x.shape
+    return _batched_ws("nvfp4_quantize_masked_batched_ws", x, b, m, k, k, workspace, mask, global_scale,
+                       gs_mode, gs_other, alpha, out_fp4, out_sf)
+
+
+def silu_mul_nvfp4_quantize_ws(x, workspace, mask=None, global_scale=None, gs_mode=GS_DYNAMIC,
+                               gs_other=None, alpha=None, out_fp4=None, out_sf=None):
+    """silu_mul_nvfp4_quantize with a workspace ([batched_ws_bytes(b, m, h)] bytes)
+    and, given gs_other [b], alpha [b] from the same call -> (fp4, sf, gs, alpha
+    or None)."""
+    _dims(x, "x", 3)
+    b, m, k2 = x.shape
+    return _batched_ws("silu_mul_nvfp4_quantize_ws", x, b, m, k2, k2 // 2, workspace, mask, global_scale,
+                       gs_mode, gs_other, alpha, out_fp4, out_sf)
 
 
 # ---- GEMM -----------------------------------------------------------------------

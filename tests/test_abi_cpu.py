@@ -38,8 +38,8 @@ def test_header_declares_the_entry_points():
         "nvfp4_gemm_ws", "nvfp4_gemm_grouped_masked_ws", "nvfp4_gemm_svdquant_ws",
         "nvfp4_gemm_w4a16", "nvfp4_quantize_lora_down",
         "nvfp4_quantize", "nvfp4_quantize_alpha", "nvfp4_quantize_ws", "nvfp4_quantize_noalloc",
-        "nvfp4_quantize_masked_batched",
-        "silu_mul_nvfp4_quantize",
+        "nvfp4_quantize_masked_batched", "nvfp4_quantize_masked_batched_ws",
+        "silu_mul_nvfp4_quantize", "silu_mul_nvfp4_quantize_ws",
         "mxfp4_quantize", "mxfp4_gemm",
     ])
 
@@ -117,6 +117,32 @@ def test_batched_validation(lib, fn):
     assert qb(lib, fn, mode=2) == UNSUP
     assert qb(lib, fn, x=P + 2) == MISAL
     assert qb(lib, fn, mask=P + 1) == MISAL
+
+
+@pytest.mark.parametrize("fn,silu", [("nvfp4_quantize_masked_batched_ws", False), ("silu_mul_nvfp4_quantize_ws", True)])
+def test_batched_ws_validation(lib, fn, silu):
+    """The batched checks, the optional alpha pair and, in DYNAMIC mode, the
+    workspace: present, at least NVFP4_BATCHED_WS_BYTES(b, m, k), 16-byte
+    aligned; STATIC mode ignores it."""
+    f = getattr(lib, fn)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    f.argtypes = [vp, i64, i64, i64, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, i64, vp]
+    b, m, kin = 2, 300, 128
+    k = kin // 2 if silu else kin
+    need = 4096 + 4 * b * ((m + 127) // 128) * ((k + 63) // 64)
+    run = lambda x=P, kk=kin, mode=1, go=None, al=None, ws=P, wsb=need, mask=None: \
+        f(x, b, m, kk, mask, P, mode, go, al, P, P, ws, wsb, None)
+    assert run(x=None) == NULLP
+    assert run(go=P) == NULLP
+    assert run(al=P) == NULLP
+    assert run(ws=None) == NULLP
+    assert run(wsb=need - 1) == SHAPE
+    assert run(ws=P + 4) == MISAL
+    assert run(go=P + 2, al=P) == MISAL
+    assert run(mask=P + 1) == MISAL
+    assert run(mode=3) == UNSUP
+    assert run(kk=40) == SHAPE
+    assert run(mode=0, ws=None, kk=40) == SHAPE   # STATIC: no workspace needed (refused here for k)
 
 
 def test_silu_width_rules(lib):

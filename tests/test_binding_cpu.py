@@ -28,6 +28,8 @@ CALLS = {
     "nvfp4_quantize_lora_down": lambda: ops.nvfp4_quantize_lora_down(bf(128, 64), bf(64), bf(32, 64)),
     "nvfp4_quantize_masked_batched": lambda: ops.nvfp4_quantize_masked_batched(bf(2, 128, 64)),
     "silu_mul_nvfp4_quantize": lambda: ops.silu_mul_nvfp4_quantize(bf(2, 128, 64)),
+    "nvfp4_quantize_masked_batched_ws": lambda: ops.nvfp4_quantize_masked_batched_ws(bf(2, 128, 64), u8(16)),
+    "silu_mul_nvfp4_quantize_ws": lambda: ops.silu_mul_nvfp4_quantize_ws(bf(2, 128, 64), u8(16)),
     "nvfp4_gemm": lambda: ops.nvfp4_gemm(u8(128, 32), u8(64, 32), u8(ops.sf_size(128, 64)),
                                          u8(ops.sf_size(64, 64)), f32(1)),
     "nvfp4_gemm_grouped_masked": lambda: ops.nvfp4_gemm_grouped_masked(

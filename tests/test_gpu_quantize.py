@@ -166,17 +166,25 @@ def test_quantize_lora_down(ops, m, k, r, dynamic):
 
 # ---- batched / masked / silu -------------------------------------------------------
 
-def run_batched(ops, x_cpu, mask, mode, silu=False, gs=None):
+def run_batched(ops, x_cpu, mask, mode, silu=False, gs=None, ws=False):
+    """ws: through the *_ws entry point, with a workspace of stale bytes and a
+    gs_other, so that alpha is checked too."""
     b, m, kin = x_cpu.shape
     K = kin // 2 if silu else kin
     say("batched", tuple(x_cpu.shape), "silu", silu, "mask", None if mask is None else mask.tolist(),
-        "mode", mode)
+        "mode", mode, "ws", ws)
     x = dev(x_cpu)
     mk = None if mask is None else dev(mask)
     gs_d = torch.zeros(b, dtype=torch.float32, device="cuda") if gs is None else dev(gs.clone())
     o4 = canary((b, m, K // 2))
     osf = canary((b, ops.sf_size(m, K)))
-    if silu:
+    if ws:
+        w = ops.batched_workspace(b, m, K, "cuda").fill_(0x5A)
+        go = (torch.rand(b, generator=torch.Generator().manual_seed(b + m + K)) * 500 + 1).to(torch.float32)
+        al = torch.full((b,), float("nan"), dtype=torch.float32, device="cuda")
+        fn = ops.silu_mul_nvfp4_quantize_ws if silu else ops.nvfp4_quantize_masked_batched_ws
+        fn(x, w, mk, gs_d, mode, gs_other=dev(go), alpha=al, out_fp4=o4, out_sf=osf)
+    elif silu:
         ops.silu_mul_nvfp4_quantize(x, mk, gs_d, mode, out_fp4=o4, out_sf=osf)
     else:
         ops.nvfp4_quantize_masked_batched(x, mk, gs_d, mode, out_fp4=o4, out_sf=osf)
@@ -186,11 +194,40 @@ def run_batched(ops, x_cpu, mask, mode, silu=False, gs=None):
                           mask=None if mask is None else mask.numpy(),
                           gs=None if gs is None else gs.numpy(), gs_mode=mode, out_fp4=fill)
     assert np.array_equal(np_bits(gs_d).view(np.uint32), g.view(np.uint32)), (np_bits(gs_d), g)
+    if ws:
+        want = (np.float32(1.0) / (g.astype(np.float32) * go.numpy())).astype(np.float32)
+        assert np.array_equal(np_bits(al).view(np.uint32), want.view(np.uint32)), (np_bits(al), want)
     gq, gsf = np_bits(o4), np_bits(osf)
     bad = np.argwhere(gq != q)
     assert len(bad) == 0, f"{len(bad)} FP4 bytes differ, first at {bad[:3].tolist()}"
     bad = np.argwhere(gsf != sf)
     assert len(bad) == 0, f"{len(bad)} scale bytes differ, first at {bad[:3].tolist()}"
+
+
+@pytest.mark.parametrize("silu", [False, True])
+@pytest.mark.parametrize("mask,k", [(None, 512), ([0, 1, 129, 200], 512), ([200, 0, 7, 130], 2048),
+                                    ([5, 0, 0, 77], 96), ([0, 0, 0, 0], 512)])
+def test_batched_ws(ops, silu, mask, k):
+    """The *_ws batched forms: the quantize pass reduces each item's partial
+    maxima from the workspace (two launches; the small items' one-launch path
+    too) and writes alpha; bytes, gs and alpha equal the oracle's."""
+    g = torch.Generator().manual_seed(41 + k)
+    x = (torch.randn(4, 200, 2 * k if silu else k, generator=g) *
+         torch.tensor([1.0, 10.0, 0.1, 3.0])[:, None, None])
+    mk = None if mask is None else torch.tensor(mask, dtype=torch.int32)
+    run_batched(ops, x.to(torch.bfloat16), mk, ops.GS_DYNAMIC, silu=silu, ws=True)
+
+
+def test_batched_ws_static(ops):
+    g = torch.Generator().manual_seed(42)
+    x = torch.randn(3, 130, 768, generator=g).to(torch.bfloat16)
+    run_batched(ops, x, torch.tensor([130, 64, 1], dtype=torch.int32), ops.GS_STATIC,
+                gs=torch.tensor([100.0, 250.0, 3.0]), ws=True)
+
+
+def test_moe_workload_ws(ops):
+    mo = synth.moe(h=8192, n=64)
+    run_batched(ops, mo.x, mo.mask, ops.GS_DYNAMIC, silu=True, ws=True)
 
 
 @pytest.mark.parametrize("mask", [None, [0, 1, 129, 200], [200, 200, 200, 200], [5, 0, 0, 77]])
