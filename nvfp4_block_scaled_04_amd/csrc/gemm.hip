@@ -96,13 +96,18 @@ struct SkPlan {
     int T, D, R, S;
 };
 
-__device__ __forceinline__ int sk_rows(const GParams& p, int e, int bm) {
-    return (clamp_rows(p.mask, e, (int)p.M) + bm - 1) / bm;
+// Live tile rows of expert `lane` (0 for lanes >= E; E <= 64): the mask is
+// read once per wave, one expert per lane, all loads in flight together.
+__device__ __forceinline__ int sk_lane_rows(const GParams& p, int bm) {
+    const int lane = (int)(threadIdx.x & 63);
+    const int v = lane < (int)p.E ? clamp_rows(p.mask, lane, (int)p.M) : 0;
+    return (v + bm - 1) / bm;
 }
 
-__device__ __forceinline__ SkPlan sk_plan(const GParams& p, int bm, int nkt, int ks) {
-    int T = 0;
-    for (int e = 0; e < (int)p.E; e++) T += sk_rows(p, e, bm) * p.tiles_n;
+__device__ __forceinline__ SkPlan sk_plan(const GParams& p, int tme_lane, int nkt, int ks) {
+    int T = tme_lane * p.tiles_n;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) T += __shfl_xor(T, off);
     const int G = p.sk_grid;
     SkPlan s;
     s.T = T;
@@ -118,15 +123,17 @@ __device__ __forceinline__ SkPlan sk_plan(const GParams& p, int bm, int nkt, int
     return s;
 }
 
-// Expert and tile coordinates of live tile idx (0 <= idx < T).
-__device__ __forceinline__ void sk_tile(const GParams& p, int bm, int idx, int& e, int& tm, int& tn) {
-    for (e = 0; e < (int)p.E - 1; e++) {
-        const int cnt = sk_rows(p, e, bm) * p.tiles_n;
-        if (idx < cnt) break;
+// Expert and tile coordinates of live tile idx (0 <= idx < T); tme_lane
+// from sk_lane_rows (every lane of the wave active).
+__device__ __forceinline__ void sk_tile(const GParams& p, int tme_lane, int idx, int& e, int& tm, int& tn) {
+    int tme = 0;
+    for (e = 0; e < (int)p.E; e++) {
+        tme = __shfl(tme_lane, e);
+        const int cnt = tme * p.tiles_n;
+        if (idx < cnt || e == (int)p.E - 1) break;
         idx -= cnt;
     }
     constexpr int G8 = 8;
-    const int tme = sk_rows(p, e, bm);
     const int per = G8 * p.tiles_n;
     const int band = idx / per, first = band * G8;
     const int rows = tme - first < G8 ? tme - first : G8;
@@ -619,7 +626,8 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, (KS == 2 ? 2 : kWavesPerEU<BM 
         // schedule exit at once)
         static_assert(EPI != EPI_SILUQ, "the split schedule stores plain or LoRA tiles");
         const int G = p.sk_grid, w = blockIdx.x, round = w / G, b = w % G;
-        const SkPlan pl = sk_plan(p, BM, nkt, KS);
+        const int tme_lane = sk_lane_rows(p, BM);
+        const SkPlan pl = sk_plan(p, tme_lane, nkt, KS);
         const int rounds = pl.D / G;
         int idx, ks0 = 0, ks1 = nkt, slot = -1, lora = 1;
         if (round < rounds) {
@@ -637,7 +645,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, (KS == 2 ? 2 : kWavesPerEU<BM 
             return;
         }
         int e, tm, tn;
-        sk_tile(p, BM, idx, e, tm, tn);
+        sk_tile(p, tme_lane, idx, e, tm, tn);
         tile(__builtin_amdgcn_readfirstlane(e), __builtin_amdgcn_readfirstlane(tm),
              __builtin_amdgcn_readfirstlane(tn), __builtin_amdgcn_readfirstlane(ks0),
              __builtin_amdgcn_readfirstlane(ks1), __builtin_amdgcn_readfirstlane(slot),
@@ -660,13 +668,14 @@ __global__ __launch_bounds__(kFixupThreads) void k_gemm_fixup(GParams p) {
     constexpr int ITEMS = BM * BN / 4;  // float4 items of one partial tile
     static_assert(ITEMS % kFixupThreads == 0, "a workgroup's items lie in one tile");
     const int nkt = (int)((p.K + 127) / 128);
-    const SkPlan pl = sk_plan(p, BM, nkt, KS);
+    const int tme_lane = sk_lane_rows(p, BM);
+    const SkPlan pl = sk_plan(p, tme_lane, nkt, KS);
     if (pl.S <= 1) return;
     const int total = pl.R * ITEMS;
     for (int g0 = blockIdx.x * kFixupThreads; g0 < total; g0 += gridDim.x * kFixupThreads) {
         const int r = g0 / ITEMS, i = g0 % ITEMS + (int)threadIdx.x;
         int e, tm, tn;
-        sk_tile(p, BM, pl.D + r, e, tm, tn);
+        sk_tile(p, tme_lane, pl.D + r, e, tm, tn);
         const int valid = clamp_rows(p.mask, e, (int)p.M);
         const int lane = i & 63, v = (i >> 6) & 3, f = i >> 8;
         const int64_t m = (int64_t)tm * BM + (f / (BN / 32)) * 32 + (lane & 31);
