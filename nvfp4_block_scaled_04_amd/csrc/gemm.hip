@@ -531,6 +531,25 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, (KS == 2 ? 2 : kWavesPerEU<BM 
     const float alpha = p.alpha[e];
     uint16_t* O = p.out + (int64_t)e * p.M * p.N;
     constexpr int CPR = WN / 8;        // 16-byte pieces per staged row
+    // the bias of this lane's columns (4 consecutive per fragment column and
+    // group: one 8-byte load each, all in flight together; 0 past N)
+    u32x2 bias_v[FN][4];
+    if (EPI != EPI_SILUQ && p.bias) {
+#pragma unroll
+        for (int in = 0; in < FN; in++)
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                const int64_t n = n0 + wn * WN + in * 32 + g * 8 + h * 4;
+                if ((p.N & 3) == 0 && n + 3 < p.N) {
+                    bias_v[in][g] = *(const u32x2*)(p.bias + n);
+                } else {
+                    uint32_t b[4];
+#pragma unroll
+                    for (int u = 0; u < 4; u++) b[u] = n + u < p.N ? (uint32_t)p.bias[n + u] : 0u;
+                    bias_v[in][g] = u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
+                }
+            }
+    }
 #pragma unroll
     for (int im = 0; im < FM; im++) {
         if (KS == 2 && im != grp) continue;  // the other K group stores this fragment row
@@ -540,12 +559,14 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, (KS == 2 ? 2 : kWavesPerEU<BM 
 #pragma unroll
             for (int g = 0; g < 4; g++) {
                 const int cl = in * 32 + g * 8 + h * 4;  // column within the wave tile
-                const int64_t n = n0 + wn * WN + cl;
                 float y[4];
 #pragma unroll
                 for (int u = 0; u < 4; u++) {
                     y[u] = alpha * acc[in][im][g * 4 + u];
-                    if (p.bias && n + u < p.N) y[u] += bf16_lo((uint32_t)p.bias[n + u]);
+                    if (EPI != EPI_SILUQ && p.bias) {
+                        const uint32_t bw = u < 2 ? bias_v[in][g].x : bias_v[in][g].y;
+                        y[u] += (u & 1) ? bf16_hi(bw) : bf16_lo(bw);
+                    }
                 }
                 *(__attribute__((address_space(3))) u32x2*)(ep + l32 * PITCH + cl * 2) =
                     u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
@@ -568,7 +589,6 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, (KS == 2 ? 2 : kWavesPerEU<BM 
                 r[1] = *(const __attribute__((address_space(3))) u32x4*)(rowp + bc * 32 + 16);
                 r[2] = *(const __attribute__((address_space(3))) u32x4*)(rowp + WN + bc * 32);
                 r[3] = *(const __attribute__((address_space(3))) u32x4*)(rowp + WN + bc * 32 + 16);
-                const u32x4 pq[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
                 const int64_t m = m0 + wm * WM + im * 32 + rl;
                 const int64_t hc = hc0 + wn * (WN / 2) + bc * 16;
                 const bool active = m < valid && hc < p.H;
@@ -578,6 +598,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, (KS == 2 ? 2 : kWavesPerEU<BM 
                 float f[16];
                 float bamax = 0.0f;
                 if (active) {
+                    const u32x4 pq[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
                     bamax = process_block<V_SILU>(r, pq, f);
                 } else {
 #pragma unroll

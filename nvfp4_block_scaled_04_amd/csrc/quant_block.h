@@ -43,12 +43,17 @@ __device__ __forceinline__ float silu_f32(float g) {
 // range, but the low half of p within 64 of 0x8000: h is bf16(p) or its
 // neighbour on the other side of p, i.e. |h| is at most the magnitude bits
 // of bf16(p) plus one).
-__device__ __forceinline__ uint32_t silu_mul_fast2s(uint32_t gw, uint32_t uw, uint32_t& rng, uint32_t& win) {
+// p = fp32(y * u) of the fast path for one element (the same operations,
+// so the same bits, as silu_mul_fast2s).
+__device__ __forceinline__ float silu_fast_p(float g, float u) {
     constexpr float kLog2e = 1.44269504088896340736f;
+    const float y = g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -kLog2e));
+    return y * u;
+}
+
+__device__ __forceinline__ uint32_t silu_mul_fast2s(uint32_t gw, uint32_t uw, uint32_t& rng, uint32_t& win) {
+    const float p0 = silu_fast_p(bf16_lo(gw), bf16_lo(uw)), p1 = silu_fast_p(bf16_hi(gw), bf16_hi(uw));
     const float g0 = bf16_lo(gw), g1 = bf16_hi(gw);
-    const float y0 = g0 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g0 * -kLog2e));
-    const float y1 = g1 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g1 * -kLog2e));
-    const float p0 = y0 * bf16_lo(uw), p1 = y1 * bf16_hi(uw);
     // (bitwise, not short-circuit, so the test stays branch-free)
     auto out_of_range = [](float g, float p) -> uint32_t {
         const uint32_t ga = f_bits(g) & 0x7FFFFFFFu, pa = f_bits(p) & 0x7FFFFFFFu;
