@@ -174,9 +174,14 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, (KS == 2 ? 2 : kWavesPerEU<BM 
     constexpr int OFF_B = BM * 64, OFF_S = OFF_B + BN * 64;
     constexpr int SC_DW = ((BM + BN) * 2 + 64 * NW - 1) / (64 * NW) * (64 * NW);
     constexpr int STAGE = OFF_S + SC_DW * 4;
-    constexpr int NFA = BM / (16 * NW), NFB = BN / (16 * NW), NSC = SC_DW / (64 * NW);  // loads per wave per step
+    // loads per wave per step (16 rows each; when a side is not a whole
+    // number of loads per wave, the last round of loads falls to the first
+    // waves only, and the step waits count nothing: two stages)
+    constexpr int NFA = (BM + 16 * NW - 1) / (16 * NW), NFB = (BN + 16 * NW - 1) / (16 * NW);
+    constexpr int NSC = SC_DW / (64 * NW);
+    constexpr bool EVEN = BM % (16 * NW) == 0 && BN % (16 * NW) == 0;
     constexpr int ND = NFA + NFB + NSC;
-    static_assert(BM % (16 * NW) == 0 && BN % (16 * NW) == 0, "whole 16-row blocks per wave");
+    static_assert(BM % 32 == 0 && BN % 32 == 0 && (EVEN || NST == 2), "whole fragments; uneven loads need two stages");
     static_assert(NST == 2 || NST == 3, "two or three LDS stages");
     __shared__ __align__(16) uint8_t smem[KS * NST * STAGE];
 
@@ -267,12 +272,14 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, (KS == 2 ? 2 : kWavesPerEU<BM 
     auto issue = [&](int step, lds_u8* st) {
 #pragma unroll
         for (int i = 0; i < NFA; i++)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (__attribute__((address_space(3))) void*)(st + (i * NW + wave) * 1024),
-                                                     16, voA[i], step * 64, 0, 0);
+            if (EVEN || (i * NW + wave) * 16 < BM)  // (wave-uniform)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (__attribute__((address_space(3))) void*)(st + (i * NW + wave) * 1024),
+                                                         16, voA[i], step * 64, 0, 0);
 #pragma unroll
         for (int i = 0; i < NFB; i++)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (__attribute__((address_space(3))) void*)(st + OFF_B + (i * NW + wave) * 1024),
-                                                     16, voB[i], step * 64, 0, 0);
+            if (EVEN || (i * NW + wave) * 16 < BN)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (__attribute__((address_space(3))) void*)(st + OFF_B + (i * NW + wave) * 1024),
+                                                         16, voB[i], step * 64, 0, 0);
 #pragma unroll
         for (int i = 0; i < NSC; i++) {
             const bool isA = (i * NW + wave) * 32 < BM;  // a wave load covers 32 tile rows: all A or all B
@@ -1059,7 +1066,7 @@ static hipError_t launch_skinny(GParams p, bool lora, hipStream_t st) {
     return hipGetLastError();
 }
 
-enum class Tile { T256x256, T128x256, T128x256K2, T128x128, Skinny };
+enum class Tile { T256x256, T256x192, T128x256, T128x256K2, T128x128, Skinny };
 
 // Workgroup tile per problem.  Larger wave tiles need fewer dequantization
 // instructions per MFMA (64x128 waves of the 256x256 and 128x256 tiles: 6,
@@ -1075,6 +1082,7 @@ static Tile pick_tile(int64_t m, int64_t n, int64_t k, int64_t E) {
     const bool even_steps = ((k + 127) / 128) % 2 == 0;
     if (m <= 64) return Tile::Skinny;
     if (tiles(256, 256) >= 2 * 256) return Tile::T256x256;
+    if (E == 1 && tiles(256, 192) <= 256 && tiles(256, 192) >= 224) return Tile::T256x192;
     if (E == 1 && tiles(128, 128) >= 3 * 256) return Tile::T128x128;
     if (tiles(128, 256) >= 128) return even_steps && tiles(128, 256) <= 256 ? Tile::T128x256K2 : Tile::T128x256;
     return Tile::T128x128;
@@ -1125,6 +1133,7 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
     }
     switch (t) {
     case Tile::T256x256: return launch_tile<256, 256, 4, 2, 2>(p, lora, st);
+    case Tile::T256x192: return launch_tile<256, 192, 4, 2, 2>(p, lora, st);
     case Tile::T128x256: return launch_tile<128, 256, 2, 2, 2>(p, lora, st);
     case Tile::T128x256K2: return launch_tile<128, 256, 2, 2, 2, 2>(p, lora, st);
     case Tile::Skinny: return launch_skinny(p, lora, st);

@@ -497,22 +497,22 @@ __global__ __launch_bounds__(256) void k_quantize_fused(QParams p) {
 // A workgroup of 16 waves owns a 16-row band and walks K in chunks of
 // kLoraChunk columns.  In a chunk, wave w holds row w of the band and lane l
 // its 16-element block l (two 16-byte loads; the wave reads 2 KB of the row
-// contiguously): the block is quantized with the smooth pass's arithmetic
-// and its raw bf16 values are parked in one of two LDS buffers.  After one
-// barrier each wave projects its 32-column slices of the chunk with
-// v_mfma_f32_16x16x32_bf16, x from LDS as the B operand and l2 * pqs as the
-// A operand, read through the caches (every workgroup reads the same L2 and
-// pqs) and split exactly into two bf16 halves: the product of two bf16
-// values has at most 16 significant bits, its bf16 rounding hi takes the top
-// 8 and the remainder lo = product - hi at most 8 more, so x * hi + x * lo
-// is x * l2 * pqs with every product exact and only fp32 accumulation
-// rounding.  The accumulators carry across chunks.  The next chunk's row
-// loads are issued before the current chunk is quantized, so HBM reads
-// overlap the arithmetic; the two LDS buffers alternate, so one barrier per
-// chunk orders parking and projection (a wave parks chunk c only after the
-// barrier of chunk c - 1, which every wave passes after projecting chunk
-// c - 2 from the same buffer).  At the end the waves' partial projections
-// are added through LDS and stored as bf16.  Any K with K % 16 == 0.
+// contiguously): the block is quantized with the smooth pass's arithmetic,
+// and the products x * pqs that the quantization forms (exact in fp32: two
+// 8-bit significands) are split exactly into two bf16 halves, hi = bf16(x *
+// pqs) and lo = x * pqs - hi (at most 8 significant bits, so exact in bf16),
+// parked in one of two pairs of LDS buffers.  After one barrier each wave
+// projects its 32-column slices of the chunk with v_mfma_f32_16x16x32_bf16:
+// l2 as read (every workgroup reads the same rows, through the caches) as
+// the A operand against hi and against lo from LDS, so every product is
+// exact and only fp32 accumulation rounds.  The accumulators carry across
+// chunks.  The next chunk's row loads are issued before the current chunk is
+// quantized, so HBM reads overlap the arithmetic; the two buffer pairs
+// alternate, so one barrier per chunk orders parking and projection (a wave
+// parks chunk c only after the barrier of chunk c - 1, which every wave
+// passes after projecting chunk c - 2 from the same pair).  At the end the
+// waves' partial projections are added through LDS and stored as bf16.  Any
+// K with K % 16 == 0.
 // ---------------------------------------------------------------------------
 
 constexpr int kLoraChunk = 1024;  // columns per chunk (64 blocks: one per lane)
@@ -522,7 +522,7 @@ template <int RT>  // rank tiles of 16
 __global__ __launch_bounds__(64 * kLoraWaves) void k_quantize_lora(QParams p, const uint16_t* l2, uint16_t* d_out,
                                                                   int rank) {
     constexpr int PITCH = kLoraChunk + 8;  // bf16 per LDS row (16 bytes of pad spread the banks)
-    constexpr int BUF = 16 * PITCH;        // bf16 per buffer
+    constexpr int BUF = 16 * PITCH;        // bf16 per buffer (hi or lo of one chunk)
     constexpr int SPW = kLoraChunk / 32 / kLoraWaves;  // projection slices per wave per chunk
     // rank 32: the projection operands of the next chunk load with its rows;
     // larger ranks load each slice's operands just before its MFMAs (the
@@ -531,7 +531,7 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_quantize_lora(QParams p, co
     constexpr int PART = (kLoraWaves - 1) * RT * 64 * 8;  // bf16-sized slots of the waves' partial sums
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    __shared__ __align__(16) uint16_t xs[2 * BUF > PART ? 2 * BUF : PART];
+    __shared__ __align__(16) uint16_t xs[4 * BUF > PART ? 4 * BUF : PART];
     __shared__ float rtab[128];
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -557,36 +557,36 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_quantize_lora(QParams p, co
         raw[1] = src[1];
         load_pqs<V_BF16_SMOOTH>(p, (int64_t)cb * 16, pq);
     };
-    // projection operands of this wave's slice j of chunk c: l2 rows and pqs
-    // at this lane's 8 columns; zeros past K
-    auto load_slice = [&](int c, int j, u32x4 (&b)[RT], u32x4& pv) {
+    // l2 operand of this wave's slice j of chunk c: ranks 16 i + r16 at this
+    // lane's 8 columns; zeros past K
+    auto load_slice = [&](int c, int j, u32x4 (&b)[RT]) {
         const int64_t col = (int64_t)c * kLoraChunk + (wave + kLoraWaves * j) * 32 + kg * 8;
         const bool ok = col < p.K;
 #pragma unroll
         for (int i = 0; i < RT; i++)
             b[i] = ok ? *(const u32x4*)(l2 + (int64_t)(i * 16 + r16) * p.K + col) : u32x4{0u, 0u, 0u, 0u};
-        pv = ok ? *(const u32x4*)(p.pqs + col) : u32x4{0u, 0u, 0u, 0u};
     };
-    auto load_proj = [&](int c, u32x4 (&b)[PREFETCH ? SPW : 1][RT], u32x4 (&pv)[PREFETCH ? SPW : 1]) {
+    auto load_proj = [&](int c, u32x4 (&b)[PREFETCH ? SPW : 1][RT]) {
 #pragma unroll
-        for (int j = 0; j < SPW; j++) load_slice(c, j, b[j], pv[j]);
+        for (int j = 0; j < SPW; j++) load_slice(c, j, b[j]);
     };
 
     f32x4 acc[RT];
 #pragma unroll
     for (int i = 0; i < RT; i++) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     u32x4 raw[2], pqb[2], nraw[2], npqb[2];
-    u32x4 bf[PREFETCH ? SPW : 1][RT], pf[PREFETCH ? SPW : 1];
+    u32x4 bf[PREFETCH ? SPW : 1][RT];
     load_rows(0, raw, pqb);
-    if constexpr (PREFETCH) load_proj(0, bf, pf);
+    if constexpr (PREFETCH) load_proj(0, bf);
     __syncthreads();  // rtab
 
     uint8_t* const q = p.out_fp4;
     for (int c = 0; c < nch; c++) {
-        uint16_t* const buf = xs + (c & 1) * BUF;
+        uint16_t* const bhi = xs + (c & 1) * 2 * BUF;
+        uint16_t* const blo = bhi + BUF;
         if (c + 1 < nch) load_rows(c + 1, nraw, npqb);  // in flight while this chunk is worked on
 
-        // ---- quantize this lane's block, park its raw values
+        // ---- quantize this lane's block
         const int cb = c * 64 + lane;  // block column
         const bool in_k = cb < nbk;
         const bool blk_ok = row_ok && in_k;
@@ -604,11 +604,25 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_quantize_lora(QParams p, co
         if ((lane & 3) == 0 && in_k)
             *(uint32_t*)(p.out_sf + ((row >> 7) * p.nct + (cb >> 2)) * 512 + (row & 31) * 16 +
                          ((row & 127) >> 5) * 4) = v;
-        // the projection's input is the raw row (x * pqs enters as is, no
-        // nan_to_num); rows past m and columns past K are 0
-        u32x4* dst = (u32x4*)(buf + wave * PITCH + lane * 16);
-        dst[0] = row_ok && in_k ? raw[0] : u32x4{0u, 0u, 0u, 0u};
-        dst[1] = row_ok && in_k ? raw[1] : u32x4{0u, 0u, 0u, 0u};
+
+        // ---- park the projection's input, the plain products x * pqs (no
+        // nan_to_num) as hi + lo; rows past m and columns past K are 0
+        uint32_t ph[8], pl[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const uint32_t xw = raw[j >> 2][j & 3], pw = pqb[j >> 2][j & 3];
+            const f32x2 prod = {bf16_lo(xw) * bf16_lo(pw), bf16_hi(xw) * bf16_hi(pw)};
+            const bf16x2 hv = __builtin_convertvector(prod, bf16x2);  // RNE
+            const f32x2 rest = {prod[0] - (float)hv[0], prod[1] - (float)hv[1]};
+            ph[j] = blk_ok ? __builtin_bit_cast(uint32_t, hv) : 0u;
+            pl[j] = blk_ok ? __builtin_bit_cast(uint32_t, __builtin_convertvector(rest, bf16x2)) : 0u;
+        }
+        u32x4* dh = (u32x4*)(bhi + wave * PITCH + lane * 16);
+        u32x4* dl = (u32x4*)(blo + wave * PITCH + lane * 16);
+        dh[0] = u32x4{ph[0], ph[1], ph[2], ph[3]};
+        dh[1] = u32x4{ph[4], ph[5], ph[6], ph[7]};
+        dl[0] = u32x4{pl[0], pl[1], pl[2], pl[3]};
+        dl[1] = u32x4{pl[4], pl[5], pl[6], pl[7]};
         __syncthreads();
 
         // ---- project this wave's slices of the chunk
@@ -617,28 +631,19 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_quantize_lora(QParams p, co
             const int sl = wave + kLoraWaves * j;
             if ((int64_t)c * kLoraChunk + sl * 32 >= p.K) break;  // uniform in the wave
             const int js = PREFETCH ? j : 0;
-            if constexpr (!PREFETCH) load_slice(c, j, bf[0], pf[0]);
-            const bf16x8 afr = __builtin_bit_cast(bf16x8, *(const u32x4*)(buf + r16 * PITCH + sl * 32 + kg * 8));
+            if constexpr (!PREFETCH) load_slice(c, j, bf[0]);
+            const int off = r16 * PITCH + sl * 32 + kg * 8;
+            const bf16x8 xh = __builtin_bit_cast(bf16x8, *(const u32x4*)(bhi + off));
+            const bf16x8 xl = __builtin_bit_cast(bf16x8, *(const u32x4*)(blo + off));
 #pragma unroll
             for (int i = 0; i < RT; i++) {
-                uint32_t hi[4], lo[4];
-#pragma unroll
-                for (int jj = 0; jj < 4; jj++) {
-                    const f32x2 prod = {bf16_lo(bf[js][i][jj]) * bf16_lo(pf[js][jj]),
-                                        bf16_hi(bf[js][i][jj]) * bf16_hi(pf[js][jj])};
-                    const bf16x2 h = __builtin_convertvector(prod, bf16x2);
-                    const f32x2 rest = {prod[0] - (float)h[0], prod[1] - (float)h[1]};
-                    hi[jj] = __builtin_bit_cast(uint32_t, h);
-                    lo[jj] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rest, bf16x2));
-                }
-                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, u32x4{hi[0], hi[1], hi[2], hi[3]}), afr, acc[i], 0, 0, 0);
-                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], lo[2], lo[3]}), afr, acc[i], 0, 0, 0);
+                const bf16x8 w = __builtin_bit_cast(bf16x8, bf[js][i]);
+                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, xh, acc[i], 0, 0, 0);
+                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, xl, acc[i], 0, 0, 0);
             }
         }
         if constexpr (PREFETCH) {
-            if (c + 1 < nch) load_proj(c + 1, bf, pf);
+            if (c + 1 < nch) load_proj(c + 1, bf);
         }
         raw[0] = nraw[0]; raw[1] = nraw[1];
         pqb[0] = npqb[0]; pqb[1] = npqb[1];

@@ -104,6 +104,7 @@ def test_bias(ops, shape):
     (3000, 4200, 144),   # 128x128 tiles (at least three per CU), ragged
     (1100, 4100, 400),   # 128x256 tiles split over two K groups, ragged M, N and K
     (640, 8000, 512),    # 128x256 tiles split over two K groups, ragged N
+    (4000, 3000, 2992),  # 256x192 tiles (16 x 16: one per CU), ragged M, N and K
 ])
 def test_tile_shapes(ops, m, n, k):
     """Each workgroup tile shape the launcher picks, with ragged edges."""
@@ -160,7 +161,7 @@ def test_svdquant_workload(ops):
                             dev(d), dev(l1), bias=dev(s.bias), out=out)
     torch.cuda.synchronize()
     assert_all_written(out_bits)
-    rows = tile_rows(s.m, 128, 16, 4)   # 32 M-tiles of the 128 x 128 launch
+    rows = tile_rows(s.m, 128, 16, 4)   # 16 rows of every 128-row band (each 256-row tile gets 32)
     assert len(rows) == 512
     ref = O.gemm_rows(qa, qb, sa, sb, alpha, s.m, s.n, s.k, rows=rows, bias=np_bits(s.bias),
                       d=np_bits(d), l1=np_bits(l1))
@@ -171,7 +172,8 @@ def test_svdquant_workload(ops):
 
 @pytest.mark.parametrize("r,m,n,k", [(32, 150, 90, 192), (64, 150, 90, 192), (128, 150, 90, 192),
                                      (64, 40, 200, 272),    # small M: the skinny kernel
-                                     (64, 1100, 4100, 400)])  # tiles split over two K groups
+                                     (64, 1100, 4100, 400),   # tiles split over two K groups
+                                     (32, 4000, 3000, 2992)])  # 256x192 tiles, ragged M, N and K
 def test_svdquant_ranks_and_ragged(ops, r, m, n, k):
     g = torch.Generator().manual_seed(r + m)
     a = torch.randn(m, k, generator=g).to(torch.bfloat16)
