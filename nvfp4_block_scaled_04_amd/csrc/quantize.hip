@@ -137,14 +137,12 @@ __global__ __launch_bounds__(256) void k_amax(QParams p) {
         load_pqs<V>(p, col, pq);
         u32x4 raw[TM::NP][NL];
 #pragma unroll
-        for (int i = 0; i < TM::NP; i++) {  // every load in flight before any use; rows past the valid ones are not read
+        for (int i = 0; i < TM::NP; i++) {  // every load in flight before any use
+            // rows past the valid ones read the last valid row again (a cache
+            // hit; not processed): unconditional loads, so the compiler can
+            // count them in flight
             const int64_t row = (int64_t)rt * 128 + rsub + TM::RPP * i;
-            if (row < valid) {
-                load_block<V>(p, e, row, col, raw[i]);
-            } else {
-#pragma unroll
-                for (int l = 0; l < NL; l++) raw[i][l] = u32x4{0u, 0u, 0u, 0u};
-            }
+            load_block<V>(p, e, row < valid ? row : valid - 1, col, raw[i]);
         }
 #pragma unroll
         for (int i = 0; i < TM::NP; i++) {
@@ -325,13 +323,11 @@ __device__ __forceinline__ void quantize_tile(const QParams& p, int wct, int rt,
 #pragma unroll
     for (int i = 0; i < TM::NP; i++) {  // every load in flight before any use
         const int64_t row = (int64_t)rt * 128 + rsub + TM::RPP * i;
-        if constexpr (V == V_SILU) {  // rows past the valid ones are not read (nor processed, below)
-            if (row < valid) {
-                load_block<V>(p, e, row, col, raw[i]);
-            } else {
-#pragma unroll
-                for (int l = 0; l < NL; l++) raw[i][l] = u32x4{0u, 0u, 0u, 0u};
-            }
+        if constexpr (V == V_SILU) {
+            // rows past the valid ones read the last valid row again (a cache
+            // hit; not processed, below): unconditional loads, so the compiler
+            // can count them in flight
+            load_block<V>(p, e, row < valid ? row : valid - 1, col, raw[i]);
         } else {
             load_block<V>(p, e, row < p.m ? row : p.m - 1, col, raw[i]);
         }
@@ -558,13 +554,17 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_quantize_lora(QParams p, co
         load_pqs<V_BF16_SMOOTH>(p, (int64_t)cb * 16, pq);
     };
     // l2 operand of this wave's slice j of chunk c: ranks 16 i + r16 at this
-    // lane's 8 columns; zeros past K
+    // lane's 8 columns (past K: column 0, and the operand is zeroed at its
+    // use).  Every load here is issued on every path, so that the compiler
+    // can count the loads in flight and wait only for the ones a use needs.
+    auto slice_ok = [&](int c, int j) {
+        return (int64_t)c * kLoraChunk + (wave + kLoraWaves * j) * 32 + kg * 8 < p.K;
+    };
     auto load_slice = [&](int c, int j, u32x4 (&b)[RT]) {
         const int64_t col = (int64_t)c * kLoraChunk + (wave + kLoraWaves * j) * 32 + kg * 8;
-        const bool ok = col < p.K;
+        const int64_t cs = col < p.K ? col : 0;
 #pragma unroll
-        for (int i = 0; i < RT; i++)
-            b[i] = ok ? *(const u32x4*)(l2 + (int64_t)(i * 16 + r16) * p.K + col) : u32x4{0u, 0u, 0u, 0u};
+        for (int i = 0; i < RT; i++) b[i] = *(const u32x4*)(l2 + (int64_t)(i * 16 + r16) * p.K + cs);
     };
     auto load_proj = [&](int c, u32x4 (&b)[PREFETCH ? SPW : 1][RT]) {
 #pragma unroll
@@ -584,7 +584,9 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_quantize_lora(QParams p, co
     for (int c = 0; c < nch; c++) {
         uint16_t* const bhi = xs + (c & 1) * 2 * BUF;
         uint16_t* const blo = bhi + BUF;
-        if (c + 1 < nch) load_rows(c + 1, nraw, npqb);  // in flight while this chunk is worked on
+        // the next chunk's rows, in flight while this chunk is worked on (the
+        // last chunk reloads itself: unconditional, like every load here)
+        load_rows(c + 1 < nch ? c + 1 : c, nraw, npqb);
 
         // ---- quantize this lane's block
         const int cb = c * 64 + lane;  // block column
@@ -635,16 +637,15 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_quantize_lora(QParams p, co
             const int off = r16 * PITCH + sl * 32 + kg * 8;
             const bf16x8 xh = __builtin_bit_cast(bf16x8, *(const u32x4*)(bhi + off));
             const bf16x8 xl = __builtin_bit_cast(bf16x8, *(const u32x4*)(blo + off));
+            const bool ok = slice_ok(c, j);
 #pragma unroll
             for (int i = 0; i < RT; i++) {
-                const bf16x8 w = __builtin_bit_cast(bf16x8, bf[js][i]);
+                const bf16x8 w = __builtin_bit_cast(bf16x8, ok ? bf[js][i] : u32x4{0u, 0u, 0u, 0u});
                 acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, xh, acc[i], 0, 0, 0);
                 acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, xl, acc[i], 0, 0, 0);
             }
         }
-        if constexpr (PREFETCH) {
-            if (c + 1 < nch) load_proj(c + 1, bf);
-        }
+        if constexpr (PREFETCH) load_proj(c + 1 < nch ? c + 1 : c, bf);
         raw[0] = nraw[0]; raw[1] = nraw[1];
         pqb[0] = npqb[0]; pqb[1] = npqb[1];
     }
