@@ -169,17 +169,28 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, (KS == 2 ? 2 : kWavesPerEU<BM 
     constexpr int NW = WGM * WGN;  // waves of one K group, WGM along M x WGN along N
     constexpr int WM = BM / WGM, WN = BN / WGN;
     constexpr int FM = WM / 32, FN = WN / 32;
-    // one LDS stage: FP4 A rows, FP4 B rows, raw scale dwords (padded to whole
-    // wave loads of 64 dwords per wave)
+    // Scale staging.  Banded (the K-split tile, whose two K groups stage
+    // their own steps): the swizzled layout keeps a 128-row band's 8 scales
+    // per row of one K step (its two column groups of 4) in 1 KB of
+    // contiguous memory, which one 16-byte load per lane copies as is (a
+    // quarter of the load instructions of the dword path; measured 1-2%
+    // faster there, 1% slower on the 256 x 256 tile, whose reads of it meet
+    // two-way bank conflicts).  Otherwise: one dword per (row, column group),
+    // two per row at 8t.
+    constexpr bool BANDED = KS == 2 && EPI != EPI_SILUQ && BM % 128 == 0 && BN % 128 == 0;
+    constexpr int NBAND = (BM + BN) / 128;
+    // one LDS stage: FP4 A rows, FP4 B rows, scales (padded to whole wave
+    // loads)
     constexpr int OFF_B = BM * 64, OFF_S = OFF_B + BN * 64;
-    constexpr int SC_DW = ((BM + BN) * 2 + 64 * NW - 1) / (64 * NW) * (64 * NW);
-    constexpr int STAGE = OFF_S + SC_DW * 4;
-    // loads per wave per step (16 rows each; when a side is not a whole
-    // number of loads per wave, the last round of loads falls to the first
+    constexpr int SC_BYTES = BANDED ? NBAND * 1024 : ((BM + BN) * 2 + 64 * NW - 1) / (64 * NW) * (64 * NW) * 4;
+    constexpr int STAGE = OFF_S + SC_BYTES;
+    // loads per wave per step (FP4: 16 rows each; when a kind of load does
+    // not divide evenly over the waves, its last round falls to the first
     // waves only, and the step waits count nothing: two stages)
     constexpr int NFA = (BM + 16 * NW - 1) / (16 * NW), NFB = (BN + 16 * NW - 1) / (16 * NW);
-    constexpr int NSC = SC_DW / (64 * NW);
-    constexpr bool EVEN = BM % (16 * NW) == 0 && BN % (16 * NW) == 0;
+    constexpr int NSC = BANDED ? (NBAND + NW - 1) / NW : SC_BYTES / 4 / (64 * NW);
+    constexpr bool EVEN_F = BM % (16 * NW) == 0 && BN % (16 * NW) == 0;
+    constexpr bool EVEN = EVEN_F && (!BANDED || NBAND % NW == 0);
     constexpr int ND = NFA + NFB + NSC;
     static_assert(BM % 32 == 0 && BN % 32 == 0 && (EVEN || NST == 2), "whole fragments; uneven loads need two stages");
     static_assert(NST == 2 || NST == 3, "two or three LDS stages");
@@ -254,6 +265,20 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, (KS == 2 ? 2 : kWavesPerEU<BM 
     }
 #pragma unroll
     for (int i = 0; i < NSC; i++) {
+        if constexpr (BANDED) {
+            // band bi: lanes 0-31 the first column group's 512 bytes, 32-63 the
+            // second's (bands past the matrix's padded rows read its last band;
+            // they feed only outputs that are never stored)
+            const int bi = i * NW + wave;
+            if (bi < BM / 128) {
+                const int64_t r0 = m0 + 128 * bi < p.rpa ? m0 + 128 * bi : p.rpa - 128;
+                voS[i] = (uint32_t)(((r0 >> 7) * p.cpa4) * 512) + lane * 16;
+            } else {
+                const int64_t r0 = n0 + 128 * (bi - BM / 128) < p.rpb ? n0 + 128 * (bi - BM / 128) : p.rpb - 128;
+                voS[i] = (uint32_t)(((r0 >> 7) * p.cpa4) * 512) + lane * 16;
+            }
+            continue;
+        }
         const int dw = (i * NW + wave) * 64 + lane;  // scale dword of the stage
         const int tr = dw >> 1, g = dw & 1;         // tile row, column group of the step
         if (tr < BM) {
@@ -272,20 +297,28 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, (KS == 2 ? 2 : kWavesPerEU<BM 
     auto issue = [&](int step, lds_u8* st) {
 #pragma unroll
         for (int i = 0; i < NFA; i++)
-            if (EVEN || (i * NW + wave) * 16 < BM)  // (wave-uniform)
+            if (EVEN_F || (i * NW + wave) * 16 < BM)  // (wave-uniform)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (__attribute__((address_space(3))) void*)(st + (i * NW + wave) * 1024),
                                                          16, voA[i], step * 64, 0, 0);
 #pragma unroll
         for (int i = 0; i < NFB; i++)
-            if (EVEN || (i * NW + wave) * 16 < BN)
+            if (EVEN_F || (i * NW + wave) * 16 < BN)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (__attribute__((address_space(3))) void*)(st + OFF_B + (i * NW + wave) * 1024),
                                                          16, voB[i], step * 64, 0, 0);
 #pragma unroll
         for (int i = 0; i < NSC; i++) {
-            const bool isA = (i * NW + wave) * 32 < BM;  // a wave load covers 32 tile rows: all A or all B
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? rSA : rSB,
-                                                     (__attribute__((address_space(3))) void*)(st + OFF_S + (i * NW + wave) * 256),
-                                                     4, voS[i], step * 1024, 0, 0);
+            if constexpr (BANDED) {
+                const int bi = i * NW + wave;
+                if (NBAND % NW == 0 || bi < NBAND)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(bi < BM / 128 ? rSA : rSB,
+                                                             (__attribute__((address_space(3))) void*)(st + OFF_S + bi * 1024),
+                                                             16, voS[i], step * 1024, 0, 0);
+            } else {
+                const bool isA = (i * NW + wave) * 32 < BM;  // a wave load covers 32 tile rows: all A or all B
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? rSA : rSB,
+                                                         (__attribute__((address_space(3))) void*)(st + OFF_S + (i * NW + wave) * 256),
+                                                         4, voS[i], step * 1024, 0, 0);
+            }
         }
     };
 
@@ -303,8 +336,12 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, (KS == 2 ? 2 : kWavesPerEU<BM 
     const int ra_off = (wm * WM + l32) * 64, rb_off = OFF_B + (wn * WN + l32) * 64;
     const int xr = swz(l32);
     const int cq0 = ((h ^ xr) << 4), cq1 = (((2 + h) ^ xr) << 4);
-    const int sa_off = OFF_S + (wm * WM + l32) * 8;
-    const int sb_off = OFF_S + (BM + wn * WN + l32) * 8;
+    // this lane's first scale dword (fragment 0); banded: column group x of
+    // tile row t at byte 1024 * (t >> 7) + 16 * (t & 31) + 4 * ((t >> 5) & 3)
+    // of the region, y 512 bytes further
+    auto band_off = [&](int f) { return OFF_S + (f >> 2) * 1024 + (f & 3) * 4 + l32 * 16; };  // fragment row f
+    const int sa_off = BANDED ? 0 : OFF_S + (wm * WM + l32) * 8;
+    const int sb_off = BANDED ? 0 : OFF_S + (BM + wn * WN + l32) * 8;
     const int hsh = 16 * h;  // this lane's blocks sit in the high half of each scale dword when h = 1
 
     // fragment registers of one half step q (lane: 32 elements = 4 dwords per
@@ -317,10 +354,25 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS, (KS == 2 ? 2 : kWavesPerEU<BM 
     // row's or zeros, and must not contribute.
     auto load_scales = [&](const lds_u8* st, int step) {
         u32x2 ra[FM], rb[FN];
+        if constexpr (BANDED) {
 #pragma unroll
-        for (int i = 0; i < FM; i++) ra[i] = *(const __attribute__((address_space(3))) u32x2*)(st + sa_off + i * 256);
+            for (int i = 0; i < FM; i++) {
+                const int o = band_off(wm * FM + i);
+                ra[i] = u32x2{*(const __attribute__((address_space(3))) uint32_t*)(st + o),
+                              *(const __attribute__((address_space(3))) uint32_t*)(st + o + 512)};
+            }
 #pragma unroll
-        for (int i = 0; i < FN; i++) rb[i] = *(const __attribute__((address_space(3))) u32x2*)(st + sb_off + i * 256);
+            for (int i = 0; i < FN; i++) {
+                const int o = band_off(BM / 32 + wn * FN + i);
+                rb[i] = u32x2{*(const __attribute__((address_space(3))) uint32_t*)(st + o),
+                              *(const __attribute__((address_space(3))) uint32_t*)(st + o + 512)};
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < FM; i++) ra[i] = *(const __attribute__((address_space(3))) u32x2*)(st + sa_off + i * 256);
+#pragma unroll
+            for (int i = 0; i < FN; i++) rb[i] = *(const __attribute__((address_space(3))) u32x2*)(st + sb_off + i * 256);
+        }
         uint32_t m0w = 0xFFFFFFFFu, m1w = 0xFFFFFFFFu;
         if constexpr (!ALIGNED) {
             const int left = p.nblk - step * 8;  // valid blocks in this step (<= 0 past the end)
