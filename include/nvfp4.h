@@ -241,6 +241,16 @@ int silu_mul_nvfp4_quantize(const void *x, int64_t b, int64_t m, int64_t k2,
  */
 #define NVFP4_BATCHED_WS_BYTES(b, m, k) \
     (4096 + 4 * (int64_t)(b) * (((int64_t)(m) + 127) / 128) * (((int64_t)(k) + 63) / 64))
+/*
+ * silu_mul_nvfp4_quantize_ws with workspace_bytes >= NVFP4_SILU_WS_BYTES(b,
+ * m, k) (k = k2/2) in DYNAMIC mode: the workspace also holds h = bf16(silu(g)
+ * * u) of the valid rows, which the amax pass stores and the quantize pass
+ * reads back, so silu is evaluated once instead of twice.  Same bytes out,
+ * same errors; smaller workspaces (down to NVFP4_BATCHED_WS_BYTES) take the
+ * two-evaluation path.
+ */
+#define NVFP4_SILU_WS_BYTES(b, m, k) \
+    ((NVFP4_BATCHED_WS_BYTES(b, m, k) + 255) / 256 * 256 + 2 * (int64_t)(b) * (int64_t)(m) * (int64_t)(k))
 int nvfp4_quantize_masked_batched_ws(const void *x, int64_t b, int64_t m, int64_t k,
                                      const int32_t *mask, float *global_scale, int gs_mode,
                                      const float *gs_other, float *alpha,

@@ -170,6 +170,9 @@ static int batched_common(const void* x, int64_t b, int64_t m, int64_t k_in, boo
     a.b = b; a.m = m; a.k_in = k_in; a.silu = silu; a.dynamic = gs_mode == NVFP4_GS_DYNAMIC;
     a.gs_other = gs_other; a.alpha_out = alpha;
     a.ws = use_ws ? (float*)workspace : nullptr;
+    // silu with room for h after the partials: silu is evaluated once
+    if (silu && use_ws && workspace_bytes >= NVFP4_SILU_WS_BYTES(b, m, k))
+        a.hbuf = (uint16_t*)((char*)workspace + (NVFP4_BATCHED_WS_BYTES(b, m, k) + 255) / 256 * 256);
     return launch_status(nvfp4::launch_quantize(a, (hipStream_t)stream));
 }
 

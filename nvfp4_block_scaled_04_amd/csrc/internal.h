@@ -23,6 +23,8 @@ struct QuantizeArgs {
     float* ws = nullptr;              // DYNAMIC: the partial maxima (two launches instead of three), or
                                       // null; b == 1 without mask and silu: >= kQuantizeWsFloats floats,
                                       // otherwise >= b * ceil(m/128) * ceil(K/64) floats
+    uint16_t* hbuf = nullptr;         // silu with ws: room for h [b, m, K] bf16 (then silu is evaluated
+                                      // once, by the amax pass), or null
 };
 
 // Floats of workspace a DYNAMIC single-tensor quantization uses for its

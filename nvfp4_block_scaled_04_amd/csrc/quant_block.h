@@ -100,6 +100,42 @@ __device__ __forceinline__ void silu_exact_into(const u32x4 (&r)[4], int bit, ui
         if (jj == j) w[jj] = (w[jj] & ~(0xFFFFu << sh)) | (h << sh);
 }
 
+// h = silu(g) * u (bf16) of a block's 16 elements, as 8 words of bf16 pairs:
+// the fast path for all of them, then the exact path for the flagged ones
+// (rare: one divergent branch per block).
+__device__ __forceinline__ void silu_block_words(const u32x4 (&r)[4], uint32_t (&w)[8]) {
+    uint32_t need = 0;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const uint32_t gw = j < 4 ? r[0][j] : r[1][j - 4];
+        const uint32_t uw = j < 4 ? r[2][j] : r[3][j - 4];
+        uint32_t bad;
+        w[j] = silu_mul_fast2(gw, uw, bad);
+        need |= bad << (2 * j);
+    }
+    // The flagged elements one at a time through a single inlined copy of
+    // the exact path (a call would make the wave wait for every load it has
+    // in flight).
+    while (need) {
+        const int bit = __builtin_ctz(need);
+        need &= need - 1;
+        silu_exact_into(r, bit, w);
+    }
+}
+
+// Largest |nan_to_num(v)| over the 16 bf16 values of 8 words.
+__device__ __forceinline__ float bf16_words_amax(const uint32_t (&w)[8]) {
+    const uint32_t mb = __builtin_elementwise_max(absmax_bits_bf16x8(w), absmax_bits_bf16x8(w + 4));
+    if (mb < 0x7F80u) return bits_f(mb << 16);
+    float a = 0.0f;  // inf or NaN present
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+        const float v = nan_to_num((j & 1) ? bf16_hi(w[j >> 1]) : bf16_lo(w[j >> 1]));
+        a = __builtin_fmaxf(a, __builtin_fabsf(v));
+    }
+    return a;
+}
+
 // 16-byte loads behind one 16-element block of a row.
 template <int V>
 constexpr int loads_per_block() {
@@ -117,25 +153,7 @@ __device__ __forceinline__ float process_block(const u32x4 (&r)[loads_per_block<
 #pragma unroll
             for (int j = 0; j < 4; j++) { w[j] = r[0][j]; w[4 + j] = r[1][j]; }
         } else {
-            // fast path for all 16 elements, then the exact path for the
-            // flagged ones (rare: one divergent branch per block)
-            uint32_t need = 0;
-#pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const uint32_t gw = j < 4 ? r[0][j] : r[1][j - 4];
-                const uint32_t uw = j < 4 ? r[2][j] : r[3][j - 4];
-                uint32_t bad;
-                w[j] = silu_mul_fast2(gw, uw, bad);
-                need |= bad << (2 * j);
-            }
-            // The flagged elements one at a time through a single inlined
-            // copy of the exact path (a call would make the wave wait for
-            // every load it has in flight).
-            while (need) {
-                const int bit = __builtin_ctz(need);
-                need &= need - 1;
-                silu_exact_into(r, bit, w);
-            }
+            silu_block_words(r, w);
         }
         // bf16 magnitudes compare as integers; inf / NaN patterns sort above
         // every finite one
@@ -230,15 +248,7 @@ __device__ __forceinline__ float silu_block_amax(const u32x4 (&r)[4], float thr)
         need &= need - 1;
         silu_exact_into(r, bit, w);
     }
-    const uint32_t mb = __builtin_elementwise_max(absmax_bits_bf16x8(w), absmax_bits_bf16x8(w + 4));
-    if (mb < 0x7F80u) return bits_f(mb << 16);
-    float a = 0.0f;  // inf or NaN present: nan_to_num
-#pragma unroll
-    for (int j = 0; j < 16; j++) {
-        const float v = nan_to_num((j & 1) ? bf16_hi(w[j >> 1]) : bf16_lo(w[j >> 1]));
-        a = __builtin_fmaxf(a, __builtin_fabsf(v));
-    }
-    return a;
+    return bf16_words_amax(w);
 }
 
 // The 16 values of a block times the element factor r = gs / dec(s), as 16

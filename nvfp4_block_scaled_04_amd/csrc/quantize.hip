@@ -63,6 +63,7 @@ struct QParams {
     int nparts;            // partials per item
     const float* gs_other; // [b] the GEMM partner's global scales, when alpha_out is set
     float* alpha_out;      // [b] or null: alpha = 1 / (gs * gs_other)
+    uint16_t* hbuf;        // silu, DYNAMIC, large workspace: the amax pass's h [b, m, K] bf16 (valid rows)
 };
 
 // alpha of item e from its final global scale, with the arithmetic of k_alpha
@@ -118,8 +119,11 @@ __device__ __forceinline__ float* partials(const QParams& p, int e) {
 // DYNAMIC mode: amax partials, finish, then quantize.
 // ---------------------------------------------------------------------------
 
-template <int V, int CT>
+// HOUT (silu only): every block's exact h is also stored to p.hbuf, which
+// the quantize pass then reads as a plain bf16 input (silu evaluated once).
+template <int V, int CT, bool HOUT = false>
 __global__ __launch_bounds__(256) void k_amax(QParams p) {
+    static_assert(!HOUT || V == V_SILU, "h is stored by the silu pass");
     using TM = TileMap<CT>;
     constexpr int NL = loads_per_block<V>();
     const int tile = blockIdx.x, e = blockIdx.y;
@@ -148,7 +152,14 @@ __global__ __launch_bounds__(256) void k_amax(QParams p) {
         for (int i = 0; i < TM::NP; i++) {
             const int64_t row = (int64_t)rt * 128 + rsub + TM::RPP * i;
             if (col_ok && row < valid) {
-                if constexpr (V == V_SILU) {
+                if constexpr (HOUT) {
+                    uint32_t w[8];
+                    silu_block_words(raw[i], w);
+                    u32x4* hp = (u32x4*)(p.hbuf + ((int64_t)e * p.m + row) * p.K + col);
+                    hp[0] = u32x4{w[0], w[1], w[2], w[3]};
+                    hp[1] = u32x4{w[4], w[5], w[6], w[7]};
+                    amax = __builtin_fmaxf(amax, bf16_words_amax(w));
+                } else if constexpr (V == V_SILU) {
                     amax = __builtin_fmaxf(amax, silu_block_amax(raw[i], amax));
                 } else {
                     float f[16];
@@ -322,15 +333,11 @@ __device__ __forceinline__ void quantize_tile(const QParams& p, int wct, int rt,
     u32x4 raw[TM::NP][NL];
 #pragma unroll
     for (int i = 0; i < TM::NP; i++) {  // every load in flight before any use
+        // rows past the valid ones read the last valid row again (a cache
+        // hit; not processed, below): unconditional loads, so the compiler
+        // can count them in flight
         const int64_t row = (int64_t)rt * 128 + rsub + TM::RPP * i;
-        if constexpr (V == V_SILU) {
-            // rows past the valid ones read the last valid row again (a cache
-            // hit; not processed, below): unconditional loads, so the compiler
-            // can count them in flight
-            load_block<V>(p, e, row < valid ? row : valid - 1, col, raw[i]);
-        } else {
-            load_block<V>(p, e, row < p.m ? row : p.m - 1, col, raw[i]);
-        }
+        load_block<V>(p, e, row < valid ? row : valid - 1, col, raw[i]);
     }
     // element factors r = gs / dec(s) for every scale code (0 for code 0),
     // computed while the loads are in flight
@@ -346,10 +353,10 @@ __device__ __forceinline__ void quantize_tile(const QParams& p, int wct, int rt,
         const int64_t row = (int64_t)rt * 128 + rl;
         const bool active = col_ok && row < valid;
         uint32_t sc = 0u;  // rows past the valid ones (and blocks past K): zero scale, no FP4 written
-        if (V != V_SILU || active) {  // (the silu work of padding rows is skipped; elsewhere it is cheap)
+        if (active) {
             float f[16];
             const float bamax = process_block<V>(raw[i], pq, f);
-            sc = active ? ue4m3_encode(div6(bamax) * gs) : 0u;
+            sc = ue4m3_encode(div6(bamax) * gs);
             const float r = rtab[sc];
             uint32_t w0 = 0, w1 = 0;
             w0 = NVFP4_PACK_FP4(w0, f[0] * r, f[1] * r, 0);
@@ -360,7 +367,7 @@ __device__ __forceinline__ void quantize_tile(const QParams& p, int wct, int rt,
             w1 = NVFP4_PACK_FP4(w1, f[10] * r, f[11] * r, 1);
             w1 = NVFP4_PACK_FP4(w1, f[12] * r, f[13] * r, 2);
             w1 = NVFP4_PACK_FP4(w1, f[14] * r, f[15] * r, 3);
-            if (active) *(uint2*)(q + row * (p.K / 2) + col / 2) = uint2{w0, w1};
+            *(uint2*)(q + row * (p.K / 2) + col / 2) = uint2{w0, w1};
         }
         sbuf[c * 512 + (rl & 31) * 16 + (rl >> 5) * 4 + blk] = (uint8_t)sc;
     }
@@ -746,8 +753,10 @@ static void launch_quantize_pass(const QParams& p, bool from_part, hipStream_t s
 
 // ws: DYNAMIC mode's partial maxima (a caller workspace of at least
 // kFlatAmaxGrid floats), or null.
+// hbuf (silu only, with ws): room for h [b, m, K] bf16: the amax pass
+// stores h there and the quantize pass reads it as a bf16 input.
 template <int V>
-static hipError_t launch_variant(QParams p, bool dynamic, float* ws, hipStream_t st) {
+static hipError_t launch_variant(QParams p, bool dynamic, float* ws, uint16_t* hbuf, hipStream_t st) {
     constexpr int CTA = V == V_SILU ? 1 : 2;
     // DYNAMIC mode on small items: one launch instead of three (a STATIC pass
     // is one launch anyway, and spreads over more compute units)
@@ -779,6 +788,20 @@ static hipError_t launch_variant(QParams p, bool dynamic, float* ws, hipStream_t
             } else {
                 p.part = (float*)p.out_sf;
                 p.part_stride = p.sfsz / 4;
+            }
+            if constexpr (V == V_SILU) {
+                if (ws && hbuf) {
+                    // silu once: the amax pass stores h, then a bf16 pass over h
+                    p.hbuf = hbuf;
+                    k_amax<V, CTA, true><<<dim3(p.nparts, p.b), 256, 0, st>>>(p);
+                    QParams q = p;
+                    q.x = hbuf;
+                    q.k_in = p.K;
+                    const int qct = q.b * q.m * q.K * 2 <= ((int64_t)128 << 20) ? 2 : quant_ct_for<V_BF16>(q);
+                    if (qct == 4) launch_quantize_pass<V_BF16, 4>(q, true, st);
+                    else launch_quantize_pass<V_BF16, 2>(q, true, st);
+                    return hipGetLastError();
+                }
             }
             k_amax<V, CTA><<<dim3(p.nparts, p.b), 256, 0, st>>>(p);
         }
@@ -817,13 +840,13 @@ hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t st) {
     p.alpha_out = a.alpha_out;
     const bool dyn = a.dynamic;
     float* ws = a.ws;
-    if (a.silu) return launch_variant<V_SILU>(p, dyn, ws, st);
+    if (a.silu) return launch_variant<V_SILU>(p, dyn, ws, a.hbuf, st);
     if (a.x_dtype == 0) {
-        if (a.pqs) return launch_variant<V_BF16_SMOOTH>(p, dyn, ws, st);
-        return launch_variant<V_BF16>(p, dyn, ws, st);
+        if (a.pqs) return launch_variant<V_BF16_SMOOTH>(p, dyn, ws, nullptr, st);
+        return launch_variant<V_BF16>(p, dyn, ws, nullptr, st);
     }
-    if (a.pqs) return launch_variant<V_F32_SMOOTH>(p, dyn, ws, st);
-    return launch_variant<V_F32>(p, dyn, ws, st);
+    if (a.pqs) return launch_variant<V_F32_SMOOTH>(p, dyn, ws, nullptr, st);
+    return launch_variant<V_F32>(p, dyn, ws, nullptr, st);
 }
 
 // ---------------------------------------------------------------------------

@@ -370,6 +370,17 @@ def batched_workspace(b, m, k, device):
     return torch.empty(batched_ws_bytes(b, m, k), dtype=torch.uint8, device=device)
 
 
+def silu_ws_bytes(b, m, k):
+    """NVFP4_SILU_WS_BYTES(b, m, k): a silu_mul_nvfp4_quantize_ws workspace that
+    also holds h (silu evaluated once); k = k2 / 2."""
+    return (batched_ws_bytes(b, m, k) + 255) // 256 * 256 + 2 * b * m * k
+
+
+def silu_workspace(b, m, k, device):
+    """A silu_mul_nvfp4_quantize_ws workspace with room for h (caller-owned)."""
+    return torch.empty(silu_ws_bytes(b, m, k), dtype=torch.uint8, device=device)
+
+
 def _batched_ws(fn, x, b, m, k_in, k, workspace, mask, global_scale, gs_mode, gs_other, alpha, out_fp4, out_sf):
     dev = x.device
     _dev(x, "x", BF16, b * m * k_in, dev)
@@ -411,9 +422,9 @@ def nvfp4_quantize_masked_batched_ws(x, workspace, mask=None, global_scale=None,
 
 def silu_mul_nvfp4_quantize_ws(x, workspace, mask=None, global_scale=None, gs_mode=GS_DYNAMIC,
                                gs_other=None, alpha=None, out_fp4=None, out_sf=None):
-    """silu_mul_nvfp4_quantize with a workspace ([batched_ws_bytes(b, m, h)] bytes)
-    and, given gs_other [b], alpha [b] from the same call -> (fp4, sf, gs, alpha
-    or None)."""
+    """silu_mul_nvfp4_quantize with a workspace (at least batched_ws_bytes(b, m, h)
+    bytes; silu_ws_bytes(b, m, h) or more: silu evaluated once) and, given
+    gs_other [b], alpha [b] from the same call -> (fp4, sf, gs, alpha or None)."""
     _dims(x, "x", 3)
     b, m, k2 = x.shape
     return _batched_ws("silu_mul_nvfp4_quantize_ws", x, b, m, k2, k2 // 2, workspace, mask, global_scale,

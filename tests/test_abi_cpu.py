@@ -414,3 +414,25 @@ def test_quantize_noalloc_alignment_refused(lib):
     assert f(P + 8, 0, 128, 256, None, P, 1, None, None, P, P, None) == MISAL
     assert f(P, 0, 128, 256, P + 4, P, 1, None, None, P, P, None) == MISAL
     assert f(P, 0, 128, 256, None, P, 1, P + 2, P, P, P, None) == MISAL
+
+
+def test_workspace_size_macros_match_the_binding(tmp_path):
+    """The workspace sizes the header defines (compiled with gcc) equal the
+    binding's helpers, over shapes with ragged m and k."""
+    from nvfp4_block_scaled_04_amd import ops
+    import subprocess
+    shapes = [(1, 1, 16), (8, 512, 8192), (3, 130, 1040), (4, 200, 96)]
+    src = tmp_path / "ws.c"
+    lines = ['#include <stdio.h>', '#include <stdint.h>', '#include "nvfp4.h"', "int main(void) {"]
+    for b, m, k in shapes:
+        lines.append(f'  printf("%lld %lld\\n", (long long)NVFP4_BATCHED_WS_BYTES({b}, {m}, {k}), '
+                     f'(long long)NVFP4_SILU_WS_BYTES({b}, {m}, {k}));')
+    lines += ["  return 0;", "}"]
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "ws"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run(["gcc", "-I", inc, str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    for (b, m, k), line in zip(shapes, out):
+        got = [int(v) for v in line.split()]
+        assert got == [ops.batched_ws_bytes(b, m, k), ops.silu_ws_bytes(b, m, k)], (b, m, k, got)

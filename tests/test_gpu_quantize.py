@@ -168,7 +168,8 @@ def test_quantize_lora_down(ops, m, k, r, dynamic):
 
 def run_batched(ops, x_cpu, mask, mode, silu=False, gs=None, ws=False):
     """ws: through the *_ws entry point, with a workspace of stale bytes and a
-    gs_other, so that alpha is checked too."""
+    gs_other, so that alpha is checked too; ws == "h": the silu workspace
+    with room for h (silu evaluated once, by the amax pass)."""
     b, m, kin = x_cpu.shape
     K = kin // 2 if silu else kin
     say("batched", tuple(x_cpu.shape), "silu", silu, "mask", None if mask is None else mask.tolist(),
@@ -179,7 +180,8 @@ def run_batched(ops, x_cpu, mask, mode, silu=False, gs=None, ws=False):
     o4 = canary((b, m, K // 2))
     osf = canary((b, ops.sf_size(m, K)))
     if ws:
-        w = ops.batched_workspace(b, m, K, "cuda").fill_(0x5A)
+        mkws = ops.silu_workspace if ws == "h" else ops.batched_workspace
+        w = mkws(b, m, K, "cuda").fill_(0x5A)
         go = (torch.rand(b, generator=torch.Generator().manual_seed(b + m + K)) * 500 + 1).to(torch.float32)
         al = torch.full((b,), float("nan"), dtype=torch.float32, device="cuda")
         fn = ops.silu_mul_nvfp4_quantize_ws if silu else ops.nvfp4_quantize_masked_batched_ws
@@ -218,6 +220,20 @@ def test_batched_ws(ops, silu, mask, k):
     run_batched(ops, x.to(torch.bfloat16), mk, ops.GS_DYNAMIC, silu=silu, ws=True)
 
 
+@pytest.mark.parametrize("mask,k", [(None, 512), ([0, 1, 129, 200], 512), ([200, 0, 7, 130], 2048),
+                                    ([0, 0, 0, 0], 512), ([200, 200, 200, 200], 1040)])
+def test_silu_ws_h(ops, mask, k):
+    """silu_mul_nvfp4_quantize_ws with room for h: the amax pass stores h =
+    bf16(silu(g) * u) of the valid rows and the quantize pass reads it back
+    as a bf16 input; the workspace starts as stale bytes, so a row the amax
+    pass did not store and the quantize pass read would show.  Bytes, gs and
+    alpha equal the oracle's."""
+    g = torch.Generator().manual_seed(43 + k)
+    x = (torch.randn(4, 200, 2 * k, generator=g) * torch.tensor([1.0, 10.0, 0.1, 3.0])[:, None, None])
+    mk = None if mask is None else torch.tensor(mask, dtype=torch.int32)
+    run_batched(ops, x.to(torch.bfloat16), mk, ops.GS_DYNAMIC, silu=True, ws="h")
+
+
 def test_batched_ws_static(ops):
     g = torch.Generator().manual_seed(42)
     x = torch.randn(3, 130, 768, generator=g).to(torch.bfloat16)
@@ -225,9 +241,10 @@ def test_batched_ws_static(ops):
                 gs=torch.tensor([100.0, 250.0, 3.0]), ws=True)
 
 
-def test_moe_workload_ws(ops):
+@pytest.mark.parametrize("ws", [True, "h"])
+def test_moe_workload_ws(ops, ws):
     mo = synth.moe(h=8192, n=64)
-    run_batched(ops, mo.x, mo.mask, ops.GS_DYNAMIC, silu=True, ws=True)
+    run_batched(ops, mo.x, mo.mask, ops.GS_DYNAMIC, silu=True, ws=ws)
 
 
 @pytest.mark.parametrize("mask", [None, [0, 1, 129, 200], [200, 200, 200, 200], [5, 0, 0, 77]])
