@@ -456,31 +456,31 @@ def cpu_baseline_dense(O, np, a_cpu, w_cpu, synth, target_s=12.0):
 # record is the split-tail schedule's two launches together (k_gemm and
 # k_gemm_fixup), which the bench times as the GEMM.
 MEASURED_TRAFFIC = {
-    "prefill": {"sources_sha256": "1e1b4433e0ef977947141ca80cfdfb6c698fb6c7d898933df84d7adb39fb0773"
+    "prefill": {"sources_sha256": "e03dc3ffc721ed1b41da1592c6ba52dfffc7eade77cc9034ef7fd44fa5ede027"
                           "e7afed52fec782c4327ee38521820444f93ab7eb99f899822d3ae3320f273e3a"
                           "0b8ab37c346d4290d1fdb25793ffb74b674eb91941278aed19a6fa7e4e266b6a"
-                          "00987efe9b58793d38eee7c3ac47c5f2a3e7778972573580accdbc293de72d63",
-             "fetch_kib": 276683.8, "write_kib": 262144.0, "fetch_factor": 2.0, "write_factor": 1.0},
-    "moe": {"sources_sha256": "1e1b4433e0ef977947141ca80cfdfb6c698fb6c7d898933df84d7adb39fb0773"
+                          "54b19610b17c816426fc33a6ab2620605cb533220f8d2b2ba5de96d5cd0cf1df",
+             "fetch_kib": 276649.9, "write_kib": 262144.0, "fetch_factor": 2.0, "write_factor": 1.0},
+    "moe": {"sources_sha256": "e03dc3ffc721ed1b41da1592c6ba52dfffc7eade77cc9034ef7fd44fa5ede027"
                           "e7afed52fec782c4327ee38521820444f93ab7eb99f899822d3ae3320f273e3a"
                           "0b8ab37c346d4290d1fdb25793ffb74b674eb91941278aed19a6fa7e4e266b6a"
-                          "00987efe9b58793d38eee7c3ac47c5f2a3e7778972573580accdbc293de72d63",
-             "fetch_kib": 139091.0, "write_kib": 43510.0, "fetch_factor": 2.0, "write_factor": 1.0},
-    "dense": {"sources_sha256": "1e1b4433e0ef977947141ca80cfdfb6c698fb6c7d898933df84d7adb39fb0773"
+                          "54b19610b17c816426fc33a6ab2620605cb533220f8d2b2ba5de96d5cd0cf1df",
+             "fetch_kib": 139075.5, "write_kib": 43510.0, "fetch_factor": 2.0, "write_factor": 1.0},
+    "dense": {"sources_sha256": "e03dc3ffc721ed1b41da1592c6ba52dfffc7eade77cc9034ef7fd44fa5ede027"
                           "e7afed52fec782c4327ee38521820444f93ab7eb99f899822d3ae3320f273e3a"
                           "0b8ab37c346d4290d1fdb25793ffb74b674eb91941278aed19a6fa7e4e266b6a"
-                          "00987efe9b58793d38eee7c3ac47c5f2a3e7778972573580accdbc293de72d63",
-             "fetch_kib": 18602.4, "write_kib": 16384.0, "fetch_factor": 2.0, "write_factor": 1.0},
-    "svdquant": {"sources_sha256": "1e1b4433e0ef977947141ca80cfdfb6c698fb6c7d898933df84d7adb39fb0773"
+                          "54b19610b17c816426fc33a6ab2620605cb533220f8d2b2ba5de96d5cd0cf1df",
+             "fetch_kib": 18604.9, "write_kib": 16384.0, "fetch_factor": 2.0, "write_factor": 1.0},
+    "svdquant": {"sources_sha256": "e03dc3ffc721ed1b41da1592c6ba52dfffc7eade77cc9034ef7fd44fa5ede027"
                           "e7afed52fec782c4327ee38521820444f93ab7eb99f899822d3ae3320f273e3a"
                           "0b8ab37c346d4290d1fdb25793ffb74b674eb91941278aed19a6fa7e4e266b6a"
-                          "00987efe9b58793d38eee7c3ac47c5f2a3e7778972573580accdbc293de72d63",
-             "fetch_kib": 18748.7, "write_kib": 24576.0, "fetch_factor": 2.0, "write_factor": 1.0},
-    "decode": {"sources_sha256": "1e1b4433e0ef977947141ca80cfdfb6c698fb6c7d898933df84d7adb39fb0773"
+                          "54b19610b17c816426fc33a6ab2620605cb533220f8d2b2ba5de96d5cd0cf1df",
+             "fetch_kib": 19885.1, "write_kib": 24577.9, "fetch_factor": 2.0, "write_factor": 1.0},
+    "decode": {"sources_sha256": "e03dc3ffc721ed1b41da1592c6ba52dfffc7eade77cc9034ef7fd44fa5ede027"
                           "e7afed52fec782c4327ee38521820444f93ab7eb99f899822d3ae3320f273e3a"
                           "0b8ab37c346d4290d1fdb25793ffb74b674eb91941278aed19a6fa7e4e266b6a"
-                          "00987efe9b58793d38eee7c3ac47c5f2a3e7778972573580accdbc293de72d63",
-             "fetch_kib": 6383.9, "write_kib": 128.0, "fetch_factor": 2.0, "write_factor": 1.0},
+                          "54b19610b17c816426fc33a6ab2620605cb533220f8d2b2ba5de96d5cd0cf1df",
+             "fetch_kib": 6383.6, "write_kib": 128.0, "fetch_factor": 2.0, "write_factor": 1.0},
 }
 GEMM_SOURCES = ("nvfp4_block_scaled_04_amd/csrc/gemm.hip", "nvfp4_block_scaled_04_amd/csrc/gemm_common.h",
                 "nvfp4_block_scaled_04_amd/csrc/device_common.h", "nvfp4_block_scaled_04_amd/csrc/quant_block.h")
