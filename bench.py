@@ -414,7 +414,7 @@ def swiglu_front_half(ops, synth, torch, mask_cpu, dev):
     }
 
 
-def cpu_baseline_dense(O, np, a_cpu, w_cpu, synth, target_s=12.0):
+def cpu_baseline_dense(O, np, a_cpu, w_cpu, synth, target_s=20.0):
     """The oracle on a bounded sample of the same step: the weight is
     quantized once, untimed (offline in the GPU step too); the timed part
     quantizes a slice of activation rows (dynamic gs over the slice) and
