@@ -246,7 +246,7 @@ def build_workload(name, ops, synth, torch):
         w.gemm_bytes = valid * h // 2 + E * sf_size(m, h) + E * n * h // 2 + E * sf_size(n, h) + 2 * valid * n
         w.m, w.n, w.k = valid, n, h
         w.cfg = {"experts": E, "m_max": m, "valid_rows": mo.mask.tolist(), "n": n, "k": h}
-        w.cpu_sample = None
+        w.cpu_sample = lambda O, np: cpu_baseline_moe(O, np, mo, synth)
         w.swiglu = lambda: swiglu_front_half(ops, synth, torch, mo.mask, dev)
         return w
 
@@ -309,7 +309,7 @@ def build_workload(name, ops, synth, torch):
         w.gemm_bytes = m * k // 2 + sf_size(m, k) + n * k // 2 + sf_size(n, k) + 2 * m * n + 2 * (m + n) * r + 2 * n
         w.m, w.n, w.k = m, n, k
         w.cfg = {"m": m, "n": n, "k": k, "r": r}
-        w.cpu_sample = None
+        w.cpu_sample = lambda O, np: cpu_baseline_svdquant(O, np, s, synth)
         return w
     raise ValueError(name)
 
@@ -414,12 +414,22 @@ def swiglu_front_half(ops, synth, torch, mask_cpu, dev):
     }
 
 
+def _sized_sample(run, m, target_s):
+    """Rows of a bounded oracle sample: a 64-row probe sizes the slice so
+    that the timed run takes about target_s seconds (at most m rows)."""
+    rows = min(64, m)
+    dt = run(rows)
+    if dt < target_s / 2 and rows < m:
+        rows = int(min(m, max(rows, 64 * round(rows * target_s / dt / 64))))
+        dt = run(rows)
+    return rows, dt
+
+
 def cpu_baseline_dense(O, np, a_cpu, w_cpu, synth, target_s=20.0):
     """The oracle on a bounded sample of the same step: the weight is
     quantized once, untimed (offline in the GPU step too); the timed part
     quantizes a slice of activation rows (dynamic gs over the slice) and
-    computes the GEMM for those rows.  A 64-row probe sizes the slice so the
-    timed run takes about `target_s` seconds."""
+    computes the GEMM for those rows."""
     wq = O.quantize(synth.bits(w_cpu))          # untimed, like the GPU's weights
     m, k = a_cpu.shape
     n = w_cpu.shape[0]
@@ -432,11 +442,7 @@ def cpu_baseline_dense(O, np, a_cpu, w_cpu, synth, target_s=20.0):
         O.gemm_rows(qa, wq[0], sa, wq[1], alpha, rows, n, k)
         return time.perf_counter() - t0
 
-    rows = 64
-    dt = run(rows)
-    if dt < target_s / 2:
-        rows = int(min(m, max(rows, 64 * round(rows * target_s / dt / 64))))
-        dt = run(rows)
+    rows, dt = _sized_sample(run, m, target_s)
     flops = 2.0 * rows * n * k
     return {
         "value": flops / dt / 1e12,
@@ -445,6 +451,91 @@ def cpu_baseline_dense(O, np, a_cpu, w_cpu, synth, target_s=20.0):
         "kind": "oracle",
         "sample": f"{rows} of {m} activation rows: oracle dynamic quantize of those rows + "
                   f"oracle dequant-GEMM {rows}x{n}x{k} (fp64 accumulation), {dt:.2f} s wall",
+    }
+
+
+def cpu_baseline_moe(O, np, mo, synth, target_s=20.0):
+    """The routed-expert step's oracle on a bounded sample: the first valid
+    rows of the experts in order (expert 0's, then expert 1's, ...), their
+    silu_and_mul quantization (dynamic gs per expert over its sampled rows)
+    and their rows of the expert's GEMM; the experts' weights are quantized
+    once, untimed.  Every valid row costs the same, so the rate stands for
+    the step's."""
+    valid = [int(v) for v in mo.mask.clamp(0, mo.m)]
+    n, h = mo.n, mo.h
+    wq = {}
+
+    def take(rows):  # (expert, rows of it) covering `rows` valid rows
+        out = []
+        for e, v in enumerate(valid):
+            if rows <= 0:
+                break
+            if v:
+                out.append((e, min(v, rows)))
+                rows -= min(v, rows)
+        return out
+
+    def run(rows):
+        parts = take(rows)
+        for e, _ in parts:
+            if e not in wq:
+                wq[e] = O.quantize(synth.bits(mo.w[e]))
+        xs = [synth.bits(mo.x[e, :r]) for e, r in parts]
+        t0 = time.perf_counter()
+        for (e, r), x in zip(parts, xs):
+            qa, sa, ga = O.quantize(x, prologue=O.PRO_SILU)
+            alpha = np.float32(1.0) / (ga[0] * wq[e][2][0])
+            O.gemm_rows(qa, wq[e][0], sa, wq[e][1], alpha, r, n, h)
+        return time.perf_counter() - t0
+
+    rows, dt = _sized_sample(run, sum(valid), target_s)
+    used = take(rows)
+    return {
+        "value": 2.0 * rows * n * h / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": O.num_threads(),
+        "kind": "oracle",
+        "sample": f"{rows} of the {sum(valid)} valid rows (experts {[e for e, _ in used]}): oracle silu_and_mul "
+                  f"NVFP4 quantize of those rows (dynamic gs per expert over them) + oracle dequant-GEMM {rows}"
+                  f"x{n}x{h} (fp64 accumulation), {dt:.2f} s wall",
+    }
+
+
+def cpu_baseline_svdquant(O, np, s, synth, target_s=20.0):
+    """The SVDQuant step's oracle on a bounded sample of activation rows:
+    smooth quantize with a static gs (the oracle's global scale of the whole
+    smoothed activation, untimed, as the step's is calibrated offline), the
+    LoRA-down projection d (rounded to bf16 as the kernel stores it), and the
+    GEMM rows with the LoRA-up term and bias; the weight is quantized once,
+    untimed."""
+    import torch
+    wq = O.quantize(synth.bits(s.w))
+    m, n, k = s.m, s.n, s.k
+    pqs = synth.bits(s.pqs)
+    amax = float((s.x.float() * s.pqs.float()).abs().max())   # bf16 x bf16: exact in fp32
+    gs = np.float32(O.global_scale(amax))
+    al = np.float32(1.0) / (gs * wq[2][0])
+    l2 = synth.bits(s.l2.to(torch.bfloat16))
+    l1 = synth.bits((s.l1_raw / float(al)).to(torch.bfloat16))
+    bias = synth.bits(s.bias)
+
+    def run(rows):
+        x = synth.bits(s.x[:rows])
+        t0 = time.perf_counter()
+        qa, sa, _ = O.quantize(x, prologue=O.PRO_SMOOTH, pqs=pqs, gs=np.array([gs], np.float32),
+                               gs_mode=O.STATIC)
+        d = O.f64_to_bf16_via_f32(O.lora_down(x, pqs, l2))
+        O.gemm_rows(qa, wq[0], sa, wq[1], al, rows, n, k, bias=bias, d=d, l1=l1)
+        return time.perf_counter() - t0
+
+    rows, dt = _sized_sample(run, m, target_s)
+    return {
+        "value": 2.0 * rows * n * (k + s.r) / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": O.num_threads(),
+        "kind": "oracle",
+        "sample": f"{rows} of {m} activation rows: oracle smooth quantize (static gs) + LoRA-down + "
+                  f"dequant-GEMM {rows}x{n}x{k} with the rank-{s.r} LoRA-up and bias (fp64), {dt:.2f} s wall",
     }
 
 
