@@ -23,8 +23,9 @@
 // (BM/WGM) x (BN/WGN), each wave a grid of 32 x 32 MFMA fragments: 4 x 2
 // waves of 64 x 128 for the 256 x 256 tile (two waves per SIMD, so one
 // wave's dequantization and LDS waits overlap the other's MFMAs; measured
-// 2% faster than 2 x 2 waves of 128 x 128 with one wave per SIMD), 2 x 2
-// waves for the smaller tiles.  K advances
+// 2% faster than 2 x 2 waves of 128 x 128 with one wave per SIMD), 4 x 2
+// waves of 64 x 96 for the 256 x 192 tile, 2 x 2 waves for the smaller
+// tiles.  K advances
 // 128 elements (64 bytes of a row) per step.  A step's FP4 rows and raw scale
 // bytes go from global memory straight into LDS (buffer loads with the LDS
 // bit: no registers), two or three stages deep, so a step's loads are issued
@@ -1122,12 +1123,14 @@ enum class Tile { T256x256, T256x192, T128x256, T128x256K2, T128x128, Skinny };
 
 // Workgroup tile per problem.  Larger wave tiles need fewer dequantization
 // instructions per MFMA (64x128 waves of the 256x256 and 128x256 tiles: 6,
-// 64x64 waves of the 128x128 tile: 8), and two waves per SIMD hide one
-// wave's dequantization behind the other's MFMAs, but the grid must still
-// spread evenly over the 256 CUs (measured on the workload shapes: the
-// 256x256 tile needs at least two tiles per CU; the 128x128 tile wins when
-// it gives three per CU; with at most one 128x256 tile per CU the K loop is
-// split over two wave groups so each SIMD still holds two waves).
+// 64x96 waves of the 256x192 tile: 6.7, 64x64 waves of the 128x128 tile:
+// 8), and two waves per SIMD hide one wave's dequantization behind the
+// other's MFMAs, but the grid must still spread evenly over the 256 CUs
+// (measured on the workload shapes: the 256x256 tile needs at least two
+// tiles per CU; a single problem that makes one round of 256x192 tiles
+// takes them; the 128x128 tile wins when it gives three per CU; with at most
+// one 128x256 tile per CU the K loop is split over two wave groups so each
+// SIMD still holds two waves).
 
 static Tile pick_tile(int64_t m, int64_t n, int64_t k, int64_t E) {
     auto tiles = [&](int64_t bm, int64_t bn) { return E * ((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
