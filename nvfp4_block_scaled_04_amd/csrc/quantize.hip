@@ -498,48 +498,49 @@ __global__ __launch_bounds__(256) void k_quantize_fused(QParams p) {
 // mm_nvfp4_svdquant: a is the NVFP4 quantization of x * pqs, and d = x @
 // (pqs[:, None] * L2^T) is its rank-r projection): one read of x feeds both.
 // A workgroup of 16 waves owns a 16-row band and walks K in chunks of
-// kLoraChunk columns.  In a chunk, wave w holds row w of the band and lane l
-// its 16-element block l (two 16-byte loads; the wave reads 2 KB of the row
-// contiguously): the block is quantized with the smooth pass's arithmetic,
-// and the products x * pqs that the quantization forms (exact in fp32: two
-// 8-bit significands) are split exactly into two bf16 halves, hi = bf16(x *
-// pqs) and lo = x * pqs - hi (at most 8 significant bits, so exact in bf16),
-// parked in one of two pairs of LDS buffers.  After one barrier each wave
-// projects its 32-column slices of the chunk with v_mfma_f32_16x16x32_bf16:
-// l2 as read (every workgroup reads the same rows, through the caches) as
-// the A operand against hi and against lo from LDS, so every product is
-// exact and only fp32 accumulation rounds.  The accumulators carry across
-// chunks.  The next chunk's row loads are issued before the current chunk is
-// quantized, so HBM reads overlap the arithmetic; the two buffer pairs
-// alternate, so one barrier per chunk orders parking and projection (a wave
-// parks chunk c only after the barrier of chunk c - 1, which every wave
-// passes after projecting chunk c - 2 from the same pair).  At the end the
-// waves' partial projections are added through LDS and stored as bf16.  Any
-// K with K % 16 == 0.
+// kLoraChunk columns; in a chunk, wave w owns the band's 16 rows x 64
+// columns 64w.. (lane l: row l/4, 16-element block l%4; each row's 128
+// bytes read contiguously by four lanes), so a wave needs no other wave's
+// data until the end: the block is quantized with the smooth pass's
+// arithmetic, and the products x * pqs that the quantization forms (exact in
+// fp32: two 8-bit significands) are split exactly into two bf16 halves, hi =
+// bf16(x * pqs) and lo = x * pqs - hi (at most 8 significant bits, so exact
+// in bf16), written to the wave's own LDS buffers and read back in the MFMA
+// operand layout (the wave's LDS accesses execute in order; no workgroup
+// barrier).  The wave then projects its two 32-column slices with
+// v_mfma_f32_16x16x32_bf16: l2 as read (every workgroup reads the same rows,
+// through the caches) as the A operand against hi and against lo, so every
+// product is exact and only fp32 accumulation rounds.  The accumulators carry
+// across chunks; the next two chunks' rows (ranks above 64: the next one's)
+// are in flight while a chunk is worked on.  At the end the waves' partial projections are added through LDS (one
+// barrier) and stored as bf16.  Any K with K % 16 == 0.
 // ---------------------------------------------------------------------------
 
-constexpr int kLoraChunk = 1024;  // columns per chunk (64 blocks: one per lane)
-constexpr int kLoraWaves = 16;    // = rows per band
+constexpr int kLoraWaves = 16;                 // = rows per band
+constexpr int kLoraSlab = 64;                  // columns of a wave per chunk
+constexpr int kLoraChunk = kLoraWaves * kLoraSlab;
 
 template <int RT>  // rank tiles of 16
 __global__ __launch_bounds__(64 * kLoraWaves) void k_quantize_lora(QParams p, const uint16_t* l2, uint16_t* d_out,
                                                                   int rank) {
-    constexpr int PITCH = kLoraChunk + 8;  // bf16 per LDS row (16 bytes of pad spread the banks)
-    constexpr int BUF = 16 * PITCH;        // bf16 per buffer (hi or lo of one chunk)
-    constexpr int SPW = kLoraChunk / 32 / kLoraWaves;  // projection slices per wave per chunk
+    constexpr int XP = kLoraSlab + 8;  // bf16 per LDS row of a wave's buffer (16 bytes of pad spread the banks)
+    constexpr int WBUF = 16 * XP;      // bf16 per buffer (hi or lo of the wave's 16 x 64 slab)
+    constexpr int SPW = kLoraSlab / 32;  // projection slices per wave per chunk
     // rank 32: the projection operands of the next chunk load with its rows;
     // larger ranks load each slice's operands just before its MFMAs (the
     // register file of a 16-wave workgroup holds no more)
     constexpr bool PREFETCH = RT <= 2;
     constexpr int PART = (kLoraWaves - 1) * RT * 64 * 8;  // bf16-sized slots of the waves' partial sums
+    constexpr int XS = kLoraWaves * 2 * WBUF;
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    __shared__ __align__(16) uint16_t xs[4 * BUF > PART ? 4 * BUF : PART];
+    __shared__ __align__(16) uint16_t xs[XS > PART ? XS : PART];
     __shared__ float rtab[128];
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int64_t m0 = (int64_t)blockIdx.x * 16;
-    const int64_t row = m0 + wave;                 // this wave's row of the band
+    const int lr = lane >> 2, lb = lane & 3;  // this lane's row of the band, block of the slab
+    const int64_t row = m0 + lr;
     const bool row_ok = row < p.m;
     const uint16_t* xrow = (const uint16_t*)p.x + (row_ok ? row : p.m - 1) * p.k_in;
     const int nbk = (int)(p.K / 16);
@@ -550,10 +551,12 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_quantize_lora(QParams p, co
         const float dec = ue4m3_decode((uint32_t)t);
         rtab[t] = dec == 0.0f ? 0.0f : gs / dec;
     }
+    uint16_t* const bhi = xs + wave * 2 * WBUF;
+    uint16_t* const blo = bhi + WBUF;
 
     // this lane's block of chunk c (past K: the last block, never stored)
     auto load_rows = [&](int c, u32x4 (&raw)[2], u32x4 (&pq)[2]) {
-        int cb = c * 64 + lane;
+        int cb = c * (kLoraChunk / 16) + wave * (kLoraSlab / 16) + lb;
         cb = cb < nbk ? cb : nbk - 1;
         const u32x4* src = (const u32x4*)(xrow + (int64_t)cb * 16);
         raw[0] = src[0];
@@ -564,11 +567,11 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_quantize_lora(QParams p, co
     // lane's 8 columns (past K: column 0, and the operand is zeroed at its
     // use).  Every load here is issued on every path, so that the compiler
     // can count the loads in flight and wait only for the ones a use needs.
-    auto slice_ok = [&](int c, int j) {
-        return (int64_t)c * kLoraChunk + (wave + kLoraWaves * j) * 32 + kg * 8 < p.K;
+    auto slice_col = [&](int c, int j) {
+        return (int64_t)c * kLoraChunk + wave * kLoraSlab + j * 32 + kg * 8;
     };
     auto load_slice = [&](int c, int j, u32x4 (&b)[RT]) {
-        const int64_t col = (int64_t)c * kLoraChunk + (wave + kLoraWaves * j) * 32 + kg * 8;
+        const int64_t col = slice_col(c, j);
         const int64_t cs = col < p.K ? col : 0;
 #pragma unroll
         for (int i = 0; i < RT; i++) b[i] = *(const u32x4*)(l2 + (int64_t)(i * 16 + r16) * p.K + cs);
@@ -581,22 +584,26 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_quantize_lora(QParams p, co
     f32x4 acc[RT];
 #pragma unroll
     for (int i = 0; i < RT; i++) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    u32x4 raw[2], pqb[2], nraw[2], npqb[2];
+    // rows of chunks c, c + 1 and (rank 32 and 64) c + 2: one or two chunks in
+    // flight while one is worked on (chunk indices past the end repeat the
+    // last chunk); the larger ranks' registers hold one
+    constexpr bool DEEP = RT <= 4;
+    u32x4 raw[2], pqb[2], nraw[2], npqb[2], n2raw[2], n2pqb[2];
     u32x4 bf[PREFETCH ? SPW : 1][RT];
     load_rows(0, raw, pqb);
+    if constexpr (DEEP) load_rows(1 < nch ? 1 : 0, nraw, npqb);
     if constexpr (PREFETCH) load_proj(0, bf);
     __syncthreads();  // rtab
 
     uint8_t* const q = p.out_fp4;
     for (int c = 0; c < nch; c++) {
-        uint16_t* const bhi = xs + (c & 1) * 2 * BUF;
-        uint16_t* const blo = bhi + BUF;
-        // the next chunk's rows, in flight while this chunk is worked on (the
-        // last chunk reloads itself: unconditional, like every load here)
-        load_rows(c + 1 < nch ? c + 1 : c, nraw, npqb);
+        // later chunks' rows, in flight while this chunk is worked on (past
+        // the end: the last chunk again; unconditional, like every load here)
+        if constexpr (DEEP) load_rows(c + 2 < nch ? c + 2 : nch - 1, n2raw, n2pqb);
+        else load_rows(c + 1 < nch ? c + 1 : c, nraw, npqb);
 
         // ---- quantize this lane's block
-        const int cb = c * 64 + lane;  // block column
+        const int cb = c * (kLoraChunk / 16) + wave * (kLoraSlab / 16) + lb;  // block column
         const bool in_k = cb < nbk;
         const bool blk_ok = row_ok && in_k;
         float f[16];
@@ -605,46 +612,52 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_quantize_lora(QParams p, co
         uint32_t w0, w1;
         pack_block(f, rtab[sc], w0, w1);
         if (blk_ok) *(uint2*)(q + row * (p.K / 2) + (int64_t)cb * 8) = uint2{w0, w1};
-        // the 4 scale bytes of a swizzle dword sit in 4 neighbouring lanes;
-        // rows past m (up to the padded 128) and blocks past K write 0
-        uint32_t v = sc << (8 * (lane & 3));
+        // the 4 scale bytes of a swizzle dword sit in 4 neighbouring lanes
+        // (blocks lb = 0..3 of the row's column group); rows past m (up to the
+        // padded 128) and blocks past K write 0
+        uint32_t v = sc << (8 * lb);
         v |= __shfl_xor(v, 1);
         v |= __shfl_xor(v, 2);
-        if ((lane & 3) == 0 && in_k)
+        if (lb == 0 && in_k)
             *(uint32_t*)(p.out_sf + ((row >> 7) * p.nct + (cb >> 2)) * 512 + (row & 31) * 16 +
                          ((row & 127) >> 5) * 4) = v;
 
-        // ---- park the projection's input, the plain products x * pqs (no
-        // nan_to_num) as hi + lo; rows past m and columns past K are 0
+        // ---- the projection's input, the plain products x * pqs (no
+        // nan_to_num) as hi + lo, into the wave's buffers; rows past m and
+        // columns past K are 0
         uint32_t ph[8], pl[8];
 #pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const uint32_t xw = raw[j >> 2][j & 3], pw = pqb[j >> 2][j & 3];
+        for (int jj = 0; jj < 8; jj++) {
+            const uint32_t xw = raw[jj >> 2][jj & 3], pw = pqb[jj >> 2][jj & 3];
             const f32x2 prod = {bf16_lo(xw) * bf16_lo(pw), bf16_hi(xw) * bf16_hi(pw)};
             const bf16x2 hv = __builtin_convertvector(prod, bf16x2);  // RNE
             const f32x2 rest = {prod[0] - (float)hv[0], prod[1] - (float)hv[1]};
-            ph[j] = blk_ok ? __builtin_bit_cast(uint32_t, hv) : 0u;
-            pl[j] = blk_ok ? __builtin_bit_cast(uint32_t, __builtin_convertvector(rest, bf16x2)) : 0u;
+            ph[jj] = blk_ok ? __builtin_bit_cast(uint32_t, hv) : 0u;
+            pl[jj] = blk_ok ? __builtin_bit_cast(uint32_t, __builtin_convertvector(rest, bf16x2)) : 0u;
         }
-        u32x4* dh = (u32x4*)(bhi + wave * PITCH + lane * 16);
-        u32x4* dl = (u32x4*)(blo + wave * PITCH + lane * 16);
+        u32x4* dh = (u32x4*)(bhi + lr * XP + lb * 16);
+        u32x4* dl = (u32x4*)(blo + lr * XP + lb * 16);
         dh[0] = u32x4{ph[0], ph[1], ph[2], ph[3]};
         dh[1] = u32x4{ph[4], ph[5], ph[6], ph[7]};
         dl[0] = u32x4{pl[0], pl[1], pl[2], pl[3]};
         dl[1] = u32x4{pl[4], pl[5], pl[6], pl[7]};
-        __syncthreads();
+        // the wave's own writes, read back by other lanes of the wave: LDS
+        // accesses of one wave execute in order; keep the compiler from
+        // moving them across
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
         // ---- project this wave's slices of the chunk
 #pragma unroll
         for (int j = 0; j < SPW; j++) {
-            const int sl = wave + kLoraWaves * j;
-            if ((int64_t)c * kLoraChunk + sl * 32 >= p.K) break;  // uniform in the wave
+            if ((int64_t)c * kLoraChunk + wave * kLoraSlab + j * 32 >= p.K) break;  // uniform in the wave
             const int js = PREFETCH ? j : 0;
             if constexpr (!PREFETCH) load_slice(c, j, bf[0]);
-            const int off = r16 * PITCH + sl * 32 + kg * 8;
+            const int off = r16 * XP + j * 32 + kg * 8;
             const bf16x8 xh = __builtin_bit_cast(bf16x8, *(const u32x4*)(bhi + off));
             const bf16x8 xl = __builtin_bit_cast(bf16x8, *(const u32x4*)(blo + off));
-            const bool ok = slice_ok(c, j);
+            const bool ok = slice_col(c, j) < p.K;
 #pragma unroll
             for (int i = 0; i < RT; i++) {
                 const bf16x8 w = __builtin_bit_cast(bf16x8, ok ? bf[js][i] : u32x4{0u, 0u, 0u, 0u});
@@ -652,11 +665,19 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_quantize_lora(QParams p, co
                 acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, xl, acc[i], 0, 0, 0);
             }
         }
+        // the buffers are rewritten next chunk only after these reads
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         if constexpr (PREFETCH) load_proj(c + 1 < nch ? c + 1 : c, bf);
         raw[0] = nraw[0]; raw[1] = nraw[1];
         pqb[0] = npqb[0]; pqb[1] = npqb[1];
+        if constexpr (DEEP) {
+            nraw[0] = n2raw[0]; nraw[1] = n2raw[1];
+            npqb[0] = n2pqb[0]; npqb[1] = n2pqb[1];
+        }
     }
-    __syncthreads();  // the LDS is free: it now holds the waves' partial sums
+    __syncthreads();  // every wave is done with its buffers: the LDS now holds the waves' partial sums
     f32x4* const part = (f32x4*)xs;
     if (wave > 0)
 #pragma unroll
