@@ -70,10 +70,14 @@ def test_dynamic_pipeline_replays(ops, shape):
             assert torch.equal(t.view(torch.uint8), r.view(torch.uint8)), f"replay {rep}: {name} differs"
 
 
-def test_moe_pipeline_replays(ops):
-    """silu quantize over masked experts, per-expert alpha, grouped masked GEMM."""
+@pytest.mark.parametrize("ws", [False, True])
+def test_moe_pipeline_replays(ops, ws):
+    """silu quantize over masked experts, per-expert alpha, grouped masked
+    GEMM; with ws: the silu quantize with a workspace holding h (alpha from
+    the same call) and the grouped GEMM with its split-tail workspace, both
+    workspaces overwritten with stale bytes between replays."""
     E, m, h, n = 4, 256, 512, 768
-    say("graph moe", (E, m, h, n))
+    say("graph moe", (E, m, h, n), "ws", ws)
     mo = synth.moe(e=E, m=m, h=h, n=n)
     x = mo.x.to("cuda")
     mask = mo.mask.to("cuda")
@@ -88,10 +92,17 @@ def test_moe_pipeline_replays(ops):
     alpha = torch.empty(E, dtype=torch.float32, device="cuda")
     out = torch.zeros(E, m, n, dtype=torch.bfloat16, device="cuda")
 
+    qws = ops.silu_workspace(E, m, h, "cuda") if ws else None
+    gws = ops.gemm_workspace("cuda") if ws else None
+
     def step():
-        ops.silu_mul_nvfp4_quantize(x, mask, gsa, ops.GS_DYNAMIC, out_fp4=fa, out_sf=sfa)
-        ops.nvfp4_alpha(gsa, gsw, out=alpha)
-        ops.nvfp4_gemm_grouped_masked(fa, fw, sfa, sfw, alpha, mask, out=out)
+        if ws:
+            ops.silu_mul_nvfp4_quantize_ws(x, qws, mask, gsa, ops.GS_DYNAMIC, gs_other=gsw, alpha=alpha,
+                                           out_fp4=fa, out_sf=sfa)
+        else:
+            ops.silu_mul_nvfp4_quantize(x, mask, gsa, ops.GS_DYNAMIC, out_fp4=fa, out_sf=sfa)
+            ops.nvfp4_alpha(gsa, gsw, out=alpha)
+        ops.nvfp4_gemm_grouped_masked(fa, fw, sfa, sfw, alpha, mask, out=out, workspace=gws)
 
     step()
     torch.cuda.synchronize()
@@ -101,7 +112,7 @@ def test_moe_pipeline_replays(ops):
     ref_fa = [fa[e, :valid[e]].clone() for e in range(E)]
     g = _capture(step)
     for rep in range(3):
-        for t in (fa, sfa, gsa, alpha):
+        for t in (fa, sfa, gsa, alpha) + ((qws, gws) if ws else ()):
             t.view(torch.uint8).fill_(0x3C + rep)
         torch.cuda.synchronize()
         g.replay()
