@@ -234,6 +234,28 @@ def test_silu_ws_h(ops, mask, k):
     run_batched(ops, x.to(torch.bfloat16), mk, ops.GS_DYNAMIC, silu=True, ws="h")
 
 
+def test_silu_ws_size_boundary(ops):
+    """A workspace one byte short of NVFP4_SILU_WS_BYTES takes the path that
+    evaluates silu in both passes; exactly that size keeps h.  Both give the
+    same bytes, gs and alpha."""
+    g = torch.Generator().manual_seed(47)
+    b, m, k = 3, 300, 512
+    x = dev(torch.randn(b, m, 2 * k, generator=g).to(torch.bfloat16))
+    mk = dev(torch.tensor([300, 17, 129], dtype=torch.int32))
+    go = dev((torch.rand(b, generator=g) * 100 + 1).to(torch.float32))
+    say("silu ws size boundary", (b, m, k))
+    outs = []
+    for nbytes in (ops.silu_ws_bytes(b, m, k) - 1, ops.silu_ws_bytes(b, m, k)):
+        w = torch.full((nbytes,), 0x5A, dtype=torch.uint8, device="cuda")
+        o4 = canary((b, m, k // 2))
+        osf = canary((b, ops.sf_size(m, k)))
+        r = ops.silu_mul_nvfp4_quantize_ws(x, w, mk, None, ops.GS_DYNAMIC, gs_other=go, out_fp4=o4, out_sf=osf)
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in r])
+    for u, v in zip(*outs):
+        assert torch.equal(u.view(torch.uint8), v.view(torch.uint8))
+
+
 def test_batched_ws_static(ops):
     g = torch.Generator().manual_seed(42)
     x = torch.randn(3, 130, 768, generator=g).to(torch.bfloat16)
