@@ -87,7 +87,7 @@ def build_workload(name, ops, synth, torch):
     w.gemm_kernel = "k_gemm (block-scaled NVFP4 GEMM)"
     w.hbm_bound = False
     w.w4a16 = None
-    w.lora_down = None
+    w.lora_down = w.lora_down_unprepared = None
     w.swiglu = None
     w.mx = None
     w.library = None
@@ -277,8 +277,16 @@ def build_workload(name, ops, synth, torch):
         def quant(x, mode=ops.GS_STATIC):
             ops.nvfp4_quantize(x, gsa, mode, pre_quant_scale=pqs, out_fp4=fa, out_sf=sfa)
 
+        # the LoRA-down weight with the smoothing folded in, split into exact
+        # bf16 halves in the fused kernel's operand order: a weight transform,
+        # done once like the weight quantization
+        wl = ops.nvfp4_lora_down_prepare(pqs, l2)
+
         def lora_down(x):
             # smooth quantize and the LoRA-down projection d, one read of x
+            ops.nvfp4_quantize_lora_down_prepared(x, pqs, wl, r, gsa, ops.GS_STATIC, out_fp4=fa, out_sf=sfa, d=d)
+
+        def lora_down_unprepared(x):
             ops.nvfp4_quantize_lora_down(x, pqs, l2, gsa, ops.GS_STATIC, out_fp4=fa, out_sf=sfa, d=d)
 
         def make_steps(acts, K):
@@ -290,17 +298,20 @@ def build_workload(name, ops, synth, torch):
                 x = acts[i % len(acts)]
 
                 def pre(x=x, o=o):
-                    ops.nvfp4_quantize_lora_down(x, pqs, l2, gsa, ops.GS_STATIC, out_fp4=o[0], out_sf=o[1], d=o[2])
+                    ops.nvfp4_quantize_lora_down_prepared(x, pqs, wl, r, gsa, ops.GS_STATIC, out_fp4=o[0],
+                                                          out_sf=o[1], d=o[2])
 
                 def gemm(o=o):
                     ops.nvfp4_gemm_svdquant(o[0], fw, o[1], sfw, alpha, o[2], l1, bias=bias, out=out)
                 steps.append((pre, gemm))
             return steps
 
-        w.lora_down = lora_down
-        w.lora_down_bytes = m * k * 2 + k * 2 + r * k * 2 + m * k // 2 + sf_size(m, k) + 2 * m * r
+        w.lora_down, w.lora_down_unprepared = lora_down, lora_down_unprepared
+        w.lora_down_bytes = m * k * 2 + k * 2 + 2 * ops.lora_prepared_numel(r, k) + m * k // 2 + sf_size(m, k) \
+            + 2 * m * r
+        w.lora_down_unprepared_bytes = m * k * 2 + k * 2 + r * k * 2 + m * k // 2 + sf_size(m, k) + 2 * m * r
         w.desc = ("SVDQuant linear 4096x3072x3072, r=32: smooth NVFP4 quantize (static gs) with the LoRA-down "
-                  "projection fused -> fused GEMM + LoRA-up + bias")
+                  "projection fused (weight pqs * L2 prepared once) -> fused GEMM + LoRA-up + bias")
         w.rotate_hint = _rotation(m * k * 2)
         w.make_acts = lambda n_copies: [s.x.to(dev) for _ in range(n_copies)]
         w.make_steps, w.quant = make_steps, quant
@@ -814,9 +825,16 @@ def main():
         ld_ms = time_graph(torch, g_ld) / n_copies
         del g_ld
         ld_gbs = w.lora_down_bytes / (ld_ms * 1e-3) / 1e9
+        g_ldu = capture(torch, lambda: [w.lora_down_unprepared(a) for a in acts])
+        ldu_ms = time_graph(torch, g_ldu) / n_copies
+        del g_ldu
         ld = {"ms": round(ld_ms, 5), "gbs": round(ld_gbs, 1), "frac_hbm": round(ld_gbs / HBM_PEAK_GBS, 4),
               "bytes": w.lora_down_bytes,
-              "kernel": "k_quantize_lora (smooth quantize + LoRA-down projection, one read of x)"}
+              "kernel": ("k_quantize_lora (smooth quantize + LoRA-down projection, one read of x; the weight "
+                         "prepared once as exact bf16 halves of pqs * L2 in operand order)"),
+              "unprepared_ms": round(ldu_ms, 5),
+              "unprepared_gbs": round(w.lora_down_unprepared_bytes / (ldu_ms * 1e-3) / 1e9, 1),
+              "unprepared": "nvfp4_quantize_lora_down on the raw l2: x * pqs split into bf16 halves per element"}
     # ceilings of the memory system on this machine, timed the same way: a plain
     # elementwise copy (read + write) and a read-only reduction (torch)
     src = torch.ones(64 * 2 ** 20, dtype=torch.float32, device="cuda")

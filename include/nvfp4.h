@@ -189,6 +189,50 @@ int nvfp4_quantize_lora_down(const void *x, int64_t m, int64_t k, const void *pr
                              uint8_t *out_fp4, uint8_t *out_sf, void *d, void *stream);
 
 /*
+ * Elements (bf16) of the prepared LoRA-down weight for rank r and width k:
+ * two halves x r ranks x k rounded up to 32 columns.
+ */
+#define NVFP4_LORA_PREPARED_ELEMS(r, k) (2 * (int64_t)(r) * (((int64_t)(k) + 31) / 32 * 32))
+
+/*
+ * The LoRA-down weight with the smoothing folded in, prepared once for
+ * nvfp4_quantize_lora_down_prepared (flashinfer docs,
+ * flashinfer.gemm.mm_nvfp4_svdquant, parameter d: the factor
+ * pqs[:, None] * L2^T is fixed once the layer is calibrated).  Each product
+ * pqs[k] * l2[p, k] (exact in fp32) is written as two bf16 halves whose sum
+ * is that product exactly:
+ *   hi[p, k] = bf16(pqs[k] * l2[p, k])   (round to nearest even),
+ *   lo[p, k] = bf16(pqs[k] * l2[p, k] - hi[p, k])   (exact).
+ * w_out holds NVFP4_LORA_PREPARED_ELEMS(r, k) bf16 in the order the fused
+ * kernel reads its MFMA operands: fragment (h, t, s) (h = 0 hi, 1 lo; rank
+ * tile t of 16 ranks; column slice s of 32) starts at element
+ * ((h * r/16 + t) * ceil(k/32) + s) * 512, and its element l * 8 + e
+ * (l = 0..63, e = 0..7) is half h of rank 16 t + l % 16 at column
+ * 32 s + 8 (l / 16) + e, or 0 where that column is >= k.
+ *   pre_quant_scale: [k] bf16; l2: [r, k] bf16, row-major.
+ * Exact while the products are finite and not below fp32's normal range.
+ * Requires r in {32, 64, 96, 128} (NVFP4_BAD_RANK otherwise), k >= 16,
+ * k % 16 == 0, 16-byte aligned pointers.  Device pointers owned by the
+ * caller; nothing is allocated.
+ */
+int nvfp4_lora_down_prepare(const void *pre_quant_scale, const void *l2, int64_t r, int64_t k,
+                            void *w_out, void *stream);
+
+/*
+ * nvfp4_quantize_lora_down with the weight from nvfp4_lora_down_prepare
+ * (w_prepared: NVFP4_LORA_PREPARED_ELEMS(r, k) bf16) in place of l2: the
+ * same out_fp4, out_sf and global_scale bytes, and
+ * d = bf16(sum_k x[i,k] * (hi[p,k] + lo[p,k])), every product exact and
+ * accumulated in fp32, so d meets the same bound against
+ * sum_k x[i,k] * pqs[k] * l2[p,k].  x enters the projection as is
+ * (non-finite values propagate).  Arguments, requirements and errors are
+ * those of nvfp4_quantize_lora_down.
+ */
+int nvfp4_quantize_lora_down_prepared(const void *x, int64_t m, int64_t k, const void *pre_quant_scale,
+                                      const void *w_prepared, int64_t r, float *global_scale, int gs_mode,
+                                      uint8_t *out_fp4, uint8_t *out_sf, void *d, void *stream);
+
+/*
  * Batched, optionally masked quantization (flashinfer PR #1774, the
  * nvfp4_batched_quantize op and its per-item global scale).
  *   x:            [b, m, k] bf16.

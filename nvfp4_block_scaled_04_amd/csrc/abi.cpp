@@ -121,9 +121,9 @@ int nvfp4_quantize_noalloc(const void* x, int x_dtype, int64_t m, int64_t k, con
                            out_sf, ws, stream);
 }
 
-int nvfp4_quantize_lora_down(const void* x, int64_t m, int64_t k, const void* pre_quant_scale,
-                             const void* l2, int64_t r, float* global_scale, int gs_mode, uint8_t* out_fp4,
-                             uint8_t* out_sf, void* d, void* stream) {
+static int lora_down_common(const void* x, int64_t m, int64_t k, const void* pre_quant_scale, const void* l2,
+                            int64_t r, float* global_scale, int gs_mode, uint8_t* out_fp4, uint8_t* out_sf, void* d,
+                            bool prepared, void* stream) {
     if (!x || !pre_quant_scale || !l2 || !global_scale || !out_fp4 || !out_sf || !d) return NVFP4_NULL_POINTER;
     if (gs_mode != NVFP4_GS_STATIC && gs_mode != NVFP4_GS_DYNAMIC) return NVFP4_UNSUPPORTED;
     if (r <= 0 || r % 32 != 0 || r > 128) return NVFP4_BAD_RANK;
@@ -135,8 +135,32 @@ int nvfp4_quantize_lora_down(const void* x, int64_t m, int64_t k, const void* pr
     a.x = x; a.x_dtype = NVFP4_BF16; a.pqs = pre_quant_scale; a.mask = nullptr;
     a.gs = global_scale; a.out_fp4 = out_fp4; a.out_sf = out_sf;
     a.b = 1; a.m = m; a.k_in = k; a.silu = false; a.dynamic = gs_mode == NVFP4_GS_DYNAMIC;
-    return launch_status(nvfp4::launch_quantize_lora(a, (const uint16_t*)l2, (uint16_t*)d, (int)r,
+    return launch_status(nvfp4::launch_quantize_lora(a, (const uint16_t*)l2, (uint16_t*)d, (int)r, prepared,
                                                       (hipStream_t)stream));
+}
+
+int nvfp4_quantize_lora_down(const void* x, int64_t m, int64_t k, const void* pre_quant_scale,
+                             const void* l2, int64_t r, float* global_scale, int gs_mode, uint8_t* out_fp4,
+                             uint8_t* out_sf, void* d, void* stream) {
+    return lora_down_common(x, m, k, pre_quant_scale, l2, r, global_scale, gs_mode, out_fp4, out_sf, d, false,
+                            stream);
+}
+
+int nvfp4_lora_down_prepare(const void* pre_quant_scale, const void* l2, int64_t r, int64_t k, void* w_out,
+                            void* stream) {
+    if (!pre_quant_scale || !l2 || !w_out) return NVFP4_NULL_POINTER;
+    if (r <= 0 || r % 32 != 0 || r > 128) return NVFP4_BAD_RANK;
+    if (k < 16 || k % 16 != 0 || !dim_ok(k)) return NVFP4_BAD_SHAPE;
+    if (!aligned16(pre_quant_scale) || !aligned16(l2) || !aligned16(w_out)) return NVFP4_MISALIGNED;
+    return launch_status(nvfp4::launch_lora_split((const uint16_t*)pre_quant_scale, (const uint16_t*)l2,
+                                                  (uint16_t*)w_out, (int)r, k, (hipStream_t)stream));
+}
+
+int nvfp4_quantize_lora_down_prepared(const void* x, int64_t m, int64_t k, const void* pre_quant_scale,
+                                      const void* w_prepared, int64_t r, float* global_scale, int gs_mode,
+                                      uint8_t* out_fp4, uint8_t* out_sf, void* d, void* stream) {
+    return lora_down_common(x, m, k, pre_quant_scale, w_prepared, r, global_scale, gs_mode, out_fp4, out_sf, d,
+                            true, stream);
 }
 
 // The batched forms (k_in: the input row width, 2K for silu): every check of

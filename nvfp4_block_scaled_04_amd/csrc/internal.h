@@ -38,9 +38,13 @@ hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t st);
 hipError_t scratch_for_current_device(float** ptr);
 // Smooth quantize of a bf16 [m, k] (a.pqs set, a.b = 1) with the LoRA-down
 // projection d = bf16((x * pqs) @ l2^T), l2 bf16 [rank, k]; rank in
-// {32, 64, 96, 128}, any k % 16 == 0.
-hipError_t launch_quantize_lora(const QuantizeArgs& a, const uint16_t* l2, uint16_t* d, int rank,
+// {32, 64, 96, 128}, any k % 16 == 0.  prepared: l2 is instead the split
+// weight [2, rank, k] that launch_lora_split writes.
+hipError_t launch_quantize_lora(const QuantizeArgs& a, const uint16_t* l2, uint16_t* d, int rank, bool prepared,
                                 hipStream_t st);
+// w [2, rank, k] = the hi and lo bf16 halves of pqs[k] * l2[p, k].
+hipError_t launch_lora_split(const uint16_t* pqs, const uint16_t* l2, uint16_t* w, int rank, int64_t K,
+                             hipStream_t st);
 hipError_t launch_alpha(const float* ga, const float* gb, float* alpha, int64_t n, hipStream_t st);
 
 struct GemmArgs {

@@ -514,13 +514,21 @@ __global__ __launch_bounds__(256) void k_quantize_fused(QParams p) {
 // across chunks; the next two chunks' rows (ranks above 64: the next one's)
 // are in flight while a chunk is worked on.  At the end the waves' partial projections are added through LDS (one
 // barrier) and stored as bf16.  Any K with K % 16 == 0.
+//
+// PREP: the weight arrives prepared, w = pqs[:, None] * L2^T split exactly
+// into hi + lo bf16 halves ([2, r, K], k_lora_split below), so x itself (bf16,
+// exact) is the MFMA operand: nothing is split per element, and only x passes
+// through the wave's LDS buffer (one buffer instead of two), against hi and
+// against lo.  (A lane layout in which the registers x arrives in are
+// already the MFMA operand, row = lane % 16, puts 16 rows in every 16-lane
+// group of a load and measured 35% slower than the split it replaces.)
 // ---------------------------------------------------------------------------
 
 constexpr int kLoraWaves = 16;                 // = rows per band
 constexpr int kLoraSlab = 64;                  // columns of a wave per chunk
 constexpr int kLoraChunk = kLoraWaves * kLoraSlab;
 
-template <int RT>  // rank tiles of 16
+template <int RT, bool PREP>  // rank tiles of 16; prepared (split) weight
 __global__ __launch_bounds__(64 * kLoraWaves) void k_quantize_lora(QParams p, const uint16_t* l2, uint16_t* d_out,
                                                                   int rank) {
     constexpr int XP = kLoraSlab + 8;  // bf16 per LDS row of a wave's buffer (16 bytes of pad spread the banks)
@@ -529,9 +537,10 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_quantize_lora(QParams p, co
     // rank 32: the projection operands of the next chunk load with its rows;
     // larger ranks load each slice's operands just before its MFMAs (the
     // register file of a 16-wave workgroup holds no more)
-    constexpr bool PREFETCH = RT <= 2;
+    constexpr bool PREFETCH = RT <= 2 && !PREP;
     constexpr int PART = (kLoraWaves - 1) * RT * 64 * 8;  // bf16-sized slots of the waves' partial sums
-    constexpr int XS = kLoraWaves * 2 * WBUF;
+    constexpr int XS = kLoraWaves * (PREP ? 1 : 2) * WBUF;
+    constexpr int NH = PREP ? 2 : 1;  // weight operands per rank tile and slice (PREP: hi, lo)
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     __shared__ __align__(16) uint16_t xs[XS > PART ? XS : PART];
@@ -551,7 +560,7 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_quantize_lora(QParams p, co
         const float dec = ue4m3_decode((uint32_t)t);
         rtab[t] = dec == 0.0f ? 0.0f : gs / dec;
     }
-    uint16_t* const bhi = xs + wave * 2 * WBUF;
+    uint16_t* const bhi = xs + wave * (PREP ? 1 : 2) * WBUF;  // PREP: x itself
     uint16_t* const blo = bhi + WBUF;
 
     // this lane's block of chunk c (past K: the last block, never stored)
@@ -570,13 +579,27 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_quantize_lora(QParams p, co
     auto slice_col = [&](int c, int j) {
         return (int64_t)c * kLoraChunk + wave * kLoraSlab + j * 32 + kg * 8;
     };
-    auto load_slice = [&](int c, int j, u32x4 (&b)[RT]) {
-        const int64_t col = slice_col(c, j);
-        const int64_t cs = col < p.K ? col : 0;
+    // (PREP: the prepared weight is stored in this operand's order, one
+    // 1024-byte fragment per half, rank tile and 32-column slice, so a wave
+    // reads each contiguously; slices past the end read slice 0)
+    const int64_t nsl = (p.K + 31) / 32;
+    auto load_slice = [&](int c, int j, u32x4 (&b)[RT][NH]) {
+        if constexpr (PREP) {
+            int64_t sl = (int64_t)c * (kLoraChunk / 32) + wave * (kLoraSlab / 32) + j;
+            sl = sl < nsl ? sl : 0;
 #pragma unroll
-        for (int i = 0; i < RT; i++) b[i] = *(const u32x4*)(l2 + (int64_t)(i * 16 + r16) * p.K + cs);
+            for (int i = 0; i < RT; i++)
+#pragma unroll
+                for (int h = 0; h < NH; h++)
+                    b[i][h] = *(const u32x4*)(l2 + (((int64_t)(h * RT + i) * nsl + sl) * 64 + lane) * 8);
+        } else {
+            const int64_t col = slice_col(c, j);
+            const int64_t cs = col < p.K ? col : 0;
+#pragma unroll
+            for (int i = 0; i < RT; i++) b[i][0] = *(const u32x4*)(l2 + (int64_t)(i * 16 + r16) * p.K + cs);
+        }
     };
-    auto load_proj = [&](int c, u32x4 (&b)[PREFETCH ? SPW : 1][RT]) {
+    auto load_proj = [&](int c, u32x4 (&b)[PREFETCH ? SPW : 1][RT][NH]) {
 #pragma unroll
         for (int j = 0; j < SPW; j++) load_slice(c, j, b[j]);
     };
@@ -589,7 +612,7 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_quantize_lora(QParams p, co
     // last chunk); the larger ranks' registers hold one
     constexpr bool DEEP = RT <= 4;
     u32x4 raw[2], pqb[2], nraw[2], npqb[2], n2raw[2], n2pqb[2];
-    u32x4 bf[PREFETCH ? SPW : 1][RT];
+    u32x4 bf[PREFETCH ? SPW : 1][RT][NH];
     load_rows(0, raw, pqb);
     if constexpr (DEEP) load_rows(1 < nch ? 1 : 0, nraw, npqb);
     if constexpr (PREFETCH) load_proj(0, bf);
@@ -622,25 +645,33 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_quantize_lora(QParams p, co
             *(uint32_t*)(p.out_sf + ((row >> 7) * p.nct + (cb >> 2)) * 512 + (row & 31) * 16 +
                          ((row & 127) >> 5) * 4) = v;
 
+
         // ---- the projection's input, the plain products x * pqs (no
         // nan_to_num) as hi + lo, into the wave's buffers; rows past m and
         // columns past K are 0
+        // (PREP: x itself, the smoothing being in the weight)
         uint32_t ph[8], pl[8];
 #pragma unroll
         for (int jj = 0; jj < 8; jj++) {
             const uint32_t xw = raw[jj >> 2][jj & 3], pw = pqb[jj >> 2][jj & 3];
-            const f32x2 prod = {bf16_lo(xw) * bf16_lo(pw), bf16_hi(xw) * bf16_hi(pw)};
-            const bf16x2 hv = __builtin_convertvector(prod, bf16x2);  // RNE
-            const f32x2 rest = {prod[0] - (float)hv[0], prod[1] - (float)hv[1]};
-            ph[jj] = blk_ok ? __builtin_bit_cast(uint32_t, hv) : 0u;
-            pl[jj] = blk_ok ? __builtin_bit_cast(uint32_t, __builtin_convertvector(rest, bf16x2)) : 0u;
+            if constexpr (PREP) {
+                ph[jj] = blk_ok ? xw : 0u;
+            } else {
+                const f32x2 prod = {bf16_lo(xw) * bf16_lo(pw), bf16_hi(xw) * bf16_hi(pw)};
+                const bf16x2 hv = __builtin_convertvector(prod, bf16x2);  // RNE
+                const f32x2 rest = {prod[0] - (float)hv[0], prod[1] - (float)hv[1]};
+                ph[jj] = blk_ok ? __builtin_bit_cast(uint32_t, hv) : 0u;
+                pl[jj] = blk_ok ? __builtin_bit_cast(uint32_t, __builtin_convertvector(rest, bf16x2)) : 0u;
+            }
         }
         u32x4* dh = (u32x4*)(bhi + lr * XP + lb * 16);
-        u32x4* dl = (u32x4*)(blo + lr * XP + lb * 16);
         dh[0] = u32x4{ph[0], ph[1], ph[2], ph[3]};
         dh[1] = u32x4{ph[4], ph[5], ph[6], ph[7]};
-        dl[0] = u32x4{pl[0], pl[1], pl[2], pl[3]};
-        dl[1] = u32x4{pl[4], pl[5], pl[6], pl[7]};
+        if constexpr (!PREP) {
+            u32x4* dl = (u32x4*)(blo + lr * XP + lb * 16);
+            dl[0] = u32x4{pl[0], pl[1], pl[2], pl[3]};
+            dl[1] = u32x4{pl[4], pl[5], pl[6], pl[7]};
+        }
         // the wave's own writes, read back by other lanes of the wave: LDS
         // accesses of one wave execute in order; keep the compiler from
         // moving them across
@@ -656,13 +687,24 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_quantize_lora(QParams p, co
             if constexpr (!PREFETCH) load_slice(c, j, bf[0]);
             const int off = r16 * XP + j * 32 + kg * 8;
             const bf16x8 xh = __builtin_bit_cast(bf16x8, *(const u32x4*)(bhi + off));
-            const bf16x8 xl = __builtin_bit_cast(bf16x8, *(const u32x4*)(blo + off));
-            const bool ok = slice_col(c, j) < p.K;
+            if constexpr (PREP) {
+                // x against hi and against lo (x past K is 0; the weight
+                // read there is column 0, finite)
 #pragma unroll
-            for (int i = 0; i < RT; i++) {
-                const bf16x8 w = __builtin_bit_cast(bf16x8, ok ? bf[js][i] : u32x4{0u, 0u, 0u, 0u});
-                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, xh, acc[i], 0, 0, 0);
-                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, xl, acc[i], 0, 0, 0);
+                for (int i = 0; i < RT; i++)
+#pragma unroll
+                    for (int h = 0; h < 2; h++)
+                        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bf[js][i][h]),
+                                                                         xh, acc[i], 0, 0, 0);
+            } else {
+                const bool ok = slice_col(c, j) < p.K;
+                const bf16x8 xl = __builtin_bit_cast(bf16x8, *(const u32x4*)(blo + off));
+#pragma unroll
+                for (int i = 0; i < RT; i++) {
+                    const bf16x8 w = __builtin_bit_cast(bf16x8, ok ? bf[js][i][0] : u32x4{0u, 0u, 0u, 0u});
+                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, xh, acc[i], 0, 0, 0);
+                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, xl, acc[i], 0, 0, 0);
+                }
             }
         }
         // the buffers are rewritten next chunk only after these reads
@@ -697,6 +739,45 @@ __global__ __launch_bounds__(64 * kLoraWaves) void k_quantize_lora(QParams p, co
     }
 }
 
+// The prepared LoRA-down weight (flashinfer mm_nvfp4_svdquant, parameter d:
+// the factor pqs[:, None] * L2^T) as two bf16 halves, hi = bf16 of pqs[k] *
+// l2[p, k] (round to nearest even; the fp32 product of two bf16 values is
+// exact) and lo = bf16 of that product minus hi (exact: at most 8
+// significant bits remain), stored in the order k_quantize_lora<RT, true>
+// reads them as MFMA operands: fragment (h, t, s) = half h, rank tile t (16
+// ranks), slice s (32 columns) is 64 lanes x 8 bf16, lane l holding rank
+// 16 t + l % 16 at columns 32 s + 8 (l / 16) .. + 7 (zero past K).  One
+// thread per lane of a (t, s) fragment pair (hi and lo).
+__global__ void k_lora_split(const uint16_t* pqs, const uint16_t* l2, uint16_t* w, int64_t rank, int64_t K) {
+    const int64_t nsl = (K + 31) / 32, rt = rank / 16;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (t, s, lane)
+    if (i >= rt * nsl * 64) return;
+    const int lane = (int)(i & 63);
+    const int64_t ts = i >> 6, t = ts / nsl, sl = ts - t * nsl;
+    const int64_t row = t * 16 + (lane & 15), col = sl * 32 + (lane >> 4) * 8;
+    u32x4 hi = u32x4{0u, 0u, 0u, 0u}, lo = hi;
+    if (col < K) {  // K % 16 == 0: the 8 columns are all in or all out
+        const u32x4 a = *(const u32x4*)(l2 + row * K + col);
+        const u32x4 sc = *(const u32x4*)(pqs + col);
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const float p0 = bf16_lo(a[j]) * bf16_lo(sc[j]), p1 = bf16_hi(a[j]) * bf16_hi(sc[j]);
+            const uint32_t h = pack_bf16x2(p0, p1);
+            hi[j] = h;
+            lo[j] = pack_bf16x2(p0 - bf16_lo(h), p1 - bf16_hi(h));
+        }
+    }
+    *(u32x4*)(w + ((t * nsl + sl) * 64 + lane) * 8) = hi;
+    *(u32x4*)(w + (((rt + t) * nsl + sl) * 64 + lane) * 8) = lo;
+}
+
+hipError_t launch_lora_split(const uint16_t* pqs, const uint16_t* l2, uint16_t* w, int rank, int64_t K,
+                             hipStream_t st) {
+    const int64_t n = (int64_t)(rank / 16) * ((K + 31) / 32) * 64;
+    k_lora_split<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(pqs, l2, w, rank, K);
+    return hipGetLastError();
+}
+
 // The flat amax pass's grid: one workgroup per 256 x 4 loads of 16 bytes, at
 // most kFlatAmaxGrid; its partials go to ws, or (ws null) to the scale
 // buffer, which then also bounds their number.
@@ -714,7 +795,7 @@ static void launch_amax_flat(QParams& p, float* ws, hipStream_t st) {
     k_amax_flat<V><<<(unsigned)g, 256, 0, st>>>(p);
 }
 
-hipError_t launch_quantize_lora(const QuantizeArgs& a, const uint16_t* l2, uint16_t* d, int rank,
+hipError_t launch_quantize_lora(const QuantizeArgs& a, const uint16_t* l2, uint16_t* d, int rank, bool prepared,
                                 hipStream_t st) {
     QParams p{};
     p.x = a.x;
@@ -735,11 +816,20 @@ hipError_t launch_quantize_lora(const QuantizeArgs& a, const uint16_t* l2, uint1
     }
     const dim3 grid((unsigned)(p.nrt * 8));  // 16-row bands over the padded rows (their scales are zeroed)
     constexpr int nt = 64 * kLoraWaves;
+    if (prepared) {
+        switch (rank / 16) {
+        case 2: k_quantize_lora<2, true><<<grid, nt, 0, st>>>(p, l2, d, rank); break;
+        case 4: k_quantize_lora<4, true><<<grid, nt, 0, st>>>(p, l2, d, rank); break;
+        case 6: k_quantize_lora<6, true><<<grid, nt, 0, st>>>(p, l2, d, rank); break;
+        default: k_quantize_lora<8, true><<<grid, nt, 0, st>>>(p, l2, d, rank); break;
+        }
+        return hipGetLastError();
+    }
     switch (rank / 16) {
-    case 2: k_quantize_lora<2><<<grid, nt, 0, st>>>(p, l2, d, rank); break;
-    case 4: k_quantize_lora<4><<<grid, nt, 0, st>>>(p, l2, d, rank); break;
-    case 6: k_quantize_lora<6><<<grid, nt, 0, st>>>(p, l2, d, rank); break;
-    default: k_quantize_lora<8><<<grid, nt, 0, st>>>(p, l2, d, rank); break;
+    case 2: k_quantize_lora<2, false><<<grid, nt, 0, st>>>(p, l2, d, rank); break;
+    case 4: k_quantize_lora<4, false><<<grid, nt, 0, st>>>(p, l2, d, rank); break;
+    case 6: k_quantize_lora<6, false><<<grid, nt, 0, st>>>(p, l2, d, rank); break;
+    default: k_quantize_lora<8, false><<<grid, nt, 0, st>>>(p, l2, d, rank); break;
     }
     return hipGetLastError();
 }

@@ -20,6 +20,8 @@ EXPORTS = (
     "nvfp4_quantize_ws",
     "nvfp4_quantize_noalloc",
     "nvfp4_quantize_lora_down",
+    "nvfp4_lora_down_prepare",
+    "nvfp4_quantize_lora_down_prepared",
     "nvfp4_quantize_masked_batched",
     "nvfp4_quantize_masked_batched_ws",
     "silu_mul_nvfp4_quantize",
@@ -59,6 +61,8 @@ def _load():
         "nvfp4_quantize_ws": [vp, i32, i64, i64, vp, vp, i32, vp, vp, vp, vp, vp, i64, vp],
         "nvfp4_quantize_noalloc": [vp, i32, i64, i64, vp, vp, i32, vp, vp, vp, vp, vp],
         "nvfp4_quantize_lora_down": [vp, i64, i64, vp, vp, i64, vp, i32, vp, vp, vp, vp],
+        "nvfp4_lora_down_prepare": [vp, vp, i64, i64, vp, vp],
+        "nvfp4_quantize_lora_down_prepared": [vp, i64, i64, vp, vp, i64, vp, i32, vp, vp, vp, vp],
         "nvfp4_quantize_masked_batched": [vp, i64, i64, i64, vp, vp, i32, vp, vp, vp],
         "silu_mul_nvfp4_quantize": [vp, i64, i64, i64, vp, vp, i32, vp, vp, vp],
         "nvfp4_quantize_masked_batched_ws": [vp, i64, i64, i64, vp, vp, i32, vp, vp, vp, vp, vp, i64, vp],
@@ -278,21 +282,11 @@ def nvfp4_quantize_noalloc(x, global_scale, gs_other=None, alpha=None, gs_mode=G
     return out_fp4, out_sf, global_scale, alpha
 
 
-def nvfp4_quantize_lora_down(x, pre_quant_scale, l2, global_scale=None, gs_mode=GS_DYNAMIC,
-                             out_fp4=None, out_sf=None, d=None):
-    """Smooth NVFP4 quantize of bf16 x [m, k] (pre_quant_scale [k] bf16) and the
-    SVDQuant LoRA-down d = bf16((x * pqs) @ l2^T), l2 [r, k] bf16, in one read
-    of x.  Returns (fp4 [m, k/2], sf, global_scale [1], d [m, r])."""
-    _dims(x, "x", 2)
-    _dims(l2, "l2", 2)
+def _lora_down(fn, name, x, pre_quant_scale, w, r, global_scale, gs_mode, out_fp4, out_sf, d):
     m, k = x.shape
-    r = l2.shape[0]
     dev_ = x.device
     _dev(x, "x", BF16, m * k, dev_)
     _dev(pre_quant_scale, "pre_quant_scale", BF16, k, dev_)
-    if l2.shape[1] != k:
-        raise ValueError(f"l2 must be [r, {k}], got {tuple(l2.shape)}")
-    _dev(l2, "l2", BF16, r * k, dev_)
     if global_scale is None:
         global_scale = torch.zeros(1, dtype=torch.float32, device=dev_)
     if out_fp4 is None:
@@ -305,10 +299,64 @@ def nvfp4_quantize_lora_down(x, pre_quant_scale, l2, global_scale=None, gs_mode=
     _dev(out_fp4, "out_fp4", BYTES, m * (k // 2), dev_)
     _dev(out_sf, "out_sf", BYTES, sf_size(m, k), dev_)
     _dev(d, "d", BF16, m * r, dev_)
-    rc = _lib.nvfp4_quantize_lora_down(_ptr(x), m, k, _ptr(pre_quant_scale), _ptr(l2), r, _ptr(global_scale),
-                                       gs_mode, _ptr(out_fp4), _ptr(out_sf), _ptr(d), _stream(dev_))
-    _check(rc, "nvfp4_quantize_lora_down")
+    rc = fn(_ptr(x), m, k, _ptr(pre_quant_scale), _ptr(w), r, _ptr(global_scale), gs_mode, _ptr(out_fp4),
+            _ptr(out_sf), _ptr(d), _stream(dev_))
+    _check(rc, name)
     return out_fp4, out_sf, global_scale, d
+
+
+def nvfp4_quantize_lora_down(x, pre_quant_scale, l2, global_scale=None, gs_mode=GS_DYNAMIC,
+                             out_fp4=None, out_sf=None, d=None):
+    """Smooth NVFP4 quantize of bf16 x [m, k] (pre_quant_scale [k] bf16) and the
+    SVDQuant LoRA-down d = bf16((x * pqs) @ l2^T), l2 [r, k] bf16, in one read
+    of x.  Returns (fp4 [m, k/2], sf, global_scale [1], d [m, r])."""
+    _dims(x, "x", 2)
+    _dims(l2, "l2", 2)
+    m, k = x.shape
+    r = l2.shape[0]
+    if l2.shape[1] != k:
+        raise ValueError(f"l2 must be [r, {k}], got {tuple(l2.shape)}")
+    _dev(l2, "l2", BF16, r * k, x.device)
+    return _lora_down(_lib.nvfp4_quantize_lora_down, "nvfp4_quantize_lora_down", x, pre_quant_scale, l2, r,
+                      global_scale, gs_mode, out_fp4, out_sf, d)
+
+
+def lora_prepared_numel(r, k):
+    """bf16 elements of the prepared LoRA-down weight (NVFP4_LORA_PREPARED_ELEMS):
+    hi and lo, r ranks, k rounded up to 32 columns."""
+    return 2 * r * ((k + 31) // 32 * 32)
+
+
+def nvfp4_lora_down_prepare(pre_quant_scale, l2, out=None):
+    """The LoRA-down weight with the smoothing folded in, pqs[:, None] * L2^T,
+    as the exact sum of two bf16 halves (hi = bf16(pqs * l2), lo = bf16(pqs *
+    l2 - hi)), in the fused kernel's MFMA operand order (nvfp4.h gives it):
+    returns a flat bf16 tensor of lora_prepared_numel(r, k) elements for
+    nvfp4_quantize_lora_down_prepared.  A weight transform: run it once."""
+    _dims(l2, "l2", 2)
+    r, k = l2.shape
+    dev_ = l2.device
+    _dev(l2, "l2", BF16, r * k, dev_)
+    _dev(pre_quant_scale, "pre_quant_scale", BF16, k, dev_)
+    n = lora_prepared_numel(r, k)
+    if out is None:
+        out = torch.empty(n, dtype=torch.bfloat16, device=dev_)
+    _dev(out, "out", BF16, n, dev_)
+    rc = _lib.nvfp4_lora_down_prepare(_ptr(pre_quant_scale), _ptr(l2), r, k, _ptr(out), _stream(dev_))
+    _check(rc, "nvfp4_lora_down_prepare")
+    return out
+
+
+def nvfp4_quantize_lora_down_prepared(x, pre_quant_scale, w_prepared, r, global_scale=None, gs_mode=GS_DYNAMIC,
+                                      out_fp4=None, out_sf=None, d=None):
+    """nvfp4_quantize_lora_down with the rank-r weight from
+    nvfp4_lora_down_prepare in place of l2: the same quantized bytes, and
+    d = bf16(x @ (hi + lo)^T).  Returns (fp4, sf, global_scale, d)."""
+    _dims(x, "x", 2)
+    m, k = x.shape
+    _dev(w_prepared, "w_prepared", BF16, lora_prepared_numel(r, k), x.device)
+    return _lora_down(_lib.nvfp4_quantize_lora_down_prepared, "nvfp4_quantize_lora_down_prepared", x,
+                      pre_quant_scale, w_prepared, r, global_scale, gs_mode, out_fp4, out_sf, d)
 
 
 def nvfp4_quantize_masked_batched(x, mask=None, global_scale=None, gs_mode=GS_DYNAMIC,

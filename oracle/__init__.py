@@ -218,6 +218,22 @@ def lora_down(x_bf16, pqs_bf16, l2_bf16):
     return (x * p[None, :]) @ l2.T
 
 
+def lora_weight_split(pqs_bf16, l2_bf16):
+    """The LoRA-down weight with the smoothing folded in ([SVD] flashinfer
+    mm_nvfp4_svdquant, parameter d: the factor pqs[:, None] * L2^T), each
+    product p = pqs[k] * l2[j, k] written as two bf16 halves that sum to it
+    exactly: hi = bf16(p) (round to nearest even) and lo = bf16(p - hi).  The
+    fp32 product of two bf16 values is exact (two 8-bit significands), and so
+    is p - hi (at most 8 significant bits remain), for products in fp32's
+    normal range.  pqs_bf16: uint16 [k]; l2_bf16: uint16 [r, k].  Returns
+    uint16 [2, r, k]: the hi rows, then the lo rows."""
+    l2 = bf16_to_f32(np.asarray(l2_bf16, dtype=np.uint16))
+    p = l2 * bf16_to_f32(np.asarray(pqs_bf16, dtype=np.uint16))[None, :]
+    hi = f32_to_bf16(p).reshape(p.shape)
+    lo = f32_to_bf16(p - bf16_to_f32(hi)).reshape(p.shape)
+    return np.stack([hi, lo])
+
+
 def gemm_w4a16_rows(a_bf16, b, b_sf, alpha, m, n, k, rows=None, bias=None):
     """fp64 alpha * (A @ Bdq^T) + bias for the given rows of the bf16
     activation A ([NVF] f16a_nvfp4weight_scaled_mm); a_bf16: uint16 bit

@@ -37,6 +37,7 @@ def test_header_declares_the_entry_points():
         "nvfp4_gemm_grouped_masked_silu_quantize", "nvfp4_gemm_svdquant",
         "nvfp4_gemm_ws", "nvfp4_gemm_grouped_masked_ws", "nvfp4_gemm_svdquant_ws",
         "nvfp4_gemm_w4a16", "nvfp4_quantize_lora_down",
+        "nvfp4_lora_down_prepare", "nvfp4_quantize_lora_down_prepared",
         "nvfp4_quantize", "nvfp4_quantize_alpha", "nvfp4_quantize_ws", "nvfp4_quantize_noalloc",
         "nvfp4_quantize_masked_batched", "nvfp4_quantize_masked_batched_ws",
         "silu_mul_nvfp4_quantize", "silu_mul_nvfp4_quantize_ws",
@@ -336,6 +337,35 @@ def test_lora_down_validation(lib):
     assert run(d=P + 8) == MISAL
 
 
+def test_lora_down_prepared_validation(lib):
+    f = lib.nvfp4_quantize_lora_down_prepared
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                  ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    run = lambda x=P, m=64, k=256, pqs=P, w=P, r=32, gs=P, mode=1, o4=P, osf=P, d=P: \
+        f(x, m, k, pqs, w, r, gs, mode, o4, osf, d, None)
+    assert run(x=None) == NULLP
+    assert run(w=None) == NULLP
+    assert run(r=48) == RANK
+    assert run(r=0) == RANK
+    assert run(k=8) == SHAPE
+    assert run(m=0) == SHAPE
+    assert run(mode=3) == UNSUP
+    assert run(w=P + 4) == MISAL
+    g = lib.nvfp4_lora_down_prepare
+    g.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    prep = lambda pqs=P, l2=P, r=32, k=256, w=P: g(pqs, l2, r, k, w, None)
+    assert prep(pqs=None) == NULLP
+    assert prep(l2=None) == NULLP
+    assert prep(w=None) == NULLP
+    assert prep(r=16) == RANK
+    assert prep(r=256) == RANK
+    assert prep(k=0) == SHAPE
+    assert prep(k=264) == SHAPE   # k % 16 != 0
+    assert prep(k=1 << 31) == SHAPE
+    assert prep(w=P + 2) == MISAL
+    assert prep(pqs=P + 8) == MISAL
+
+
 def test_alpha_validation(lib):
     f = lib.nvfp4_alpha
     assert f(ctypes.c_void_p(None), ctypes.c_void_p(P), ctypes.c_void_p(P), ctypes.c_int64(1),
@@ -436,3 +466,23 @@ def test_workspace_size_macros_match_the_binding(tmp_path):
     for (b, m, k), line in zip(shapes, out):
         got = [int(v) for v in line.split()]
         assert got == [ops.batched_ws_bytes(b, m, k), ops.silu_ws_bytes(b, m, k)], (b, m, k, got)
+
+
+def test_prepared_lora_size_macro_matches_the_binding(tmp_path):
+    """NVFP4_LORA_PREPARED_ELEMS (compiled with gcc) equals the binding's
+    lora_prepared_numel, with k a multiple of 32 and not."""
+    from nvfp4_block_scaled_04_amd import ops
+    import subprocess
+    shapes = [(32, 16), (32, 3072), (64, 1040), (96, 272), (128, 8192)]
+    src = tmp_path / "lp.c"
+    lines = ['#include <stdio.h>', '#include <stdint.h>', '#include "nvfp4.h"', "int main(void) {"]
+    for r, k in shapes:
+        lines.append(f'  printf("%lld\\n", (long long)NVFP4_LORA_PREPARED_ELEMS({r}, {k}));')
+    lines += ["  return 0;", "}"]
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "lp"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run(["gcc", "-I", inc, str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()
+    assert [int(v) for v in out] == [ops.lora_prepared_numel(r, k) for r, k in shapes]
+    assert ops.lora_prepared_numel(32, 1040) == 2 * 32 * 1056

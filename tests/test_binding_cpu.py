@@ -26,6 +26,9 @@ CALLS = {
     "nvfp4_quantize_noalloc": lambda: ops.nvfp4_quantize_noalloc(bf(128, 64), f32(1), out_fp4=u8(128, 32),
                                                                  out_sf=u8(ops.sf_size(128, 64))),
     "nvfp4_quantize_lora_down": lambda: ops.nvfp4_quantize_lora_down(bf(128, 64), bf(64), bf(32, 64)),
+    "nvfp4_lora_down_prepare": lambda: ops.nvfp4_lora_down_prepare(bf(64), bf(32, 64)),
+    "nvfp4_quantize_lora_down_prepared": lambda: ops.nvfp4_quantize_lora_down_prepared(
+        bf(128, 64), bf(64), bf(ops.lora_prepared_numel(32, 64)), 32),
     "nvfp4_quantize_masked_batched": lambda: ops.nvfp4_quantize_masked_batched(bf(2, 128, 64)),
     "silu_mul_nvfp4_quantize": lambda: ops.silu_mul_nvfp4_quantize(bf(2, 128, 64)),
     "nvfp4_quantize_masked_batched_ws": lambda: ops.nvfp4_quantize_masked_batched_ws(bf(2, 128, 64), u8(16)),

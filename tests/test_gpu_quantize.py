@@ -127,29 +127,60 @@ def test_repeat_is_identical(ops):
         assert torch.equal(u, v)
 
 
+def lora_fragments(split, r, k):
+    """The oracle's split weight [2, r, k] laid out as the prepared weight
+    the header describes: fragment (h, t, s) of 64 lanes x 8 elements, lane l
+    holding rank 16 t + l % 16 at columns 32 s + 8 (l / 16) .. + 7, zero
+    past k."""
+    ns = (k + 31) // 32
+    pad = np.zeros((2, r, ns * 32), dtype=np.uint16)
+    pad[:, :, :k] = split
+    out = np.zeros((2, r // 16, ns, 64, 8), dtype=np.uint16)
+    for lane in range(64):
+        ranks = np.arange(r // 16) * 16 + lane % 16
+        for sl in range(ns):
+            c0 = 32 * sl + 8 * (lane // 16)
+            out[:, :, sl, lane, :] = pad[:, ranks, c0:c0 + 8]
+    return out.ravel()
+
+
 @pytest.mark.parametrize("m,k,r,dynamic", [(4096, 3072, 32, False), (100, 400, 64, True), (17, 272, 32, True),
                                           (300, 4096, 128, True), (130, 96, 96, False),
                                           (200, 8192, 32, True),     # K past the old 4096 limit: 8 chunks
                                           (130, 5136, 64, False),    # 5 chunks and one block
                                           (64, 1024, 96, True), (40, 1040, 128, False)])
-def test_quantize_lora_down(ops, m, k, r, dynamic):
+@pytest.mark.parametrize("prepared", [False, True])
+def test_quantize_lora_down(ops, m, k, r, dynamic, prepared):
     """Smooth quantize with the LoRA-down projection fused: the FP4 and scale
     bytes and gs must equal the oracle's smooth quantization exactly, and
     d = (x * pqs) @ L2^T must meet the GEMM bar against the oracle's fp64
     projection (every product is exact in the kernel; only fp32 accumulation
     and the bf16 output round).  The first case is the SVDQuant workload's
-    activation."""
+    activation.  prepared: through nvfp4_quantize_lora_down_prepared, with
+    the weight from nvfp4_lora_down_prepare (bit-exact against the oracle's
+    split)."""
     from gpu_util import row_tolerance_check
     s = synth.svdquant(m=m, n=64, k=k, r=r)
     l2 = s.l2.to(torch.bfloat16)
-    say("quantize + lora-down", (m, k, r), "dynamic", dynamic)
+    say("quantize + lora-down", (m, k, r), "dynamic", dynamic, "prepared", prepared)
     mode = ops.GS_DYNAMIC if dynamic else ops.GS_STATIC
     gs_static = None if dynamic else np.float32(2688.0 / 7.5)
     gs_d = torch.tensor([0.0 if gs_static is None else gs_static], dtype=torch.float32, device="cuda")
     o4 = canary((m, k // 2))
     osf = canary((ops.sf_size(m, k),))
     d = torch.full((m, r), 0x7FA5, dtype=torch.int16, device="cuda").view(torch.bfloat16)
-    ops.nvfp4_quantize_lora_down(dev(s.x), dev(s.pqs), dev(l2), gs_d, mode, out_fp4=o4, out_sf=osf, d=d)
+    if prepared:
+        w = torch.full((ops.lora_prepared_numel(r, k),), 0x7FA5, dtype=torch.int16,
+                       device="cuda").view(torch.bfloat16)
+        ops.nvfp4_lora_down_prepare(dev(s.pqs), dev(l2), out=w)
+        torch.cuda.synchronize()
+        ref_w = lora_fragments(O.lora_weight_split(np_bits(s.pqs), np_bits(l2)), r, k)
+        bad = np.argwhere(np_bits(w) != ref_w)
+        assert len(bad) == 0, f"{len(bad)} prepared weight elements differ, first at {bad[:3].tolist()}"
+        ops.nvfp4_quantize_lora_down_prepared(dev(s.x), dev(s.pqs), w, r, gs_d, mode, out_fp4=o4, out_sf=osf,
+                                              d=d)
+    else:
+        ops.nvfp4_quantize_lora_down(dev(s.x), dev(s.pqs), dev(l2), gs_d, mode, out_fp4=o4, out_sf=osf, d=d)
     torch.cuda.synchronize()
     q, sf, g = O.quantize(np_bits(s.x), prologue=O.PRO_SMOOTH, pqs=np_bits(s.pqs),
                           gs=None if gs_static is None else np.array([gs_static], np.float32), gs_mode=mode)

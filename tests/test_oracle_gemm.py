@@ -225,6 +225,66 @@ def test_lora_down_unit_rows_select_smoothed_columns():
     assert np.array_equal(d, ref.numpy())
 
 
+def _split_inputs(seed, r, k, spread=0.5):
+    g = torch.Generator().manual_seed(seed)
+    p = torch.exp(spread * torch.randn(k, generator=g)).to(torch.bfloat16)
+    l2 = (0.02 * torch.randn(r, k, generator=g)).to(torch.bfloat16)
+    return p, l2
+
+
+def test_lora_weight_split_sums_to_the_product_exactly():
+    """hi + lo is pqs[k] * l2[j, k] exactly (fp64 holds the product of two
+    bf16 values exactly), for every element; a dropped lo, a wrong sign or a
+    transposed pqs index fails here."""
+    p, l2 = _split_inputs(43, 6, 96, spread=3.0)
+    w = O.lora_weight_split(synth.bits(p), synth.bits(l2))
+    assert w.shape == (2, 6, 96) and w.dtype == np.uint16
+    hi = O.bf16_to_f32(w[0]).astype(np.float64)
+    lo = O.bf16_to_f32(w[1]).astype(np.float64)
+    exact = l2.double().numpy() * p.double().numpy()[None, :]
+    assert np.array_equal(hi + lo, exact)
+    assert np.count_nonzero(lo) > 0.5 * lo.size   # the low halves are really used
+
+
+def test_lora_weight_split_hi_is_the_nearest_bf16():
+    """hi is the bf16 nearest the product (brute force over its two
+    neighbours, ties to the even code), and torch's own fp32 -> bf16
+    rounding of the product gives the same bits."""
+    p, l2 = _split_inputs(44, 4, 64, spread=2.0)
+    w = O.lora_weight_split(synth.bits(p), synth.bits(l2))
+    exact = l2.double().numpy() * p.double().numpy()[None, :]
+    hi = w[0].astype(np.int64)
+    for delta in (-1, 1):
+        nb = O.bf16_to_f32((hi + delta).astype(np.uint16)).astype(np.float64)
+        d_hi = np.abs(exact - O.bf16_to_f32(w[0]).astype(np.float64))
+        d_nb = np.abs(exact - nb)
+        assert np.all((d_hi < d_nb) | ((d_hi == d_nb) & (hi % 2 == 0)))
+    prod32 = (l2.float() * p.float()[None, :]).to(torch.bfloat16)
+    assert np.array_equal(w[0], synth.bits(prod32))
+
+
+def test_lora_weight_split_unit_scale_is_the_weight():
+    """pqs = 1: hi is l2 itself and lo is +0."""
+    _, l2 = _split_inputs(45, 3, 32)
+    ones = torch.ones(32, dtype=torch.bfloat16)
+    w = O.lora_weight_split(synth.bits(ones), synth.bits(l2))
+    assert np.array_equal(w[0], synth.bits(l2))
+    assert np.all(w[1] == 0)
+
+
+def test_lora_weight_split_projection_equals_lora_down():
+    """x @ (hi + lo)^T in fp64 equals the oracle's LoRA-down projection of
+    the smoothed activation (the same exact products, summed in another
+    order)."""
+    g = torch.Generator().manual_seed(46)
+    x = torch.randn(7, 80, generator=g).to(torch.bfloat16)
+    p, l2 = _split_inputs(47, 5, 80)
+    w = O.lora_weight_split(synth.bits(p), synth.bits(l2))
+    wf = O.bf16_to_f32(w[0]).astype(np.float64) + O.bf16_to_f32(w[1]).astype(np.float64)
+    d = O.lora_down(synth.bits(x), synth.bits(p), synth.bits(l2))
+    assert np.allclose(x.double().numpy() @ wf.T, d, rtol=1e-13, atol=1e-15)
+
+
 def unit_scale_operand(rng, E, rows, k, codes=None):
     """E matrices of random e2m1 codes (all 16) with every block scale 1.0
     (ue4m3 code 0x38), padding scale bytes 0."""
