@@ -87,6 +87,7 @@ def build_workload(name, ops, synth, torch):
     w.gemm_kernel = "k_gemm (block-scaled NVFP4 GEMM)"
     w.hbm_bound = False
     w.w4a16 = None
+    w.linear_small = None
     w.lora_down = w.lora_down_unprepared = None
     w.swiglu = None
     w.mx = None
@@ -174,6 +175,13 @@ def build_workload(name, ops, synth, torch):
             w.w4a16 = lambda a, i: ops.nvfp4_gemm_w4a16(a, weights[i % len(weights)][0], weights[i % len(weights)][1],
                                                         alpha_w, out=out_w)
             w.w4a16_bytes = w_bytes + m * k * 2 + 2 * m * n
+            # the whole step in one launch (nvfp4_linear_small: the dynamic
+            # quantization on chip, then the GEMM); step i reads weight copy i
+            out_ls = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+            gs_ls = torch.zeros(1, dtype=torch.float32, device=dev)
+            w.linear_small = lambda a, i: ops.nvfp4_linear_small(a, weights[i % len(weights)][0],
+                                                                 weights[i % len(weights)][1], gsw, out=out_ls,
+                                                                 gs_out=gs_ls)
         w.cpu_sample = lambda O, np: cpu_baseline_dense(O, np, a_cpu, w_cpu, synth)
         if name in ("prefill", "dense"):
             w.mx = lambda acts: mx_setting(ops, torch, acts, w_cpu, dev)
@@ -819,6 +827,21 @@ def main():
         w4 = {"ms": round(w4_ms, 5), "gbs": round(w4_gbs, 1), "frac_hbm": round(w4_gbs / HBM_PEAK_GBS, 4),
               "bytes": w.w4a16_bytes, "weights": "cold (one weight copy per launch, caches flushed first)",
               "kernel": "k_gemm_w4a16 (bf16 activation x NVFP4 weight, no activation quantize)"}
+    ls = None
+    if w.linear_small is not None:
+        # the same steps as one launch each, on the same cold weight copies
+        g_ls = capture(torch, lambda: [w.linear_small(acts[i % n_copies], i) for i in range(K)])
+        settle(torch, g_ls.replay)
+        flush_caches(torch)
+        torch.cuda.synchronize()
+        ls_ms = time_graph(torch, g_ls, reps=1) / K
+        del g_ls
+        ls_gbs = w.w4a16_bytes / (ls_ms * 1e-3) / 1e9
+        ls = {"ms": round(ls_ms, 5), "tflops": round(w.flops / (ls_ms * 1e-3) / 1e12, 2),
+              "gbs": round(ls_gbs, 1), "frac_hbm": round(ls_gbs / HBM_PEAK_GBS, 4), "bytes": w.w4a16_bytes,
+              "weights": "cold (one weight copy per launch, caches flushed first)",
+              "kernel": ("k_linear_small (nvfp4_linear_small: the activation's dynamic quantization into LDS "
+                         "in every workgroup, then the skinny GEMM; bit for bit the quantize + alpha + GEMM calls)")}
     ld = None
     if w.lora_down is not None:
         g_ld = capture(torch, lambda: [w.lora_down(a) for a in acts])
@@ -917,6 +940,8 @@ def main():
                            "algorithmic_bytes_per_launch": w.gemm_bytes}
     if w4 is not None:
         res["w4a16"] = w4
+    if ls is not None:
+        res["linear_small"] = ls
     if ld is not None:
         res["quantize_lora_down"] = ld
     if w.mx is not None:

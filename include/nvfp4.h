@@ -431,6 +431,31 @@ int nvfp4_gemm_w4a16(const void *a, const uint8_t *b, const uint8_t *b_sf, const
                      const void *bias, void *out, int64_t m, int64_t n, int64_t k, void *stream);
 
 /*
+ * Dynamic-scale NVFP4 linear for a few activation rows (decode), in one
+ * launch.  The result is exactly that of three calls: nvfp4_quantize of x in
+ * DYNAMIC mode (FastVideo PR #1350, _global_sf: gs = 448*6 / amax(x);
+ * TensorRT-LLM NVFP4LinearMethod.create_weights: e2m1 with an FP8 scale per
+ * 16 elements), alpha = 1 / (gs * gs_b) as nvfp4_alpha forms it, and
+ * nvfp4_gemm of that activation against the NVFP4 weight (NVIDIA/Fuser PR
+ * #5737: dequantize, then a plain linear):
+ *   out = bf16(alpha * (Aq @ Bq^T) (+ bias)),
+ * bit for bit.  The quantized activation itself stays on chip.
+ *   x: [m, k] bf16 row-major, 16-byte aligned, 1 <= m <= 16;
+ *   k: a multiple of 128, 128 <= k <= 4096;
+ *   b: [n, k/2] uint8 packed e2m1; b_sf: pad_up(n,128)*pad_up(k/16,4) ue4m3
+ *   in the 128x4 swizzled layout; gs_b: device fp32 [1], the weight's global
+ *   scale; bias: NULL or [n] bf16; out: [m, n] bf16;
+ *   gs_out: NULL, or device fp32 [1] that receives the activation's gs.
+ * All pointers are device pointers owned by the caller; nothing is
+ * allocated.  Returns NVFP4_NULL_POINTER, NVFP4_BAD_SHAPE, NVFP4_MISALIGNED,
+ * or NVFP4_UNSUPPORTED for m > 16, k % 128 != 0 or k > 4096 (use the three
+ * calls there), before launching anything.
+ */
+int nvfp4_linear_small(const void *x, int64_t m, int64_t k, const uint8_t *b, const uint8_t *b_sf,
+                       const float *gs_b, const void *bias, void *out, int64_t n, float *gs_out,
+                       void *stream);
+
+/*
  * MX setting of the quantizer (flashinfer PR #1774: fp4_quantize's block
  * width and ue8m0 flags, there 16 / off; the other setting read as the OCP
  * Microscaling Formats v1.0 MXFP4 conversion): per 32 consecutive elements of

@@ -15,7 +15,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnvfp4_amd.so")
-SOURCES = ["quantize.hip", "gemm.hip", "mx.hip", "abi.cpp"]
+SOURCES = ["quantize.hip", "gemm.hip", "linear_small.hip", "mx.hip", "abi.cpp"]
 
 
 def hipcc():

@@ -344,6 +344,21 @@ int nvfp4_gemm_w4a16(const void* a, const uint8_t* b, const uint8_t* b_sf, const
     return launch_status(nvfp4::launch_gemm_w4a16(g, (hipStream_t)stream));
 }
 
+int nvfp4_linear_small(const void* x, int64_t m, int64_t k, const uint8_t* b, const uint8_t* b_sf,
+                       const float* gs_b, const void* bias, void* out, int64_t n, float* gs_out, void* stream) {
+    if (!x || !b || !b_sf || !gs_b || !out) return NVFP4_NULL_POINTER;
+    if (!dim_ok(m) || !dim_ok(n) || k < 16 || k % 16 != 0 || k > kMaxDim) return NVFP4_BAD_SHAPE;
+    if (m > nvfp4::kLinearSmallMaxRows || k % 128 != 0 || k > nvfp4::kLinearSmallMaxK) return NVFP4_UNSUPPORTED;
+    if ((n + 15) / 16 > ((int64_t)1 << 31) - 1 || !gemm_sf_ok(n, k / 16)) return NVFP4_BAD_SHAPE;
+    if (!aligned16(x) || !aligned16(b) || !aligned16(b_sf) || !aligned16(out) || ((uintptr_t)gs_b & 3u) ||
+        ((uintptr_t)gs_out & 3u) || (bias && !aligned16(bias)))
+        return NVFP4_MISALIGNED;
+    nvfp4::LinearSmallArgs a{};
+    a.x = x; a.b = b; a.b_sf = b_sf; a.gs_b = gs_b; a.bias = (const uint16_t*)bias;
+    a.out = (uint16_t*)out; a.gs_out = gs_out; a.m = m; a.n = n; a.k = k;
+    return launch_status(nvfp4::launch_linear_small(a, (hipStream_t)stream));
+}
+
 int mxfp4_quantize(const void* x, int x_dtype, int64_t m, int64_t k, uint8_t* out_fp4, uint8_t* out_sf,
                    void* stream) {
     if (!x || !out_fp4 || !out_sf) return NVFP4_NULL_POINTER;

@@ -84,6 +84,22 @@ struct SiluQuantOut {
 };
 hipError_t launch_gemm_silu_quantize(const GemmArgs& g, const SiluQuantOut& q, hipStream_t st);
 
+// Dynamic-scale NVFP4 linear for at most 16 activation rows in one launch:
+// nvfp4_quantize (DYNAMIC) of x, alpha = 1 / (gs * gs_b[0]), nvfp4_gemm.
+constexpr int64_t kLinearSmallMaxRows = 16;
+constexpr int kLinearSmallMaxK = 4096;  // the quantized activation (9 bytes per column) in LDS, x in registers
+struct LinearSmallArgs {
+    const void* x;          // [m, k] bf16
+    const uint8_t* b;       // [n, k/2]
+    const uint8_t* b_sf;    // pad_up(n,128) * pad_up(k/16,4)
+    const float* gs_b;      // [1] the weight's global scale
+    const uint16_t* bias;   // [n] or null
+    uint16_t* out;          // [m, n]
+    float* gs_out;          // [1] the activation's global scale, or null
+    int64_t m, n, k;        // m <= kLinearSmallMaxRows; k % 128 == 0, k <= kLinearSmallMaxK
+};
+hipError_t launch_linear_small(const LinearSmallArgs& a, hipStream_t st);
+
 // MX setting (32-element blocks, ue8m0 scales, no global scale).
 struct MxQuantizeArgs {
     const void* x;        // [m, k] bf16 or fp32

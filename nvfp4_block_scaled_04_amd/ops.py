@@ -34,6 +34,7 @@ EXPORTS = (
     "nvfp4_gemm_grouped_masked_ws",
     "nvfp4_gemm_svdquant_ws",
     "nvfp4_gemm_w4a16",
+    "nvfp4_linear_small",
     "nvfp4_alpha",
     "mxfp4_quantize",
     "mxfp4_gemm",
@@ -75,6 +76,7 @@ def _load():
         "nvfp4_gemm_grouped_masked_ws": [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, i64, vp],
         "nvfp4_gemm_svdquant_ws": [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, i64, vp],
         "nvfp4_gemm_w4a16": [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp],
+        "nvfp4_linear_small": [vp, i64, i64, vp, vp, vp, vp, vp, i64, vp, vp],
         "nvfp4_alpha": [vp, vp, vp, i64, vp],
         "mxfp4_quantize": [vp, i32, i64, i64, vp, vp, vp],
         "mxfp4_gemm": [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, vp],
@@ -632,6 +634,33 @@ def nvfp4_gemm_w4a16(a, b, b_sf, alpha, bias=None, out=None):
     rc = _lib.nvfp4_gemm_w4a16(_ptr(a), _ptr(b), _ptr(b_sf), _ptr(alpha), _ptr(bias), _ptr(out), m, n, k,
                                _stream(a.device))
     _check(rc, "nvfp4_gemm_w4a16")
+    return out
+
+
+def nvfp4_linear_small(x, b, b_sf, gs_b, bias=None, out=None, gs_out=None):
+    """x: [m, k] bf16 (m <= 16), b: [n, k/2] packed FP4 weight with its scales
+    and global scale gs_b -> out [m, n] bf16: the dynamic quantization of x,
+    alpha = 1/(gs*gs_b) and the NVFP4 GEMM in one launch (bit for bit the
+    three calls).  gs_out, if given, receives the activation's global scale."""
+    _dims(x, "x", 2)
+    _dims(b, "b", 2)
+    m, k = x.shape
+    n = b.shape[0]
+    dev = x.device
+    if b.shape[1] * 2 != k:
+        raise ValueError(f"b must be [n, {k // 2}] packed FP4, got {tuple(b.shape)}")
+    if out is None:
+        out = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+    _dev(x, "x", BF16, m * k, dev)
+    _dev(b, "b", BYTES, n * (k // 2), dev)
+    _dev(b_sf, "b_sf", BYTES, sf_size(n, k), dev)
+    _dev(gs_b, "gs_b", F32, 1, dev)
+    _opt(bias, "bias", BF16, n, dev)
+    _opt(gs_out, "gs_out", F32, 1, dev)
+    _dev(out, "out", BF16, m * n, dev)
+    rc = _lib.nvfp4_linear_small(_ptr(x), m, k, _ptr(b), _ptr(b_sf), _ptr(gs_b), _ptr(bias), _ptr(out), n,
+                                 _ptr(gs_out), _stream(dev))
+    _check(rc, "nvfp4_linear_small")
     return out
 
 

@@ -36,7 +36,7 @@ def test_header_declares_the_entry_points():
         "nvfp4_alpha", "nvfp4_gemm", "nvfp4_gemm_grouped_masked",
         "nvfp4_gemm_grouped_masked_silu_quantize", "nvfp4_gemm_svdquant",
         "nvfp4_gemm_ws", "nvfp4_gemm_grouped_masked_ws", "nvfp4_gemm_svdquant_ws",
-        "nvfp4_gemm_w4a16", "nvfp4_quantize_lora_down",
+        "nvfp4_gemm_w4a16", "nvfp4_linear_small", "nvfp4_quantize_lora_down",
         "nvfp4_lora_down_prepare", "nvfp4_quantize_lora_down_prepared",
         "nvfp4_quantize", "nvfp4_quantize_alpha", "nvfp4_quantize_ws", "nvfp4_quantize_noalloc",
         "nvfp4_quantize_masked_batched", "nvfp4_quantize_masked_batched_ws",
@@ -317,6 +317,30 @@ def test_w4a16_validation(lib):
     assert run(a=P + 8) == MISAL
     assert run(bias=P + 2) == MISAL
     assert run(alpha=P + 1) == MISAL
+
+
+def test_linear_small_validation(lib):
+    f = lib.nvfp4_linear_small
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64] + [ctypes.c_void_p] * 5 + \
+        [ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    run = lambda x=P, m=16, k=4096, b=P, sf=P, gsb=P, bias=None, out=P, n=4096, gso=None: \
+        f(x, m, k, b, sf, gsb, bias, out, n, gso, None)
+    assert run(x=None) == NULLP
+    assert run(b=None) == NULLP
+    assert run(sf=None) == NULLP
+    assert run(gsb=None) == NULLP
+    assert run(out=None) == NULLP
+    assert run(m=0) == SHAPE
+    assert run(n=0) == SHAPE
+    assert run(k=40) == SHAPE
+    assert run(m=17) == UNSUP        # more than 16 rows: the three calls
+    assert run(k=4096 + 128) == UNSUP
+    assert run(k=1040) == UNSUP      # k % 128 != 0
+    assert run(x=P + 8) == MISAL
+    assert run(out=P + 8) == MISAL
+    assert run(bias=P + 2) == MISAL
+    assert run(gsb=P + 1) == MISAL
+    assert run(gso=P + 2) == MISAL
 
 
 def test_lora_down_validation(lib):

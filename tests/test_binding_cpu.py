@@ -52,6 +52,7 @@ CALLS = {
         u8(128, 32), u8(64, 32), u8(ops.sf_size(128, 64)), u8(ops.sf_size(64, 64)), f32(1), bf(128, 32), bf(64, 32),
         workspace=u8(16)),
     "nvfp4_gemm_w4a16": lambda: ops.nvfp4_gemm_w4a16(bf(16, 64), u8(64, 32), u8(ops.sf_size(64, 64)), f32(1)),
+    "nvfp4_linear_small": lambda: ops.nvfp4_linear_small(bf(16, 128), u8(64, 64), u8(ops.sf_size(64, 128)), f32(1)),
     "nvfp4_alpha": lambda: ops.nvfp4_alpha(f32(1), f32(1)),
     "mxfp4_quantize": lambda: ops.mxfp4_quantize(bf(128, 64)),
     "mxfp4_gemm": lambda: ops.mxfp4_gemm(u8(128, 32), u8(64, 32), u8(ops.sf_size_mx(128, 64)),
