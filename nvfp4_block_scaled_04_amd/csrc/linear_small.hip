@@ -100,20 +100,27 @@ __global__ __launch_bounds__(kLsThreads) void k_linear_small(LParams p) {
     };
     load_b(c0);
 
-    // 2. the activation: thread t owns blocks q = t + 512 j of the 16 x K/16
-    //    block grid (row q / (K/16)); rows past M read row M - 1 again and
-    //    are not quantized
-    const int nbr = (int)(p.K / 16);  // blocks per row
-    const int nbt = 16 * nbr;         // blocks of the 16-row grid
+    // 2. the activation: thread t owns the blocks of LDS slots s = t + 512 j
+    //    (slot s = 2 (64 c + l) + half: chunk c, lane l = row + 16 g of the
+    //    K loop, half of its 32 columns), so consecutive lanes write
+    //    consecutive LDS bytes; block (row, 8c + 2g + half) of the 16 x K/16
+    //    grid.  Rows past M read row M - 1 again and are not quantized.
+    const int nbt = (int)p.K;  // slots = 16 rows x K/16 blocks
+    auto slot_block = [&](int s_, int& row, int& kb) {
+        const int l = (s_ >> 1) & 63;
+        row = l & 15;
+        kb = (s_ >> 7) * 8 + (l >> 4) * 2 + (s_ & 1);
+    };
     u32x4 raw[JB][2];
     u32x4 pq[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
 #pragma unroll
     for (int j = 0; j < JB; j++) {
         int q = t + kLsThreads * j;
         q = q < nbt ? q : nbt - 1;
-        int row = q / nbr;
+        int row, kb;
+        slot_block(q, row, kb);
         row = row < p.M ? row : (int)p.M - 1;
-        const u32x4* src = (const u32x4*)(p.x + (int64_t)row * p.K + (int64_t)(q % nbr) * 16);
+        const u32x4* src = (const u32x4*)(p.x + (int64_t)row * p.K + (int64_t)kb * 16);
         raw[j][0] = src[0];
         raw[j][1] = src[1];
     }
@@ -121,9 +128,11 @@ __global__ __launch_bounds__(kLsThreads) void k_linear_small(LParams p) {
 #pragma unroll
     for (int j = 0; j < JB; j++) {
         const int q = t + kLsThreads * j;
+        int row, kb;
+        slot_block(q, row, kb);
         float f[16];
         const float bm = process_block<V_BF16>(raw[j], pq, f);
-        if (q < nbt && q / nbr < p.M) am = __builtin_fmaxf(am, bm);
+        if (q < nbt && row < p.M) am = __builtin_fmaxf(am, bm);
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) am = __builtin_fmaxf(am, __shfl_xor(am, off));
@@ -137,24 +146,26 @@ __global__ __launch_bounds__(kLsThreads) void k_linear_small(LParams p) {
     const float alpha = 1.0f / (gs * p.gs_b[0]);
     if (blockIdx.x == 0 && t == 0 && p.gs_out) p.gs_out[0] = gs;
 
-    // 3. quantize into LDS (rows past M: zero codes and scales)
+    // 3. quantize into LDS (rows past M: zero codes and scales); the two
+    //    halves of a lane's 32 columns sit in neighbouring lanes, whose scale
+    //    bytes leave as one 16-bit store
 #pragma unroll
     for (int j = 0; j < JB; j++) {
-        const int q = t + kLsThreads * j;
+        const int q = t + kLsThreads * j;  // the same for every lane of a wave: K is a multiple of 128
+        int row, kb;
+        slot_block(q, row, kb);
+        uint32_t w0 = 0, w1 = 0, sc = 0;
+        if (row < p.M) {
+            float f[16];
+            const float bm = process_block<V_BF16>(raw[j], pq, f);  // the block's maximum again
+            sc = ue4m3_encode(div6(bm) * gs);
+            const float dec = ue4m3_decode(sc);
+            pack_block(f, dec == 0.0f ? 0.0f : gs / dec, w0, w1);
+        }
+        const uint32_t sc_next = (uint32_t)__shfl_xor((int)sc, 1);
         if (q < nbt) {
-            const int row = q / nbr, kb = q % nbr;
-            uint32_t w0 = 0, w1 = 0, sc = 0;
-            if (row < p.M) {
-                float f[16];
-                const float bm = process_block<V_BF16>(raw[j], pq, f);  // the block's maximum again
-                sc = ue4m3_encode(div6(bm) * gs);
-                const float dec = ue4m3_decode(sc);
-                pack_block(f, dec == 0.0f ? 0.0f : gs / dec, w0, w1);
-            }
-            const int c = kb >> 3, gg = (kb & 7) >> 1, half = kb & 1;
-            const int l = row + 16 * gg;
-            *(u32x2*)(a_fp4 + (c * 64 + l) * 16 + half * 8) = u32x2{w0, w1};
-            a_sf[(c * 64 + l) * 2 + half] = (uint8_t)sc;
+            *(u32x2*)(a_fp4 + q * 8) = u32x2{w0, w1};
+            if ((q & 1) == 0) *(uint16_t*)(a_sf + q) = (uint16_t)(sc | (sc_next << 8));
         }
     }
     __syncthreads();
