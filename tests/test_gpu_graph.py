@@ -70,6 +70,40 @@ def test_dynamic_pipeline_replays(ops, shape):
             assert torch.equal(t.view(torch.uint8), r.view(torch.uint8)), f"replay {rep}: {name} differs"
 
 
+def test_linear_small_replays(ops):
+    """The one-launch decode linear captured once, replayed three times with
+    its output and gs scribbled in between; every replay equals the eager
+    call, which equals the three captured-apart calls (quantize, alpha, GEMM)."""
+    m, n, k = 16, 4096, 4096
+    say("graph linear_small", (m, n, k))
+    d, _ = synth.dense(m=m, n=n, k=k)
+    x = d.a.to("cuda")
+    fw, sfw, gsw = ops.nvfp4_quantize(d.w.to("cuda"))
+    out = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
+    gs = torch.zeros(1, dtype=torch.float32, device="cuda")
+
+    def step():
+        ops.nvfp4_linear_small(x, fw, sfw, gsw, out=out, gs_out=gs)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (out, gs)]
+    fa, sfa, gsa = ops.nvfp4_quantize(x)
+    three = ops.nvfp4_gemm(fa, fw, sfa, sfw, ops.nvfp4_alpha(gsa, gsw))
+    torch.cuda.synchronize()
+    assert torch.equal(three.view(torch.uint8), ref[0].view(torch.uint8))
+    assert torch.equal(gsa.view(torch.uint8), ref[1].view(torch.uint8))
+    g = _capture(step)
+    for rep in range(3):
+        for t in (out, gs):
+            t.view(torch.uint8).fill_(0xA5 + rep)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, t, r in zip(("out", "gs"), (out, gs), ref):
+            assert torch.equal(t.view(torch.uint8), r.view(torch.uint8)), f"replay {rep}: {name} differs"
+
+
 @pytest.mark.parametrize("ws", [False, True])
 def test_moe_pipeline_replays(ops, ws):
     """silu quantize over masked experts, per-expert alpha, grouped masked
