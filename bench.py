@@ -569,31 +569,31 @@ def cpu_baseline_svdquant(O, np, s, synth, target_s=20.0):
 # record is the split-tail schedule's two launches together (k_gemm and
 # k_gemm_fixup), which the bench times as the GEMM.
 MEASURED_TRAFFIC = {
-    "prefill": {"sources_sha256": "3474cfa9f02c69a414b62200726720fa6e20d5c565a314b88a2f129c09709fa7"
-                          "e7afed52fec782c4327ee38521820444f93ab7eb99f899822d3ae3320f273e3a"
+    "prefill": {"sources_sha256": "23c0338bd9c1335a9e56f0ab048ab04c418de029918179069bdb4be93c069bc8"
+                          "c7df1564c2660c5b6936c0d9acdfca2473753bd4dac2d6c405d89edece56c024"
                           "0b8ab37c346d4290d1fdb25793ffb74b674eb91941278aed19a6fa7e4e266b6a"
                           "54b19610b17c816426fc33a6ab2620605cb533220f8d2b2ba5de96d5cd0cf1df",
-             "fetch_kib": 276647.3, "write_kib": 262144.0, "fetch_factor": 2.0, "write_factor": 1.0},
-    "moe": {"sources_sha256": "3474cfa9f02c69a414b62200726720fa6e20d5c565a314b88a2f129c09709fa7"
-                          "e7afed52fec782c4327ee38521820444f93ab7eb99f899822d3ae3320f273e3a"
+             "fetch_kib": 276682.1, "write_kib": 262144.0, "fetch_factor": 2.0, "write_factor": 1.0},
+    "moe": {"sources_sha256": "23c0338bd9c1335a9e56f0ab048ab04c418de029918179069bdb4be93c069bc8"
+                          "c7df1564c2660c5b6936c0d9acdfca2473753bd4dac2d6c405d89edece56c024"
                           "0b8ab37c346d4290d1fdb25793ffb74b674eb91941278aed19a6fa7e4e266b6a"
                           "54b19610b17c816426fc33a6ab2620605cb533220f8d2b2ba5de96d5cd0cf1df",
-             "fetch_kib": 139083.6, "write_kib": 43510.0, "fetch_factor": 2.0, "write_factor": 1.0},
-    "dense": {"sources_sha256": "3474cfa9f02c69a414b62200726720fa6e20d5c565a314b88a2f129c09709fa7"
-                          "e7afed52fec782c4327ee38521820444f93ab7eb99f899822d3ae3320f273e3a"
+             "fetch_kib": 139075.5, "write_kib": 43510.0, "fetch_factor": 2.0, "write_factor": 1.0},
+    "dense": {"sources_sha256": "23c0338bd9c1335a9e56f0ab048ab04c418de029918179069bdb4be93c069bc8"
+                          "c7df1564c2660c5b6936c0d9acdfca2473753bd4dac2d6c405d89edece56c024"
                           "0b8ab37c346d4290d1fdb25793ffb74b674eb91941278aed19a6fa7e4e266b6a"
                           "54b19610b17c816426fc33a6ab2620605cb533220f8d2b2ba5de96d5cd0cf1df",
-             "fetch_kib": 18605.0, "write_kib": 16384.0, "fetch_factor": 2.0, "write_factor": 1.0},
-    "svdquant": {"sources_sha256": "3474cfa9f02c69a414b62200726720fa6e20d5c565a314b88a2f129c09709fa7"
-                          "e7afed52fec782c4327ee38521820444f93ab7eb99f899822d3ae3320f273e3a"
+             "fetch_kib": 18604.5, "write_kib": 16384.0, "fetch_factor": 2.0, "write_factor": 1.0},
+    "svdquant": {"sources_sha256": "23c0338bd9c1335a9e56f0ab048ab04c418de029918179069bdb4be93c069bc8"
+                          "c7df1564c2660c5b6936c0d9acdfca2473753bd4dac2d6c405d89edece56c024"
                           "0b8ab37c346d4290d1fdb25793ffb74b674eb91941278aed19a6fa7e4e266b6a"
                           "54b19610b17c816426fc33a6ab2620605cb533220f8d2b2ba5de96d5cd0cf1df",
-             "fetch_kib": 19885.2, "write_kib": 24578.1, "fetch_factor": 2.0, "write_factor": 1.0},
-    "decode": {"sources_sha256": "3474cfa9f02c69a414b62200726720fa6e20d5c565a314b88a2f129c09709fa7"
-                          "e7afed52fec782c4327ee38521820444f93ab7eb99f899822d3ae3320f273e3a"
+             "fetch_kib": 19884.5, "write_kib": 24577.9, "fetch_factor": 2.0, "write_factor": 1.0},
+    "decode": {"sources_sha256": "23c0338bd9c1335a9e56f0ab048ab04c418de029918179069bdb4be93c069bc8"
+                          "c7df1564c2660c5b6936c0d9acdfca2473753bd4dac2d6c405d89edece56c024"
                           "0b8ab37c346d4290d1fdb25793ffb74b674eb91941278aed19a6fa7e4e266b6a"
                           "54b19610b17c816426fc33a6ab2620605cb533220f8d2b2ba5de96d5cd0cf1df",
-             "fetch_kib": 6383.7, "write_kib": 128.0, "fetch_factor": 2.0, "write_factor": 1.0},
+             "fetch_kib": 6383.1, "write_kib": 128.0, "fetch_factor": 2.0, "write_factor": 1.0},
 }
 GEMM_SOURCES = ("nvfp4_block_scaled_04_amd/csrc/gemm.hip", "nvfp4_block_scaled_04_amd/csrc/gemm_common.h",
                 "nvfp4_block_scaled_04_amd/csrc/device_common.h", "nvfp4_block_scaled_04_amd/csrc/quant_block.h")

@@ -54,25 +54,6 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 // term; or silu_and_mul of the gate | up output quantized to NVFP4.
 enum Epilogue { EPI_PLAIN = 0, EPI_LORA = 1, EPI_SILUQ = 2 };
 
-// 8 FP4 codes of one dword times one block scale -> 8 fp16 (exact).
-__device__ __forceinline__ f16x8 dequant8(uint32_t w, _Float16 s) {
-    const f16x2 ss = f16x2{s, s};
-    const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * ss;
-    const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * ss;
-    const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * ss;
-    const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * ss;
-    return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-}
-
-__device__ __forceinline__ uint32_t word(const u32x4& v, int j) {
-    return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
-}
-
-// Byte offset of scale (row, block column c) in the swizzled layout.
-__device__ __forceinline__ int64_t scale_byte_off(int64_t row, int c, int cpa4) {
-    return ((row >> 7) * cpa4 + (c >> 2)) * 512 + (row & 31) * 16 + ((row & 127) >> 5) * 4 + (c & 3);
-}
-
 // Waves per SIMD each configuration is compiled for: a 128x128 wave tile
 // takes the whole register file (256 accumulators per lane); smaller wave
 // tiles are held to 256 registers so two waves share a SIMD.

@@ -44,6 +44,26 @@ struct GParams {
     int sk_grid;         // workgroups of the persistent launch
 };
 
+// 8 FP4 codes of one dword times one block scale -> 8 fp16 (exact): the
+// operand formation of the NVFP4 kernels.
+__device__ __forceinline__ f16x8 dequant8(uint32_t w, _Float16 s) {
+    const f16x2 ss = f16x2{s, s};
+    const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * ss;
+    const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * ss;
+    const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * ss;
+    const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * ss;
+    return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+__device__ __forceinline__ uint32_t word(const u32x4& v, int j) {
+    return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
+}
+
+// Byte offset of scale (row, block column c) in the swizzled layout.
+__device__ __forceinline__ int64_t scale_byte_off(int64_t row, int c, int cpa4) {
+    return ((row >> 7) * cpa4 + (c >> 2)) * 512 + (row & 31) * 16 + ((row & 127) >> 5) * 4 + (c & 3);
+}
+
 // Raw buffer resource (gfx9 word 3: 32-bit untyped records).  Loads past
 // `bytes` return zeros.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {

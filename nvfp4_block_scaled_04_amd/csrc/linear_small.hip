@@ -41,26 +41,6 @@ struct LParams {
     int cpa4;              // pad_up(K/16,4)/4 of the weight's scale layout
 };
 
-// 8 FP4 codes of one dword times one block scale -> 8 fp16 (exact): the
-// operand formation of the skinny GEMM.
-__device__ __forceinline__ f16x8 ls_dequant8(uint32_t w, _Float16 s) {
-    const f16x2 ss = f16x2{s, s};
-    const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * ss;
-    const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * ss;
-    const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * ss;
-    const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * ss;
-    return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-}
-
-__device__ __forceinline__ uint32_t ls_word(const u32x4& v, int j) {
-    return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
-}
-
-// Byte offset of weight scale (row, block column c) in the swizzled layout.
-__device__ __forceinline__ int64_t ls_scale_off(int64_t row, int c, int cpa4) {
-    return ((row >> 7) * cpa4 + (c >> 2)) * 512 + (row & 31) * 16 + ((row & 127) >> 5) * 4 + (c & 3);
-}
-
 // JB: activation blocks per thread (16 rows x K/16 blocks over 512 threads).
 template <int JB>
 __global__ __launch_bounds__(kLsThreads) void k_linear_small(LParams p) {
@@ -95,7 +75,7 @@ __global__ __launch_bounds__(kLsThreads) void k_linear_small(LParams p) {
             int c = cb + u < c1 ? cb + u : c1 - 1;  // past the range: reload, never used
             c = c < 0 ? 0 : c;                      // a wave without chunks (nch < 8 waves)
             fb[u] = *(const u32x4*)(B + (int64_t)c * 64 + g * 16);
-            sb[u] = *(const uint16_t*)(p.b_sf + ls_scale_off(brow, c * 8 + 2 * g, p.cpa4));
+            sb[u] = *(const uint16_t*)(p.b_sf + scale_byte_off(brow, c * 8 + 2 * g, p.cpa4));
         }
     };
     load_b(c0);
@@ -184,8 +164,8 @@ __global__ __launch_bounds__(kLsThreads) void k_linear_small(LParams p) {
             const f16x2 ssb = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb[u], 1.0f, false);
 #pragma unroll
             for (int jw = 0; jw < 4; jw++) {
-                const f16x8 oa = ls_dequant8(ls_word(fa, jw), ssa[jw >> 1]);
-                const f16x8 ob = ls_dequant8(ls_word(fb[u], jw), ssb[jw >> 1]);
+                const f16x8 oa = dequant8(word(fa, jw), ssa[jw >> 1]);
+                const f16x8 ob = dequant8(word(fb[u], jw), ssb[jw >> 1]);
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ob, oa, acc, 0, 0, 0);
             }
         }
