@@ -16,8 +16,8 @@
 // chunks its waves need are already in flight by then.  The K loop is the
 // skinny GEMM's (a 16 x 16 output tile per workgroup, the K chunks split
 // over eight waves, v_mfma_f32_16x16x32_f16 on exactly dequantized fp16
-// operands, partial tiles added in wave order), so the output equals the
-// two-launch path bit for bit.
+// operands, partial tiles added in wave order), so the output equals that
+// of the separate quantize, alpha and GEMM calls bit for bit.
 #include "device_common.h"
 #include "gemm_common.h"
 #include "internal.h"
